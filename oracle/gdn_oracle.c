@@ -1,0 +1,178 @@
+/*
+ * Test infrastructure, not product code: only tests/, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.
+ *
+ * Plain fp64 CPU oracle of the gated delta rule, written as the token-by-token
+ * recurrence that the chunked form of the MaxText PR "Add context parallelism
+ * to the Gated Delta Net (Qwen3-Next / Qwen3.5)" rearranges (section "Why",
+ * the affine chunk equations for h_out and o; the page calls the method a
+ * "sequential recurrence" in its "Limitation" section).
+ *
+ * With the state kept K-major, h in R^{K x V} (the page's U is (B,H,K,V); the
+ * serving RFC "RFC(qwen35): TP Phase 2", section "Partition Contract", keeps
+ * the recurrent state as [H_v, K, V] f32), one token t does
+ *
+ *     alpha = exp(g_t)
+ *     h     <- alpha * h
+ *     delta  = beta_t * (v_t - h^T k_t)          (length V)
+ *     h     <- h + k_t delta^T
+ *     o_t    = h^T q_t                           (length V)
+ *
+ * which is S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ * o_t = S_t q_t with S = h^T.  No blocking, no reordering, no fast math:
+ * exp() is the host libm, every loop runs in the textbook order.
+ *
+ * Layouts (row-major, contiguous):
+ *   batch mode   q,k [B,S,H,K]  v,o [B,S,H,V]  g,beta [B,S,H]  h0,hT [B,H,K,V]
+ *   packed mode  q,k [T,H,K]    v,o [T,H,V]    g,beta [T,H]    h0,hT [N,H,K,V]
+ *                with sequence n owning tokens cu[n] .. cu[n+1]-1.
+ * h0 may be NULL (zero initial state); o and hT may be NULL (not written).
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One independent chain (one sequence, one head).  `tok_*` are the strides,
+ * in elements, between consecutive tokens of the chain. */
+static void run_chain(int S, int K, int V,
+                      const double *q, const double *k, const double *v,
+                      long tok_qk, long tok_v,
+                      const double *g, const double *beta, long tok_gb,
+                      double *h, /* K*V: in initial state, out final state */
+                      double *o, long tok_o,
+                      double *delta /* V scratch */)
+{
+    for (int t = 0; t < S; ++t) {
+        const double *qt = q ? q + (long)t * tok_qk : NULL;
+        const double *kt = k + (long)t * tok_qk;
+        const double *vt = v + (long)t * tok_v;
+        const double alpha = exp(g[(long)t * tok_gb]);
+        const double b = beta[(long)t * tok_gb];
+
+        for (int i = 0; i < K; ++i)
+            for (int j = 0; j < V; ++j)
+                h[(long)i * V + j] *= alpha;
+
+        for (int j = 0; j < V; ++j) {
+            double hk = 0.0;
+            for (int i = 0; i < K; ++i)
+                hk += h[(long)i * V + j] * kt[i];
+            delta[j] = b * (vt[j] - hk);
+        }
+
+        for (int i = 0; i < K; ++i)
+            for (int j = 0; j < V; ++j)
+                h[(long)i * V + j] += kt[i] * delta[j];
+
+        if (o) {
+            double *ot = o + (long)t * tok_o;
+            for (int j = 0; j < V; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < K; ++i)
+                    acc += h[(long)i * V + j] * qt[i];
+                ot[j] = acc;
+            }
+        }
+    }
+}
+
+static int pick_threads(int nthreads)
+{
+#ifdef _OPENMP
+    return nthreads > 0 ? nthreads : omp_get_max_threads();
+#else
+    (void)nthreads;
+    return 1;
+#endif
+}
+
+/* Batch mode: B sequences of S tokens each, H heads.  Returns 0 on success. */
+int gdn_oracle_forward(int B, int S, int H, int K, int V,
+                       const double *q, const double *k, const double *v,
+                       const double *g, const double *beta,
+                       const double *h0, double *o, double *hT, int nthreads)
+{
+    if (B < 0 || S < 0 || H <= 0 || K <= 0 || V <= 0 || !k || !v || !g || !beta)
+        return 1;
+    if (o && !q)
+        return 1;
+    const long KV = (long)K * V;
+    const int nchains = B * H;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(pick_threads(nthreads))
+    for (int c = 0; c < nchains; ++c) {
+        const int b = c / H, hh = c % H;
+        double *h = (double *)malloc(sizeof(double) * (size_t)KV);
+        double *delta = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!h || !delta) {
+            bad = 1;
+            free(h);
+            free(delta);
+            continue;
+        }
+        if (h0)
+            memcpy(h, h0 + (long)c * KV, sizeof(double) * (size_t)KV);
+        else
+            memset(h, 0, sizeof(double) * (size_t)KV);
+        const long tok0 = (long)b * S * H + hh; /* token 0 of this chain, in [B,S,H] units */
+        run_chain(S, K, V,
+                  q ? q + tok0 * K : NULL, k + tok0 * K, v + tok0 * V,
+                  (long)H * K, (long)H * V,
+                  g + tok0, beta + tok0, H,
+                  h, o ? o + tok0 * V : NULL, (long)H * V, delta);
+        if (hT)
+            memcpy(hT + (long)c * KV, h, sizeof(double) * (size_t)KV);
+        free(h);
+        free(delta);
+    }
+    return bad;
+}
+
+/* Packed mode: N sequences laid end to end on one token axis of T = cu[N]
+ * tokens; sequence n owns tokens cu[n] .. cu[n+1]-1.  Returns 0 on success. */
+int gdn_oracle_forward_packed(int N, const int *cu, int H, int K, int V,
+                              const double *q, const double *k, const double *v,
+                              const double *g, const double *beta,
+                              const double *h0, double *o, double *hT, int nthreads)
+{
+    if (N < 0 || !cu || H <= 0 || K <= 0 || V <= 0 || !k || !v || !g || !beta)
+        return 1;
+    if (o && !q)
+        return 1;
+    for (int n = 0; n < N; ++n)
+        if (cu[n + 1] < cu[n] || cu[0] != 0)
+            return 1;
+    const long KV = (long)K * V;
+    const int nchains = N * H;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(pick_threads(nthreads))
+    for (int c = 0; c < nchains; ++c) {
+        const int n = c / H, hh = c % H;
+        double *h = (double *)malloc(sizeof(double) * (size_t)KV);
+        double *delta = (double *)malloc(sizeof(double) * (size_t)V);
+        if (!h || !delta) {
+            bad = 1;
+            free(h);
+            free(delta);
+            continue;
+        }
+        if (h0)
+            memcpy(h, h0 + (long)c * KV, sizeof(double) * (size_t)KV);
+        else
+            memset(h, 0, sizeof(double) * (size_t)KV);
+        const long tok0 = (long)cu[n] * H + hh;
+        run_chain(cu[n + 1] - cu[n], K, V,
+                  q ? q + tok0 * K : NULL, k + tok0 * K, v + tok0 * V,
+                  (long)H * K, (long)H * V,
+                  g + tok0, beta + tok0, H,
+                  h, o ? o + tok0 * V : NULL, (long)H * V, delta);
+        if (hT)
+            memcpy(hT + (long)c * KV, h, sizeof(double) * (size_t)KV);
+        free(h);
+        free(delta);
+    }
+    return bad;
+}
