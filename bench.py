@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked gated delta rule forward on one MI355X.
+
+A step is one full forward over the 64k-token, 32-head, K = V = 128 sequence
+split into 4 contiguous segments: the carrying zero-state scan (phase 1), the
+exclusive segment scan (phase 2) and the emitting scan (phase 3), i.e. every
+entry point of the chunked path, on bf16 inputs with fp32 state.  Inputs are
+seeded synthetic tensors already resident in HBM when timing starts.
+
+Prints one JSON line: tokens/s of that step, the roofline of its dominant
+kernel (HIP events around that kernel's launches on its stream), the fp64 CPU
+oracle timed on a bounded sample of the same workload on the host cores, and
+secondary measurements (monolithic scan, 4k sequence, packed batch, decode).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN fwd tokens/s at H=32,K=V=128,S=64k (1 GPU); % MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0       # dense MFMA, MI355X
+PEAK_F32_VALU_TFLOPS = 157.3    # fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+
+def flops_per_token_head(C, K, V):
+    """Canonical chunked work (dense tiles): the two C x C Gram matrices, T applied
+    to [beta gamma K | beta V], the three K x V state products and attn @ delta."""
+    return 2 * (2 * C * K + C * (K + V) + 3 * K * V + C * V)
+
+
+def carry_flops_per_token_head(C, K, V):
+    """Zero-state pass carrying X = [M | h]: Gram k k^T, T applied to
+    [beta gamma K | beta V], and w X, k_tilde^T delta_X over K + V columns."""
+    return 2 * C * K + 2 * C * (K + V) + 4 * K * (K + V)
+
+
+def bytes_per_token_head(K, V, s_in, s_out):
+    """q, k, v in, o out, g and beta fp32."""
+    return (2 * K + V) * s_in + V * s_out + 8
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--segments", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target duration of the oracle sample")
+    return ap.parse_args()
+
+
+class StreamTimer:
+    """HIP events recorded on the launching stream around named kernels."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = {}
+
+    def around(self, name, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record(t.cuda.current_stream())
+        out = fn()
+        b.record(t.cuda.current_stream())
+        self.marks.setdefault(name, []).append((a, b))
+        return out
+
+    def avg_ms(self):
+        return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.marks.items()}
+
+
+def time_steps(torch, step, steps, warmup):
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    timer = StreamTimer(torch)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(torch.cuda.current_stream())
+    for _ in range(steps):
+        step(timer)
+    end.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, timer.avg_ms()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(sequence or head sharding across GPUs is not built)",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import chunked_gated_delta_gdn_amd as gdn
+    from chunked_gated_delta_gdn_amd import binding
+    from workloads import workload, make_decode_inputs
+
+    binding.library()          # fail loudly before anything else if the library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf = torch.bfloat16
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- headline workload
+    log("bench: generating the 64k-token workload")
+    x = workload(2)
+    B, S, H, K, V, C = x.B, x.S, x.H, x.K, x.V, x.C
+    R = args.segments
+    q = torch.from_numpy(x.q).to(bf).to(dev)
+    k = torch.from_numpy(x.k).to(bf).to(dev)
+    v = torch.from_numpy(x.v).to(bf).to(dev)
+    g = torch.from_numpy(x.g).to(dev)
+    beta = torch.from_numpy(x.beta).to(dev)
+    h0 = torch.from_numpy(x.h0).to(dev)
+    backend = binding.gdn_scan_backend(gdn.problem_for(k, v, C, n_segments=R))
+
+    def seg_step(timer):
+        tm = timer.around if timer else (lambda _n, f: f())
+        if R == 1:
+            return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h0, chunk_size=C))
+        M, U = tm("scan_carry", lambda: gdn.scan_carry(k, v, g, beta, chunk_size=C, n_segments=R))
+        h_in, _ = tm("segment_compose", lambda: gdn.segment_compose(M, U, h0))
+        return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h_in, chunk_size=C,
+                                                     n_segments=R))
+
+    log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps (R={R})")
+    ms, kern = time_steps(torch, seg_step, args.steps, args.warmup)
+    tokens = B * S
+    value = tokens / (ms * 1e-3)
+
+    # dominant kernel and its roofline
+    dom = max(kern, key=kern.get)
+    th = tokens * H
+    if dom == "scan_emit":
+        flops = flops_per_token_head(C, K, V) * th
+        nbytes = bytes_per_token_head(K, V, 2, 2) * th + (R + 1) * H * K * V * 4
+    elif dom == "scan_carry":
+        flops = carry_flops_per_token_head(C, K, V) * th
+        nbytes = (K + V) * 2 * th + 8 * th + R * H * K * (K + V) * 4
+    else:
+        flops = 2 * R * H * K * K * V
+        nbytes = R * H * (K * K + 2 * K * V) * 4
+    t_dom = kern[dom] * 1e-3
+    if backend == 1:
+        roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "alu", "achieved": flops / t_dom / 1e12, "peak": PEAK_F32_VALU_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["kernel_ms"] = kern[dom]
+    roof["algorithmic_flops_per_launch"] = flops
+    roof["algorithmic_bytes_per_launch"] = nbytes
+    roof["hbm_frac_at_algorithmic_bytes"] = nbytes / t_dom / 1e9 / PEAK_HBM_GBS
+    useful = flops_per_token_head(C, K, V) * th
+    result = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; q,k L2-normalised, beta sigmoid, g -softplus)",
+        "config": {"workload": f"B{B} H{H} S{S} K{K} V{V} C{C}, {R} contiguous segments "
+                               "(three-phase pass), bf16 q/k/v/o, fp32 g/beta/state",
+                   "B": B, "H": H, "S": S, "K": K, "V": V, "C": C, "segments": R,
+                   "parallelism": "1 GPU"},
+        "roofline": roof,
+        "kernels_ms": kern,
+        "useful_tflops": useful / (ms * 1e-3) / 1e12,
+        "scan_backend": "mfma" if backend == 1 else "valu",
+    }
+    del seg_step
+
+    # ---------------------------------------------------------------- secondary lines
+    extra = {}
+    if not args.no_extra:
+        def mono(timer):
+            tm = timer.around if timer else (lambda _n, f: f())
+            return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h0, chunk_size=C))
+        steps2 = max(3, args.steps // 4)
+        ms1, k1 = time_steps(torch, mono, steps2, 2)
+        extra["monolithic_64k"] = {"tokens_per_s": tokens / (ms1 * 1e-3), "ms": ms1}
+        del q, k, v, g, beta, h0
+        torch.cuda.empty_cache()
+
+        for wl, name in ((1, "seq4k_h16"), (3, "packed8_32k")):
+            log(f"bench: {name}")
+            y = workload(wl)
+            t = lambda a, dt=None: (torch.from_numpy(a).to(dt) if dt else torch.from_numpy(a)).to(dev)
+            yq, yk, yv = t(y.q, bf), t(y.k, bf), t(y.v, bf)
+            yg, yb, yh = t(y.g), t(y.beta), t(y.h0)
+            cu = y.cu_seqlens
+
+            def fwd(timer, yq=yq, yk=yk, yv=yv, yg=yg, yb=yb, yh=yh, cu=cu):
+                tm = timer.around if timer else (lambda _n, f: f())
+                return tm("scan_emit", lambda: gdn.scan_emit(yq, yk, yv, yg, yb, h_in=yh,
+                                                             chunk_size=64, cu_seqlens=cu))
+            ms2, _ = time_steps(torch, fwd, steps2, 2)
+            extra[name] = {"tokens_per_s": y.real_tokens / (ms2 * 1e-3), "ms": ms2}
+            del yq, yk, yv, yg, yb, yh
+
+        log("bench: decode")
+        nsteps = 128
+        d = make_decode_inputs(4, 256, 32, 128, 128, nsteps, dtype="bf16")
+        dq, dk, dv = (torch.from_numpy(a).to(bf).to(dev) for a in (d.q, d.k, d.v))
+        dg, db = torch.from_numpy(d.g).to(dev), torch.from_numpy(d.beta).to(dev)
+        state = torch.from_numpy(d.state0).to(dev)
+        dout = torch.empty((256, 32, 128), dtype=bf, device=dev)
+
+        def dec(timer):
+            for s_ in range(nsteps):
+                if timer:
+                    timer.around("decode_step", lambda: gdn.decode_step(
+                        dq[s_], dk[s_], dv[s_], dg[s_], db[s_], state, out=dout))
+                else:
+                    gdn.decode_step(dq[s_], dk[s_], dv[s_], dg[s_], db[s_], state, out=dout)
+        ms3, k3 = time_steps(torch, dec, 2, 1)
+        step_bytes = 2 * 256 * 32 * 128 * 128 * 4 + 256 * 32 * ((2 * 128 + 128) * 2 + 128 * 2 + 8)
+        t_step = k3["decode_step"] * 1e-3
+        extra["decode_b256_h32"] = {
+            "tokens_per_s": 256 * nsteps / (ms3 * 1e-3), "ms_per_128_steps": ms3,
+            "us_per_step_kernel": t_step * 1e6,
+            "roofline": {"bound": "hbm", "achieved": step_bytes / t_step / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": step_bytes / t_step / 1e9 / PEAK_HBM_GBS},
+        }
+        del dq, dk, dv, dg, db, state
+    result["extra"] = extra
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        nh = max(1, min(H, threads))
+        log(f"bench: oracle baseline on {nh} heads, {threads} threads")
+        probe = 256
+        t0 = time.perf_counter()
+        oracle.forward(x.q[:, :probe, :nh], x.k[:, :probe, :nh], x.v[:, :probe, :nh],
+                       x.g[:, :probe, :nh], x.beta[:, :probe, :nh], h0=x.h0[:, :nh],
+                       nthreads=min(threads, nh))
+        dt = max(time.perf_counter() - t0, 1e-6)
+        ns = int(min(S, max(probe, probe * args.cpu_seconds / dt)))
+        t0 = time.perf_counter()
+        oracle.forward(x.q[:, :ns, :nh], x.k[:, :ns, :nh], x.v[:, :ns, :nh],
+                       x.g[:, :ns, :nh], x.beta[:, :ns, :nh], h0=x.h0[:, :nh],
+                       nthreads=min(threads, nh))
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {
+            "value": ns * nh / H / dt, "unit": "tokens/s", "cores": min(threads, nh),
+            "kind": "oracle",
+            "sample": f"first {ns} tokens x {nh} of {H} heads of the 64k-token workload, fp64 "
+                      f"token recurrence, {dt:.1f} s; tokens/s counts whole {H}-head tokens",
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

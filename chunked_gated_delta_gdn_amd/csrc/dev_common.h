@@ -1,0 +1,46 @@
+// Device helpers shared by the kernels: element types and conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// bfloat16 stored as its 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const void *p, int64_t i) {
+        return static_cast<const float *>(p)[i];
+    }
+    static __device__ __forceinline__ void store(void *p, int64_t i, float x) {
+        static_cast<float *>(p)[i] = x;
+    }
+};
+
+template <> struct Elem<bf16_t> {
+    static __device__ __forceinline__ float load(const void *p, int64_t i) {
+        return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
+    }
+    static __device__ __forceinline__ void store(void *p, int64_t i, float x) {
+        static_cast<uint16_t *>(p)[i] = f32_to_bf16(x);
+    }
+};
+
+}  // namespace gdn

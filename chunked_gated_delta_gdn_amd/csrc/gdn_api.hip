@@ -1,0 +1,358 @@
+// Host side of the C ABI declared in include/gdn.h: argument validation,
+// chain tables, workspace sizing and kernel dispatch.  Every check runs
+// before the first launch, so a failing call writes nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+hipError_t launch_scan_generic(int K, int V, int C, int dtype, bool carry, const ScanArgs &a,
+                               hipStream_t s);
+hipError_t launch_scan_mfma(int K, int V, int C, int dtype, bool carry, const ScanArgs &a,
+                            hipStream_t s, bool *handled);
+bool mfma_scan_available(int K, int V, int C, int dtype);
+
+bool shape_supported(int K, int V, int C) {
+    return (K == 32 && V == 32 && C == 16) || (K == 128 && V == 128 && C == 64);
+}
+
+hipError_t launch_scan(int K, int V, int C, int dtype, bool carry, const ScanArgs &a,
+                       hipStream_t s) {
+    bool handled = false;
+    hipError_t e = launch_scan_mfma(K, V, C, dtype, carry, a, s, &handled);
+    if (handled) return e;
+    return launch_scan_generic(K, V, C, dtype, carry, a, s);
+}
+}  // namespace gdn
+
+using namespace gdn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdn_status fail(gdn_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Resolved {
+    int N = 0;            // sequences (B or n_seqs)
+    int R = 1;            // segments per sequence
+    int64_t T = 0;        // tokens on the flattened axis
+    int64_t n_chunks = 0; // chunks over all sequences
+    ChainTable ct;
+};
+
+gdn_status resolve(const gdn_problem *p, Resolved &out) {
+    if (!p) return fail(GDN_EINVAL, "problem descriptor is NULL");
+    if (p->B < 1 || p->S < 0 || p->H < 1 || p->K < 1 || p->V < 1 || p->C < 1)
+        return fail(GDN_EINVAL, "bad sizes B=%d S=%d H=%d K=%d V=%d C=%d", p->B, p->S, p->H,
+                    p->K, p->V, p->C);
+    if (!shape_supported(p->K, p->V, p->C))
+        return fail(GDN_EUNSUPPORTED, "(K,V,C)=(%d,%d,%d) not built; supported (32,32,16), "
+                                      "(128,128,64)", p->K, p->V, p->C);
+    if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
+        return fail(GDN_EUNSUPPORTED, "dtype %d not supported", p->dtype);
+    if (p->n_seqs < 0) return fail(GDN_EINVAL, "n_seqs %d < 0", p->n_seqs);
+    memset(&out.ct, 0, sizeof(out.ct));
+    const int C = p->C;
+    if (p->n_seqs > 0) {
+        if (p->B != 1) return fail(GDN_EINVAL, "packed mode needs B == 1 (got %d)", p->B);
+        if (p->n_seqs > GDN_MAX_SEQS)
+            return fail(GDN_EUNSUPPORTED, "%d sequences > GDN_MAX_SEQS", p->n_seqs);
+        if (!p->cu_seqlens) return fail(GDN_EINVAL, "cu_seqlens is NULL in packed mode");
+        if (p->n_segments != 1)
+            return fail(GDN_EUNSUPPORTED, "segments are not supported in packed mode");
+        const int32_t *cu = p->cu_seqlens;
+        if (cu[0] != 0) return fail(GDN_EORDER, "cu_seqlens[0] = %d, must be 0", cu[0]);
+        int64_t chunks = 0;
+        for (int n = 0; n < p->n_seqs; ++n) {
+            if (cu[n + 1] < cu[n])
+                return fail(GDN_EORDER, "cu_seqlens decreases at %d (%d -> %d)", n, cu[n],
+                            cu[n + 1]);
+            out.ct.seq_start[n] = cu[n];
+            out.ct.chunk_start[n] = (int32_t)chunks;
+            chunks += cdiv(cu[n + 1] - cu[n], C);
+        }
+        if (cu[p->n_seqs] != p->S)
+            return fail(GDN_EINVAL, "cu_seqlens[n_seqs] = %d != S = %d", cu[p->n_seqs], p->S);
+        out.ct.seq_start[p->n_seqs] = cu[p->n_seqs];
+        out.ct.chunk_start[p->n_seqs] = (int32_t)chunks;
+        out.ct.packed = 1;
+        out.ct.n_seqs = p->n_seqs;
+        out.ct.n_seg = 1;
+        out.ct.seg_start[0] = 0;
+        out.ct.seg_start[1] = 0x3fffffff;
+        out.N = p->n_seqs;
+        out.R = 1;
+        out.n_chunks = chunks;
+    } else {
+        const int R = p->n_segments;
+        if (R < 1) return fail(GDN_EINVAL, "n_segments %d < 1", R);
+        if (R > GDN_MAX_SEGMENTS)
+            return fail(GDN_EUNSUPPORTED, "%d segments > GDN_MAX_SEGMENTS", R);
+        const int64_t nc = cdiv(p->S, C);
+        if (R > 1 && R > nc)
+            return fail(GDN_EINVAL, "%d segments but only %lld chunks", R, (long long)nc);
+        if (p->seg_starts) {
+            const int32_t *ss = p->seg_starts;
+            if (ss[0] != 0) return fail(GDN_EORDER, "seg_starts[0] = %d, must be 0", ss[0]);
+            for (int r = 0; r < R; ++r) {
+                if (ss[r] % C != 0)
+                    return fail(GDN_EORDER, "seg_starts[%d] = %d is not a multiple of C = %d", r,
+                                ss[r], C);
+                if (r > 0 && ss[r] <= ss[r - 1])
+                    return fail(GDN_EORDER, "segments must be contiguous and in order: "
+                                            "seg_starts[%d] = %d <= seg_starts[%d] = %d",
+                                r, ss[r], r - 1, ss[r - 1]);
+                if (R > 1 && ss[r] >= p->S)
+                    return fail(GDN_EORDER, "seg_starts[%d] = %d >= S = %d", r, ss[r], p->S);
+                out.ct.seg_start[r] = ss[r];
+            }
+        } else {
+            for (int r = 0; r < R; ++r) out.ct.seg_start[r] = (int32_t)((r * nc / R) * C);
+        }
+        out.ct.seg_start[R] = p->S;
+        out.ct.packed = 0;
+        out.ct.n_seqs = p->B;
+        out.ct.seq_len = p->S;
+        out.ct.n_seg = R;
+        out.N = p->B;
+        out.R = R;
+        out.n_chunks = (int64_t)p->B * nc;
+    }
+    out.T = p->n_seqs > 0 ? (int64_t)p->S : (int64_t)p->B * p->S;
+    const int64_t wgs = (int64_t)out.N * out.R * p->H * (p->K + p->V);
+    if (wgs > 0x7fffffffLL || out.n_chunks * p->H > 0x7fffffffLL)
+        return fail(GDN_EUNSUPPORTED, "problem too large for one launch");
+    return GDN_OK;
+}
+
+size_t elem_size(int dtype) { return dtype == GDN_F32 ? 4 : 2; }
+
+gdn_status check_ptr(const void *ptr, const char *name, bool required) {
+    if (!ptr) return required ? fail(GDN_EINVAL, "%s is NULL", name) : GDN_OK;
+    if (!aligned16(ptr)) return fail(GDN_EINVAL, "%s is not 16-byte aligned", name);
+    return GDN_OK;
+}
+
+#define GDN_TRY(expr)                      \
+    do {                                   \
+        gdn_status _st = (expr);           \
+        if (_st != GDN_OK) return _st;     \
+    } while (0)
+
+gdn_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(GDN_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return GDN_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b) return false;
+    const char *pa = static_cast<const char *>(a), *pb = static_cast<const char *>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_validate(const gdn_problem *p) {
+    g_err[0] = 0;
+    Resolved r;
+    return resolve(p, r);
+}
+
+size_t gdn_wy_workspace_bytes(const gdn_problem *p) {
+    Resolved r;
+    if (resolve(p, r) != GDN_OK) return 0;
+    return (size_t)r.n_chunks * p->H * p->C * (p->K + p->V) * elem_size(p->dtype);
+}
+
+size_t gdn_segment_workspace_bytes(const gdn_problem *p) {
+    Resolved r;
+    if (resolve(p, r) != GDN_OK) return 0;
+    return (size_t)r.R * r.N * p->H * p->K * (size_t)(p->K + p->V) * sizeof(float);
+}
+
+gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
+                             const float *g, const float *beta, void *wy, void *stream) {
+    g_err[0] = 0;
+    Resolved r;
+    GDN_TRY(resolve(p, r));
+    const bool any = r.T > 0;
+    GDN_TRY(check_ptr(k, "k", any));
+    GDN_TRY(check_ptr(v, "v", any));
+    GDN_TRY(check_ptr(g, "g", any));
+    GDN_TRY(check_ptr(beta, "beta", any));
+    GDN_TRY(check_ptr(wy, "wy", r.n_chunks > 0));
+    if (r.n_chunks == 0) return GDN_OK;
+    PrepArgs a;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.wy_w = wy;
+    a.wy_u = static_cast<char *>(wy) + (size_t)r.n_chunks * p->H * p->C * p->K * elem_size(p->dtype);
+    a.H = p->H;
+    a.n_chunks = r.n_chunks;
+    a.ct = r.ct;
+    (void)hipGetLastError();
+    return launched(launch_prepare(p->K, p->V, p->C, p->dtype, a, (hipStream_t)stream),
+                    "gdn_chunk_prepare");
+}
+
+gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const void *k,
+                    const void *v, const float *g, const float *beta, const void *wy,
+                    const float *h_in, void *o, float *h_out, float *M_out, float *U_out,
+                    void *stream) {
+    g_err[0] = 0;
+    Resolved r;
+    GDN_TRY(resolve(p, r));
+    if (mode != GDN_SCAN_EMIT && mode != GDN_SCAN_CARRY)
+        return fail(GDN_EINVAL, "unknown scan mode %d", mode);
+    const bool carry = mode == GDN_SCAN_CARRY;
+    const bool any = r.T > 0;
+    GDN_TRY(check_ptr(k, "k", any));
+    GDN_TRY(check_ptr(v, "v", any));
+    GDN_TRY(check_ptr(g, "g", any));
+    GDN_TRY(check_ptr(beta, "beta", any));
+    GDN_TRY(check_ptr(wy, "wy", false));
+    if (carry) {
+        GDN_TRY(check_ptr(M_out, "M_out", true));
+        GDN_TRY(check_ptr(U_out, "U_out", true));
+    } else {
+        GDN_TRY(check_ptr(q, "q", any));
+        GDN_TRY(check_ptr(o, "o", any));
+        GDN_TRY(check_ptr(h_in, "h_in", false));
+        GDN_TRY(check_ptr(h_out, "h_out", false));
+        if (h_out && h_in && r.R > 1) {
+            const size_t state = (size_t)p->H * p->K * p->V * sizeof(float);
+            if (overlaps(h_in, state * r.R * r.N, h_out, state * r.N))
+                return fail(GDN_EINVAL, "h_out may alias h_in only with one segment");
+        }
+    }
+    ScanArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.wy_w = wy;
+    a.wy_u = wy ? static_cast<const char *>(wy) +
+                      (size_t)r.n_chunks * p->H * p->C * p->K * elem_size(p->dtype)
+                : nullptr;
+    a.h_in = carry ? nullptr : h_in;
+    a.o = carry ? nullptr : o;
+    a.h_out = carry ? nullptr : h_out;
+    a.M_out = carry ? M_out : nullptr;
+    a.U_out = carry ? U_out : nullptr;
+    a.H = p->H;
+    a.n_chains = r.N * r.R;
+    a.ct = r.ct;
+    (void)hipGetLastError();
+    return launched(launch_scan(p->K, p->V, p->C, p->dtype, carry, a, (hipStream_t)stream),
+                    "gdn_scan");
+}
+
+gdn_status gdn_segment_compose(int32_t R, int32_t N, int32_t H, int32_t K, int32_t V,
+                               const float *M, const float *U, const float *h0, float *h_in,
+                               float *h_final, void *stream) {
+    g_err[0] = 0;
+    if (R < 1 || N < 0 || H < 1 || K < 1 || V < 1)
+        return fail(GDN_EINVAL, "bad sizes R=%d N=%d H=%d K=%d V=%d", R, N, H, K, V);
+    if (!((K == 32 && V == 32) || (K == 128 && V == 128)))
+        return fail(GDN_EUNSUPPORTED, "(K,V)=(%d,%d) not built", K, V);
+    if (N == 0) return GDN_OK;
+    GDN_TRY(check_ptr(M, "M", true));
+    GDN_TRY(check_ptr(U, "U", true));
+    GDN_TRY(check_ptr(h0, "h0", false));
+    GDN_TRY(check_ptr(h_in, "h_in", true));
+    GDN_TRY(check_ptr(h_final, "h_final", false));
+    const size_t nh = (size_t)N * H;
+    const size_t sz_state = (size_t)K * V * sizeof(float);
+    const size_t sz_hin = R * nh * sz_state;
+    if (overlaps(h_in, sz_hin, M, R * nh * K * K * sizeof(float)) ||
+        overlaps(h_in, sz_hin, U, R * nh * sz_state) || overlaps(h_in, sz_hin, h0, nh * sz_state) ||
+        overlaps(h_final, nh * sz_state, h_in, sz_hin) ||
+        overlaps(h_final, nh * sz_state, M, R * nh * K * K * sizeof(float)) ||
+        overlaps(h_final, nh * sz_state, U, R * nh * sz_state))
+        return fail(GDN_EINVAL, "h_in / h_final must not alias the inputs or each other");
+    ComposeArgs a;
+    a.M = M;
+    a.U = U;
+    a.h0 = h0;
+    a.h_in = h_in;
+    a.h_final = h_final;
+    a.R = R;
+    a.N = N;
+    a.H = H;
+    (void)hipGetLastError();
+    return launched(launch_compose(K, V, a, (hipStream_t)stream), "gdn_segment_compose");
+}
+
+gdn_status gdn_decode_step(int32_t B, int32_t H, int32_t K, int32_t V, int32_t dtype,
+                           const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, void *o, void *stream) {
+    g_err[0] = 0;
+    if (B < 0 || H < 1 || K < 1 || V < 1)
+        return fail(GDN_EINVAL, "bad sizes B=%d H=%d K=%d V=%d", B, H, K, V);
+    if (!((K == 32 && V == 32) || (K == 128 && V == 128)))
+        return fail(GDN_EUNSUPPORTED, "(K,V)=(%d,%d) not built", K, V);
+    if (dtype != GDN_F32 && dtype != GDN_BF16)
+        return fail(GDN_EUNSUPPORTED, "dtype %d not supported", dtype);
+    if (B == 0) return GDN_OK;
+    if ((int64_t)B * H > 0x7fffffffLL) return fail(GDN_EUNSUPPORTED, "B*H too large");
+    GDN_TRY(check_ptr(q, "q", true));
+    GDN_TRY(check_ptr(k, "k", true));
+    GDN_TRY(check_ptr(v, "v", true));
+    GDN_TRY(check_ptr(g, "g", true));
+    GDN_TRY(check_ptr(beta, "beta", true));
+    GDN_TRY(check_ptr(state, "state", true));
+    GDN_TRY(check_ptr(o, "o", true));
+    DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.o = o;
+    a.B = B;
+    a.H = H;
+    (void)hipGetLastError();
+    return launched(launch_decode(K, V, dtype, a, (hipStream_t)stream), "gdn_decode_step");
+}
+
+int32_t gdn_scan_backend(const gdn_problem *p) {
+    Resolved r;
+    if (resolve(p, r) != GDN_OK) return -1;
+    return mfma_scan_available(p->K, p->V, p->C, p->dtype) ? 1 : 0;
+}
+
+const char *gdn_status_string(int32_t status) {
+    switch (status) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_EINVAL: return "GDN_EINVAL: invalid argument";
+        case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED: shape or dtype not supported";
+        case GDN_EORDER: return "GDN_EORDER: segments or sequences not contiguous and in order";
+        case GDN_ELAUNCH: return "GDN_ELAUNCH: kernel launch failed";
+        default: return "unknown gdn_status";
+    }
+}
+
+const char *gdn_last_error(void) { return g_err; }
+
+int32_t gdn_version(void) { return 100; }
+
+}  // extern "C"

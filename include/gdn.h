@@ -1,0 +1,187 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule forward library.
+ *
+ * The operation is the chunked gated delta rule of the MaxText PR "Add
+ * context parallelism to the Gated Delta Net (Qwen3-Next / Qwen3.5)":
+ *   - per chunk of C tokens, the WY factors w, u of the affine chunk map
+ *     h_out = (gamma I - k_tilde^T w) h + k_tilde^T u = M h + U and the chunk
+ *     output o = (q_g - attn_i w) h + attn_i u (section "Why");
+ *   - the sequential scan of that map over chunks;
+ *   - the three-phase segment pass (section "Implementation"): a zero-state
+ *     pass carrying M (low-rank update M <- gamma M - k_tilde^T (w M)), an
+ *     exclusive prefix scan over the (M_r, U_r) pairs, and a re-pass from the
+ *     true incoming state;
+ *   - the single-token recurrent decode step on the fp32 state, whose layout
+ *     [H_v, K, V] f32 per request follows "RFC(qwen35): TP Phase 2",
+ *     section "Partition Contract".
+ *
+ * Per token (K-major state h in R^{K x V}):
+ *   h <- exp(g_t) h;  delta = beta_t (v_t - h^T k_t);  h <- h + k_t delta^T;
+ *   o_t = h^T q_t.
+ * The query is used unscaled: a caller wanting 1/sqrt(K) pre-scales q.
+ *
+ * Conventions for every entry point
+ *   - Tensors are caller-owned device buffers, row-major, contiguous, 16-byte
+ *     aligned.  The library allocates nothing and keeps no state apart from a
+ *     thread-local error message.
+ *   - q, k, v and o share one dtype (GDN_F32 or GDN_BF16).  g (log-decay,
+ *     alpha = exp(g)) and beta are fp32.  Every state, M and U is fp32.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue work
+ *     and return without synchronising.
+ *   - Every argument is checked before anything is launched; a call that
+ *     returns an error has written nothing.  HIP launch failures surface as
+ *     GDN_ELAUNCH.  No C++ exception crosses the ABI.
+ *   - Supported (K, V, C): (32, 32, 16) and (128, 128, 64).  Anything else is
+ *     GDN_EUNSUPPORTED; there is no fallback.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_EINVAL = 1,        /* null pointer, bad size, misaligned buffer          */
+    GDN_EUNSUPPORTED = 2,  /* shape / dtype combination not built                */
+    GDN_EORDER = 3,        /* segments or sequence offsets not contiguous+ordered */
+    GDN_ELAUNCH = 4        /* HIP reported an error at launch                    */
+} gdn_status;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum gdn_scan_mode {
+    GDN_SCAN_EMIT = 0,   /* outputs o and the final state                           */
+    GDN_SCAN_CARRY = 1   /* zero-state pass per segment emitting (M_r, U_r), no o   */
+} gdn_scan_mode;
+
+#define GDN_MAX_SEQS 256
+#define GDN_MAX_SEGMENTS 64
+
+/*
+ * Problem description (host memory; read during the call only).
+ *
+ * Batch mode (n_seqs == 0): B independent sequences of S tokens each;
+ *   q, k [B,S,H,K]; v, o [B,S,H,V]; g, beta [B,S,H]; states [B,H,K,V].
+ * Packed mode (n_seqs > 0, B == 1): n_seqs sequences laid end to end on one
+ *   token axis of S tokens, sequence n owning tokens cu_seqlens[n] ..
+ *   cu_seqlens[n+1]-1 (cu_seqlens[0] == 0, non-decreasing, cu_seqlens[n_seqs]
+ *   == S, at most GDN_MAX_SEQS sequences); q, k [S,H,K], ...; states
+ *   [n_seqs,H,K,V].  Sequences need not be multiples of C: a ragged tail is
+ *   masked exactly like padding (g = 0, q = k = v = 0, beta = 0), which the
+ *   MaxText PR ("Implementation") shows is a no-op for the recurrence.
+ *
+ * Segments (batch mode only): every sequence is cut into n_segments
+ *   contiguous, in-order pieces starting at seg_starts[r] (relative to the
+ *   sequence start).  seg_starts[0] == 0, strictly increasing, multiples of
+ *   C, all < S, otherwise GDN_EORDER -- a sequential recurrence needs
+ *   contiguous, in-order slices (MaxText PR, section "Limitation").
+ *   seg_starts == NULL splits the chunks as evenly as possible.
+ *   Packed mode requires n_segments == 1.
+ */
+typedef struct gdn_problem {
+    int32_t B, S, H, K, V, C;
+    int32_t dtype;                /* gdn_dtype of q, k, v, o and of the WY workspace */
+    int32_t n_seqs;               /* 0: batch mode; >0: packed mode                 */
+    const int32_t *cu_seqlens;    /* host pointer, n_seqs + 1 entries (packed mode) */
+    int32_t n_segments;           /* R >= 1                                          */
+    const int32_t *seg_starts;    /* host pointer, R entries, or NULL                */
+} gdn_problem;
+
+/* Check a problem description without touching the GPU. */
+gdn_status gdn_validate(const gdn_problem *p);
+
+/* Bytes of the WY workspace written by gdn_chunk_prepare: for every chunk
+ * (batch: B * ceil(S/C); packed: sum over sequences of ceil(len/C)) and head,
+ * w [C,K] then, after all w blocks, u [C,V], in the problem's dtype.
+ * Returns 0 for an invalid problem. */
+size_t gdn_wy_workspace_bytes(const gdn_problem *p);
+
+/* Bytes of the segment transition pairs M [R,N,H,K,K] plus U [R,N,H,K,V]
+ * (fp32; N = B or n_seqs): R*N*H*K*(K+V)*4, independent of S -- the
+ * sequence-length-independent cross-rank payload of the MaxText PR
+ * ("Measured results", "Tests").  Returns 0 for an invalid problem. */
+size_t gdn_segment_workspace_bytes(const gdn_problem *p);
+
+/*
+ * gdn_chunk_prepare -- per-chunk WY factors (MaxText PR, "Why": the w and u
+ * of the affine chunk form; "Implementation": _gdn_chunk_prepare).
+ * For each chunk and head, with G the within-chunk cumulative log-decay:
+ *   A[r,s] = beta_r exp(G_r - G_s) k_r.k_s (s < r),  T = (I + A)^{-1},
+ *   w = T diag(beta exp(G)) K_c,  u = T diag(beta) V_c.
+ * k, v, g, beta as in the problem; wy receives gdn_wy_workspace_bytes(p)
+ * bytes (w blocks [n_chunks,H,C,K] followed by u blocks [n_chunks,H,C,V]).
+ * Rows past the end of a ragged chunk are zero.  Segments are ignored.
+ */
+gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
+                             const float *g, const float *beta, void *wy, void *stream);
+
+/*
+ * gdn_scan -- the inter-chunk affine scan (MaxText PR, "Why" equations;
+ * "Implementation" phases 1 and 3).
+ *
+ * wy: NULL recomputes the WY factors inside the scan; otherwise a workspace
+ *   filled by gdn_chunk_prepare for the same problem and inputs is reused.
+ *
+ * GDN_SCAN_EMIT: for every segment r of every sequence n, starts from
+ *   h_in[r,n] (h_in [R,N,H,K,V] fp32; NULL = zero state for every segment),
+ *   runs the chunk map over the segment, writes o for its tokens, and the
+ *   last segment writes the final state to h_out [N,H,K,V] (nullable).
+ *   h_out may alias h_in only when R == 1.  q, o required.
+ * GDN_SCAN_CARRY: for every segment, a zero-state pass carrying the composed
+ *   transition: writes M_out [R,N,H,K,K] and U_out [R,N,H,K,V] with
+ *   h_end = M_r h_start + U_r.  q, o, h_in, h_out are ignored.
+ */
+gdn_status gdn_scan(const gdn_problem *p, int32_t mode,
+                    const void *q, const void *k, const void *v,
+                    const float *g, const float *beta, const void *wy,
+                    const float *h_in, void *o, float *h_out,
+                    float *M_out, float *U_out, void *stream);
+
+/*
+ * gdn_segment_compose -- exclusive prefix scan over segment pairs (MaxText
+ * PR, "Implementation" phase 2):
+ *   h_in[0] = h0 (NULL = zero), h_in[r+1] = M[r] h_in[r] + U[r],
+ *   h_final = M[R-1] h_in[R-1] + U[R-1] (nullable output).
+ * M [R,N,H,K,K], U and h_in [R,N,H,K,V], h0 and h_final [N,H,K,V], fp32.
+ * h_in must not alias M, U or h0.
+ */
+gdn_status gdn_segment_compose(int32_t R, int32_t N, int32_t H, int32_t K, int32_t V,
+                               const float *M, const float *U, const float *h0,
+                               float *h_in, float *h_final, void *stream);
+
+/*
+ * gdn_decode_step -- one token per sequence, in place on the fp32 state
+ * (the per-token recurrence above; the "GDR decode kernel" of
+ * "RFC(qwen35): TP Phase 2", section "Kernel Work", state [H_v,K,V] f32).
+ * q, k [B,H,K]; v, o [B,H,V] in `dtype`; g, beta [B,H] fp32;
+ * state [B,H,K,V] fp32, read and written once.
+ */
+gdn_status gdn_decode_step(int32_t B, int32_t H, int32_t K, int32_t V, int32_t dtype,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, float *state, void *o,
+                           void *stream);
+
+/* Which units run gdn_scan for this problem: 1 = matrix cores (bf16 MFMA
+ * kernel), 0 = fp32 vector ALU kernel, -1 = invalid problem.  Lets callers
+ * and benchmarks name the roofline that bounds the call. */
+int32_t gdn_scan_backend(const gdn_problem *p);
+
+/* Static description of a status code. */
+const char *gdn_status_string(int32_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *gdn_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

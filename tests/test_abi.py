@@ -1,0 +1,55 @@
+"""The C-ABI library loads and exports every entry point include/gdn.h declares (CPU only)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from chunked_gated_delta_gdn_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ["gdn_chunk_prepare", "gdn_scan", "gdn_segment_compose", "gdn_decode_step"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = b.library()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    assert set(declared_functions()) <= exported
+
+
+def test_binding_mirrors_the_abi_names():
+    for name in declared_functions():
+        if name in ("gdn_status_string", "gdn_last_error"):
+            continue
+        assert hasattr(b, name), name
+
+
+def test_status_strings_and_version():
+    lib = b.library()
+    for code in range(5):
+        assert lib.gdn_status_string(code).decode().startswith("GDN_")
+    assert b.gdn_version() >= 100
+
+
+def test_problem_struct_layout_matches_c():
+    import ctypes
+    assert ctypes.sizeof(b.GdnProblem) == 56
+    assert b.GdnProblem.cu_seqlens.offset == 32
+    assert b.GdnProblem.n_segments.offset == 40
+    assert b.GdnProblem.seg_starts.offset == 48

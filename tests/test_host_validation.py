@@ -1,0 +1,143 @@
+"""Host-side argument validation of the C ABI (CPU only: every case here is
+rejected before anything touches a GPU)."""
+import json
+import os
+
+import pytest
+
+from chunked_gated_delta_gdn_amd import binding as b
+
+FAKE = 0x7f0000000000        # a 16-byte aligned address that is never dereferenced
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def prob(**kw):
+    args = dict(B=1, S=256, H=2, K=32, V=32, C=16, dtype=b.GDN_F32)
+    args.update(kw)
+    cu = args.pop("cu_seqlens", None)
+    R = args.pop("n_segments", 1)
+    ss = args.pop("seg_starts", None)
+    return b.make_problem(cu_seqlens=cu, n_segments=R, seg_starts=ss, **args)
+
+
+def status(p):
+    return b.gdn_validate(p, raise_on_error=False)
+
+
+def test_valid_problems():
+    assert status(prob()) == b.GDN_OK
+    assert status(prob(K=128, V=128, C=64, dtype=b.GDN_BF16, S=65536, H=32, n_segments=4)) == 0
+    assert status(prob(S=0)) == b.GDN_OK
+    assert status(prob(S=250, n_segments=4)) == b.GDN_OK
+    assert status(prob(S=100, cu_seqlens=[0, 30, 30, 100])) == b.GDN_OK
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(S=-1), dict(H=0), dict(K=0), dict(C=0)])
+def test_bad_sizes(kw):
+    assert status(prob(**kw)) == b.GDN_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(K=64, V=64, C=32), dict(C=32), dict(K=128, V=64, C=64),
+                                dict(dtype=7)])
+def test_unsupported_shapes(kw):
+    assert status(prob(**kw)) == b.GDN_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("ss", [[0, 16, 8, 32], [0, 8, 32, 64], [16, 32, 48, 64],
+                                [0, 64, 64, 128], [0, 64, 128, 256]])
+def test_segments_must_be_contiguous_in_order_and_chunk_aligned(ss):
+    """MaxText PR, section 'Limitation': a sequential recurrence needs contiguous,
+    in-order slices; anything else is an error, never a silent wrong result."""
+    assert status(prob(n_segments=4, seg_starts=ss)) == b.GDN_EORDER
+
+
+def test_too_many_segments():
+    assert status(prob(S=32, n_segments=3)) == b.GDN_EINVAL
+    assert status(prob(S=4096, n_segments=b.GDN_MAX_SEGMENTS + 1)) == b.GDN_EUNSUPPORTED
+
+
+def test_packed_mode_rules():
+    assert status(prob(S=100, cu_seqlens=[0, 60, 50, 100])) == b.GDN_EORDER
+    assert status(prob(S=100, cu_seqlens=[5, 60, 100])) == b.GDN_EORDER
+    assert status(prob(S=100, cu_seqlens=[0, 60, 90])) == b.GDN_EINVAL
+    assert status(prob(S=100, B=2, cu_seqlens=[0, 100])) == b.GDN_EINVAL
+    assert status(prob(S=100, cu_seqlens=[0, 100], n_segments=2)) == b.GDN_EUNSUPPORTED
+    many = list(range(0, b.GDN_MAX_SEQS + 2))
+    assert status(prob(S=many[-1], cu_seqlens=many)) == b.GDN_EUNSUPPORTED
+
+
+def test_workspace_sizes():
+    p = prob(S=250, B=3)                      # 16 chunks per sequence, ragged tail
+    assert b.gdn_wy_workspace_bytes(p) == 3 * 16 * 2 * 16 * (32 + 32) * 4
+    p = prob(S=100, cu_seqlens=[0, 17, 17, 100], dtype=b.GDN_BF16)   # 2 + 0 + 6 chunks
+    assert b.gdn_wy_workspace_bytes(p) == 8 * 2 * 16 * 64 * 2
+    assert b.gdn_wy_workspace_bytes(prob(C=5)) == 0
+
+
+def test_segment_payload_is_sequence_length_independent():
+    """The (M_r, U_r) payload is cp*B*H*K*(K+V) fp32 elements whatever S is
+    (MaxText PR, sections 'Tests' and 'Measured results')."""
+    with open(os.path.join(GOLDEN, "segment_payload.json")) as f:
+        d = json.load(f)
+    elems = 1
+    for x in d["hlo_shape"]:
+        elems *= x
+    assert elems == d["cp"] * d["BH"] * d["K"] * (d["K"] + d["V"])
+    sizes = set()
+    for S in d["seq_lens"]:
+        p = prob(B=1, H=d["BH"], S=S, K=d["K"], V=d["V"], C=64, n_segments=d["cp"])
+        sizes.add(b.gdn_segment_workspace_bytes(p))
+    assert sizes == {elems * 4}
+
+
+def _scan_status(p, mode=b.GDN_SCAN_EMIT, **ptrs):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, wy=None, h_in=None, o=FAKE,
+                h_out=None, M=None, U=None)
+    args.update(ptrs)
+    lib = b.library()
+    import ctypes
+    return lib.gdn_scan(ctypes.byref(p), mode, args["q"], args["k"], args["v"], args["g"],
+                        args["beta"], args["wy"], args["h_in"], args["o"], args["h_out"],
+                        args["M"], args["U"], None)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "o"])
+def test_scan_rejects_null_inputs(name):
+    assert _scan_status(prob(), **{name: None}) == b.GDN_EINVAL
+
+
+@pytest.mark.parametrize("name", ["q", "k", "g", "o", "h_in", "wy"])
+def test_scan_rejects_misaligned_pointers(name):
+    assert _scan_status(prob(), **{name: FAKE + 4}) == b.GDN_EINVAL
+
+
+def test_scan_rejects_bad_mode_and_missing_carry_outputs():
+    assert _scan_status(prob(), mode=5) == b.GDN_EINVAL
+    assert _scan_status(prob(), mode=b.GDN_SCAN_CARRY) == b.GDN_EINVAL
+    assert _scan_status(prob(), mode=b.GDN_SCAN_CARRY, M=FAKE) == b.GDN_EINVAL
+
+
+def test_scan_rejects_state_alias_with_segments():
+    p = prob(n_segments=4)
+    assert _scan_status(p, h_in=FAKE, h_out=FAKE) == b.GDN_EINVAL
+
+
+def test_error_messages_name_the_problem():
+    st = _scan_status(prob(n_segments=4, seg_starts=[0, 32, 16, 64]))
+    assert st == b.GDN_EORDER
+    assert b"contiguous and in order" in b.library().gdn_last_error()
+
+
+def test_compose_and_decode_validation():
+    lib = b.library()
+    assert lib.gdn_segment_compose(0, 1, 1, 32, 32, FAKE, FAKE, None, FAKE, None, None) == b.GDN_EINVAL
+    assert lib.gdn_segment_compose(2, 1, 1, 64, 64, FAKE, FAKE, None, FAKE, None, None) == b.GDN_EUNSUPPORTED
+    assert lib.gdn_segment_compose(2, 1, 1, 32, 32, FAKE, FAKE, None, None, None, None) == b.GDN_EINVAL
+    # h_in aliasing M is refused
+    assert lib.gdn_segment_compose(2, 1, 1, 32, 32, FAKE, FAKE + (1 << 20), None, FAKE, None,
+                                   None) == b.GDN_EINVAL
+    assert lib.gdn_decode_step(4, 2, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EUNSUPPORTED
+    assert lib.gdn_decode_step(4, 2, 32, 32, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EUNSUPPORTED
+    assert lib.gdn_decode_step(4, 2, 32, 32, 0, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EINVAL
+    assert lib.gdn_decode_step(4, 0, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EINVAL
+    assert lib.gdn_decode_step(0, 2, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_OK

@@ -32,9 +32,10 @@ __all__ = ["GdnInputs", "DecodeInputs", "round_bf16", "bf16_bits", "make_inputs"
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to the nearest bfloat16 (ties to even); returns fp32."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
-    return bits.astype(np.uint32).view(np.float32)
+    bits = x.view(np.uint32)
+    bits = (bits + (np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1)))) \
+        & np.uint32(0xFFFF0000)
+    return bits.view(np.float32)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
