@@ -23,13 +23,15 @@
 //    kept in fp32 MFMA accumulators for the whole chain, and run the chunk
 //    step for chunk j.  Waves 4-7 (producers) work ahead, so the
 //    latency-bound preparation overlaps the scan; one barrier per chunk:
-//      wave 4: Gram k k^T and the inverse T = (I + A)^{-1} for chunk j+1, all
-//              on MFMA: diagonal 16 x 16 blocks by the product
+//      wave 4: the inverse T = (I + A)^{-1} for chunk j+1, all on MFMA:
+//              diagonal 16 x 16 blocks by the product
 //              (I - N)(I + N^2)(I + N^4)(I + N^8), off-diagonal blocks by block
 //              recursion on T^T so that T comes out row-major, ready as the A
 //              operand of T diag(beta);
 //      wave 5: loads k, g, beta of chunk j+2 (issued one chunk earlier still,
-//              so two chunks are in flight);
+//              so two chunks are in flight), stores k, the cumulative decay,
+//              and, from the k rows still in its registers, the Gram k k^T
+//              with the decay factors of A;
 //      wave 6: loads q (one chunk ahead), writes it for the consumers, and
 //              forms attn from the Gram k q^T;
 //      wave 7: k^T by identity MFMAs (the operand of K^T delta) and the
@@ -65,26 +67,33 @@ __device__ __forceinline__ f32x4 mma16(const bf16x4 &a, const bf16x4 &b, const f
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Round to bf16 (nearest even) two values at a time into one 32-bit register
+// (a single v_cvt_pk_bf16_f32), then reinterpret: converting whole bf16
+// vectors that feed an MFMA otherwise costs a conversion and a permute per
+// element.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
 __device__ __forceinline__ bf16x4 to4(const f32x4 &x) {
-    bf16x4 r;
-    r[0] = (bf16)x[0]; r[1] = (bf16)x[1]; r[2] = (bf16)x[2]; r[3] = (bf16)x[3];
-    return r;
+    return __builtin_bit_cast(bf16x4, make_uint2(cvt2(x[0], x[1]), cvt2(x[2], x[3])));
+}
+__device__ __forceinline__ bf16x8 join(const bf16x4 &lo, const bf16x4 &hi) {
+    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8, make_uint4(l.x, l.y, h.x, h.y));
 }
 // Two accumulator tiles (rows 0-15, 16-31 of a 32-row block) -> the bf16
 // operand that reduces over those 32 rows.
 __device__ __forceinline__ bf16x8 pack_pair(const f32x4 &lo, const f32x4 &hi) {
-    bf16x8 r;
-    r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
-    r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
-    return r;
-}
-__device__ __forceinline__ bf16x8 join(const bf16x4 &lo, const bf16x4 &hi) {
-    bf16x8 r;
-    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-    return r;
+    return __builtin_bit_cast(bf16x8, make_uint4(cvt2(lo[0], lo[1]), cvt2(lo[2], lo[3]),
+                                                 cvt2(hi[0], hi[1]), cvt2(hi[2], hi[3])));
 }
 __device__ __forceinline__ bf16x8 as8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Decays are kept as log2 values, so exp(G_r - G_s) is one v_exp_f32.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Workgroup barrier that waits for this wave's LDS operations only (global
 // loads issued earlier stay in flight).
@@ -111,27 +120,54 @@ struct Lds {
     bf16 kT[2][K * C];      // k transposed, narrow tiles
     bf16 attn[2][C * C];    // attn, narrow tiles
     bf16 tb[2][C * C];      // T diag(beta), narrow tiles
-    float graw[3][C], braw[3][C];   // g, beta of the chunk (zero past its end)
-    float gam[2][C];        // exp(G_r)
+    uint2 ab[2][10][64];    // loader -> wave 4, per lane 4 bf16: the 6 off-diagonal
+                            // blocks of A (B layout) and the 4 raw diagonal blocks of k k^T
+    float G2[2][C];         // cumulative log-decay of the chunk, times log2(e)
+    float B[2][C];          // beta (zero past the chunk end)
+    float gam[2][C];        // exp(G_r); gam[63] = exp(G_C)
     float kdec[2][C];       // exp(G_C - G_r)
-    float gC[2][4];         // exp(G_C)
-    float p0G[C];           // scratch of wave 4
-    float p2G[C];           // scratch of wave 6
 };
 
-// 16 x 32 tile of a bf16 row-major matrix in the MFMA register layout: lane
-// (i, g) holds elements 32 kk + 4g .. +3 and 32 kk + 16 + 4g .. +3 of its row.
+// Whole rows of a 64 x 128 bf16 chunk tile: lane l of load m covers row
+// 4m + l/16, elements 8 (l % 16) .. +7 (16 B), so one instruction reads four
+// full rows.
 //
-// Rows past the end of a ragged chunk: callers clamp the row to the last
-// valid token instead of zeroing it, so every load is unconditional and stays
-// in flight.  This is exact because those rows get g = 0 and beta = 0 (the
-// padding of the MaxText PR, section "Implementation"): their rows of A and of
-// T diag(beta), and the columns of T diag(beta), vanish, so a duplicated k, q
-// or v row only ever meets a zero factor and its outputs are not stored.
-__device__ __forceinline__ uint4 load_slots(const bf16 *rowp, int kk, int lg) {
-    const uint2 lo = *reinterpret_cast<const uint2 *>(rowp + 32 * kk + 4 * lg);
-    const uint2 hi = *reinterpret_cast<const uint2 *>(rowp + 32 * kk + 16 + 4 * lg);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+// Rows past the end of a ragged chunk repeat the last valid row instead of
+// being zeroed, so every load is unconditional and stays in flight.  This is
+// exact because those rows get g = 0 and beta = 0 (the padding of the MaxText
+// PR, section "Implementation"): their rows of A and of T diag(beta), and the
+// columns of T diag(beta), vanish, so a repeated k, q or v row only ever meets
+// a zero factor, and its outputs are not stored.
+__device__ __forceinline__ void load_rows(uint4 (&t)[16], const bf16 *base, int64_t row_stride,
+                                          int L, int lane) {
+    if (L == 64) {
+        const bf16 *p = base + (int64_t)(lane >> 4) * row_stride + 8 * (lane & 15);
+        const int64_t step = 4 * row_stride;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) t[m] = *reinterpret_cast<const uint4 *>(p + m * step);
+    } else {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int r = 4 * m + (lane >> 4);
+            t[m] = *reinterpret_cast<const uint4 *>(base + (int64_t)(r < L ? r : L - 1) * row_stride +
+                                                    8 * (lane & 15));
+        }
+    }
+}
+// Store rows loaded by load_rows into a wide tile: the 16 B of elements
+// 8s .. 8s+7 split into two 8 B halves that land on k-slots 16(s&1) + 4(s/2&1)
+// and +8 of their 32-element block, i.e. chunks 4(s/4) + 2(s&1) and the next
+// one, at byte 8 (s/2 & 1) within the chunk.
+__device__ __forceinline__ void store_rows(bf16 *tile, const uint4 (&t)[16], int lane) {
+    const int s = lane & 15;
+    const int q0 = 4 * (s >> 2) + 2 * (s & 1), within = 8 * ((s >> 1) & 1);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int r = 4 * m + (lane >> 4);
+        char *b = reinterpret_cast<char *>(tile);
+        *reinterpret_cast<uint2 *>(b + woff(r, q0) + within) = make_uint2(t[m].x, t[m].y);
+        *reinterpret_cast<uint2 *>(b + woff(r, q0 + 1) + within) = make_uint2(t[m].z, t[m].w);
+    }
 }
 
 // Inclusive prefix sum over the 64 lanes.
@@ -222,6 +258,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
         bf16x4 i16;   // identity, B operand of a 16x16x16 product
 #pragma unroll
         for (int e = 0; e < 4; ++e) i16[e] = (bf16)((4 * lg + e == li) ? 1.f : 0.f);
+        const uint32_t out_off = (uint32_t)((h * V + col_w + 4 * lg) * 2);   // bytes within a row
 
         if (n_chunks > 0) load_v(0);
         lds_barrier();   // iteration -2: k of chunk 0 loaded
@@ -334,7 +371,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                 }
             }
             // X = gamma_C X + K^T diag(kdec) delta
-            const float gc = sm.gC[b2][0];
+            const float gc = gam[63];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
 #pragma unroll
@@ -347,14 +384,18 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                 }
             }
             if (EMIT) {
-                bf16 *go = static_cast<bf16 *>(a.o);
+                // O tile c in B layout (lane (j, g): rows 4g..4g+3, column j) ->
+                // transposed by an identity product: lane (j, g) then holds row j,
+                // columns 4g..4g+3, i.e. 8 contiguous bytes of the output row.
+                char *ob = reinterpret_cast<char *>(static_cast<bf16 *>(a.o) + tok(j, 0) * rowV);
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * c + 4 * lg + e;
-                        if (r < L) go[tok(j, r) * rowV + h * V + col_w + li] = (bf16)O[c][e];
-                    }
+                for (int c = 0; c < 4; ++c) {
+                    const f32x4 ot = mma16(to4(O[c]), i16, zero4());
+                    const uint2 v = __builtin_bit_cast(uint2, to4(ot));
+                    const int r = 16 * c + li;
+                    if (L == C || r < L)
+                        *reinterpret_cast<uint2 *>(ob + (uint32_t)r * (uint32_t)(rowV * 2) + out_off) = v;
+                }
             }
             lds_barrier();
         }
@@ -398,30 +439,65 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
     auto clampj = [&](int64_t j) { return j < n_chunks ? j : n_chunks - 1; };
     if (role == 1) {
         // ---------------- loader: k rows, g, beta; two register sets ----------------
-        uint4 kA_[4][4], kB_[4][4];
+        uint4 kA_[16], kB_[16];
         float gA, bA, gB, bB;
-        auto issue = [&](uint4 (&t)[4][4], float &gv_, float &bv_, int64_t j) {
+        auto issue = [&](uint4 (&t)[16], float &gv_, float &bv_, int64_t j) {
             const int L = chunk_len(j);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int r = 16 * c + li;
-                const bf16 *rowp = gk + tok(j, r < L ? r : L - 1) * rowK + h * K;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) t[c][kk] = load_slots(rowp, kk, lg);
-            }
+            load_rows(t, gk + tok(j, 0) * rowK + h * K, rowK, L, lane);
             const int64_t tg = tok(j, lane < L ? lane : L - 1) * H + h;
             gv_ = a.g[tg];
             bv_ = a.beta[tg];
         };
-        auto store = [&](const uint4 (&t)[4][4], float gv_, float bv_, int64_t j) {
-            const int b3 = (int)(j % 3);
+        auto store = [&](const uint4 (&t)[16], float gv_, float bv_, int64_t j) {
+            const int b3 = (int)(j % 3), b2 = (int)(j & 1);
+            const int L = chunk_len(j);
+            store_rows(sm.kR[b3], t, lane);
+            // the k rows back in MFMA operand layout (this wave's own writes)
+            bf16x8 kt[4][4];
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    stv(sm.kR[b3], woff(16 * c + li, 4 * kk + lg), as8(t[c][kk]));
-            sm.graw[b3][lane] = gv_;   // raw: readers zero the rows past the chunk end
-            sm.braw[b3][lane] = bv_;
+                for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], woff(16 * c + li, 4 * kk + lg));
+            // rows past the chunk end get g = 0, beta = 0
+            sm.G2[b2][lane] = wave_cumsum(lane < L ? gv_ : 0.f, lane) * kLog2e;
+            sm.B[b2][lane] = lane < L ? bv_ : 0.f;
+            // factors at rows 16t + 4g + e (B layout rows) and 16t + j (B layout column)
+            f32x4 Gr4[4], Br4[4];
+            float Gc[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                Gr4[u] = *reinterpret_cast<const f32x4 *>(&sm.G2[b2][16 * u + 4 * lg]);
+                Br4[u] = *reinterpret_cast<const f32x4 *>(&sm.B[b2][16 * u + 4 * lg]);
+                Gc[u] = sm.G2[b2][16 * u + li];
+            }
+            // Gram k k^T from the k rows in registers: lane (j, g) element e of block
+            // (a, b) is k_{16a+4g+e} . k_{16b+j}.  Off-diagonal blocks leave as
+            // A = beta_r exp(G_r - G_s) k_r . k_s, diagonal blocks raw.
+            f32x4 acc[10];
+#pragma unroll
+            for (int i = 0; i < 10; ++i) acc[i] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                int i = 0;
+#pragma unroll
+                for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+                    for (int bb = 0; bb <= aa; ++bb, ++i) acc[i] = mma32(kt[aa][kk], kt[bb][kk], acc[i]);
+            }
+            int i = 0, idx = 0;
+#pragma unroll
+            for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+                for (int bb = 0; bb <= aa; ++bb, ++i) {
+                    if (aa > bb) {
+                        f32x4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[e] = Br4[aa][e] * ex2(Gr4[aa][e] - Gc[bb]) * acc[i][e];
+                        sm.ab[b2][idx++][lane] = __builtin_bit_cast(uint2, to4(v));
+                    } else {
+                        sm.ab[b2][6 + aa][lane] = __builtin_bit_cast(uint2, to4(acc[i]));
+                    }
+                }
         };
         issue(kA_, gA, bA, 0);
         for (int64_t it = -2; it < n_chunks; it += 2) {
@@ -441,50 +517,55 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             for (int64_t it = -2; it < n_chunks; ++it) lds_barrier();
             return;
         }
-        uint4 qA_[4][4], qB_[4][4];
-        auto issue = [&](uint4 (&t)[4][4], int64_t j) {
-            const int L = chunk_len(j);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int r = 16 * c + li;
-                const bf16 *rowp = gq + tok(j, r < L ? r : L - 1) * rowK + h * K;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) t[c][kk] = load_slots(rowp, kk, lg);
-            }
+        uint4 qA_[16], qB_[16];
+        auto issue = [&](uint4 (&t)[16], int64_t j) {
+            load_rows(t, gq + tok(j, 0) * rowK + h * K, rowK, chunk_len(j), lane);
         };
-        auto work = [&](const uint4 (&qa)[4][4], int64_t jn) {
+        auto work = [&](const uint4 (&qraw)[16], int64_t jn) {
             const int b2 = (int)(jn & 1), b3 = (int)(jn % 3);
             const int L = chunk_len(jn);
             const bf16 *kR = sm.kR[b3];
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) stv(sm.qR[b2], woff(16 * c + li, 4 * kk + lg), as8(qa[c][kk]));
-            const float G = wave_cumsum(lane < L ? sm.graw[b3][lane] : 0.f, lane);
-            sm.p2G[lane] = G;
+            store_rows(sm.qR[b2], qraw, lane);
+
+            const float *G2 = sm.G2[b2];
+            (void)L;
             // Gram block (b, a) of K Q^T: lane (j, g) element e holds
             // k_{16b+4g+e} . q_{16a+j} = raw attn[r = 16a + j][s = 16b + 4g + e]
+            f32x4 acc[10];
+#pragma unroll
+            for (int i = 0; i < 10; ++i) acc[i] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 qa[4], kb[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    qa[c] = ldv(sm.qR[b2], woff(16 * c + li, 4 * kk + lg));
+                    kb[c] = ldv(kR, woff(16 * c + li, 4 * kk + lg));
+                }
+                int i = 0;
+#pragma unroll
+                for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+                    for (int bb = 0; bb <= aa; ++bb, ++i) acc[i] = mma32(kb[bb], qa[aa], acc[i]);
+            }
             bf16x4 at[4][4];
+            {
+                int i = 0;
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                bf16x8 kb[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) kb[kk] = ldv(kR, woff(16 * bb + li, 4 * kk + lg));
-                const f32x4 Gs = *reinterpret_cast<const f32x4 *>(&sm.p2G[16 * bb + 4 * lg]);
-#pragma unroll
-                for (int aa = bb; aa < 4; ++aa) {
-                    f32x4 acc = zero4();
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) acc = mma32(kb[kk], as8(qa[aa][kk]), acc);
+                for (int aa = 0; aa < 4; ++aa) {
                     const int r = 16 * aa + li;
-                    const float Gr = sm.p2G[r];
-                    f32x4 v;
+                    const float Gr = G2[r];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = 16 * bb + 4 * lg + e;
-                        v[e] = (s <= r) ? __expf(Gr - Gs[e]) * acc[e] : 0.f;
+                    for (int bb = 0; bb <= aa; ++bb, ++i) {
+                        const f32x4 Gs = *reinterpret_cast<const f32x4 *>(&G2[16 * bb + 4 * lg]);
+                        f32x4 v;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int s_ = 16 * bb + 4 * lg + e;
+                            v[e] = (s_ <= r) ? ex2(Gr - Gs[e]) * acc[i][e] : 0.f;
+                        }
+                        at[aa][bb] = to4(v);
                     }
-                    at[aa][bb] = to4(v);
                 }
             }
             bf16x4 z4;
@@ -510,26 +591,29 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
         }
         return;
     }
+    // identity selectors (B operands) picking columns 0-15 / 16-31 of a 32-wide block
+    bf16x8 id0, id1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bool hit = 4 * lg + (e & 3) == li;
+        id0[e] = (bf16)((hit && (e >> 2) == 0) ? 1.f : 0.f);
+        id1[e] = (bf16)((hit && (e >> 2) == 1) ? 1.f : 0.f);
+    }
     for (int64_t it = -2; it < n_chunks; ++it) {
         const int64_t jn = it + 1;   // chunk being prepared
         if (jn >= 0 && jn < n_chunks) {
             const int b2 = (int)(jn & 1), b3 = (int)(jn % 3);
             const bf16 *kR = sm.kR[b3];
-            const int L = chunk_len(jn);
-            const float G = wave_cumsum(lane < L ? sm.graw[b3][lane] : 0.f, lane);
+            const float *G2 = sm.G2[b2];
             if (role == 3) {
                 // ---- per-row factors, and k^T by identity products
-                const float GC = __shfl(G, 63);
-                sm.gam[b2][lane] = __expf(G);
-                sm.kdec[b2][lane] = __expf(GC - G);
-                if (lane == 0) sm.gC[b2][0] = __expf(GC);
+                const float g2 = G2[lane];
+                sm.gam[b2][lane] = ex2(g2);
+                sm.kdec[b2][lane] = ex2(G2[63] - g2);
                 bf16 *kT = sm.kT[b2];
 #pragma unroll
                 for (int n = 0; n < 8; ++n) {
-                    bf16x8 id;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        id[e] = (bf16)(((e >> 2) == (n & 1) && 4 * lg + (e & 3) == li) ? 1.f : 0.f);
+                    const bf16x8 id = (n & 1) ? id1 : id0;
                     f32x4 d[4];
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
@@ -540,95 +624,73 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                         stv(kT, noff(16 * n + li, 4 * kk + lg), pack_pair(d[2 * kk], d[2 * kk + 1]));
                 }
             } else {
-                // ---- role 0: A = beta_r exp(G_r - G_s) k_r . k_s and T = (I + A)^{-1}
-                sm.p0G[lane] = G;
-                const float *braw = sm.braw[b3];
-                bf16x8 ka[4][4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) ka[c][kk] = ldv(kR, woff(16 * c + li, 4 * kk + lg));
-                // factors at rows 16t + 4g + e (B layout rows) and 16t + j (B layout column)
+                // ---- role 0: T = (I + A)^{-1}, A from the loader
+                const float *Bv = sm.B[b2];
                 f32x4 Gr4[4], Br4[4];
                 float Gc[4], Bc[4];
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    Gr4[t] = *reinterpret_cast<const f32x4 *>(&sm.p0G[16 * t + 4 * lg]);
-                    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&braw[16 * t + 4 * lg]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) Br4[t][e] = (16 * t + 4 * lg + e < L) ? b4[e] : 0.f;
-                    Gc[t] = sm.p0G[16 * t + li];
-                    Bc[t] = (16 * t + li < L) ? braw[16 * t + li] : 0.f;
+                    Gr4[t] = *reinterpret_cast<const f32x4 *>(&G2[16 * t + 4 * lg]);
+                    Br4[t] = *reinterpret_cast<const f32x4 *>(&Bv[16 * t + 4 * lg]);
+                    Gc[t] = G2[16 * t + li];
+                    Bc[t] = Bv[16 * t + li];
                 }
-                // Gram blocks; AB[a][b] (a > b): B layout of A_ab; NB / NA: B / A layout of A_aa
+                // AB[a][b] (a > b): B layout of A_ab; NB / NA: B / A layout of A_aa
                 bf16x4 AB[4][4], NB[4], NA[4];
+                {
+                    const uint2 *ab = &sm.ab[b2][0][lane];
+                    AB[1][0] = __builtin_bit_cast(bf16x4, ab[0 * 64]);
+                    AB[2][0] = __builtin_bit_cast(bf16x4, ab[1 * 64]);
+                    AB[2][1] = __builtin_bit_cast(bf16x4, ab[2 * 64]);
+                    AB[3][0] = __builtin_bit_cast(bf16x4, ab[3 * 64]);
+                    AB[3][1] = __builtin_bit_cast(bf16x4, ab[4 * 64]);
+                    AB[3][2] = __builtin_bit_cast(bf16x4, ab[5 * 64]);
 #pragma unroll
-                for (int aa = 0; aa < 4; ++aa)
+                    for (int aa = 0; aa < 4; ++aa) {
+                        // raw k_{16a+4g+e} . k_{16a+j} (symmetric): B layout entry
+                        // (r = 16a+4g+e, s = 16a+j) if s < r, A layout entry (r' = 16a+j,
+                        // s' = 16a+4g+e) if s' < r'
+                        const bf16x4 kk4 = __builtin_bit_cast(bf16x4, ab[(6 + aa) * 64]);
+                        f32x4 vb, va;
 #pragma unroll
-                    for (int bb = 0; bb <= aa; ++bb) {
-                        f32x4 acc = zero4();
-#pragma unroll
-                        for (int kk = 0; kk < 4; ++kk) acc = mma32(ka[aa][kk], ka[bb][kk], acc);
-                        if (aa > bb) {
-                            f32x4 v;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)   // r = 16aa+4g+e > s = 16bb+j
-                                v[e] = Br4[aa][e] * __expf(Gr4[aa][e] - Gc[bb]) * acc[e];
-                            AB[aa][bb] = to4(v);
-                        } else {
-                            f32x4 vb, va;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int x = 4 * lg + e;   // B layout row / A layout column
-                                const float ex = __expf(-fabsf(Gr4[aa][e] - Gc[aa]));
-                                vb[e] = (li < x) ? Br4[aa][e] * ex * acc[e] : 0.f;
-                                va[e] = (x < li) ? Bc[aa] * ex * acc[e] : 0.f;
-                            }
-                            NB[aa] = to4(vb);
-                            NA[aa] = to4(va);
+                        for (int e = 0; e < 4; ++e) {
+                            const int x = 4 * lg + e;
+                            const float ex = ex2(-fabsf(Gr4[aa][e] - Gc[aa]));
+                            const float kv = (float)kk4[e];
+                            vb[e] = (li < x) ? Br4[aa][e] * ex * kv : 0.f;
+                            va[e] = (x < li) ? Bc[aa] * ex * kv : 0.f;
                         }
+                        NB[aa] = to4(vb);
+                        NA[aa] = to4(va);
                     }
-                // diagonal inverses: P = B layout of T_aa, Q = A layout of T_aa
-                f32x4 Pf[4], Qf[4];
+                }
+                // diagonal inverses T_aa = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
+                // with N = A_aa (N^16 = 0).  P accumulates in B layout,
+                // P <- P + N^(2^k) P; powers are formed in both layouts
+                // (N^2 = N N in B layout, (N^2)^T = N^T N^T is the A layout).
+                // Q, the A layout of T_aa, is P transposed by an identity product.
+                bf16x4 i16;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) i16[e] = (bf16)((4 * lg + e == li) ? 1.f : 0.f);
+                f32x4 Qf[4];
                 bf16x4 P[4], Q[4];
 #pragma unroll
                 for (int aa = 0; aa < 4; ++aa) {
-                    auto plus_i = [&](const f32x4 &m) {
-                        f32x4 r = m;
+                    const bf16x4 n2b = to4(mma16(NA[aa], NB[aa], zero4()));
+                    const bf16x4 n2a = to4(mma16(NB[aa], NA[aa], zero4()));
+                    const bf16x4 n4b = to4(mma16(n2a, n2b, zero4()));
+                    const bf16x4 n4a = to4(mma16(n2b, n2a, zero4()));
+                    const bf16x4 n8a = to4(mma16(n4b, n4a, zero4()));
+                    f32x4 p;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) r[e] += (4 * lg + e == li) ? 1.f : 0.f;
-                        return to4(r);
-                    };
-                    const f32x4 n2b = mma16(NA[aa], NB[aa], zero4());
-                    const f32x4 n2a = mma16(NB[aa], NA[aa], zero4());
-                    const bf16x4 n2b_ = to4(n2b), n2a_ = to4(n2a);
-                    const f32x4 n4b = mma16(n2a_, n2b_, zero4());
-                    const f32x4 n4a = mma16(n2b_, n2a_, zero4());
-                    const bf16x4 n4b_ = to4(n4b), n4a_ = to4(n4a);
-                    const f32x4 n8b = mma16(n4a_, n4b_, zero4());
-                    const f32x4 n8a = mma16(n4b_, n4a_, zero4());
-                    const bf16x4 i2a = plus_i(n2a), i2b = plus_i(n2b);
-                    const bf16x4 i4a = plus_i(n4a), i4b = plus_i(n4b);
-                    const bf16x4 i8a = plus_i(n8a), i8b = plus_i(n8b);
-                    f32x4 p1, q1;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float id = (4 * lg + e == li) ? 1.f : 0.f;
-                        p1[e] = id - (float)NB[aa][e];
-                        q1[e] = id - (float)NA[aa][e];
-                    }
-                    f32x4 p = mma16(i2a, to4(p1), zero4());
-                    p = mma16(i4a, to4(p), zero4());
-                    p = mma16(i8a, to4(p), zero4());
-                    f32x4 q = mma16(i2b, to4(q1), zero4());
-                    q = mma16(i4b, to4(q), zero4());
-                    q = mma16(i8b, to4(q), zero4());
-                    Pf[aa] = p;
-                    Qf[aa] = q;
+                    for (int e = 0; e < 4; ++e) p[e] = ((4 * lg + e == li) ? 1.f : 0.f) - (float)NB[aa][e];
+                    p = mma16(n2a, to4(p), p);
+                    p = mma16(n4a, to4(p), p);
+                    p = mma16(n8a, to4(p), p);
                     P[aa] = to4(p);
-                    Q[aa] = to4(q);
+                    Qf[aa] = mma16(P[aa], i16, zero4());
+                    Q[aa] = to4(Qf[aa]);
                 }
-                (void)Pf;
                 // off-diagonal blocks of T^T (B layout) = blocks of T (A layout):
                 // U_ij = -(T^T)_ii sum_{k=i+1..j} (A^T)_ik (T^T)_kj,  i < j
                 f32x4 U01, U12, U23, U02, U13, U03;
