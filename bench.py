@@ -13,8 +13,10 @@ oracle timed on a bounded sample of the same workload on the host cores, and
 secondary measurements (monolithic scan, 4k sequence, packed batch, decode).
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -54,7 +56,51 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_scan_mfma_seq64k_4seg.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "chunked_gated_delta_gdn_amd", "csrc", f)
+                  for f in ("scan_mfma.hip", "dev_common.h", "gdn_internal.h")]
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    src = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    row = re.search(rf"traffic_bytes_per_launch\[{kernel}\]:\s*([0-9.e+]+)", text)
+    if not src or not row or src.group(1) != kernel_source_digest():
+        return None
+    return float(row.group(1))
+
+
+def copy_calibration(torch):
+    """A plain device copy of COPY_BYTES, read once and written once per launch
+    (elementwise negation, so it is an ordinary shader kernel that the counters see)."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": COPY_BYTES,
+                      "copy_calibration_bytes_written": COPY_BYTES, "launches": 3,
+                      "kernel_source_digest": kernel_source_digest()}), flush=True)
 
 
 class StreamTimer:
@@ -103,6 +149,9 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import chunked_gated_delta_gdn_amd as gdn
     from chunked_gated_delta_gdn_amd import binding
     from workloads import workload, make_decode_inputs
@@ -160,7 +209,7 @@ def main():
         roof = {"bound": "alu", "achieved": flops / t_dom / 1e12, "peak": PEAK_F32_VALU_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom)
     roof["kernel"] = dom
     roof["kernel_ms"] = kern[dom]
     roof["algorithmic_flops_per_launch"] = flops
@@ -252,16 +301,20 @@ def main():
                        nthreads=min(threads, nh))
         dt = max(time.perf_counter() - t0, 1e-6)
         ns = int(min(S, max(probe, probe * args.cpu_seconds / dt)))
+        # when the whole sequence is shorter than the target, repeat it
+        reps = max(1, int(round(args.cpu_seconds / (dt * ns / probe))))
         t0 = time.perf_counter()
-        oracle.forward(x.q[:, :ns, :nh], x.k[:, :ns, :nh], x.v[:, :ns, :nh],
-                       x.g[:, :ns, :nh], x.beta[:, :ns, :nh], h0=x.h0[:, :nh],
-                       nthreads=min(threads, nh))
+        for _ in range(reps):
+            oracle.forward(x.q[:, :ns, :nh], x.k[:, :ns, :nh], x.v[:, :ns, :nh],
+                           x.g[:, :ns, :nh], x.beta[:, :ns, :nh], h0=x.h0[:, :nh],
+                           nthreads=min(threads, nh))
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {
-            "value": ns * nh / H / dt, "unit": "tokens/s", "cores": min(threads, nh),
+            "value": reps * ns * nh / H / dt, "unit": "tokens/s", "cores": min(threads, nh),
             "kind": "oracle",
-            "sample": f"first {ns} tokens x {nh} of {H} heads of the 64k-token workload, fp64 "
-                      f"token recurrence, {dt:.1f} s; tokens/s counts whole {H}-head tokens",
+            "sample": f"first {ns} tokens x {nh} of {H} heads of the 64k-token workload, "
+                      f"{reps} pass(es), fp64 token recurrence, {dt:.1f} s; tokens/s counts "
+                      f"whole {H}-head tokens",
         }
     print(json.dumps(result), flush=True)
 
