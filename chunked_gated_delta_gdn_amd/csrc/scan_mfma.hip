@@ -138,21 +138,34 @@ struct Lds {
 // PR, section "Implementation"): their rows of A and of T diag(beta), and the
 // columns of T diag(beta), vanish, so a repeated k, q or v row only ever meets
 // a zero factor, and its outputs are not stored.
-__device__ __forceinline__ void load_rows(uint4 (&t)[16], const bf16 *base, int64_t row_stride,
+//
+// Loads go through a buffer resource whose base is row 0 of the chunk (wave
+// uniform, in scalar registers) with a 32-bit per-lane byte offset, so a load
+// needs one vector register for its address and no 64-bit vector arithmetic.
+// The host guarantees that 64 rows of any tensor span less than 2 GiB.
+constexpr uint32_t kRsrcWord3 = 0x00020000;   // gfx9 family: 32-bit raw data, no swizzle
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff,
+                                             (int)kRsrcWord3);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+}
+__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+__device__ __forceinline__ void load_rows(uint4 (&t)[16], const bf16 *base, uint32_t row_bytes,
                                           int L, int lane) {
-    if (L == 64) {
-        const bf16 *p = base + (int64_t)(lane >> 4) * row_stride + 8 * (lane & 15);
-        const int64_t step = 4 * row_stride;
+    const __amdgpu_buffer_rsrc_t r = rsrc(base);
+    // row offsets grow with the row, so clamping the offset clamps the row
+    const uint32_t lim = (uint32_t)(L - 1) * row_bytes;
+    const uint32_t own = (uint32_t)(lane >> 4) * row_bytes;
+    const uint32_t col = 16u * (lane & 15);
 #pragma unroll
-        for (int m = 0; m < 16; ++m) t[m] = *reinterpret_cast<const uint4 *>(p + m * step);
-    } else {
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int r = 4 * m + (lane >> 4);
-            t[m] = *reinterpret_cast<const uint4 *>(base + (int64_t)(r < L ? r : L - 1) * row_stride +
-                                                    8 * (lane & 15));
-        }
-    }
+    for (int m = 0; m < 16; ++m) t[m] = bload16(r, min(own + (uint32_t)(4 * m) * row_bytes, lim) + col, 0);
 }
 // Store rows loaded by load_rows into a wide tile: the 16 B of elements
 // 8s .. 8s+7 split into two 8 B halves that land on k-slots 16(s&1) + 4(s/2&1)
@@ -170,13 +183,22 @@ __device__ __forceinline__ void store_rows(bf16 *tile, const uint4 (&t)[16], int
     }
 }
 
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ float wave_cumsum(float x, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
+// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips):
+// shifts by 1, 2, 4, 8 within each row of 16 lanes (lanes whose source lies
+// before the row start read 0), then lane 15 of rows 0 and 2 is added to rows
+// 1 and 3, and lane 31 to rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_mov0(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                                 ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_cumsum(float x) {
+    x += dpp_mov0<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_mov0<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_mov0<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_mov0<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_mov0<0x142, 0xa>(x);   // row_bcast:15 into rows 1, 3
+    x += dpp_mov0<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
     return x;
 }
 
@@ -202,6 +224,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
     const int64_t n_chunks = (sp.t1 - sp.t0 + C - 1) / C;
     const int64_t rowK = (int64_t)H * K;   // element stride between tokens of q, k
     const int64_t rowV = (int64_t)H * V;
+    const uint32_t row_bytes_k = (uint32_t)(rowK * 2), row_bytes_v = (uint32_t)(rowV * 2);
 
     const bf16 *gq = static_cast<const bf16 *>(a.q);
     const bf16 *gk = static_cast<const bf16 *>(a.k);
@@ -237,6 +260,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
         // value rows of this wave's columns, A layout of a 16x16x16 operand:
         // lane (i, g) holds v[16 c + i][col 4g .. 4g+3]
         uint2 vA[NCT][4];
+        const uint32_t v_row = (uint32_t)li * row_bytes_v;
         auto load_v = [&](int64_t j) {
             if (is_M) {
 #pragma unroll
@@ -246,14 +270,13 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                 return;
             }
             const int L = chunk_len(j);
+            const __amdgpu_buffer_rsrc_t vr = rsrc(gv + tok(j, 0) * rowV + h * V + col_w);
+            const uint32_t lim = (uint32_t)(L - 1) * row_bytes_v;
 #pragma unroll
             for (int n = 0; n < NCT; ++n)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int r = 16 * c + li;
-                    vA[n][c] = *reinterpret_cast<const uint2 *>(
-                        gv + tok(j, r < L ? r : L - 1) * rowV + h * V + col_w + 16 * n + 4 * lg);
-                }
+                for (int c = 0; c < 4; ++c)
+                    vA[n][c] = bload8(vr, min(v_row + (uint32_t)(16 * c) * row_bytes_v, lim) + 2u * (16 * n + 4 * lg));
         };
         bf16x4 i16;   // identity, B operand of a 16x16x16 product
 #pragma unroll
@@ -443,10 +466,11 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
         float gA, bA, gB, bB;
         auto issue = [&](uint4 (&t)[16], float &gv_, float &bv_, int64_t j) {
             const int L = chunk_len(j);
-            load_rows(t, gk + tok(j, 0) * rowK + h * K, rowK, L, lane);
-            const int64_t tg = tok(j, lane < L ? lane : L - 1) * H + h;
-            gv_ = a.g[tg];
-            bv_ = a.beta[tg];
+            load_rows(t, gk + tok(j, 0) * rowK + h * K, row_bytes_k, L, lane);
+            const int64_t t0 = tok(j, 0) * H + h;
+            const uint32_t go = min((uint32_t)lane, (uint32_t)(L - 1)) * (uint32_t)(4 * H);
+            gv_ = bload4f(rsrc(a.g + t0), go);
+            bv_ = bload4f(rsrc(a.beta + t0), go);
         };
         auto store = [&](const uint4 (&t)[16], float gv_, float bv_, int64_t j) {
             const int b3 = (int)(j % 3), b2 = (int)(j & 1);
@@ -459,7 +483,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], woff(16 * c + li, 4 * kk + lg));
             // rows past the chunk end get g = 0, beta = 0
-            sm.G2[b2][lane] = wave_cumsum(lane < L ? gv_ : 0.f, lane) * kLog2e;
+            sm.G2[b2][lane] = wave_cumsum(lane < L ? gv_ : 0.f) * kLog2e;
             sm.B[b2][lane] = lane < L ? bv_ : 0.f;
             // factors at rows 16t + 4g + e (B layout rows) and 16t + j (B layout column)
             f32x4 Gr4[4], Br4[4];
@@ -519,7 +543,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
         }
         uint4 qA_[16], qB_[16];
         auto issue = [&](uint4 (&t)[16], int64_t j) {
-            load_rows(t, gq + tok(j, 0) * rowK + h * K, rowK, chunk_len(j), lane);
+            load_rows(t, gq + tok(j, 0) * rowK + h * K, row_bytes_k, chunk_len(j), lane);
         };
         auto work = [&](const uint4 (&qraw)[16], int64_t jn) {
             const int b2 = (int)(jn & 1), b3 = (int)(jn % 3);
