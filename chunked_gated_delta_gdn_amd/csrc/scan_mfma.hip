@@ -9,6 +9,12 @@
 //   h     <- gamma_C h + K^T diag(exp(G_C - G)) delta.
 // (w = T diag(beta gamma) K and u = T diag(beta) V are never formed: their
 // products with h are taken as T diag(beta) applied to V - diag(gamma) K h.)
+// With A = diag(beta) A0, where A0[r,s] = exp(G_r - G_s) k_r.k_s, the identity
+// (I + diag(beta) A0)^{-1} diag(beta) = diag(beta) (I + A0 diag(beta))^{-1}
+// moves beta off T: the kernel inverts T' = (I + A0 diag(beta))^{-1}, whose
+// strictly lower part scales columns by beta, and delta = diag(beta) T' R,
+// with the row factor beta folded into exp(G_C - G_r) for the state update
+// and applied to D before attn D for o.
 // In the carrying mode the state is X = [M | h], started from [I | 0], with
 // V = 0 on the M columns: the low-rank update M <- gamma M - k_tilde^T (w M)
 // of section "Implementation".
@@ -119,13 +125,14 @@ struct Lds {
     bf16 qR[2][C * K];      // q rows, wide tiles
     bf16 kT[2][K * C];      // k transposed, narrow tiles
     bf16 attn[2][C * C];    // attn, narrow tiles
-    bf16 tb[2][C * C];      // T diag(beta), narrow tiles
+    bf16 tb[2][C * C];      // T' = (I + A0 diag(beta))^{-1}, narrow tiles
     uint2 ab[2][10][64];    // loader -> wave 4, per lane 4 bf16: the 6 off-diagonal
                             // blocks of A (B layout) and the 4 raw diagonal blocks of k k^T
     float G2[2][C];         // cumulative log-decay of the chunk, times log2(e)
     float B[2][C];          // beta (zero past the chunk end)
     float gam[2][C];        // exp(G_r); gam[63] = exp(G_C)
-    float kdec[2][C];       // exp(G_C - G_r)
+    float kdec[2][C];       // exp(G_C - G_r) beta_r
+    float bet[2][C];        // beta, for the consumers (B is rewritten while they run)
 };
 
 // Whole rows of a 64 x 128 bf16 chunk tile: lane l of load m covers row
@@ -135,9 +142,11 @@ struct Lds {
 // Rows past the end of a ragged chunk repeat the last valid row instead of
 // being zeroed, so every load is unconditional and stays in flight.  This is
 // exact because those rows get g = 0 and beta = 0 (the padding of the MaxText
-// PR, section "Implementation"): their rows of A and of T diag(beta), and the
-// columns of T diag(beta), vanish, so a repeated k, q or v row only ever meets
-// a zero factor, and its outputs are not stored.
+// PR, section "Implementation"): the columns of A0 diag(beta) vanish there, so
+// T' has identity columns and, being lower triangular, no entries from such
+// rows into valid rows; delta = diag(beta) T' R is zero on them, and their
+// outputs are not stored.  A repeated k, q or v row therefore never reaches a
+// valid output.
 //
 // Loads go through a buffer resource whose base is row 0 of the chunk (wave
 // uniform, in scalar registers) with a 32-bit per-lane byte offset, so a load
@@ -290,6 +299,16 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             const int b2 = (int)(j & 1), b3 = (int)(j % 3);
             const int L = chunk_len(j);
             const bf16 *kR = sm.kR[b3];
+            // LDS operands are read in batches ahead of the products that use
+            // them (the scheduler would otherwise place each read just before its
+            // product and pay the LDS latency once per product).  Group
+            // barriers interleave the reads of the next phase with the current
+            // phase's products.
+            // -- k tiles of the chunk
+            bf16x8 ka[16];   // [kk][c]
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ka[i] = ldv(kR, woff(16 * (i & 3) + li, 4 * (i >> 2) + lg));
+            __builtin_amdgcn_sched_barrier(0);
             // value tiles of this chunk in B layout, then prefetch the next chunk's
             f32x4 Vt[NCT][4];
 #pragma unroll
@@ -298,113 +317,141 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                 for (int c = 0; c < 4; ++c)
                     Vt[n][c] = mma16(__builtin_bit_cast(bf16x4, vA[n][c]), i16, zero4());
             if (j + 1 < n_chunks) load_v(j + 1);
-
             bf16x8 hb[NCT][4];
 #pragma unroll
             for (int n = 0; n < NCT; ++n)
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) hb[n][kk] = pack_pair(X[n][2 * kk], X[n][2 * kk + 1]);
-            // Y = K X
+            // -- Y = K X, reading the q tiles meanwhile
             f32x4 Y[NCT][4];
 #pragma unroll
             for (int n = 0; n < NCT; ++n)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) Y[n][c] = zero4();
+            bf16x8 qa[16];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+            for (int i = 0; i < 16; ++i) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const bf16x8 ka = ldv(kR, woff(16 * c + li, 4 * kk + lg));
-#pragma unroll
-                    for (int n = 0; n < NCT; ++n) Y[n][c] = mma32(ka, hb[n][kk], Y[n][c]);
-                }
-            // O = Q X  (scaled by gamma_r below)
-            f32x4 O[4];
-            if (EMIT) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) O[c] = zero4();
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        O[c] = mma32(ldv(sm.qR[b2], woff(16 * c + li, 4 * kk + lg)), hb[0][kk], O[c]);
+                for (int n = 0; n < NCT; ++n) Y[n][i & 3] = mma32(ka[i], hb[n][i >> 2], Y[n][i & 3]);
+                if (EMIT) qa[i] = ldv(sm.qR[b2], woff(16 * (i & 3) + li, 4 * (i >> 2) + lg));
             }
-            // R = V - gamma (K X), packed as the operand reducing over the chunk
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NCT, 0);
+                if (EMIT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // -- O = Q X (emitting), reading T' and the decays meanwhile
             const float *gam = sm.gam[b2];
             const float *kdec = sm.kdec[b2];
+            f32x4 O[4];
+            bf16x8 ta[6];    // T' tiles (c, kk), kk <= c / 2
+            f32x4 gv[4], kv[4], bv[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) O[c] = zero4();
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (EMIT) O[i & 3] = mma32(qa[i], hb[0][i >> 2], O[i & 3]);
+                if (i < 6) {
+                    const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
+                    ta[i] = ldv(sm.tb[b2], noff(16 * c + li, 4 * kk + lg));
+                } else if (i < 10) {
+                    gv[i - 6] = *reinterpret_cast<const f32x4 *>(&gam[16 * (i - 6) + 4 * lg]);
+                } else if (i < 14) {
+                    kv[i - 10] = *reinterpret_cast<const f32x4 *>(&kdec[16 * (i - 10) + 4 * lg]);
+                }
+                if (EMIT && i >= 12)
+                    bv[i - 12] = *reinterpret_cast<const f32x4 *>(&sm.bet[b2][16 * (i - 12) + 4 * lg]);
+            }
+            if (EMIT) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (i >= 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // -- R = V - gamma (K X), packed as the operand reducing over the chunk
             bf16x8 R[NCT][2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const f32x4 g0 = *reinterpret_cast<const f32x4 *>(&gam[32 * kk + 4 * lg]);
-                const f32x4 g1 = *reinterpret_cast<const f32x4 *>(&gam[32 * kk + 16 + 4 * lg]);
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int n = 0; n < NCT; ++n) {
                     f32x4 lo, hi;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        lo[e] = Vt[n][2 * kk][e] - g0[e] * Y[n][2 * kk][e];
-                        hi[e] = Vt[n][2 * kk + 1][e] - g1[e] * Y[n][2 * kk + 1][e];
+                        lo[e] = Vt[n][2 * kk][e] - gv[2 * kk][e] * Y[n][2 * kk][e];
+                        hi[e] = Vt[n][2 * kk + 1][e] - gv[2 * kk + 1][e] * Y[n][2 * kk + 1][e];
                     }
                     R[n][kk] = pack_pair(lo, hi);
                 }
-            }
-            // delta = T diag(beta) R   (T lower triangular: row tile c needs kk <= c/2)
+            // -- D = T' R (delta = diag(beta) D), reading the attn tiles and k^T meanwhile
             f32x4 D[NCT][4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int n = 0; n < NCT; ++n)
 #pragma unroll
-                for (int n = 0; n < NCT; ++n) D[n][c] = zero4();
+                for (int c = 0; c < 4; ++c) D[n][c] = zero4();
+            bf16x8 at6[6], kt16[16];
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    if (kk <= (c >> 1)) {
-                        const bf16x8 ta = ldv(sm.tb[b2], noff(16 * c + li, 4 * kk + lg));
+            for (int i = 0; i < 6; ++i) {
+                const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
 #pragma unroll
-                        for (int n = 0; n < NCT; ++n) D[n][c] = mma32(ta, R[n][kk], D[n][c]);
-                    }
+                for (int n = 0; n < NCT; ++n) D[n][c] = mma32(ta[i], R[n][kk], D[n][c]);
+                if (EMIT) at6[i] = ldv(sm.attn[b2], noff(16 * c + li, 4 * kk + lg));
+                // k^T tiles m = 2t + kk for t = i
+                kt16[2 * i] = ldv(sm.kT[b2], noff(16 * i + li, lg));
+                kt16[2 * i + 1] = ldv(sm.kT[b2], noff(16 * i + li, 4 + lg));
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 12; i < 16; ++i) kt16[i] = ldv(sm.kT[b2], noff(16 * (i >> 1) + li, 4 * (i & 1) + lg));
             bf16x8 dk[NCT][2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const f32x4 k0 = *reinterpret_cast<const f32x4 *>(&kdec[32 * kk + 4 * lg]);
-                const f32x4 k1 = *reinterpret_cast<const f32x4 *>(&kdec[32 * kk + 16 + 4 * lg]);
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int n = 0; n < NCT; ++n) {
                     f32x4 lo, hi;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        lo[e] = k0[e] * D[n][2 * kk][e];
-                        hi[e] = k1[e] * D[n][2 * kk + 1][e];
+                        lo[e] = kv[2 * kk][e] * D[n][2 * kk][e];
+                        hi[e] = kv[2 * kk + 1][e] * D[n][2 * kk + 1][e];
                     }
                     dk[n][kk] = pack_pair(lo, hi);
                 }
-            }
             if (EMIT) {
+                // delta = diag(beta) D
                 bf16x8 db[2];
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) db[kk] = pack_pair(D[0][2 * kk], D[0][2 * kk + 1]);
+                for (int kk = 0; kk < 2; ++kk) {
+                    f32x4 lo, hi;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const f32x4 gr = *reinterpret_cast<const f32x4 *>(&gam[16 * c + 4 * lg]);
+                    for (int e = 0; e < 4; ++e) {
+                        lo[e] = bv[2 * kk][e] * D[0][2 * kk][e];
+                        hi[e] = bv[2 * kk + 1][e] * D[0][2 * kk + 1][e];
+                    }
+                    db[kk] = pack_pair(lo, hi);
+                }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) O[c][e] *= gr[e];
+                for (int c = 0; c < 4; ++c)
 #pragma unroll
-                    for (int kk = 0; kk < 2; ++kk)
-                        if (kk <= (c >> 1))
-                            O[c] = mma32(ldv(sm.attn[b2], noff(16 * c + li, 4 * kk + lg)), db[kk], O[c]);
+                    for (int e = 0; e < 4; ++e) O[c][e] *= gv[c][e];
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
+                    O[c] = mma32(at6[i], db[kk], O[c]);
                 }
             }
-            // X = gamma_C X + K^T diag(kdec) delta
+            // -- X = gamma_C X + K^T diag(exp(G_C - G)) delta = gamma_C X + K^T diag(kdec) D
             const float gc = gam[63];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
 #pragma unroll
                 for (int n = 0; n < NCT; ++n) X[n][t] *= gc;
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 ka = ldv(sm.kT[b2], noff(16 * t + li, 4 * kk + lg));
+                for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                    for (int n = 0; n < NCT; ++n) X[n][t] = mma32(ka, dk[n][kk], X[n][t]);
-                }
+                    for (int n = 0; n < NCT; ++n) X[n][t] = mma32(kt16[2 * t + kk], dk[n][kk], X[n][t]);
             }
             if (EMIT) {
                 // O tile c in B layout (lane (j, g): rows 4g..4g+3, column j) ->
@@ -486,17 +533,18 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             sm.G2[b2][lane] = wave_cumsum(lane < L ? gv_ : 0.f) * kLog2e;
             sm.B[b2][lane] = lane < L ? bv_ : 0.f;
             // factors at rows 16t + 4g + e (B layout rows) and 16t + j (B layout column)
-            f32x4 Gr4[4], Br4[4];
-            float Gc[4];
+            f32x4 Gr4[4];
+            float Gc[4], Bc[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 Gr4[u] = *reinterpret_cast<const f32x4 *>(&sm.G2[b2][16 * u + 4 * lg]);
-                Br4[u] = *reinterpret_cast<const f32x4 *>(&sm.B[b2][16 * u + 4 * lg]);
                 Gc[u] = sm.G2[b2][16 * u + li];
+                Bc[u] = sm.B[b2][16 * u + li];
             }
             // Gram k k^T from the k rows in registers: lane (j, g) element e of block
-            // (a, b) is k_{16a+4g+e} . k_{16b+j}.  Off-diagonal blocks leave as
-            // A = beta_r exp(G_r - G_s) k_r . k_s, diagonal blocks raw.
+            // (a, b) is k_{16a+4g+e} . k_{16b+j}.  Off-diagonal blocks leave
+            // negated, as -exp(G_r - G_s) k_r . k_s beta_s (the sign of the block
+            // recursion of T' folded in), diagonal blocks raw.
             f32x4 acc[10];
 #pragma unroll
             for (int i = 0; i < 10; ++i) acc[i] = zero4();
@@ -516,7 +564,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                     if (aa > bb) {
                         f32x4 v;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = Br4[aa][e] * ex2(Gr4[aa][e] - Gc[bb]) * acc[i][e];
+                        for (int e = 0; e < 4; ++e) v[e] = -Bc[bb] * ex2(Gr4[aa][e] - Gc[bb]) * acc[i][e];
                         sm.ab[b2][idx++][lane] = __builtin_bit_cast(uint2, to4(v));
                     } else {
                         sm.ab[b2][6 + aa][lane] = __builtin_bit_cast(uint2, to4(acc[i]));
@@ -633,7 +681,9 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                 // ---- per-row factors, and k^T by identity products
                 const float g2 = G2[lane];
                 sm.gam[b2][lane] = ex2(g2);
-                sm.kdec[b2][lane] = ex2(G2[63] - g2);
+                const float bl = sm.B[b2][lane];
+                sm.kdec[b2][lane] = ex2(G2[63] - g2) * bl;
+                sm.bet[b2][lane] = bl;
                 bf16 *kT = sm.kT[b2];
 #pragma unroll
                 for (int n = 0; n < 8; ++n) {
@@ -648,7 +698,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                         stv(kT, noff(16 * n + li, 4 * kk + lg), pack_pair(d[2 * kk], d[2 * kk + 1]));
                 }
             } else {
-                // ---- role 0: T = (I + A)^{-1}, A from the loader
+                // ---- role 0: T' = (I + A0 diag(beta))^{-1}, A0 diag(beta) from the loader
                 const float *Bv = sm.B[b2];
                 f32x4 Gr4[4], Br4[4];
                 float Gc[4], Bc[4];
@@ -659,7 +709,8 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                     Gc[t] = G2[16 * t + li];
                     Bc[t] = Bv[16 * t + li];
                 }
-                // AB[a][b] (a > b): B layout of A_ab; NB / NA: B / A layout of A_aa
+                // A' = A0 diag(beta).  AB[a][b] (a > b): B layout of -A'_ab; NB / NA:
+                // B / A layout of A'_aa
                 bf16x4 AB[4][4], NB[4], NA[4];
                 {
                     const uint2 *ab = &sm.ab[b2][0][lane];
@@ -681,8 +732,8 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                             const int x = 4 * lg + e;
                             const float ex = ex2(-fabsf(Gr4[aa][e] - Gc[aa]));
                             const float kv = (float)kk4[e];
-                            vb[e] = (li < x) ? Br4[aa][e] * ex * kv : 0.f;
-                            va[e] = (x < li) ? Bc[aa] * ex * kv : 0.f;
+                            vb[e] = (li < x) ? Bc[aa] * ex * kv : 0.f;
+                            va[e] = (x < li) ? Br4[aa][e] * ex * kv : 0.f;
                         }
                         NB[aa] = to4(vb);
                         NA[aa] = to4(va);
@@ -716,43 +767,36 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                     Q[aa] = to4(Qf[aa]);
                 }
                 // off-diagonal blocks of T^T (B layout) = blocks of T (A layout):
-                // U_ij = -(T^T)_ii sum_{k=i+1..j} (A^T)_ik (T^T)_kj,  i < j
+                // U_ij = -(T'^T)_ii sum_{k=i+1..j} (A'^T)_ik (T'^T)_kj,  i < j
+                // (the minus sign travels with AB)
                 f32x4 U01, U12, U23, U02, U13, U03;
                 {
                     f32x4 y = mma16(AB[1][0], Q[1], zero4());
-                    U01 = -mma16(P[0], to4(y), zero4());
+                    U01 = mma16(P[0], to4(y), zero4());
                     y = mma16(AB[2][1], Q[2], zero4());
-                    U12 = -mma16(P[1], to4(y), zero4());
+                    U12 = mma16(P[1], to4(y), zero4());
                     y = mma16(AB[3][2], Q[3], zero4());
-                    U23 = -mma16(P[2], to4(y), zero4());
+                    U23 = mma16(P[2], to4(y), zero4());
                     y = mma16(AB[1][0], to4(U12), zero4());
                     y = mma16(AB[2][0], Q[2], y);
-                    U02 = -mma16(P[0], to4(y), zero4());
+                    U02 = mma16(P[0], to4(y), zero4());
                     y = mma16(AB[2][1], to4(U23), zero4());
                     y = mma16(AB[3][1], Q[3], y);
-                    U13 = -mma16(P[1], to4(y), zero4());
+                    U13 = mma16(P[1], to4(y), zero4());
                     y = mma16(AB[1][0], to4(U13), zero4());
                     y = mma16(AB[2][0], to4(U23), y);
                     y = mma16(AB[3][0], Q[3], y);
-                    U03 = -mma16(P[0], to4(y), zero4());
+                    U03 = mma16(P[0], to4(y), zero4());
                 }
-                // T diag(beta): in the A layout of block (rb, cb), element e of lane
-                // (i, g) is column 16 cb + 4g + e -> scale by beta there.
-                auto sc = [&](const f32x4 &m, int cb) {
-                    f32x4 r;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) r[e] = m[e] * Br4[cb][e];
-                    return to4(r);
-                };
                 bf16x4 z4;
                 z4[0] = z4[1] = z4[2] = z4[3] = (bf16)0.f;
                 bf16 *tb = sm.tb[b2];
-                stv(tb, noff(0 + li, 0 + lg), join(sc(Qf[0], 0), z4));
-                stv(tb, noff(16 + li, 0 + lg), join(sc(U01, 0), sc(Qf[1], 1)));
-                stv(tb, noff(32 + li, 0 + lg), join(sc(U02, 0), sc(U12, 1)));
-                stv(tb, noff(32 + li, 4 + lg), join(sc(Qf[2], 2), z4));
-                stv(tb, noff(48 + li, 0 + lg), join(sc(U03, 0), sc(U13, 1)));
-                stv(tb, noff(48 + li, 4 + lg), join(sc(U23, 2), sc(Qf[3], 3)));
+                stv(tb, noff(0 + li, 0 + lg), join(to4(Qf[0]), z4));
+                stv(tb, noff(16 + li, 0 + lg), join(to4(U01), to4(Qf[1])));
+                stv(tb, noff(32 + li, 0 + lg), join(to4(U02), to4(U12)));
+                stv(tb, noff(32 + li, 4 + lg), join(to4(Qf[2]), z4));
+                stv(tb, noff(48 + li, 0 + lg), join(to4(U03), to4(U13)));
+                stv(tb, noff(48 + li, 4 + lg), join(to4(U23), to4(Qf[3])));
             }
         }
         lds_barrier();
