@@ -241,6 +241,20 @@ def main():
         steps2 = max(3, args.steps // 4)
         ms1, k1 = time_steps(torch, mono, steps2, 2)
         extra["monolithic_64k"] = {"tokens_per_s": tokens / (ms1 * 1e-3), "ms": ms1}
+
+        # per-chunk WY preparation (gdn_chunk_prepare) of the same workload: an HBM
+        # stream of k, v, g, beta in and w, u out
+        def prep(timer):
+            tm = timer.around if timer else (lambda _n, f: f())
+            return tm("chunk_prepare", lambda: gdn.chunk_prepare(k, v, g, beta, chunk_size=C))
+        ms_p, k_p = time_steps(torch, prep, steps2, 2)
+        prep_bytes = th * ((K + V) * 2 + 8 + (K + V) * 2)
+        t_p = k_p["chunk_prepare"] * 1e-3
+        extra["chunk_prepare_64k"] = {
+            "tokens_per_s": tokens / (ms_p * 1e-3), "ms": ms_p,
+            "roofline": {"bound": "hbm", "achieved": prep_bytes / t_p / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": prep_bytes / t_p / 1e9 / PEAK_HBM_GBS},
+        }
         del q, k, v, g, beta, h0
         torch.cuda.empty_cache()
 

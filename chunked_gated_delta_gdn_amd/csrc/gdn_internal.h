@@ -94,6 +94,8 @@ struct ComposeArgs {
 hipError_t launch_scan(int K, int V, int C, int dtype, bool carry, const ScanArgs &a,
                        hipStream_t s);
 hipError_t launch_prepare(int K, int V, int C, int dtype, const PrepArgs &a, hipStream_t s);
+bool mfma_prepare_available(int K, int V, int C, int dtype);
+hipError_t launch_prepare_mfma(const PrepArgs &a, hipStream_t s);
 hipError_t launch_decode(int K, int V, int dtype, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_compose(int K, int V, const ComposeArgs &a, hipStream_t s);
 

@@ -345,6 +345,7 @@ hipError_t launch_scan_generic(int K, int V, int C, int dtype, bool carry, const
 }
 
 hipError_t launch_prepare(int K, int V, int C, int dtype, const PrepArgs &a, hipStream_t s) {
+    if (mfma_prepare_available(K, V, C, dtype)) return launch_prepare_mfma(a, s);
     if (K == 32 && V == 32 && C == 16) {
         return dtype == GDN_F32 ? launch_prepare_t<float, 32, 32, 16>(a, s)
                                 : launch_prepare_t<bf16_t, 32, 32, 16>(a, s);

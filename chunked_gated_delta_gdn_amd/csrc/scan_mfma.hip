@@ -51,74 +51,14 @@
 //    across them.
 #include "dev_common.h"
 #include "gdn_internal.h"
+#include "mfma_tile.h"
 
 namespace gdn {
 namespace {
+using namespace mfma;
 
 constexpr int K = 128, V = 128, C = 64;
 constexpr int NT = 512;   // 8 waves
-
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short short4v __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mma32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16(const bf16x4 &a, const bf16x4 &b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4v, a),
-                                                       __builtin_bit_cast(short4v, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// Round to bf16 (nearest even) two values at a time into one 32-bit register
-// (a single v_cvt_pk_bf16_f32), then reinterpret: converting whole bf16
-// vectors that feed an MFMA otherwise costs a conversion and a permute per
-// element.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
-}
-__device__ __forceinline__ bf16x4 to4(const f32x4 &x) {
-    return __builtin_bit_cast(bf16x4, make_uint2(cvt2(x[0], x[1]), cvt2(x[2], x[3])));
-}
-__device__ __forceinline__ bf16x8 join(const bf16x4 &lo, const bf16x4 &hi) {
-    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
-    return __builtin_bit_cast(bf16x8, make_uint4(l.x, l.y, h.x, h.y));
-}
-// Two accumulator tiles (rows 0-15, 16-31 of a 32-row block) -> the bf16
-// operand that reduces over those 32 rows.
-__device__ __forceinline__ bf16x8 pack_pair(const f32x4 &lo, const f32x4 &hi) {
-    return __builtin_bit_cast(bf16x8, make_uint4(cvt2(lo[0], lo[1]), cvt2(lo[2], lo[3]),
-                                                 cvt2(hi[0], hi[1]), cvt2(hi[2], hi[3])));
-}
-__device__ __forceinline__ bf16x8 as8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
-
-// Decays are kept as log2 values, so exp(G_r - G_s) is one v_exp_f32.
-constexpr float kLog2e = 1.4426950408889634f;
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Workgroup barrier that waits for this wave's LDS operations only (global
-// loads issued earlier stay in flight).
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// LDS tiles.  A row of a "wide" tile holds 128 bf16 (16 chunks of 16 B), a row
-// of a "narrow" tile 64 bf16 (8 chunks).  Chunk q of row r lives at chunk
-// q ^ (r & 7).  Within a 32-element block, chunk g holds the k-slots
-// 8g .. 8g+7, i.e. logical elements 4g .. 4g+3 and 16+4g .. 16+4g+3.
-__device__ __forceinline__ int woff(int r, int q) { return r * 256 + ((q ^ (r & 7)) << 4); }
-__device__ __forceinline__ int noff(int r, int q) { return r * 128 + ((q ^ (r & 7)) << 4); }
-__device__ __forceinline__ bf16x8 ldv(const bf16 *base, int byte_off) {
-    return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(base) + byte_off);
-}
-__device__ __forceinline__ void stv(bf16 *base, int byte_off, const bf16x8 &v) {
-    *reinterpret_cast<bf16x8 *>(reinterpret_cast<char *>(base) + byte_off) = v;
-}
 
 struct Lds {
     bf16 kR[3][C * K];      // k rows, wide tiles (loader writes j+2, producers read j+1, consumers j)
@@ -134,82 +74,6 @@ struct Lds {
     float kdec[2][C];       // exp(G_C - G_r) beta_r
     float bet[2][C];        // beta, for the consumers (B is rewritten while they run)
 };
-
-// Whole rows of a 64 x 128 bf16 chunk tile: lane l of load m covers row
-// 4m + l/16, elements 8 (l % 16) .. +7 (16 B), so one instruction reads four
-// full rows.
-//
-// Rows past the end of a ragged chunk repeat the last valid row instead of
-// being zeroed, so every load is unconditional and stays in flight.  This is
-// exact because those rows get g = 0 and beta = 0 (the padding of the MaxText
-// PR, section "Implementation"): the columns of A0 diag(beta) vanish there, so
-// T' has identity columns and, being lower triangular, no entries from such
-// rows into valid rows; delta = diag(beta) T' R is zero on them, and their
-// outputs are not stored.  A repeated k, q or v row therefore never reaches a
-// valid output.
-//
-// Loads go through a buffer resource whose base is row 0 of the chunk (wave
-// uniform, in scalar registers) with a 32-bit per-lane byte offset, so a load
-// needs one vector register for its address and no 64-bit vector arithmetic.
-// The host guarantees that 64 rows of any tensor span less than 2 GiB.
-constexpr uint32_t kRsrcWord3 = 0x00020000;   // gfx9 family: 32-bit raw data, no swizzle
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff,
-                                             (int)kRsrcWord3);
-}
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
-}
-__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
-}
-__device__ __forceinline__ void load_rows(uint4 (&t)[16], const bf16 *base, uint32_t row_bytes,
-                                          int L, int lane) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(base);
-    // row offsets grow with the row, so clamping the offset clamps the row
-    const uint32_t lim = (uint32_t)(L - 1) * row_bytes;
-    const uint32_t own = (uint32_t)(lane >> 4) * row_bytes;
-    const uint32_t col = 16u * (lane & 15);
-#pragma unroll
-    for (int m = 0; m < 16; ++m) t[m] = bload16(r, min(own + (uint32_t)(4 * m) * row_bytes, lim) + col, 0);
-}
-// Store rows loaded by load_rows into a wide tile: the 16 B of elements
-// 8s .. 8s+7 split into two 8 B halves that land on k-slots 16(s&1) + 4(s/2&1)
-// and +8 of their 32-element block, i.e. chunks 4(s/4) + 2(s&1) and the next
-// one, at byte 8 (s/2 & 1) within the chunk.
-__device__ __forceinline__ void store_rows(bf16 *tile, const uint4 (&t)[16], int lane) {
-    const int s = lane & 15;
-    const int q0 = 4 * (s >> 2) + 2 * (s & 1), within = 8 * ((s >> 1) & 1);
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int r = 4 * m + (lane >> 4);
-        char *b = reinterpret_cast<char *>(tile);
-        *reinterpret_cast<uint2 *>(b + woff(r, q0) + within) = make_uint2(t[m].x, t[m].y);
-        *reinterpret_cast<uint2 *>(b + woff(r, q0 + 1) + within) = make_uint2(t[m].z, t[m].w);
-    }
-}
-
-// Inclusive prefix sum over the 64 lanes with DPP moves (no LDS round trips):
-// shifts by 1, 2, 4, 8 within each row of 16 lanes (lanes whose source lies
-// before the row start read 0), then lane 15 of rows 0 and 2 is added to rows
-// 1 and 3, and lane 31 to rows 2 and 3.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_mov0(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                                 ROWS, 0xf, false));
-}
-__device__ __forceinline__ float wave_cumsum(float x) {
-    x += dpp_mov0<0x111, 0xf>(x);   // row_shr:1
-    x += dpp_mov0<0x112, 0xf>(x);   // row_shr:2
-    x += dpp_mov0<0x114, 0xf>(x);   // row_shr:4
-    x += dpp_mov0<0x118, 0xf>(x);   // row_shr:8
-    x += dpp_mov0<0x142, 0xa>(x);   // row_bcast:15 into rows 1, 3
-    x += dpp_mov0<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
-    return x;
-}
 
 template <bool EMIT>
 __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_units) {
@@ -532,44 +396,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             // rows past the chunk end get g = 0, beta = 0
             sm.G2[b2][lane] = wave_cumsum(lane < L ? gv_ : 0.f) * kLog2e;
             sm.B[b2][lane] = lane < L ? bv_ : 0.f;
-            // factors at rows 16t + 4g + e (B layout rows) and 16t + j (B layout column)
-            f32x4 Gr4[4];
-            float Gc[4], Bc[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                Gr4[u] = *reinterpret_cast<const f32x4 *>(&sm.G2[b2][16 * u + 4 * lg]);
-                Gc[u] = sm.G2[b2][16 * u + li];
-                Bc[u] = sm.B[b2][16 * u + li];
-            }
-            // Gram k k^T from the k rows in registers: lane (j, g) element e of block
-            // (a, b) is k_{16a+4g+e} . k_{16b+j}.  Off-diagonal blocks leave
-            // negated, as -exp(G_r - G_s) k_r . k_s beta_s (the sign of the block
-            // recursion of T' folded in), diagonal blocks raw.
-            f32x4 acc[10];
-#pragma unroll
-            for (int i = 0; i < 10; ++i) acc[i] = zero4();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                int i = 0;
-#pragma unroll
-                for (int aa = 0; aa < 4; ++aa)
-#pragma unroll
-                    for (int bb = 0; bb <= aa; ++bb, ++i) acc[i] = mma32(kt[aa][kk], kt[bb][kk], acc[i]);
-            }
-            int i = 0, idx = 0;
-#pragma unroll
-            for (int aa = 0; aa < 4; ++aa)
-#pragma unroll
-                for (int bb = 0; bb <= aa; ++bb, ++i) {
-                    if (aa > bb) {
-                        f32x4 v;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = -Bc[bb] * ex2(Gr4[aa][e] - Gc[bb]) * acc[i][e];
-                        sm.ab[b2][idx++][lane] = __builtin_bit_cast(uint2, to4(v));
-                    } else {
-                        sm.ab[b2][6 + aa][lane] = __builtin_bit_cast(uint2, to4(acc[i]));
-                    }
-                }
+            gram_to_ab(kt, sm.G2[b2], sm.B[b2], sm.ab[b2], lane);
         };
         issue(kA_, gA, bA, 0);
         for (int64_t it = -2; it < n_chunks; it += 2) {
@@ -698,105 +525,8 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                         stv(kT, noff(16 * n + li, 4 * kk + lg), pack_pair(d[2 * kk], d[2 * kk + 1]));
                 }
             } else {
-                // ---- role 0: T' = (I + A0 diag(beta))^{-1}, A0 diag(beta) from the loader
-                const float *Bv = sm.B[b2];
-                f32x4 Gr4[4], Br4[4];
-                float Gc[4], Bc[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    Gr4[t] = *reinterpret_cast<const f32x4 *>(&G2[16 * t + 4 * lg]);
-                    Br4[t] = *reinterpret_cast<const f32x4 *>(&Bv[16 * t + 4 * lg]);
-                    Gc[t] = G2[16 * t + li];
-                    Bc[t] = Bv[16 * t + li];
-                }
-                // A' = A0 diag(beta).  AB[a][b] (a > b): B layout of -A'_ab; NB / NA:
-                // B / A layout of A'_aa
-                bf16x4 AB[4][4], NB[4], NA[4];
-                {
-                    const uint2 *ab = &sm.ab[b2][0][lane];
-                    AB[1][0] = __builtin_bit_cast(bf16x4, ab[0 * 64]);
-                    AB[2][0] = __builtin_bit_cast(bf16x4, ab[1 * 64]);
-                    AB[2][1] = __builtin_bit_cast(bf16x4, ab[2 * 64]);
-                    AB[3][0] = __builtin_bit_cast(bf16x4, ab[3 * 64]);
-                    AB[3][1] = __builtin_bit_cast(bf16x4, ab[4 * 64]);
-                    AB[3][2] = __builtin_bit_cast(bf16x4, ab[5 * 64]);
-#pragma unroll
-                    for (int aa = 0; aa < 4; ++aa) {
-                        // raw k_{16a+4g+e} . k_{16a+j} (symmetric): B layout entry
-                        // (r = 16a+4g+e, s = 16a+j) if s < r, A layout entry (r' = 16a+j,
-                        // s' = 16a+4g+e) if s' < r'
-                        const bf16x4 kk4 = __builtin_bit_cast(bf16x4, ab[(6 + aa) * 64]);
-                        f32x4 vb, va;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int x = 4 * lg + e;
-                            const float ex = ex2(-fabsf(Gr4[aa][e] - Gc[aa]));
-                            const float kv = (float)kk4[e];
-                            vb[e] = (li < x) ? Bc[aa] * ex * kv : 0.f;
-                            va[e] = (x < li) ? Br4[aa][e] * ex * kv : 0.f;
-                        }
-                        NB[aa] = to4(vb);
-                        NA[aa] = to4(va);
-                    }
-                }
-                // diagonal inverses T_aa = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
-                // with N = A_aa (N^16 = 0).  P accumulates in B layout,
-                // P <- P + N^(2^k) P; powers are formed in both layouts
-                // (N^2 = N N in B layout, (N^2)^T = N^T N^T is the A layout).
-                // Q, the A layout of T_aa, is P transposed by an identity product.
-                bf16x4 i16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) i16[e] = (bf16)((4 * lg + e == li) ? 1.f : 0.f);
-                f32x4 Qf[4];
-                bf16x4 P[4], Q[4];
-#pragma unroll
-                for (int aa = 0; aa < 4; ++aa) {
-                    const bf16x4 n2b = to4(mma16(NA[aa], NB[aa], zero4()));
-                    const bf16x4 n2a = to4(mma16(NB[aa], NA[aa], zero4()));
-                    const bf16x4 n4b = to4(mma16(n2a, n2b, zero4()));
-                    const bf16x4 n4a = to4(mma16(n2b, n2a, zero4()));
-                    const bf16x4 n8a = to4(mma16(n4b, n4a, zero4()));
-                    f32x4 p;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) p[e] = ((4 * lg + e == li) ? 1.f : 0.f) - (float)NB[aa][e];
-                    p = mma16(n2a, to4(p), p);
-                    p = mma16(n4a, to4(p), p);
-                    p = mma16(n8a, to4(p), p);
-                    P[aa] = to4(p);
-                    Qf[aa] = mma16(P[aa], i16, zero4());
-                    Q[aa] = to4(Qf[aa]);
-                }
-                // off-diagonal blocks of T^T (B layout) = blocks of T (A layout):
-                // U_ij = -(T'^T)_ii sum_{k=i+1..j} (A'^T)_ik (T'^T)_kj,  i < j
-                // (the minus sign travels with AB)
-                f32x4 U01, U12, U23, U02, U13, U03;
-                {
-                    f32x4 y = mma16(AB[1][0], Q[1], zero4());
-                    U01 = mma16(P[0], to4(y), zero4());
-                    y = mma16(AB[2][1], Q[2], zero4());
-                    U12 = mma16(P[1], to4(y), zero4());
-                    y = mma16(AB[3][2], Q[3], zero4());
-                    U23 = mma16(P[2], to4(y), zero4());
-                    y = mma16(AB[1][0], to4(U12), zero4());
-                    y = mma16(AB[2][0], Q[2], y);
-                    U02 = mma16(P[0], to4(y), zero4());
-                    y = mma16(AB[2][1], to4(U23), zero4());
-                    y = mma16(AB[3][1], Q[3], y);
-                    U13 = mma16(P[1], to4(y), zero4());
-                    y = mma16(AB[1][0], to4(U13), zero4());
-                    y = mma16(AB[2][0], to4(U23), y);
-                    y = mma16(AB[3][0], Q[3], y);
-                    U03 = mma16(P[0], to4(y), zero4());
-                }
-                bf16x4 z4;
-                z4[0] = z4[1] = z4[2] = z4[3] = (bf16)0.f;
-                bf16 *tb = sm.tb[b2];
-                stv(tb, noff(0 + li, 0 + lg), join(to4(Qf[0]), z4));
-                stv(tb, noff(16 + li, 0 + lg), join(to4(U01), to4(Qf[1])));
-                stv(tb, noff(32 + li, 0 + lg), join(to4(U02), to4(U12)));
-                stv(tb, noff(32 + li, 4 + lg), join(to4(Qf[2]), z4));
-                stv(tb, noff(48 + li, 0 + lg), join(to4(U03), to4(U13)));
-                stv(tb, noff(48 + li, 4 + lg), join(to4(U23), to4(Qf[3])));
+                // ---- role 0: T' = (I + A0 diag(beta))^{-1} from the loader's Gram tiles
+                invert_tprime(sm.ab[b2], G2, sm.B[b2], sm.tb[b2], nullptr, lane);
             }
         }
         lds_barrier();

@@ -208,6 +208,45 @@ def test_chunk_prepare_wy_factors(wl, tol):
     assert ew <= tol and eu <= tol
 
 
+def test_chunk_prepare_wy_seq4k():
+    """WY factors of the whole 4k-token, 16-head workload (the matrix-core
+    preparation path at full size)."""
+    x = workload(1)
+    d = device_inputs(x)
+    wy = gdn.chunk_prepare(d["k"], d["v"], d["g"], d["beta"], chunk_size=x.C)
+    w, u = gdn.split_wy(wy, d["k"], d["v"], x.C)
+    w_ref, u_ref = oracle.chunk_wy(x.k, x.v, x.g, x.beta, x.C)
+    w = w.float().cpu().numpy().reshape(w_ref.shape)
+    u = u.float().cpu().numpy().reshape(u_ref.shape)
+    ew, eu = rel_err(w, w_ref), rel_err(u, u_ref)
+    say(f"  wy {x.name}: err(w)={ew:.3e} err(u)={eu:.3e}")
+    assert ew <= TOL["bf16"] and eu <= TOL["bf16"]
+
+
+def test_chunk_prepare_packed_ragged_and_empty():
+    """WY factors of unpadded packed sequences (ragged tails, one empty), in
+    global chunk order, at K = V = 128."""
+    x = make_inputs(12, 1, 400, 2, 128, 128, 64, "bf16", 0.0, name="prep-packed")
+    cu = np.array([0, 70, 70, 200, 329, 400], dtype=np.int32)
+    d = device_inputs(x)
+    wy = gdn.chunk_prepare(d["k"], d["v"], d["g"], d["beta"], chunk_size=64, cu_seqlens=cu)
+    w, u = gdn.split_wy(wy, d["k"], d["v"], 64)
+    ws, us = [], []
+    for n in range(len(cu) - 1):
+        a, b = int(cu[n]), int(cu[n + 1])
+        if b == a:
+            continue
+        wr, ur = oracle.chunk_wy(x.k[:, a:b], x.v[:, a:b], x.g[:, a:b], x.beta[:, a:b], 64)
+        ws.append(wr[0])
+        us.append(ur[0])
+    w_ref, u_ref = np.concatenate(ws), np.concatenate(us)
+    assert w.shape == w_ref.shape and u.shape == u_ref.shape
+    w, u = w.float().cpu().numpy(), u.float().cpu().numpy()
+    ew, eu = rel_err(w, w_ref), rel_err(u, u_ref)
+    say(f"  wy packed cu={cu.tolist()}: err(w)={ew:.3e} err(u)={eu:.3e}")
+    assert ew <= TOL["bf16"] and eu <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("wl", [0, 1])
 def test_carry_pairs_match_transition(wl):
     x = workload(wl, H=2, S=512, decay="slow")
