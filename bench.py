@@ -242,6 +242,21 @@ def main():
         ms1, k1 = time_steps(torch, mono, steps2, 2)
         extra["monolithic_64k"] = {"tokens_per_s": tokens / (ms1 * 1e-3), "ms": ms1}
 
+        # the same three-phase pass with the WY factors prepared once and reused by
+        # both passes (the pages' own arrangement), for comparison
+        def seg_wy(timer):
+            tm = timer.around if timer else (lambda _n, f: f())
+            wy = tm("chunk_prepare", lambda: gdn.chunk_prepare(k, v, g, beta, chunk_size=C))
+            M, U = tm("scan_carry", lambda: gdn.scan_carry(k, v, g, beta, wy=wy, chunk_size=C,
+                                                           n_segments=R))
+            h_in, _ = tm("segment_compose", lambda: gdn.segment_compose(M, U, h0))
+            return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h_in, wy=wy,
+                                                         chunk_size=C, n_segments=R))
+        if R > 1:
+            ms_w, k_w = time_steps(torch, seg_wy, steps2, 2)
+            extra["segmented_64k_wy_reused"] = {"tokens_per_s": tokens / (ms_w * 1e-3), "ms": ms_w,
+                                                "kernels_ms": k_w}
+
         # per-chunk WY preparation (gdn_chunk_prepare) of the same workload: an HBM
         # stream of k, v, g, beta in and w, u out
         def prep(timer):

@@ -60,7 +60,9 @@ using namespace mfma;
 constexpr int K = 128, V = 128, C = 64;
 constexpr int NT = 512;   // 8 waves
 
-struct Lds {
+template <bool WY> struct Lds;
+// WY factors recomputed in the kernel
+template <> struct Lds<false> {
     bf16 kR[3][C * K];      // k rows, wide tiles (loader writes j+2, producers read j+1, consumers j)
     bf16 qR[2][C * K];      // q rows, wide tiles
     bf16 kT[2][K * C];      // k transposed, narrow tiles
@@ -74,12 +76,26 @@ struct Lds {
     float kdec[2][C];       // exp(G_C - G_r) beta_r
     float bet[2][C];        // beta, for the consumers (B is rewritten while they run)
 };
+// WY factors read from a workspace: w rows replace the k rows as the
+// consumers' operand, there is no Gram or T'; k is read only by producers, so
+// two buffers suffice
+template <> struct Lds<true> {
+    bf16 kR[2][C * K];      // k rows (loader writes j+2, producers read j+1)
+    bf16 qR[2][C * K];      // q rows
+    bf16 wR[2][C * K];      // w rows (w wave writes j+1, consumers read j)
+    bf16 kT[2][K * C];      // k transposed
+    bf16 attn[2][C * C];    // attn
+    float G2[2][C];         // cumulative log2-decay
+    float gam[2][C];        // exp(G_r)
+    float kdec[2][C];       // exp(G_C - G_r)
+};
 
-template <bool EMIT>
+template <bool EMIT, bool WY>
 __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_units) {
     constexpr int CPW = EMIT ? 16 : 32;   // state columns per consumer wave
     constexpr int NCT = CPW / 16;
-    __shared__ Lds sm;
+    __shared__ Lds<WY> sm;
+    auto kslot = [](int64_t j) { return WY ? (int)(j & 1) : (int)(j % 3); };
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -142,6 +158,17 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                     for (int c = 0; c < 4; ++c) vA[n][c] = make_uint2(0, 0);
                 return;
             }
+            if (WY) {
+                // u rows of the chunk (every row present; zero past the chunk end)
+                const __amdgpu_buffer_rsrc_t ur = rsrc(static_cast<const bf16 *>(a.wy_u) +
+                                                       ((sp.chunk0 + j) * H + h) * (int64_t)C * V + col_w);
+#pragma unroll
+                for (int n = 0; n < NCT; ++n)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        vA[n][c] = bload8(ur, (uint32_t)(16 * c + li) * (V * 2) + 2u * (16 * n + 4 * lg));
+                return;
+            }
             const int L = chunk_len(j);
             const __amdgpu_buffer_rsrc_t vr = rsrc(gv + tok(j, 0) * rowV + h * V + col_w);
             const uint32_t lim = (uint32_t)(L - 1) * row_bytes_v;
@@ -160,9 +187,12 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
         lds_barrier();   // iteration -2: k of chunk 0 loaded
         lds_barrier();   // iteration -1: chunk 0 prepared
         for (int64_t j = 0; j < n_chunks; ++j) {
-            const int b2 = (int)(j & 1), b3 = (int)(j % 3);
+            const int b2 = (int)(j & 1);
             const int L = chunk_len(j);
-            const bf16 *kR = sm.kR[b3];
+            // operand of Y = K X (recomputing) or of Y = w X (WY given)
+            const bf16 *kR;
+            if constexpr (WY) kR = sm.wR[b2];
+            else kR = sm.kR[kslot(j)];
             // LDS operands are read in batches ahead of the products that use
             // them (the scheduler would otherwise place each read just before its
             // product and pay the LDS latency once per product).  Group
@@ -218,50 +248,63 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                 if (EMIT) O[i & 3] = mma32(qa[i], hb[0][i >> 2], O[i & 3]);
                 if (i < 6) {
                     const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
-                    ta[i] = ldv(sm.tb[b2], noff(16 * c + li, 4 * kk + lg));
+                    if constexpr (!WY) ta[i] = ldv(sm.tb[b2], noff(16 * c + li, 4 * kk + lg));
                 } else if (i < 10) {
                     gv[i - 6] = *reinterpret_cast<const f32x4 *>(&gam[16 * (i - 6) + 4 * lg]);
                 } else if (i < 14) {
                     kv[i - 10] = *reinterpret_cast<const f32x4 *>(&kdec[16 * (i - 10) + 4 * lg]);
                 }
-                if (EMIT && i >= 12)
-                    bv[i - 12] = *reinterpret_cast<const f32x4 *>(&sm.bet[b2][16 * (i - 12) + 4 * lg]);
+                if constexpr (EMIT && !WY)
+                    if (i >= 12) bv[i - 12] = *reinterpret_cast<const f32x4 *>(&sm.bet[b2][16 * (i - 12) + 4 * lg]);
             }
             if (EMIT) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    if (i >= 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (i < 14 && (!WY || i >= 6)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (!WY && i >= 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            // -- R = V - gamma (K X), packed as the operand reducing over the chunk
-            bf16x8 R[NCT][2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int n = 0; n < NCT; ++n) {
-                    f32x4 lo, hi;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        lo[e] = Vt[n][2 * kk][e] - gv[2 * kk][e] * Y[n][2 * kk][e];
-                        hi[e] = Vt[n][2 * kk + 1][e] - gv[2 * kk + 1][e] * Y[n][2 * kk + 1][e];
-                    }
-                    R[n][kk] = pack_pair(lo, hi);
-                }
-            // -- D = T' R (delta = diag(beta) D), reading the attn tiles and k^T meanwhile
             f32x4 D[NCT][4];
+            if constexpr (WY) {
+                // -- delta = u - w X (the row factors are inside u and w)
 #pragma unroll
-            for (int n = 0; n < NCT; ++n)
+                for (int n = 0; n < NCT; ++n)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) D[n][c] = zero4();
+                    for (int c = 0; c < 4; ++c) D[n][c] = Vt[n][c] - Y[n][c];
+            } else {
+                // -- R = V - gamma (K X), packed as the operand reducing over the chunk
+                bf16x8 R[NCT][2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int n = 0; n < NCT; ++n) {
+                        f32x4 lo, hi;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            lo[e] = Vt[n][2 * kk][e] - gv[2 * kk][e] * Y[n][2 * kk][e];
+                            hi[e] = Vt[n][2 * kk + 1][e] - gv[2 * kk + 1][e] * Y[n][2 * kk + 1][e];
+                        }
+                        R[n][kk] = pack_pair(lo, hi);
+                    }
+                // -- D = T' R (delta = diag(beta) D)
+#pragma unroll
+                for (int n = 0; n < NCT; ++n)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) D[n][c] = zero4();
+#pragma unroll
+                for (int i = 0; i < 6; ++i) {
+                    const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
+#pragma unroll
+                    for (int n = 0; n < NCT; ++n) D[n][c] = mma32(ta[i], R[n][kk], D[n][c]);
+                }
+            }
+            // reading the attn tiles and k^T meanwhile
             bf16x8 at6[6], kt16[16];
 #pragma unroll
             for (int i = 0; i < 6; ++i) {
                 const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
-#pragma unroll
-                for (int n = 0; n < NCT; ++n) D[n][c] = mma32(ta[i], R[n][kk], D[n][c]);
                 if (EMIT) at6[i] = ldv(sm.attn[b2], noff(16 * c + li, 4 * kk + lg));
                 // k^T tiles m = 2t + kk for t = i
                 kt16[2 * i] = ldv(sm.kT[b2], noff(16 * i + li, lg));
@@ -284,15 +327,15 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                     dk[n][kk] = pack_pair(lo, hi);
                 }
             if (EMIT) {
-                // delta = diag(beta) D
+                // delta = diag(beta) D (recomputing) or D (WY given)
                 bf16x8 db[2];
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     f32x4 lo, hi;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        lo[e] = bv[2 * kk][e] * D[0][2 * kk][e];
-                        hi[e] = bv[2 * kk + 1][e] * D[0][2 * kk + 1][e];
+                        lo[e] = WY ? D[0][2 * kk][e] : bv[2 * kk][e] * D[0][2 * kk][e];
+                        hi[e] = WY ? D[0][2 * kk + 1][e] : bv[2 * kk + 1][e] * D[0][2 * kk + 1][e];
                     }
                     db[kk] = pack_pair(lo, hi);
                 }
@@ -384,19 +427,21 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             bv_ = bload4f(rsrc(a.beta + t0), go);
         };
         auto store = [&](const uint4 (&t)[16], float gv_, float bv_, int64_t j) {
-            const int b3 = (int)(j % 3), b2 = (int)(j & 1);
+            const int b3 = kslot(j), b2 = (int)(j & 1);
             const int L = chunk_len(j);
             store_rows(sm.kR[b3], t, lane);
-            // the k rows back in MFMA operand layout (this wave's own writes)
-            bf16x8 kt[4][4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], woff(16 * c + li, 4 * kk + lg));
             // rows past the chunk end get g = 0, beta = 0
             sm.G2[b2][lane] = wave_cumsum(lane < L ? gv_ : 0.f) * kLog2e;
-            sm.B[b2][lane] = lane < L ? bv_ : 0.f;
-            gram_to_ab(kt, sm.G2[b2], sm.B[b2], sm.ab[b2], lane);
+            if constexpr (!WY) {
+                // the k rows back in MFMA operand layout (this wave's own writes)
+                bf16x8 kt[4][4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], woff(16 * c + li, 4 * kk + lg));
+                sm.B[b2][lane] = lane < L ? bv_ : 0.f;
+                gram_to_ab(kt, sm.G2[b2], sm.B[b2], sm.ab[b2], lane);
+            }
         };
         issue(kA_, gA, bA, 0);
         for (int64_t it = -2; it < n_chunks; it += 2) {
@@ -421,7 +466,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             load_rows(t, gq + tok(j, 0) * rowK + h * K, row_bytes_k, chunk_len(j), lane);
         };
         auto work = [&](const uint4 (&qraw)[16], int64_t jn) {
-            const int b2 = (int)(jn & 1), b3 = (int)(jn % 3);
+            const int b2 = (int)(jn & 1), b3 = kslot(jn);
             const int L = chunk_len(jn);
             const bf16 *kR = sm.kR[b3];
             store_rows(sm.qR[b2], qraw, lane);
@@ -490,6 +535,29 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
         }
         return;
     }
+    if (WY && role == 0) {
+        // -------- w rows of the WY workspace (one chunk ahead) -> wR --------
+        uint4 wA_[16], wB_[16];
+        auto issue = [&](uint4 (&t)[16], int64_t j) {
+            load_rows(t, static_cast<const bf16 *>(a.wy_w) + ((sp.chunk0 + j) * H + h) * (int64_t)C * K, K * 2, C,
+                      lane);
+        };
+        auto put = [&](const uint4 (&t)[16], int64_t jn) {
+            if constexpr (WY) store_rows(sm.wR[jn & 1], t, lane);
+        };
+        issue(wA_, 0);
+        lds_barrier();   // iteration -2
+        for (int64_t it = -1; it < n_chunks; it += 2) {
+            issue(wB_, clampj(it + 2));
+            if (it + 1 < n_chunks) put(wA_, it + 1);
+            lds_barrier();
+            if (it + 1 >= n_chunks) break;
+            issue(wA_, clampj(it + 3));
+            if (it + 2 < n_chunks) put(wB_, it + 2);
+            lds_barrier();
+        }
+        return;
+    }
     // identity selectors (B operands) picking columns 0-15 / 16-31 of a 32-wide block
     bf16x8 id0, id1;
 #pragma unroll
@@ -501,16 +569,20 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
     for (int64_t it = -2; it < n_chunks; ++it) {
         const int64_t jn = it + 1;   // chunk being prepared
         if (jn >= 0 && jn < n_chunks) {
-            const int b2 = (int)(jn & 1), b3 = (int)(jn % 3);
+            const int b2 = (int)(jn & 1), b3 = kslot(jn);
             const bf16 *kR = sm.kR[b3];
             const float *G2 = sm.G2[b2];
             if (role == 3) {
                 // ---- per-row factors, and k^T by identity products
                 const float g2 = G2[lane];
                 sm.gam[b2][lane] = ex2(g2);
-                const float bl = sm.B[b2][lane];
-                sm.kdec[b2][lane] = ex2(G2[63] - g2) * bl;
-                sm.bet[b2][lane] = bl;
+                if constexpr (WY) {
+                    sm.kdec[b2][lane] = ex2(G2[63] - g2);
+                } else {
+                    const float bl = sm.B[b2][lane];
+                    sm.kdec[b2][lane] = ex2(G2[63] - g2) * bl;
+                    sm.bet[b2][lane] = bl;
+                }
                 bf16 *kT = sm.kT[b2];
 #pragma unroll
                 for (int n = 0; n < 8; ++n) {
@@ -526,7 +598,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                 }
             } else {
                 // ---- role 0: T' = (I + A0 diag(beta))^{-1} from the loader's Gram tiles
-                invert_tprime(sm.ab[b2], G2, sm.B[b2], sm.tb[b2], nullptr, lane);
+                if constexpr (!WY) invert_tprime(sm.ab[b2], G2, sm.B[b2], sm.tb[b2], nullptr, lane);
             }
         }
         lds_barrier();
@@ -542,17 +614,17 @@ bool mfma_scan_available(int K_, int V_, int C_, int dtype) {
 hipError_t launch_scan_mfma(int K_, int V_, int C_, int dtype, bool carry, const ScanArgs &a,
                             hipStream_t s, bool *handled) {
     *handled = false;
-    if (!mfma_scan_available(K_, V_, C_, dtype) || a.wy_w != nullptr) return hipSuccess;
+    if (!mfma_scan_available(K_, V_, C_, dtype)) return hipSuccess;
     *handled = true;
     const int64_t units = (int64_t)a.n_chains * a.H;
     if (units == 0) return hipSuccess;
     const int64_t grid = ((units + 7) / 8) * 16;   // two column halves, 8 ids apart
-    if (carry)
-        hipLaunchKernelGGL(scan_mfma_kernel<false>, dim3((unsigned)grid), dim3(NT), 0, s, a,
-                           (int)units);
-    else
-        hipLaunchKernelGGL(scan_mfma_kernel<true>, dim3((unsigned)grid), dim3(NT), 0, s, a,
-                           (int)units);
+    const dim3 g((unsigned)grid), b(NT);
+    const bool wy = a.wy_w != nullptr;
+    if (carry && wy) hipLaunchKernelGGL((scan_mfma_kernel<false, true>), g, b, 0, s, a, (int)units);
+    else if (carry) hipLaunchKernelGGL((scan_mfma_kernel<false, false>), g, b, 0, s, a, (int)units);
+    else if (wy) hipLaunchKernelGGL((scan_mfma_kernel<true, true>), g, b, 0, s, a, (int)units);
+    else hipLaunchKernelGGL((scan_mfma_kernel<true, false>), g, b, 0, s, a, (int)units);
     return hipGetLastError();
 }
 

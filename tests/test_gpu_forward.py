@@ -78,6 +78,26 @@ def test_seq4k_bf16_reuse_wy():
     check(x, o, hT, o_ref, h_ref, what="wy reused")
 
 
+def test_seq4k_bf16_reuse_wy_slow_decay_segments():
+    """WY factors reused by the carrying and emitting passes, with slow decay so
+    the segment transitions M are far from zero."""
+    x = workload(1, H=4, decay="slow")
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, n_segments=4, reuse_wy=True)
+    check(x, o, hT, o_ref, h_ref, what="wy reused, 4 segments")
+
+
+def test_packed_ragged_reuse_wy():
+    """WY factors reused on unpadded packed sequences at K = V = 128."""
+    rng = np.random.default_rng(13)
+    x = make_inputs(13, 1, 500, 2, 128, 128, 64, "bf16", 0.0, name="packed-ragged-wy")
+    x.cu_seqlens = np.array([0, 100, 100, 231, 420, 500], dtype=np.int32)
+    x.h0 = rng.standard_normal((5, 2, 128, 128)).astype(np.float32) * 0.02
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, reuse_wy=True)
+    check(x, o[0], hT, o_ref, h_ref, what="wy reused")
+
+
 def test_seq64k_four_segments_sampled_heads():
     """The 64k-token, 32-head, 4-segment workload in the launch configuration the
     benchmark times; the oracle recomputes two sampled heads in full."""
