@@ -4,8 +4,11 @@
 A step is one full forward over the 64k-token, 32-head, K = V = 128 sequence
 split into 4 contiguous segments: the carrying zero-state scan (phase 1), the
 exclusive segment scan (phase 2) and the emitting scan (phase 3), i.e. every
-entry point of the chunked path, on bf16 inputs with fp32 state.  Inputs are
-seeded synthetic tensors already resident in HBM when timing starts.
+entry point of the chunked path, on bf16 inputs with fp32 state, scheduled by
+forward_segmented (segment 0 emitted from the initial state beside the
+carrying pass of the middle segments; no carrying pass for segment 0's M or for
+the last segment).  Inputs are seeded synthetic tensors already resident in HBM
+when timing starts.
 
 Prints one JSON line: tokens/s of that step, the roofline of its dominant
 kernel (HIP events around that kernel's launches on its stream), the fp64 CPU
@@ -83,7 +86,7 @@ def measured_traffic(kernel):
     except OSError:
         return None
     src = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
-    row = re.search(rf"traffic_bytes_per_launch\[{kernel}\]:\s*([0-9.e+]+)", text)
+    row = re.search(rf"traffic_bytes_per_launch\[{re.escape(kernel)}\]:\s*([0-9.e+]+)", text)
     if not src or not row or src.group(1) != kernel_source_digest():
         return None
     return float(row.group(1))
@@ -110,12 +113,13 @@ class StreamTimer:
         self.torch = torch
         self.marks = {}
 
-    def around(self, name, fn):
+    def around(self, name, fn, stream=None):
         t = self.torch
+        st = stream if stream is not None else t.cuda.current_stream()
         a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
-        a.record(t.cuda.current_stream())
+        a.record(st)
         out = fn()
-        b.record(t.cuda.current_stream())
+        b.record(st)
         self.marks.setdefault(name, []).append((a, b))
         return out
 
@@ -176,31 +180,33 @@ def main():
     backend = binding.gdn_scan_backend(gdn.problem_for(k, v, C, n_segments=R))
 
     def seg_step(timer):
-        tm = timer.around if timer else (lambda _n, f: f())
+        tm = timer.around if timer else (lambda _n, f, _s=None: f())
         if R == 1:
             return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h0, chunk_size=C))
-        M, U = tm("scan_carry", lambda: gdn.scan_carry(k, v, g, beta, chunk_size=C, n_segments=R))
-        h_in, _ = tm("segment_compose", lambda: gdn.segment_compose(M, U, h0))
-        return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h_in, chunk_size=C,
-                                                     n_segments=R))
+        return gdn.forward_segmented(q, k, v, g, beta, h0=h0, chunk_size=C, n_segments=R, timer=tm)
 
     log(f"bench: timing {args.steps} steps after {args.warmup} warm-up steps (R={R})")
     ms, kern = time_steps(torch, seg_step, args.steps, args.warmup)
     tokens = B * S
     value = tokens / (ms * 1e-3)
 
-    # dominant kernel and its roofline
+    # dominant kernel and its roofline.  Tokens per launch: segment 0 (first
+    # emitting pass), segments 1 .. R-2 (carrying pass), segments 1 .. R-1 (emitting)
     dom = max(kern, key=kern.get)
     th = tokens * H
-    if dom == "scan_emit":
-        flops = flops_per_token_head(C, K, V) * th
-        nbytes = bytes_per_token_head(K, V, 2, 2) * th + (R + 1) * H * K * V * 4
+    bnd = gdn.segment_bounds(S, C, R)
+    n_tok = {"scan_emit_first": bnd[1], "scan_carry": bnd[R - 1] - bnd[1],
+             "scan_emit": S - bnd[1] if R > 1 else S}
+    n_seg = {"scan_emit_first": 1, "scan_carry": R - 2, "scan_emit": max(R - 1, 1)}
+    if dom in ("scan_emit", "scan_emit_first"):
+        flops = flops_per_token_head(C, K, V) * n_tok[dom] * H
+        nbytes = bytes_per_token_head(K, V, 2, 2) * n_tok[dom] * H + (n_seg[dom] + 1) * H * K * V * 4
     elif dom == "scan_carry":
-        flops = carry_flops_per_token_head(C, K, V) * th
-        nbytes = (K + V) * 2 * th + 8 * th + R * H * K * (K + V) * 4
+        flops = carry_flops_per_token_head(C, K, V) * n_tok[dom] * H
+        nbytes = ((K + V) * 2 + 8) * n_tok[dom] * H + (R - 2) * H * K * (K + V) * 4
     else:
-        flops = 2 * R * H * K * K * V
-        nbytes = R * H * (K * K + 2 * K * V) * 4
+        flops = 2 * (R - 2) * H * K * K * V
+        nbytes = (R - 2) * H * (K * K + 2 * K * V) * 4
     t_dom = kern[dom] * 1e-3
     if backend == 1:
         roof = {"bound": "mfma", "achieved": flops / t_dom / 1e12, "peak": PEAK_BF16_TFLOPS,
@@ -209,8 +215,12 @@ def main():
         roof = {"bound": "alu", "achieved": flops / t_dom / 1e12, "peak": PEAK_F32_VALU_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom)
+    roof["traffic"] = measured_traffic(f"{dom}@{n_tok.get(dom, S)}x{H}")
     roof["kernel"] = dom
+    # workgroups of the launch: two per (segment, head); the chip runs one per CU
+    wgs = 2 * n_seg.get(dom, R) * H
+    roof["workgroups"] = wgs
+    roof["frac_of_occupied_cus"] = roof["frac"] * 256 / min(wgs, 256)
     roof["kernel_ms"] = kern[dom]
     roof["algorithmic_flops_per_launch"] = flops
     roof["algorithmic_bytes_per_launch"] = nbytes
@@ -222,7 +232,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; q,k L2-normalised, beta sigmoid, g -softplus)",
         "config": {"workload": f"B{B} H{H} S{S} K{K} V{V} C{C}, {R} contiguous segments "
-                               "(three-phase pass), bf16 q/k/v/o, fp32 g/beta/state",
+                               "(three-phase pass, overlapped schedule), bf16 q/k/v/o, "
+                               "fp32 g/beta/state",
                    "B": B, "H": H, "S": S, "K": K, "V": V, "C": C, "segments": R,
                    "parallelism": "1 GPU"},
         "roofline": roof,
@@ -241,6 +252,19 @@ def main():
         steps2 = max(3, args.steps // 4)
         ms1, k1 = time_steps(torch, mono, steps2, 2)
         extra["monolithic_64k"] = {"tokens_per_s": tokens / (ms1 * 1e-3), "ms": ms1}
+
+        # the plain three-phase pass: carrying pass over every segment, scan, emitting
+        # pass over every segment
+        def plain(timer):
+            tm = timer.around if timer else (lambda _n, f: f())
+            M, U = tm("scan_carry", lambda: gdn.scan_carry(k, v, g, beta, chunk_size=C, n_segments=R))
+            h_in, _ = tm("segment_compose", lambda: gdn.segment_compose(M, U, h0))
+            return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h_in, chunk_size=C,
+                                                         n_segments=R))
+        if R > 1:
+            ms_pl, k_pl = time_steps(torch, plain, steps2, 2)
+            extra["segmented_64k_plain_schedule"] = {"tokens_per_s": tokens / (ms_pl * 1e-3),
+                                                     "ms": ms_pl, "kernels_ms": k_pl}
 
         # the same three-phase pass with the WY factors prepared once and reused by
         # both passes (the pages' own arrangement), for comparison

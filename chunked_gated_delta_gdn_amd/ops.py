@@ -13,6 +13,7 @@ import torch
 from . import binding as _b
 
 __all__ = ["problem_for", "chunk_prepare", "scan_emit", "scan_carry", "segment_compose",
+           "segment_bounds", "forward_segmented",
            "decode_step", "forward"]
 
 
@@ -171,13 +172,98 @@ def decode_step(q, k, v, g, beta, state, out=None):
     return o
 
 
+def segment_bounds(S, chunk_size, n_segments, seg_starts=None):
+    """Token offsets of the segments and the end: the library's split when
+    seg_starts is None (chunk r*n_chunks//R starts segment r)."""
+    if seg_starts is not None:
+        return [int(x) for x in seg_starts] + [S]
+    nc = -(-S // chunk_size)
+    return [(r * nc // n_segments) * chunk_size for r in range(n_segments)] + [S]
+
+
+_side = {}
+
+
+def _side_stream(dev):
+    s = _side.get(dev)
+    if s is None:
+        s = torch.cuda.Stream(device=dev)   # default priority
+        _side[dev] = s
+    return s
+
+
+def _untimed(_name, fn, _stream=None):
+    return fn()
+
+
+def forward_segmented(q, k, v, g, beta, h0=None, chunk_size=64, n_segments=2, seg_starts=None,
+                      output_final_state=True, timer=_untimed):
+    """The three-phase segment pass on one sequence (B == 1), without its two
+    redundant pieces: segment 0 starts from the true initial state, so it needs
+    no carried M and is emitted directly (its final state is the state entering
+    segment 1); the last segment is emitted from its incoming state, so it needs
+    no carrying pass.  The emitting pass of segment 0 runs on a second stream
+    beside the carrying pass of segments 1 .. R-2; then the segment scan seeded
+    with segment 0's final state, then the emitting pass of segments 1 .. R-1.
+
+    ``timer(name, fn, stream)`` wraps each launch (for per-kernel timing)."""
+    B, S, H, K, V = _check_inputs(q, k, v, g, beta)
+    if B != 1:
+        raise ValueError("forward_segmented takes one sequence (B == 1)")
+    R = n_segments
+    _b.gdn_validate(problem_for(k, v, chunk_size, None, R, seg_starts))
+    dev = k.device
+    if h0 is not None:
+        _need(h0, "h0", (B, H, K, V), torch.float32, dev)
+    bnd = segment_bounds(S, chunk_size, R, seg_starts)
+    s1, sl = bnd[1], bnd[R - 1]
+    o = torch.empty((B, S, H, V), dtype=k.dtype, device=dev)
+    main, side = torch.cuda.current_stream(dev), _side_stream(dev)
+    sl0 = slice(0, s1)
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        _, h1 = timer("scan_emit_first", lambda: scan_emit(
+            q[:, sl0], k[:, sl0], v[:, sl0], g[:, sl0], beta[:, sl0], h_in=h0,
+            chunk_size=chunk_size, out=o[:, sl0]), side)
+    if R > 2:
+        mid = slice(s1, sl)
+        M, U = timer("scan_carry", lambda: scan_carry(
+            k[:, mid], v[:, mid], g[:, mid], beta[:, mid], chunk_size=chunk_size,
+            n_segments=R - 2, seg_starts=[b - s1 for b in bnd[1:R - 1]]), main)
+    main.wait_stream(side)
+    h1.record_stream(main)
+    if R > 2:
+        # states entering segments 1 .. R-1: the scan's outputs, then its final state
+        h_all = torch.empty((R - 1, B, H, K, V), dtype=torch.float32, device=dev)
+        timer("segment_compose", lambda: _b.gdn_segment_compose(
+            R - 2, B, H, K, V, _addr(M), _addr(U), _addr(h1), _addr(h_all), _addr(h_all[R - 2]),
+            _stream(dev)), main)
+    else:
+        h_all = h1
+    rest = slice(s1, S)
+    _, hT = timer("scan_emit", lambda: scan_emit(
+        q[:, rest], k[:, rest], v[:, rest], g[:, rest], beta[:, rest], h_in=h_all,
+        chunk_size=chunk_size, n_segments=R - 1, seg_starts=[b - s1 for b in bnd[1:R]],
+        output_final_state=output_final_state, out=o[:, rest]), main)
+    return o, hT
+
+
 def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segments=1,
-            seg_starts=None, reuse_wy=False, output_final_state=True):
+            seg_starts=None, reuse_wy=False, output_final_state=True, schedule="auto"):
     """Chunked gated delta rule forward: returns (o, final state or None).
 
     n_segments > 1 runs the three-phase segment pass; reuse_wy prepares the WY
     factors once (``gdn_chunk_prepare``) and hands them to both scans instead of
-    recomputing them inside each scan."""
+    recomputing them inside each scan.  schedule="auto" uses forward_segmented
+    for one sequence with recomputed WY factors, "plain" always runs the full
+    carrying pass over every segment."""
+    if schedule not in ("auto", "plain"):
+        raise ValueError(f"unknown schedule {schedule!r}")
+    if (schedule == "auto" and n_segments > 1 and cu_seqlens is None and not reuse_wy
+            and k.shape[0] == 1):
+        return forward_segmented(q, k, v, g, beta, h0=h0, chunk_size=chunk_size,
+                                 n_segments=n_segments, seg_starts=seg_starts,
+                                 output_final_state=output_final_state)
     wy = chunk_prepare(k, v, g, beta, chunk_size, cu_seqlens) if reuse_wy else None
     if n_segments == 1:
         return scan_emit(q, k, v, g, beta, h_in=h0, wy=wy, chunk_size=chunk_size,

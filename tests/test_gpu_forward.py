@@ -71,6 +71,27 @@ def test_seq4k_bf16_segments_slow_decay(R):
     check(x, o, hT, o_ref, h_ref, what=f"slow R={R}")
 
 
+@pytest.mark.parametrize("schedule", ["auto", "plain"])
+@pytest.mark.parametrize("R", [2, 3, 4])
+def test_seq4k_bf16_segment_schedules(schedule, R):
+    """Both schedules of the segment pass (overlapped: segment 0 emitted from h0
+    beside the carrying pass of the middle segments; plain: carrying pass over
+    every segment), slow decay so M matters."""
+    x = workload(1, H=4, decay="slow")
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, n_segments=R, schedule=schedule)
+    check(x, o, hT, o_ref, h_ref, what=f"R={R} schedule={schedule}")
+
+
+@pytest.mark.parametrize("schedule", ["auto", "plain"])
+def test_tiny_f32_segment_schedules_uneven(schedule):
+    """fp32 vector-ALU path, explicit uneven segment starts, both schedules."""
+    x = workload(0, decay="slow")
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, n_segments=3, seg_starts=[0, 48, 208], schedule=schedule)
+    check(x, o, hT, o_ref, h_ref, what=f"starts 0,48,208 schedule={schedule}")
+
+
 def test_seq4k_bf16_reuse_wy():
     x = workload(1, H=4)
     o_ref, h_ref = oracle_forward(x)
