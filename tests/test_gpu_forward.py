@@ -314,3 +314,73 @@ def test_segment_compose_matches_oracle_scan():
     ref_in, ref_fin = oracle.exclusive_scan(M, U, h0)
     assert rel_err(h_in.cpu().numpy(), ref_in) <= 1e-5
     assert rel_err(h_fin.cpu().numpy(), ref_fin) <= 1e-5
+
+
+# ---- limits and degenerate cases ------------------------------------------------------------
+
+def test_packed_max_sequences():
+    """GDN_MAX_SEQS (256) packed sequences of mixed lengths, some empty, some
+    shorter than a chunk, at K = V = 128."""
+    rng = np.random.default_rng(21)
+    lens = rng.integers(0, 150, size=256)
+    lens[::17] = 0
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = make_inputs(21, 1, int(cu[-1]), 2, 128, 128, 64, "bf16", 0.0, name="packed-256")
+    x.cu_seqlens = cu
+    x.h0 = rng.standard_normal((256, 2, 128, 128)).astype(np.float32) * 0.02
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x)
+    check(x, o[0], hT, o_ref, h_ref, what=f"256 sequences, {int(cu[-1])} tokens")
+    for n in np.nonzero(lens == 0)[0]:
+        np.testing.assert_array_equal(hT[n], x.h0[n])
+
+
+def test_too_many_sequences_rejected():
+    x = make_inputs(22, 1, 257, 1, 32, 32, 16, "f32", 0.0)
+    d = device_inputs(x)
+    cu = np.arange(258, dtype=np.int32)
+    with pytest.raises(ValueError):
+        gdn.scan_emit(d["q"], d["k"], d["v"], d["g"], d["beta"], chunk_size=16, cu_seqlens=cu)
+
+
+@pytest.mark.parametrize("schedule", ["auto", "plain"])
+def test_max_segments(schedule):
+    """GDN_MAX_SEGMENTS (64) one-chunk segments, slow decay."""
+    x = make_inputs(23, 1, 64 * 64, 2, 128, 128, 64, "bf16", 0.02, decay="slow", name="64-segments")
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, n_segments=64, schedule=schedule)
+    check(x, o, hT, o_ref, h_ref, what=f"R=64 schedule={schedule}")
+
+
+def test_batch_of_two_with_segments():
+    """B = 2 sequences, each cut into 3 segments (the plain schedule)."""
+    x = make_inputs(24, 2, 1000, 2, 128, 128, 64, "bf16", 0.02, decay="slow", name="B2-segments")
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, n_segments=3)
+    check(x, o, hT, o_ref, h_ref, what="B=2 R=3")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_beta_zero_is_pure_decay(dtype):
+    """beta = 0: the state only decays, o_t = exp(G_t) h0^T q_t (the closed form
+    the oracle is pinned to)."""
+    K = 32 if dtype == "f32" else 128
+    C = 16 if dtype == "f32" else 64
+    # slow decay: under the workload decay the state falls to ~1e-105 over 300
+    # tokens, below fp32 range
+    x = make_inputs(25, 1, 300, 2, K, K, C, dtype, 0.05, decay="slow", name="beta0")
+    x.beta[:] = 0
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, n_segments=2)
+    check(x, o, hT, o_ref, h_ref, what="beta=0")
+    G = np.cumsum(x.g[0].astype(np.float64), axis=0)           # [S,H]
+    o_cf = np.exp(G)[:, :, None] * np.einsum("shk,hkv->shv", x.q[0].astype(np.float64), x.h0[0])
+    assert rel_err(o[0], o_cf) <= TOL[dtype]
+
+
+def test_no_decay_4k():
+    """g = 0 (alpha = 1) over 4k tokens, 4 segments: no forgetting at all."""
+    x = workload(1, H=4, decay="none")
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, n_segments=4)
+    check(x, o, hT, o_ref, h_ref, what="g=0 R=4")
