@@ -312,6 +312,9 @@ __device__ __forceinline__ void invert_tprime(const uint2 (*ab)[64], const float
                     stv(tb, noff(48 + li, 0 + lg), join(to4(U03), to4(U13)));
                     stv(tb, noff(48 + li, 4 + lg), join(to4(U23), to4(Qf[3])));
     if (tg) {
+        // tg may share memory with ab (the preparation kernel overlays them):
+        // keep every read of ab above the writes of tg
+        asm volatile("" ::: "memory");
         // T' diag(gamma): element e of lane (i, g) in block (rb, cb) is column
         // 16 cb + 4g + e of T'
         f32x4 gm[4];

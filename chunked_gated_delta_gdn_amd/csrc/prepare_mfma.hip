@@ -34,8 +34,10 @@ struct PrepLds {
     bf16 kR[C * K];        // k rows, wide tiles
     bf16 vR[C * V];        // v rows, wide tiles
     bf16 tb[C * C];        // T'
-    bf16 tg[C * C];        // T' diag(gamma)
-    uint2 ab[10][64];      // Gram tiles (see gram_to_ab)
+    union {
+        uint2 ab[10][64];  // Gram tiles (see gram_to_ab), read by invert_tprime first,
+        bf16 tg[C * C];    // then overwritten by T' diag(gamma): 3 workgroups fit a CU
+    };
     float G2[C];           // cumulative log2-decay (zero past the chunk end)
     float B[C];            // beta (zero past the chunk end)
 };
