@@ -227,6 +227,7 @@ __device__ __forceinline__ void invert_tprime(const uint2 (*ab)[64], const float
                     // A' = A0 diag(beta).  AB[a][b] (a > b): B layout of -A'_ab; NB / NA:
                     // B / A layout of A'_aa
                     bf16x4 AB[4][4], NB[4], NA[4];
+                    f32x4 p[4];   // I - N per diagonal block, from N before rounding
                     {
                         const uint2 *abl = &ab[0][lane];
                         AB[1][0] = __builtin_bit_cast(bf16x4, abl[0 * 64]);
@@ -252,6 +253,8 @@ __device__ __forceinline__ void invert_tprime(const uint2 (*ab)[64], const float
                             }
                             NB[aa] = to4(vb);
                             NA[aa] = to4(va);
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) p[aa][e] = ((4 * lg + e == li) ? 1.f : 0.f) - vb[e];
                         }
                     }
                     // diagonal inverses T_aa = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
@@ -259,49 +262,60 @@ __device__ __forceinline__ void invert_tprime(const uint2 (*ab)[64], const float
                     // P <- P + N^(2^k) P; powers are formed in both layouts
                     // (N^2 = N N in B layout, (N^2)^T = N^T N^T is the A layout).
                     // Q, the A layout of T_aa, is P transposed by an identity product.
+                    // Each stage runs over the four (independent) blocks before the
+                    // next, so the blocks' dependent chains interleave.
                     bf16x4 i16;
     #pragma unroll
                     for (int e = 0; e < 4; ++e) i16[e] = (bf16)((4 * lg + e == li) ? 1.f : 0.f);
                     f32x4 Qf[4];
-                    bf16x4 P[4], Q[4];
+                    bf16x4 P[4], Q[4], n2b[4], n2a[4], n4b[4], n4a[4], n8a[4];
     #pragma unroll
                     for (int aa = 0; aa < 4; ++aa) {
-                        const bf16x4 n2b = to4(mma16(NA[aa], NB[aa], zero4()));
-                        const bf16x4 n2a = to4(mma16(NB[aa], NA[aa], zero4()));
-                        const bf16x4 n4b = to4(mma16(n2a, n2b, zero4()));
-                        const bf16x4 n4a = to4(mma16(n2b, n2a, zero4()));
-                        const bf16x4 n8a = to4(mma16(n4b, n4a, zero4()));
-                        f32x4 p;
-    #pragma unroll
-                        for (int e = 0; e < 4; ++e) p[e] = ((4 * lg + e == li) ? 1.f : 0.f) - (float)NB[aa][e];
-                        p = mma16(n2a, to4(p), p);
-                        p = mma16(n4a, to4(p), p);
-                        p = mma16(n8a, to4(p), p);
-                        P[aa] = to4(p);
-                        Qf[aa] = mma16(P[aa], i16, zero4());
-                        Q[aa] = to4(Qf[aa]);
+                        n2b[aa] = to4(mma16(NA[aa], NB[aa], zero4()));
+                        n2a[aa] = to4(mma16(NB[aa], NA[aa], zero4()));
                     }
+    #pragma unroll
+                    for (int aa = 0; aa < 4; ++aa) {
+                        n4b[aa] = to4(mma16(n2a[aa], n2b[aa], zero4()));
+                        n4a[aa] = to4(mma16(n2b[aa], n2a[aa], zero4()));
+                        p[aa] = mma16(n2a[aa], to4(p[aa]), p[aa]);
+                    }
+    #pragma unroll
+                    for (int aa = 0; aa < 4; ++aa) {
+                        n8a[aa] = to4(mma16(n4b[aa], n4a[aa], zero4()));
+                        p[aa] = mma16(n4a[aa], to4(p[aa]), p[aa]);
+                    }
+    #pragma unroll
+                    for (int aa = 0; aa < 4; ++aa) p[aa] = mma16(n8a[aa], to4(p[aa]), p[aa]);
+    #pragma unroll
+                    for (int aa = 0; aa < 4; ++aa) {
+                        P[aa] = to4(p[aa]);
+                        Qf[aa] = mma16(P[aa], i16, zero4());
+                    }
+    #pragma unroll
+                    for (int aa = 0; aa < 4; ++aa) Q[aa] = to4(Qf[aa]);
                     // off-diagonal blocks of T^T (B layout) = blocks of T (A layout):
                     // U_ij = -(T'^T)_ii sum_{k=i+1..j} (A'^T)_ik (T'^T)_kj,  i < j
                     // (the minus sign travels with AB)
                     f32x4 U01, U12, U23, U02, U13, U03;
                     {
-                        f32x4 y = mma16(AB[1][0], Q[1], zero4());
-                        U01 = mma16(P[0], to4(y), zero4());
-                        y = mma16(AB[2][1], Q[2], zero4());
-                        U12 = mma16(P[1], to4(y), zero4());
-                        y = mma16(AB[3][2], Q[3], zero4());
-                        U23 = mma16(P[2], to4(y), zero4());
-                        y = mma16(AB[1][0], to4(U12), zero4());
-                        y = mma16(AB[2][0], Q[2], y);
-                        U02 = mma16(P[0], to4(y), zero4());
-                        y = mma16(AB[2][1], to4(U23), zero4());
-                        y = mma16(AB[3][1], Q[3], y);
-                        U13 = mma16(P[1], to4(y), zero4());
-                        y = mma16(AB[1][0], to4(U13), zero4());
-                        y = mma16(AB[2][0], to4(U23), y);
-                        y = mma16(AB[3][0], Q[3], y);
-                        U03 = mma16(P[0], to4(y), zero4());
+                        const f32x4 y01 = mma16(AB[1][0], Q[1], zero4());
+                        const f32x4 y12 = mma16(AB[2][1], Q[2], zero4());
+                        const f32x4 y23 = mma16(AB[3][2], Q[3], zero4());
+                        U01 = mma16(P[0], to4(y01), zero4());
+                        U12 = mma16(P[1], to4(y12), zero4());
+                        U23 = mma16(P[2], to4(y23), zero4());
+                        // terms that need no level-1 result first
+                        f32x4 y02 = mma16(AB[2][0], Q[2], zero4());
+                        f32x4 y13 = mma16(AB[3][1], Q[3], zero4());
+                        f32x4 y03 = mma16(AB[3][0], Q[3], zero4());
+                        y02 = mma16(AB[1][0], to4(U12), y02);
+                        y13 = mma16(AB[2][1], to4(U23), y13);
+                        y03 = mma16(AB[2][0], to4(U23), y03);
+                        U02 = mma16(P[0], to4(y02), zero4());
+                        U13 = mma16(P[1], to4(y13), zero4());
+                        y03 = mma16(AB[1][0], to4(U13), y03);
+                        U03 = mma16(P[0], to4(y03), zero4());
                     }
                     bf16x4 z4;
                     z4[0] = z4[1] = z4[2] = z4[3] = (bf16)0.f;
