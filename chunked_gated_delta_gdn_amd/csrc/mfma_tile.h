@@ -62,10 +62,21 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // LDS tiles.  A row of a "wide" tile holds 128 bf16 (16 chunks of 16 B), a row
-// of a "narrow" tile 64 bf16 (8 chunks).  Chunk q of row r lives at chunk
-// q ^ (r & 7).  Within a 32-element block, chunk g holds the k-slots
-// 8g .. 8g+7, i.e. logical elements 4g .. 4g+3 and 16+4g .. 16+4g+3.
-__device__ __forceinline__ int woff(int r, int q) { return r * 256 + ((q ^ (r & 7)) << 4); }
+// of a "narrow" tile 64 bf16 (8 chunks).  Within a 32-element block, chunk g
+// holds the k-slots 8g .. 8g+7, i.e. logical elements 4g .. 4g+3 and
+// 16+4g .. 16+4g+3.
+// The 16-byte chunks are swizzled against LDS bank conflicts (gfx950: 64
+// banks of 4 B; a 16-byte read is served 16 lanes per pass, an 8-byte store
+// 16 lanes per pass over 32 banks; measured with the bank-conflict counter):
+//  * wide: chunk q of row r lives at chunk q ^ (r & 7) ^ (q >> 3 & 1).  The
+//    8-byte stores of store_rows (the even, then the odd chunks of one row)
+//    fall on distinct banks; a 16-byte read of one chunk by 16 consecutive
+//    rows takes two passes.  (q ^ (r & 15) ^ (q >> 3 & 1) makes those reads
+//    single-pass too, but its lane-dependent addresses cost the consumers
+//    registers they do not have.)
+//  * narrow: chunk q of row r lives at chunk q ^ (r & 7); two consecutive
+//    rows span the 64 banks.
+__device__ __forceinline__ int woff(int r, int q) { return r * 256 + ((q ^ (r & 7) ^ ((q >> 3) & 1)) << 4); }
 __device__ __forceinline__ int noff(int r, int q) { return r * 128 + ((q ^ (r & 7)) << 4); }
 __device__ __forceinline__ bf16x8 ldv(const bf16 *base, int byte_off) {
     return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(base) + byte_off);

@@ -46,7 +46,7 @@
 //    16x16x32 MFMA in one 16-byte run, with the slot order chosen so that two
 //    accumulator tiles (rows 0-15, 16-31) are directly the B operand of the
 //    next product: the sequential path never goes through LDS.  16-byte chunks
-//    are XOR-swizzled by row to keep 8-lane groups on distinct banks.
+//    are XOR-swizzled by row (woff, noff) against LDS bank conflicts.
 //  * Barriers wait for LDS traffic only, so register prefetches stay in flight
 //    across them.
 #include "dev_common.h"
