@@ -113,6 +113,10 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 __device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
 }
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint2 v) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, voff, 0, 0);
+}
 __device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
 }

@@ -14,7 +14,7 @@
 // moves beta off T: the kernel inverts T' = (I + A0 diag(beta))^{-1}, whose
 // strictly lower part scales columns by beta, and delta = diag(beta) T' R,
 // with the row factor beta folded into exp(G_C - G_r) for the state update
-// and applied to D before attn D for o.
+// and into the columns of attn for o.
 // In the carrying mode the state is X = [M | h], started from [I | 0], with
 // V = 0 on the M columns: the low-rank update M <- gamma M - k_tilde^T (w M)
 // of section "Implementation".
@@ -39,9 +39,9 @@
 //              and, from the k rows still in its registers, the Gram k k^T
 //              with the decay factors of A;
 //      wave 6: loads q (one chunk ahead), writes it for the consumers, and
-//              forms attn from the Gram k q^T;
-//      wave 7: k^T by identity MFMAs (the operand of K^T delta) and the
-//              per-row decay factors.
+//              forms attn diag(beta) from the Gram k q^T;
+//      wave 7: the per-row decay factors, and K^T diag(exp(G_C - G) beta) by
+//              identity MFMAs (the operand of the state update).
 //  * Every LDS operand tile stores the eight k-slots a lane group feeds to a
 //    16x16x32 MFMA in one 16-byte run, with the slot order chosen so that two
 //    accumulator tiles (rows 0-15, 16-31) are directly the B operand of the
@@ -65,7 +65,7 @@ template <bool WY> struct Lds;
 template <> struct Lds<false> {
     bf16 kR[3][C * K];      // k rows, wide tiles (loader writes j+2, producers read j+1, consumers j)
     bf16 qR[2][C * K];      // q rows, wide tiles
-    bf16 kT[2][K * C];      // k transposed, narrow tiles
+    bf16 kT[2][K * C];      // K^T diag(kdec), narrow tiles
     bf16 attn[2][C * C];    // attn, narrow tiles
     bf16 tb[2][C * C];      // T' = (I + A0 diag(beta))^{-1}, narrow tiles
     uint2 ab[2][10][64];    // loader -> wave 4, per lane 4 bf16: the 6 off-diagonal
@@ -73,8 +73,8 @@ template <> struct Lds<false> {
     float G2[2][C];         // cumulative log-decay of the chunk, times log2(e)
     float B[2][C];          // beta (zero past the chunk end)
     float gam[2][C];        // exp(G_r); gam[63] = exp(G_C)
-    float kdec[2][C];       // exp(G_C - G_r) beta_r
-    float bet[2][C];        // beta, for the consumers (B is rewritten while they run)
+    float kdec[2][C];       // exp(G_C - G_r) beta_r (folded into the kT tile)
+    float Gb[2][C];         // G2 - log2(beta): exp2(G2_r - Gb_s) = exp(G_r - G_s) beta_s
 };
 // WY factors read from a workspace: w rows replace the k rows as the
 // consumers' operand, there is no Gram or T'; k is read only by producers, so
@@ -83,11 +83,11 @@ template <> struct Lds<true> {
     bf16 kR[2][C * K];      // k rows (loader writes j+2, producers read j+1)
     bf16 qR[2][C * K];      // q rows
     bf16 wR[2][C * K];      // w rows (w wave writes j+1, consumers read j)
-    bf16 kT[2][K * C];      // k transposed
+    bf16 kT[2][K * C];      // K^T diag(kdec)
     bf16 attn[2][C * C];    // attn
     float G2[2][C];         // cumulative log2-decay
     float gam[2][C];        // exp(G_r)
-    float kdec[2][C];       // exp(G_C - G_r)
+    float kdec[2][C];       // exp(G_C - G_r) (folded into the kT tile)
 };
 
 template <bool EMIT, bool WY>
@@ -237,10 +237,9 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             __builtin_amdgcn_sched_barrier(0);
             // -- O = Q X (emitting), reading T' and the decays meanwhile
             const float *gam = sm.gam[b2];
-            const float *kdec = sm.kdec[b2];
             f32x4 O[4];
             bf16x8 ta[6];    // T' tiles (c, kk), kk <= c / 2
-            f32x4 gv[4], kv[4], bv[4];
+            f32x4 gv[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) O[c] = zero4();
 #pragma unroll
@@ -251,18 +250,13 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                     if constexpr (!WY) ta[i] = ldv(sm.tb[b2], noff(16 * c + li, 4 * kk + lg));
                 } else if (i < 10) {
                     gv[i - 6] = *reinterpret_cast<const f32x4 *>(&gam[16 * (i - 6) + 4 * lg]);
-                } else if (i < 14) {
-                    kv[i - 10] = *reinterpret_cast<const f32x4 *>(&kdec[16 * (i - 10) + 4 * lg]);
                 }
-                if constexpr (EMIT && !WY)
-                    if (i >= 12) bv[i - 12] = *reinterpret_cast<const f32x4 *>(&sm.bet[b2][16 * (i - 12) + 4 * lg]);
             }
             if (EMIT) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (i < 14 && (!WY || i >= 6)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    if (!WY && i >= 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (i < 10 && (!WY || i >= 6)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -313,32 +307,17 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 12; i < 16; ++i) kt16[i] = ldv(sm.kT[b2], noff(16 * (i >> 1) + li, 4 * (i & 1) + lg));
+            // D as the operand reducing over the chunk, for both products that
+            // follow: the kT tile carries the row factors of the state update and
+            // the attn tile those of the output
             bf16x8 dk[NCT][2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int n = 0; n < NCT; ++n) {
-                    f32x4 lo, hi;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        lo[e] = kv[2 * kk][e] * D[n][2 * kk][e];
-                        hi[e] = kv[2 * kk + 1][e] * D[n][2 * kk + 1][e];
-                    }
-                    dk[n][kk] = pack_pair(lo, hi);
-                }
+                for (int n = 0; n < NCT; ++n) dk[n][kk] = pack_pair(D[n][2 * kk], D[n][2 * kk + 1]);
             if (EMIT) {
-                // delta = diag(beta) D (recomputing) or D (WY given)
-                bf16x8 db[2];
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    f32x4 lo, hi;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        lo[e] = WY ? D[0][2 * kk][e] : bv[2 * kk][e] * D[0][2 * kk][e];
-                        hi[e] = WY ? D[0][2 * kk + 1][e] : bv[2 * kk + 1][e] * D[0][2 * kk + 1][e];
-                    }
-                    db[kk] = pack_pair(lo, hi);
-                }
+                // attn delta = (attn diag(beta)) D when recomputing (the attn tile carries
+                // beta on its columns), attn D when the WY factors are given
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -346,10 +325,10 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
 #pragma unroll
                 for (int i = 0; i < 6; ++i) {
                     const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
-                    O[c] = mma32(at6[i], db[kk], O[c]);
+                    O[c] = mma32(at6[i], dk[0][kk], O[c]);
                 }
             }
-            // -- X = gamma_C X + K^T diag(exp(G_C - G)) delta = gamma_C X + K^T diag(kdec) D
+            // -- X = gamma_C X + K^T diag(exp(G_C - G)) delta = gamma_C X + (K^T diag(kdec)) D
             const float gc = gam[63];
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -364,14 +343,13 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                 // O tile c in B layout (lane (j, g): rows 4g..4g+3, column j) ->
                 // transposed by an identity product: lane (j, g) then holds row j,
                 // columns 4g..4g+3, i.e. 8 contiguous bytes of the output row.
-                char *ob = reinterpret_cast<char *>(static_cast<bf16 *>(a.o) + tok(j, 0) * rowV);
+                const __amdgpu_buffer_rsrc_t orr = rsrc(static_cast<bf16 *>(a.o) + tok(j, 0) * rowV);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const f32x4 ot = mma16(to4(O[c]), i16, zero4());
                     const uint2 v = __builtin_bit_cast(uint2, to4(ot));
                     const int r = 16 * c + li;
-                    if (L == C || r < L)
-                        *reinterpret_cast<uint2 *>(ob + (uint32_t)r * (uint32_t)(rowV * 2) + out_off) = v;
+                    if (L == C || r < L) bstore8(orr, (uint32_t)r * (uint32_t)(rowV * 2) + out_off, v);
                 }
             }
             lds_barrier();
@@ -431,7 +409,8 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             const int L = chunk_len(j);
             store_rows(sm.kR[b3], t, lane);
             // rows past the chunk end get g = 0, beta = 0
-            sm.G2[b2][lane] = wave_cumsum(lane < L ? gv_ : 0.f) * kLog2e;
+            const float g2 = wave_cumsum(lane < L ? gv_ : 0.f) * kLog2e;
+            sm.G2[b2][lane] = g2;
             if constexpr (!WY) {
                 // the k rows back in MFMA operand layout (this wave's own writes)
                 bf16x8 kt[4][4];
@@ -439,7 +418,10 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], woff(16 * c + li, 4 * kk + lg));
-                sm.B[b2][lane] = lane < L ? bv_ : 0.f;
+                const float bl = lane < L ? bv_ : 0.f;
+                sm.B[b2][lane] = bl;
+                // log2(0) = -inf: padded columns of attn vanish
+                sm.Gb[b2][lane] = g2 - __builtin_amdgcn_logf(bl);
                 gram_to_ab(kt, sm.G2[b2], sm.B[b2], sm.ab[b2], lane);
             }
         };
@@ -472,6 +454,12 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             store_rows(sm.qR[b2], qraw, lane);
 
             const float *G2 = sm.G2[b2];
+            // column exponents: with G2 - log2(beta) the tile is attn diag(beta),
+            // which is what multiplies D when recomputing; plain attn for the WY
+            // factors (beta is inside u and w)
+            const float *Gcol;
+            if constexpr (WY) Gcol = G2;
+            else Gcol = sm.Gb[b2];
             (void)L;
             // Gram block (b, a) of K Q^T: lane (j, g) element e holds
             // k_{16b+4g+e} . q_{16a+j} = raw attn[r = 16a + j][s = 16b + 4g + e]
@@ -501,7 +489,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                     const float Gr = G2[r];
 #pragma unroll
                     for (int bb = 0; bb <= aa; ++bb, ++i) {
-                        const f32x4 Gs = *reinterpret_cast<const f32x4 *>(&G2[16 * bb + 4 * lg]);
+                        const f32x4 Gs = *reinterpret_cast<const f32x4 *>(&Gcol[16 * bb + 4 * lg]);
                         f32x4 v;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -573,25 +561,32 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
             const bf16 *kR = sm.kR[b3];
             const float *G2 = sm.G2[b2];
             if (role == 3) {
-                // ---- per-row factors, and k^T by identity products
+                // ---- per-row factors, and K^T diag(kdec) by identity products
                 const float g2 = G2[lane];
                 sm.gam[b2][lane] = ex2(g2);
                 if constexpr (WY) {
                     sm.kdec[b2][lane] = ex2(G2[63] - g2);
                 } else {
-                    const float bl = sm.B[b2][lane];
-                    sm.kdec[b2][lane] = ex2(G2[63] - g2) * bl;
-                    sm.bet[b2][lane] = bl;
+                    sm.kdec[b2][lane] = ex2(G2[63] - g2) * sm.B[b2][lane];
                 }
+                // kdec at rows 16c + 4g + e (this wave's own writes, read back)
+                f32x4 kd[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) kd[c] = *reinterpret_cast<const f32x4 *>(&sm.kdec[b2][16 * c + 4 * lg]);
                 bf16 *kT = sm.kT[b2];
 #pragma unroll
                 for (int n = 0; n < 8; ++n) {
                     const bf16x8 id = (n & 1) ? id1 : id0;
                     f32x4 d[4];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
+                    for (int c = 0; c < 4; ++c) {
                         d[c] = mma32(ldv(kR, woff(16 * c + li, 4 * (n >> 1) + lg)), id, zero4());
+                    }
                     // lane (j, g) of d[c] holds k[16c + 4g + e][16n + j]
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) d[c][e] *= kd[c][e];
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk)
                         stv(kT, noff(16 * n + li, 4 * kk + lg), pack_pair(d[2 * kk], d[2 * kk + 1]));
