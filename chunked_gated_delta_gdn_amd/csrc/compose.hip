@@ -5,8 +5,13 @@
 //
 // The columns of the state are independent under h <- M h + U, so one
 // workgroup owns a 16-column strip of one (sequence, head) state and walks
-// the R segments in order.  M[r] (K x K fp32) is staged whole in LDS, the
-// strip of the running state too; fp32 FMAs throughout (the state is fp32).
+// the R segments in order; everything stays fp32 (the state is fp32).
+//  * K = V = 128: fp32 matrix-core products (v_mfma_f32_16x16x4_f32).  Each
+//    of the 4 waves owns 32 rows of the new strip: its rows of M[r] go
+//    straight from memory into A operands (16-byte runs, issued before the
+//    products), the running strip sits transposed in LDS and is read as B
+//    operands, and U[r] seeds the accumulators.  One barrier per segment.
+//  * other shapes: fp32 FMAs with M[r] staged in LDS.
 // Work is R * 2*K*K*V flops per head, negligible next to the scan.
 #include "dev_common.h"
 #include "gdn_internal.h"
@@ -74,6 +79,73 @@ __global__ __launch_bounds__(kThreads) void compose_kernel(ComposeArgs a) {
     }
 }
 
+// K = V = 128 on the matrix cores.  In a 16x16x4 fp32 product lane (i, g)
+// (i = lane % 16, g = lane / 16) supplies A[i][g] and B[g][i] and receives
+// D[4g + e][i].  Step s = 4q + e of the reduction gives lane group g the
+// index k = 4 (4q + g) + e, so a lane's A operands for q are one 16-byte run
+// of its row of M, and its B operands one 16-byte run of the transposed strip.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(kThreads) void compose_mfma_kernel(ComposeArgs a) {
+    constexpr int K = 128, V = 128, NS = V / kStrip, LD = K + 4;
+    __shared__ __attribute__((aligned(16))) float hT[2][kStrip * LD];   // [column][row], two copies
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int strip = blockIdx.x % NS;
+    const int64_t nh = blockIdx.x / NS;
+    const int64_t NH = (int64_t)a.N * a.H;
+    const int c0 = strip * kStrip;
+
+    for (int e = tid; e < K * kStrip; e += kThreads) {
+        const int i = e / kStrip, jj = e % kStrip;
+        hT[0][jj * LD + i] = a.h0 ? a.h0[(nh * K + i) * V + c0 + jj] : 0.f;
+    }
+    __syncthreads();
+    int cur = 0;
+    for (int r = 0; r < a.R; ++r) {
+        const int64_t slot = (int64_t)r * NH + nh;
+        for (int e = tid; e < K * kStrip; e += kThreads) {
+            const int i = e / kStrip, jj = e % kStrip;
+            a.h_in[(slot * K + i) * V + c0 + jj] = hT[cur][jj * LD + i];
+        }
+        if (r == a.R - 1 && !a.h_final) break;
+        const float *Mr = a.M + slot * K * K;
+        f32x4 ma[2][8];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                ma[rb][q] = *reinterpret_cast<const f32x4 *>(&Mr[(32 * w + 16 * rb + li) * K + 4 * (4 * q + lg)]);
+        f32x4 acc[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rb][e] = a.U[(slot * K + 32 * w + 16 * rb + 4 * lg + e) * V + c0 + li];
+        const float *hc = hT[cur];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const f32x4 hb = *reinterpret_cast<const f32x4 *>(&hc[li * LD + 4 * (4 * q + lg)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ma[rb][q][e], hb[e], acc[rb], 0, 0, 0);
+        }
+        // lane (j, g) holds rows 32w + 16rb + 4g + e of column j
+        float *hn = hT[cur ^ 1];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) *reinterpret_cast<f32x4 *>(&hn[li * LD + 32 * w + 16 * rb + 4 * lg]) = acc[rb];
+        __syncthreads();
+        cur ^= 1;
+    }
+    if (a.h_final) {
+        for (int e = tid; e < K * kStrip; e += kThreads) {
+            const int i = e / kStrip, jj = e % kStrip;
+            a.h_final[(nh * K + i) * V + c0 + jj] = hT[cur][jj * LD + i];
+        }
+    }
+}
+
 template <int K, int V>
 hipError_t launch_t(const ComposeArgs &a, hipStream_t s) {
     const int64_t n = (int64_t)a.N * a.H * (V / kStrip);
@@ -86,7 +158,12 @@ hipError_t launch_t(const ComposeArgs &a, hipStream_t s) {
 
 hipError_t launch_compose(int K, int V, const ComposeArgs &a, hipStream_t s) {
     if (K == 32 && V == 32) return launch_t<32, 32>(a, s);
-    if (K == 128 && V == 128) return launch_t<128, 128>(a, s);
+    if (K == 128 && V == 128) {
+        const int64_t n = (int64_t)a.N * a.H * (V / kStrip);
+        if (n == 0) return hipSuccess;
+        hipLaunchKernelGGL(compose_mfma_kernel, dim3((unsigned)n), dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+    }
     return hipErrorInvalidValue;
 }
 

@@ -316,6 +316,28 @@ def test_segment_compose_matches_oracle_scan():
     assert rel_err(h_fin.cpu().numpy(), ref_fin) <= 1e-5
 
 
+@pytest.mark.parametrize("R,K,with_h0,want_final", [(1, 128, False, False), (3, 128, False, True),
+                                                     (2, 128, True, False), (4, 32, True, True)])
+def test_segment_compose_variants(R, K, with_h0, want_final):
+    """Single segment (no products), zero initial state, no final state, and the
+    K = V = 32 shape, against the oracle's exclusive scan."""
+    rng = np.random.default_rng(22 + R)
+    N, H = 1, 4
+    M = (rng.standard_normal((R, N, H, K, K)) / np.sqrt(K)).astype(np.float32)
+    U = rng.standard_normal((R, N, H, K, K)).astype(np.float32)
+    h0 = rng.standard_normal((N, H, K, K)).astype(np.float32) if with_h0 else None
+    h_in, h_fin = gdn.segment_compose(to_dev(M), to_dev(U), to_dev(h0) if with_h0 else None,
+                                      want_final=want_final)
+    torch.cuda.synchronize()
+    ref_in, ref_fin = oracle.exclusive_scan(M, U, h0)
+    say(f"  compose R={R} K={K} h0={with_h0}: err(h_in)={rel_err(h_in.cpu().numpy(), ref_in):.3e}")
+    assert rel_err(h_in.cpu().numpy(), ref_in) <= 1e-5
+    if want_final:
+        assert rel_err(h_fin.cpu().numpy(), ref_fin) <= 1e-5
+    else:
+        assert h_fin is None
+
+
 # ---- limits and degenerate cases ------------------------------------------------------------
 
 def test_packed_max_sequences():
