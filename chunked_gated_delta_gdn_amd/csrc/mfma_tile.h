@@ -176,181 +176,195 @@ __device__ __forceinline__ bf16x4 ldtr(const bf16 *base, int byte_off) {
 }
 
 // Gram tiles of one chunk (A0[r,s] = exp(G_r - G_s) k_r.k_s), from the k tile
-// in MFMA operand layout: kt[c][kk] is lane (i, g)'s operand for rows 16c + i,
-// k-block kk.  G2 is the cumulative log2-decay, Bv beta (both zero past the
-// chunk end).  Writes, per lane, the 6 off-diagonal blocks of -A0 diag(beta)
-// (B layout, in the order (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)) and the 4 raw
-// diagonal blocks of k k^T to ab[0..9][lane].
-__device__ __forceinline__ void gram_to_ab(const bf16x8 (&kt)[4][4], const float *G2, const float *Bv,
-                                           uint2 (*ab)[64], int lane) {
+// in MFMA operand layout: kt(c, kk) returns lane (i, g)'s operand for rows
+// 16c + i, k-block kk (read k-block by k-block).  G2 is the cumulative
+// log2-decay, Bv beta (both zero past the chunk end).  Blocks (a, b), b <= a,
+// are numbered i = a (a + 1) / 2 + b; MASK selects the blocks formed (several
+// waves can split them).  Writes, per lane, the off-diagonal blocks of
+// -A0 diag(beta) (B layout, block (a, b) at ab[a (a - 1) / 2 + b]) and the raw
+// diagonal blocks of k k^T (block (a, a) at ab[6 + a]).
+template <int MASK = 0x3ff, class KT>
+__device__ __forceinline__ void gram_to_ab(KT kt, const float *G2, const float *Bv, uint2 (*ab)[64], int lane) {
     const int li = lane & 15, lg = lane >> 4;
-                // factors at rows 16t + 4g + e (B layout rows) and 16t + j (B layout column)
-                f32x4 Gr4[4];
-                float Gc[4], Bc[4];
-    #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    Gr4[u] = *reinterpret_cast<const f32x4 *>(&G2[16 * u + 4 * lg]);
-                    Gc[u] = G2[16 * u + li];
-                    Bc[u] = Bv[16 * u + li];
-                }
-                // Gram k k^T from the k rows in registers: lane (j, g) element e of block
-                // (a, b) is k_{16a+4g+e} . k_{16b+j}.  Off-diagonal blocks leave
-                // negated, as -exp(G_r - G_s) k_r . k_s beta_s (the sign of the block
-                // recursion of T' folded in), diagonal blocks raw.
-                f32x4 acc[10];
-    #pragma unroll
-                for (int i = 0; i < 10; ++i) acc[i] = zero4();
-    #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    int i = 0;
-    #pragma unroll
-                    for (int aa = 0; aa < 4; ++aa)
-    #pragma unroll
-                        for (int bb = 0; bb <= aa; ++bb, ++i) acc[i] = mma32(kt[aa][kk], kt[bb][kk], acc[i]);
-                }
-                int i = 0, idx = 0;
-    #pragma unroll
-                for (int aa = 0; aa < 4; ++aa)
-    #pragma unroll
-                    for (int bb = 0; bb <= aa; ++bb, ++i) {
-                        if (aa > bb) {
-                            f32x4 v;
-    #pragma unroll
-                            for (int e = 0; e < 4; ++e) v[e] = -Bc[bb] * ex2(Gr4[aa][e] - Gc[bb]) * acc[i][e];
-                            ab[idx++][lane] = __builtin_bit_cast(uint2, to4(v));
-                        } else {
-                            ab[6 + aa][lane] = __builtin_bit_cast(uint2, to4(acc[i]));
-                        }
-                    }
+    // factors at rows 16t + 4g + e (B layout rows) and 16t + j (B layout column)
+    f32x4 Gr4[4];
+    float Gc[4], Bc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        Gr4[u] = *reinterpret_cast<const f32x4 *>(&G2[16 * u + 4 * lg]);
+        Gc[u] = G2[16 * u + li];
+        Bc[u] = Bv[16 * u + li];
+    }
+    // Gram k k^T: lane (j, g) element e of block (a, b) is k_{16a+4g+e} . k_{16b+j}.
+    // Off-diagonal blocks leave negated, as -exp(G_r - G_s) k_r . k_s beta_s (the
+    // sign of the block recursion of T' folded in), diagonal blocks raw.
+    f32x4 acc[10];
+#pragma unroll
+    for (int i = 0; i < 10; ++i) acc[i] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 kc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kc[c] = kt(c, kk);
+        int i = 0;
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+            for (int bb = 0; bb <= aa; ++bb, ++i)
+                if ((MASK >> i) & 1) acc[i] = mma32(kc[aa], kc[bb], acc[i]);
+    }
+    int i = 0;
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+        for (int bb = 0; bb <= aa; ++bb, ++i) {
+            if (!((MASK >> i) & 1)) continue;
+            if (aa > bb) {
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = -Bc[bb] * ex2(Gr4[aa][e] - Gc[bb]) * acc[i][e];
+                ab[aa * (aa - 1) / 2 + bb][lane] = __builtin_bit_cast(uint2, to4(v));
+            } else {
+                ab[6 + aa][lane] = __builtin_bit_cast(uint2, to4(acc[i]));
+            }
+        }
 }
 
-// T' = (I + A0 diag(beta))^{-1} from the tiles of gram_to_ab, as row-major
-// narrow tiles (the A operand layout of T' for a product over the chunk) in
-// tb; with tg non-null also T' diag(gamma), gamma_s = exp(G_s).
-__device__ __forceinline__ void invert_tprime(const uint2 (*ab)[64], const float *G2, const float *Bv,
-                                              bf16 *tb, bf16 *tg, int lane) {
+// Inverses of diagonal 16 x 16 blocks of T' = (I + A0 diag(beta))^{-1}, for
+// the NBLK blocks listed in blk (compile-time constants), from the raw Gram
+// blocks of gram_to_ab.  With N = (A0 diag(beta))_aa, strictly lower
+// triangular, T'_aa = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
+// (N^16 = 0).  P accumulates in B layout, P <- P + N^(2^k) P; the powers are
+// formed in both layouts (N^2 = N N in B layout, (N^2)^T = N^T N^T is the A
+// layout).  Each stage runs over all listed blocks before the next, so their
+// dependent chains interleave.  Out: P[j] (bf16 B layout of T'_aa, which as an
+// A operand is T'_aa^T) and Qf[j] (fp32 A layout of T'_aa, by an identity
+// product).
+template <int NBLK>
+__device__ __forceinline__ void diag_inverse(const int (&blk)[NBLK], const uint2 (*ab)[64], const float *G2,
+                                             const float *Bv, int lane, bf16x4 (&P)[NBLK], f32x4 (&Qf)[NBLK]) {
     const int li = lane & 15, lg = lane >> 4;
-                    f32x4 Gr4[4], Br4[4];
-                    float Gc[4], Bc[4];
-    #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        Gr4[t] = *reinterpret_cast<const f32x4 *>(&G2[16 * t + 4 * lg]);
-                        Br4[t] = *reinterpret_cast<const f32x4 *>(&Bv[16 * t + 4 * lg]);
-                        Gc[t] = G2[16 * t + li];
-                        Bc[t] = Bv[16 * t + li];
-                    }
-                    // A' = A0 diag(beta).  AB[a][b] (a > b): B layout of -A'_ab; NB / NA:
-                    // B / A layout of A'_aa
-                    bf16x4 AB[4][4], NB[4], NA[4];
-                    f32x4 p[4];   // I - N per diagonal block, from N before rounding
-                    {
-                        const uint2 *abl = &ab[0][lane];
-                        AB[1][0] = __builtin_bit_cast(bf16x4, abl[0 * 64]);
-                        AB[2][0] = __builtin_bit_cast(bf16x4, abl[1 * 64]);
-                        AB[2][1] = __builtin_bit_cast(bf16x4, abl[2 * 64]);
-                        AB[3][0] = __builtin_bit_cast(bf16x4, abl[3 * 64]);
-                        AB[3][1] = __builtin_bit_cast(bf16x4, abl[4 * 64]);
-                        AB[3][2] = __builtin_bit_cast(bf16x4, abl[5 * 64]);
-    #pragma unroll
-                        for (int aa = 0; aa < 4; ++aa) {
-                            // raw k_{16a+4g+e} . k_{16a+j} (symmetric): B layout entry
-                            // (r = 16a+4g+e, s = 16a+j) if s < r, A layout entry (r' = 16a+j,
-                            // s' = 16a+4g+e) if s' < r'
-                            const bf16x4 kk4 = __builtin_bit_cast(bf16x4, abl[(6 + aa) * 64]);
-                            f32x4 vb, va;
-    #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int x = 4 * lg + e;
-                                const float ex = ex2(-fabsf(Gr4[aa][e] - Gc[aa]));
-                                const float kv = (float)kk4[e];
-                                vb[e] = (li < x) ? Bc[aa] * ex * kv : 0.f;
-                                va[e] = (x < li) ? Br4[aa][e] * ex * kv : 0.f;
-                            }
-                            NB[aa] = to4(vb);
-                            NA[aa] = to4(va);
-    #pragma unroll
-                            for (int e = 0; e < 4; ++e) p[aa][e] = ((4 * lg + e == li) ? 1.f : 0.f) - vb[e];
-                        }
-                    }
-                    // diagonal inverses T_aa = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
-                    // with N = A_aa (N^16 = 0).  P accumulates in B layout,
-                    // P <- P + N^(2^k) P; powers are formed in both layouts
-                    // (N^2 = N N in B layout, (N^2)^T = N^T N^T is the A layout).
-                    // Q, the A layout of T_aa, is P transposed by an identity product.
-                    // Each stage runs over the four (independent) blocks before the
-                    // next, so the blocks' dependent chains interleave.
-                    bf16x4 i16;
-    #pragma unroll
-                    for (int e = 0; e < 4; ++e) i16[e] = (bf16)((4 * lg + e == li) ? 1.f : 0.f);
-                    f32x4 Qf[4];
-                    bf16x4 P[4], Q[4], n2b[4], n2a[4], n4b[4], n4a[4], n8a[4];
-    #pragma unroll
-                    for (int aa = 0; aa < 4; ++aa) {
-                        n2b[aa] = to4(mma16(NA[aa], NB[aa], zero4()));
-                        n2a[aa] = to4(mma16(NB[aa], NA[aa], zero4()));
-                    }
-    #pragma unroll
-                    for (int aa = 0; aa < 4; ++aa) {
-                        n4b[aa] = to4(mma16(n2a[aa], n2b[aa], zero4()));
-                        n4a[aa] = to4(mma16(n2b[aa], n2a[aa], zero4()));
-                        p[aa] = mma16(n2a[aa], to4(p[aa]), p[aa]);
-                    }
-    #pragma unroll
-                    for (int aa = 0; aa < 4; ++aa) {
-                        n8a[aa] = to4(mma16(n4b[aa], n4a[aa], zero4()));
-                        p[aa] = mma16(n4a[aa], to4(p[aa]), p[aa]);
-                    }
-    #pragma unroll
-                    for (int aa = 0; aa < 4; ++aa) p[aa] = mma16(n8a[aa], to4(p[aa]), p[aa]);
-    #pragma unroll
-                    for (int aa = 0; aa < 4; ++aa) {
-                        P[aa] = to4(p[aa]);
-                        Qf[aa] = mma16(P[aa], i16, zero4());
-                    }
-    #pragma unroll
-                    for (int aa = 0; aa < 4; ++aa) Q[aa] = to4(Qf[aa]);
-                    // off-diagonal blocks of T^T (B layout) = blocks of T (A layout):
-                    // U_ij = -(T'^T)_ii sum_{k=i+1..j} (A'^T)_ik (T'^T)_kj,  i < j
-                    // (the minus sign travels with AB)
-                    f32x4 U01, U12, U23, U02, U13, U03;
-                    {
-                        const f32x4 y01 = mma16(AB[1][0], Q[1], zero4());
-                        const f32x4 y12 = mma16(AB[2][1], Q[2], zero4());
-                        const f32x4 y23 = mma16(AB[3][2], Q[3], zero4());
-                        U01 = mma16(P[0], to4(y01), zero4());
-                        U12 = mma16(P[1], to4(y12), zero4());
-                        U23 = mma16(P[2], to4(y23), zero4());
-                        // terms that need no level-1 result first
-                        f32x4 y02 = mma16(AB[2][0], Q[2], zero4());
-                        f32x4 y13 = mma16(AB[3][1], Q[3], zero4());
-                        f32x4 y03 = mma16(AB[3][0], Q[3], zero4());
-                        y02 = mma16(AB[1][0], to4(U12), y02);
-                        y13 = mma16(AB[2][1], to4(U23), y13);
-                        y03 = mma16(AB[2][0], to4(U23), y03);
-                        U02 = mma16(P[0], to4(y02), zero4());
-                        U13 = mma16(P[1], to4(y13), zero4());
-                        y03 = mma16(AB[1][0], to4(U13), y03);
-                        U03 = mma16(P[0], to4(y03), zero4());
-                    }
-                    bf16x4 z4;
-                    z4[0] = z4[1] = z4[2] = z4[3] = (bf16)0.f;
-                    stv(tb, noff(0 + li, 0 + lg), join(to4(Qf[0]), z4));
-                    stv(tb, noff(16 + li, 0 + lg), join(to4(U01), to4(Qf[1])));
-                    stv(tb, noff(32 + li, 0 + lg), join(to4(U02), to4(U12)));
-                    stv(tb, noff(32 + li, 4 + lg), join(to4(Qf[2]), z4));
-                    stv(tb, noff(48 + li, 0 + lg), join(to4(U03), to4(U13)));
-                    stv(tb, noff(48 + li, 4 + lg), join(to4(U23), to4(Qf[3])));
+    bf16x4 NB[NBLK], NA[NBLK];
+    f32x4 p[NBLK];   // I - N, from N before rounding
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j) {
+        const int aa = blk[j];
+        const f32x4 Gr4 = *reinterpret_cast<const f32x4 *>(&G2[16 * aa + 4 * lg]);
+        const f32x4 Br4 = *reinterpret_cast<const f32x4 *>(&Bv[16 * aa + 4 * lg]);
+        const float Gc = G2[16 * aa + li], Bc = Bv[16 * aa + li];
+        // raw k_{16a+4g+e} . k_{16a+j} (symmetric): B layout entry (r = 16a+4g+e,
+        // s = 16a+j) if s < r, A layout entry (r' = 16a+j, s' = 16a+4g+e) if s' < r'
+        const bf16x4 kk4 = __builtin_bit_cast(bf16x4, ab[6 + aa][lane]);
+        f32x4 vb, va;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int x = 4 * lg + e;
+            const float ex = ex2(-fabsf(Gr4[e] - Gc));
+            const float kv = (float)kk4[e];
+            vb[e] = (li < x) ? Bc * ex * kv : 0.f;
+            va[e] = (x < li) ? Br4[e] * ex * kv : 0.f;
+        }
+        NB[j] = to4(vb);
+        NA[j] = to4(va);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[j][e] = ((4 * lg + e == li) ? 1.f : 0.f) - vb[e];
+    }
+    bf16x4 i16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) i16[e] = (bf16)((4 * lg + e == li) ? 1.f : 0.f);
+    bf16x4 n2b[NBLK], n2a[NBLK], n4b[NBLK], n4a[NBLK], n8a[NBLK];
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j) {
+        n2b[j] = to4(mma16(NA[j], NB[j], zero4()));
+        n2a[j] = to4(mma16(NB[j], NA[j], zero4()));
+    }
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j) {
+        n4b[j] = to4(mma16(n2a[j], n2b[j], zero4()));
+        n4a[j] = to4(mma16(n2b[j], n2a[j], zero4()));
+        p[j] = mma16(n2a[j], to4(p[j]), p[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j) {
+        n8a[j] = to4(mma16(n4b[j], n4a[j], zero4()));
+        p[j] = mma16(n4a[j], to4(p[j]), p[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j) p[j] = mma16(n8a[j], to4(p[j]), p[j]);
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j) {
+        P[j] = to4(p[j]);
+        Qf[j] = mma16(P[j], i16, zero4());
+    }
+}
+
+// The off-diagonal blocks of T' by block forward substitution on T'^T, from
+// the diagonal inverses (P, Qf of diag_inverse for blocks 0 .. 3) and the
+// off-diagonal Gram tiles, then T' as row-major narrow tiles (the A operand
+// layout of T' for a product over the chunk) in tb and, with tg non-null,
+// T' diag(gamma), gamma_s = exp(G_s).  tg may share memory with ab: every read
+// of ab comes first.
+__device__ __forceinline__ void offdiag_store(const uint2 (*ab)[64], const float *G2, const bf16x4 (&P)[4],
+                                              const f32x4 (&Qf)[4], bf16 *tb, bf16 *tg, int lane) {
+    const int li = lane & 15, lg = lane >> 4;
+    // AB[a][b] (a > b): B layout of -(A0 diag(beta))_ab
+    bf16x4 AB[4][4];
+    {
+        const uint2 *abl = &ab[0][lane];
+        AB[1][0] = __builtin_bit_cast(bf16x4, abl[0 * 64]);
+        AB[2][0] = __builtin_bit_cast(bf16x4, abl[1 * 64]);
+        AB[2][1] = __builtin_bit_cast(bf16x4, abl[2 * 64]);
+        AB[3][0] = __builtin_bit_cast(bf16x4, abl[3 * 64]);
+        AB[3][1] = __builtin_bit_cast(bf16x4, abl[4 * 64]);
+        AB[3][2] = __builtin_bit_cast(bf16x4, abl[5 * 64]);
+    }
+    bf16x4 Q[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) Q[aa] = to4(Qf[aa]);
+    // off-diagonal blocks of T^T (B layout) = blocks of T (A layout):
+    // U_ij = -(T'^T)_ii sum_{k=i+1..j} (A'^T)_ik (T'^T)_kj,  i < j
+    // (the minus sign travels with AB)
+    f32x4 U01, U12, U23, U02, U13, U03;
+    {
+        const f32x4 y01 = mma16(AB[1][0], Q[1], zero4());
+        const f32x4 y12 = mma16(AB[2][1], Q[2], zero4());
+        const f32x4 y23 = mma16(AB[3][2], Q[3], zero4());
+        U01 = mma16(P[0], to4(y01), zero4());
+        U12 = mma16(P[1], to4(y12), zero4());
+        U23 = mma16(P[2], to4(y23), zero4());
+        // terms that need no level-1 result first
+        f32x4 y02 = mma16(AB[2][0], Q[2], zero4());
+        f32x4 y13 = mma16(AB[3][1], Q[3], zero4());
+        f32x4 y03 = mma16(AB[3][0], Q[3], zero4());
+        y02 = mma16(AB[1][0], to4(U12), y02);
+        y13 = mma16(AB[2][1], to4(U23), y13);
+        y03 = mma16(AB[2][0], to4(U23), y03);
+        U02 = mma16(P[0], to4(y02), zero4());
+        U13 = mma16(P[1], to4(y13), zero4());
+        y03 = mma16(AB[1][0], to4(U13), y03);
+        U03 = mma16(P[0], to4(y03), zero4());
+    }
+    bf16x4 z4;
+    z4[0] = z4[1] = z4[2] = z4[3] = (bf16)0.f;
+    // keep every read of ab (and of whatever else shares memory with tb or tg)
+    // above the writes
+    asm volatile("" ::: "memory");
+    stv(tb, noff(0 + li, 0 + lg), join(Q[0], z4));
+    stv(tb, noff(16 + li, 0 + lg), join(to4(U01), Q[1]));
+    stv(tb, noff(32 + li, 0 + lg), join(to4(U02), to4(U12)));
+    stv(tb, noff(32 + li, 4 + lg), join(Q[2], z4));
+    stv(tb, noff(48 + li, 0 + lg), join(to4(U03), to4(U13)));
+    stv(tb, noff(48 + li, 4 + lg), join(to4(U23), Q[3]));
     if (tg) {
-        // tg may share memory with ab (the preparation kernel overlays them):
-        // keep every read of ab above the writes of tg
-        asm volatile("" ::: "memory");
         // T' diag(gamma): element e of lane (i, g) in block (rb, cb) is column
         // 16 cb + 4g + e of T'
         f32x4 gm[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t) {
+            const f32x4 Gr4 = *reinterpret_cast<const f32x4 *>(&G2[16 * t + 4 * lg]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gm[t][e] = ex2(Gr4[t][e]);
+            for (int e = 0; e < 4; ++e) gm[t][e] = ex2(Gr4[e]);
+        }
         auto sg = [&](const f32x4 &m, int cb) {
             f32x4 r;
 #pragma unroll
@@ -364,6 +378,18 @@ __device__ __forceinline__ void invert_tprime(const uint2 (*ab)[64], const float
         stv(tg, noff(48 + li, 0 + lg), join(sg(U03, 0), sg(U13, 1)));
         stv(tg, noff(48 + li, 4 + lg), join(sg(U23, 2), sg(Qf[3], 3)));
     }
+}
+
+// T' = (I + A0 diag(beta))^{-1} from the tiles of gram_to_ab, by one wave:
+// the four diagonal inverses interleaved, then the off-diagonal blocks (see
+// offdiag_store for tb and tg).
+__device__ __forceinline__ void invert_tprime(const uint2 (*ab)[64], const float *G2, const float *Bv,
+                                              bf16 *tb, bf16 *tg, int lane) {
+    const int all[4] = {0, 1, 2, 3};
+    bf16x4 P[4];
+    f32x4 Qf[4];
+    diag_inverse(all, ab, G2, Bv, lane, P, Qf);
+    offdiag_store(ab, G2, P, Qf, tb, tg, lane);
 }
 
 }  // namespace mfma

@@ -12,12 +12,16 @@
 // grid is n_chunks * H workgroups and several share a CU.
 //   * all waves load their quarter of the k and v rows (whole 256-byte rows)
 //     into operand-layout LDS tiles; wave 0 also the decays and beta;
-//   * wave 0 forms the Gram tiles and T' (and T' diag(gamma)) on MFMA;
+//   * the four waves split the ten Gram tiles, then invert one diagonal 16 x 16
+//     block of T' each; wave 0 forms the off-diagonal blocks and writes T'
+//     and T' diag(gamma) (all on MFMA);
 //   * every wave then computes 2 + 2 row blocks of w^T = K^T (T' diag(gamma))^T
 //     and u^T = V^T T'^T.  The K^T / V^T operands come from the row tiles by
 //     transposing LDS reads; an accumulator of w^T holds, per lane, 4
-//     consecutive keys of one chunk row, so rows are scaled by beta and written
-//     as 8-byte runs.
+//     consecutive keys of one chunk row, so rows are scaled by beta and staged
+//     as 8-byte runs in the (by then free) row tiles, from where the w and u
+//     blocks go out as whole rows, 16 bytes per lane (scattered 8-byte stores
+//     cost the stream about 15%).
 // Rows past the end of a ragged chunk have beta = 0 and come out as zeros.
 #include "dev_common.h"
 #include "gdn_internal.h"
@@ -33,7 +37,13 @@ constexpr int NTP = 256;   // 4 waves
 struct PrepLds {
     bf16 kR[C * K];        // k rows, wide tiles
     bf16 vR[C * V];        // v rows, wide tiles
-    bf16 tb[C * C];        // T'
+    union {
+        bf16 tb[C * C];    // T'
+        struct {           // before T' is written: the diagonal inverses, per lane
+            uint2 P[4][64];
+            f32x4 Qf[4][64];
+        } dg;
+    };
     union {
         uint2 ab[10][64];  // Gram tiles (see gram_to_ab), read by invert_tprime first,
         bf16 tg[C * C];    // then overwritten by T' diag(gamma): 3 workgroups fit a CU
@@ -109,15 +119,45 @@ __global__ __launch_bounds__(NTP) void prepare_mfma_kernel(PrepArgs a) {
         store_quarter(sm.vR, tv, lane, wv);
     }
     __syncthreads();
+    // the Gram tiles, split over the waves (blocks numbered as in gram_to_ab)
+    {
+        auto kt = [&](int c, int kk) { return ldv(sm.kR, woff(16 * c + li, 4 * kk + lg)); };
+        switch (wv) {
+            case 0: gram_to_ab<0x111>(kt, sm.G2, sm.B, sm.ab, lane); break;
+            case 1: gram_to_ab<0x222>(kt, sm.G2, sm.B, sm.ab, lane); break;
+            case 2: gram_to_ab<0x044>(kt, sm.G2, sm.B, sm.ab, lane); break;
+            default: gram_to_ab<0x088>(kt, sm.G2, sm.B, sm.ab, lane); break;
+        }
+    }
+    __syncthreads();
+    // diagonal block wv of T'
+    {
+        auto one = [&](const int (&b)[1]) {
+            bf16x4 P[1];
+            f32x4 Qf[1];
+            diag_inverse(b, sm.ab, sm.G2, sm.B, lane, P, Qf);
+            sm.dg.P[b[0]][lane] = __builtin_bit_cast(uint2, P[0]);
+            sm.dg.Qf[b[0]][lane] = Qf[0];
+        };
+        switch (wv) {
+            case 0: { const int b[1] = {0}; one(b); break; }
+            case 1: { const int b[1] = {1}; one(b); break; }
+            case 2: { const int b[1] = {2}; one(b); break; }
+            default: { const int b[1] = {3}; one(b); break; }
+        }
+    }
+    __syncthreads();
     if (wv == 0) {
-        bf16x8 kt[4][4];
+        bf16x4 P[4];
+        f32x4 Qf[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR, woff(16 * c + li, 4 * kk + lg));
-        gram_to_ab(kt, sm.G2, sm.B, sm.ab, lane);
-        // this wave's own LDS writes are ordered before its reads
-        invert_tprime(sm.ab, sm.G2, sm.B, sm.tb, sm.tg, lane);
+        for (int a = 0; a < 4; ++a) {
+            P[a] = __builtin_bit_cast(bf16x4, sm.dg.P[a][lane]);
+            Qf[a] = sm.dg.Qf[a][lane];
+        }
+        // the diagonal inverses share memory with tb: offdiag_store reads
+        // everything before its first write
+        offdiag_store(sm.ab, sm.G2, P, Qf, sm.tb, sm.tg, lane);
     }
     __syncthreads();
 
@@ -131,12 +171,11 @@ __global__ __launch_bounds__(NTP) void prepare_mfma_kernel(PrepArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) bc[c] = sm.B[16 * c + li];
     const size_t blk = (size_t)chunk * H + h;
+    bf16x4 outv[2][2][4];   // [w or u][tt][c]: out[16c + li][16(2 wv + tt) + 4 lg .. +3]
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         const bf16 *src = which == 0 ? sm.kR : sm.vR;
         const bf16 *rt = which == 0 ? sm.tg : sm.tb;
-        const int ld = which == 0 ? K : V;
-        bf16 *dst = static_cast<bf16 *>(which == 0 ? a.wy_w : a.wy_u) + blk * C * ld;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int t = 2 * wv + tt;
@@ -153,13 +192,40 @@ __global__ __launch_bounds__(NTP) void prepare_mfma_kernel(PrepArgs a) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
                     if (kk <= (c >> 1)) acc = mma32(at[kk], ldv(rt, noff(16 * c + li, 4 * kk + lg)), acc);
-                // lane (r, g): out[16c + r][16t + 4g .. +3]
                 f32x4 sv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sv[e] = acc[e] * bc[c];
-                *reinterpret_cast<uint2 *>(dst + (size_t)(16 * c + li) * ld + 16 * t + 4 * lg) =
-                    __builtin_bit_cast(uint2, to4(sv));
+                outv[which][tt][c] = to4(sv);
             }
+        }
+    }
+    // stage the rows in the row tiles (every read of them is done): row r, 16-byte
+    // chunk q at chunk q ^ (r & 15) of a 256-byte row
+    __syncthreads();
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        char *stg = reinterpret_cast<char *>(which == 0 ? sm.kR : sm.vR);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int r = 16 * c + li, q = 2 * (2 * wv + tt) + (lg >> 1);
+                *reinterpret_cast<uint2 *>(stg + r * 256 + ((q ^ (r & 15)) << 4) + 8 * (lg & 1)) =
+                    __builtin_bit_cast(uint2, outv[which][tt][c]);
+            }
+    }
+    __syncthreads();
+    // whole rows out: the w and u blocks of this (chunk, head) are contiguous
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const char *stg = reinterpret_cast<const char *>(which == 0 ? sm.kR : sm.vR);
+        char *dst = reinterpret_cast<char *>(static_cast<bf16 *>(which == 0 ? a.wy_w : a.wy_u) +
+                                             blk * C * (which == 0 ? K : V));
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e16 = m * NTP + tid, r = e16 >> 4, q = e16 & 15;
+            *reinterpret_cast<uint4 *>(dst + 16 * e16) =
+                *reinterpret_cast<const uint4 *>(stg + r * 256 + ((q ^ (r & 15)) << 4));
         }
     }
 }

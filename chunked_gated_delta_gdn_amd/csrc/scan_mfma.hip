@@ -422,7 +422,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
                 sm.B[b2][lane] = bl;
                 // log2(0) = -inf: padded columns of attn vanish
                 sm.Gb[b2][lane] = g2 - __builtin_amdgcn_logf(bl);
-                gram_to_ab(kt, sm.G2[b2], sm.B[b2], sm.ab[b2], lane);
+                gram_to_ab([&](int c, int kk) { return kt[c][kk]; }, sm.G2[b2], sm.B[b2], sm.ab[b2], lane);
             }
         };
         issue(kA_, gA, bA, 0);
