@@ -201,16 +201,16 @@ def main():
     tokens = B * S
     value = tokens / (ms * 1e-3)
 
-    # dominant kernel and its roofline.  Tokens per launch: segment 0 (first
-    # emitting pass), segments 1 .. R-2 (carrying pass), segments 1 .. R-1 (emitting)
-    # the launch with the most algorithmic work: the emitting pass over segments
-    # 1 .. R-1 (its time is within a few percent of the carrying pass it follows)
+    # dominant kernel and its roofline.  Tokens per launch: segments 0 .. R-2 (segment
+    # 0 emitted beside the carrying pass of 1 .. R-2, one launch), segments 1 .. R-1
+    # (emitting).  The launch with the most algorithmic work is the emitting pass over
+    # segments 1 .. R-1 (its time is within a few percent of the launch before it).
     dom = "scan_emit" if "scan_emit" in kern else max(kern, key=kern.get)
     th = tokens * H
     bnd = gdn.segment_bounds(S, C, R)
-    n_tok = {"scan_emit_first": bnd[1], "scan_carry": bnd[R - 1] - bnd[1],
+    n_tok = {"scan_emit_first": bnd[1], "scan_carry": bnd[R - 1] - bnd[1], "scan_head_carry": bnd[R - 1],
              "scan_emit": S - bnd[1] if R > 1 else S}
-    n_seg = {"scan_emit_first": 1, "scan_carry": R - 2, "scan_emit": max(R - 1, 1)}
+    n_seg = {"scan_emit_first": 1, "scan_carry": R - 2, "scan_head_carry": R - 1, "scan_emit": max(R - 1, 1)}
     if dom in ("scan_emit", "scan_emit_first"):
         flops = flops_per_token_head(C, K, V) * n_tok[dom] * H
         nbytes = bytes_per_token_head(K, V, 2, 2) * n_tok[dom] * H + (n_seg[dom] + 1) * H * K * V * 4

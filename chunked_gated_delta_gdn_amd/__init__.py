@@ -6,8 +6,8 @@ ABI of ``include/gdn.h``); ``binding`` mirrors that ABI with ctypes and
 library; the first call does, and raises if it has not been built.
 """
 from .ops import (chunk_prepare, decode_step, forward, forward_segmented, problem_for, scan_carry,
-                  scan_emit, segment_bounds, segment_compose, split_wy)
+                  scan_emit, scan_head_carry, segment_bounds, segment_compose, split_wy)
 
 __all__ = ["chunk_prepare", "decode_step", "forward", "forward_segmented", "problem_for",
-           "scan_carry", "scan_emit", "segment_bounds", "segment_compose", "split_wy"]
+           "scan_carry", "scan_emit", "scan_head_carry", "segment_bounds", "segment_compose", "split_wy"]
 __version__ = "0.1.0"

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EORDER, GDN_ELAUNCH = range(5)
 GDN_F32, GDN_BF16 = 0, 1
-GDN_SCAN_EMIT, GDN_SCAN_CARRY = 0, 1
+GDN_SCAN_EMIT, GDN_SCAN_CARRY, GDN_SCAN_HEAD_EMIT_CARRY = 0, 1, 2
 GDN_MAX_SEQS, GDN_MAX_SEGMENTS = 256, 64
 
 _i32 = ctypes.c_int32

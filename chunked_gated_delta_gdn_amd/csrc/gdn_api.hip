@@ -12,6 +12,8 @@ hipError_t launch_scan_generic(int K, int V, int C, int dtype, bool carry, const
                                hipStream_t s);
 hipError_t launch_scan_mfma(int K, int V, int C, int dtype, bool carry, const ScanArgs &a,
                             hipStream_t s, bool *handled);
+hipError_t launch_scan_head_mfma(int K, int V, int C, int dtype, const ScanArgs &a, const float *h_in, void *o,
+                                 float *h_out, hipStream_t s, bool *handled);
 bool mfma_scan_available(int K, int V, int C, int dtype);
 
 bool shape_supported(int K, int V, int C) {
@@ -24,6 +26,31 @@ hipError_t launch_scan(int K, int V, int C, int dtype, bool carry, const ScanArg
     hipError_t e = launch_scan_mfma(K, V, C, dtype, carry, a, s, &handled);
     if (handled) return e;
     return launch_scan_generic(K, V, C, dtype, carry, a, s);
+}
+
+hipError_t launch_scan_head(int K, int V, int C, int dtype, const ScanArgs &a, const float *h_in, void *o,
+                            float *h_out, hipStream_t s) {
+    bool handled = false;
+    hipError_t e = launch_scan_head_mfma(K, V, C, dtype, a, h_in, o, h_out, s, &handled);
+    if (handled) return e;
+    // two launches: the head segments emitted, then the others carried, each over
+    // a chain table restricted to its segments (token offsets stay absolute)
+    const int R = a.ct.n_seg;
+    ScanArgs e_args = a;
+    e_args.ct.n_seg = 1;
+    e_args.ct.seg_start[1] = a.ct.seg_start[1];
+    e_args.n_chains = a.ct.n_seqs;
+    e_args.h_in = h_in;
+    e_args.o = o;
+    e_args.h_out = h_out;
+    e_args.M_out = e_args.U_out = nullptr;
+    e = launch_scan_generic(K, V, C, dtype, false, e_args, s);
+    if (e != hipSuccess) return e;
+    ScanArgs c_args = a;
+    c_args.ct.n_seg = R - 1;
+    for (int r = 0; r < R; ++r) c_args.ct.seg_start[r] = a.ct.seg_start[r + 1];
+    c_args.n_chains = a.ct.n_seqs * (R - 1);
+    return launch_scan_generic(K, V, C, dtype, true, c_args, s);
 }
 }  // namespace gdn
 
@@ -212,6 +239,47 @@ gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
                     "gdn_chunk_prepare");
 }
 
+// GDN_SCAN_HEAD_EMIT_CARRY: segment 0 of every sequence emitted, the others carried,
+// in one launch on the matrix-core path.
+static gdn_status scan_head(const gdn_problem *p, const Resolved &r, const void *q, const void *k, const void *v,
+                            const float *g, const float *beta, const void *wy, const float *h_in, void *o,
+                            float *h_out, float *M_out, float *U_out, void *stream) {
+    if (r.ct.packed || r.R < 2)
+        return fail(GDN_EINVAL, "GDN_SCAN_HEAD_EMIT_CARRY needs batch mode and n_segments >= 2 (got %d)", r.R);
+    const bool any = r.T > 0;
+    GDN_TRY(check_ptr(q, "q", any));
+    GDN_TRY(check_ptr(k, "k", any));
+    GDN_TRY(check_ptr(v, "v", any));
+    GDN_TRY(check_ptr(g, "g", any));
+    GDN_TRY(check_ptr(beta, "beta", any));
+    GDN_TRY(check_ptr(wy, "wy", false));
+    GDN_TRY(check_ptr(o, "o", any));
+    GDN_TRY(check_ptr(h_in, "h_in", false));
+    GDN_TRY(check_ptr(h_out, "h_out", false));
+    GDN_TRY(check_ptr(M_out, "M_out", true));
+    GDN_TRY(check_ptr(U_out, "U_out", true));
+    ScanArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.wy_w = wy;
+    a.wy_u = wy ? static_cast<const char *>(wy) + (size_t)r.n_chunks * p->H * p->C * p->K * elem_size(p->dtype)
+                : nullptr;
+    a.h_in = nullptr;
+    a.o = nullptr;
+    a.h_out = nullptr;
+    a.M_out = M_out;
+    a.U_out = U_out;
+    a.H = p->H;
+    a.n_chains = r.N * (r.R - 1);
+    a.ct = r.ct;
+    (void)hipGetLastError();
+    return launched(launch_scan_head(p->K, p->V, p->C, p->dtype, a, h_in, o, h_out, (hipStream_t)stream),
+                    "gdn_scan");
+}
+
 gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const void *k,
                     const void *v, const float *g, const float *beta, const void *wy,
                     const float *h_in, void *o, float *h_out, float *M_out, float *U_out,
@@ -219,8 +287,10 @@ gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const voi
     g_err[0] = 0;
     Resolved r;
     GDN_TRY(resolve(p, r));
-    if (mode != GDN_SCAN_EMIT && mode != GDN_SCAN_CARRY)
+    if (mode != GDN_SCAN_EMIT && mode != GDN_SCAN_CARRY && mode != GDN_SCAN_HEAD_EMIT_CARRY)
         return fail(GDN_EINVAL, "unknown scan mode %d", mode);
+    if (mode == GDN_SCAN_HEAD_EMIT_CARRY) return scan_head(p, r, q, k, v, g, beta, wy, h_in, o, h_out, M_out, U_out,
+                                                           stream);
     const bool carry = mode == GDN_SCAN_CARRY;
     const bool any = r.T > 0;
     GDN_TRY(check_ptr(k, "k", any));

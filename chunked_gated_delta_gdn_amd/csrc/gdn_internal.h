@@ -93,6 +93,9 @@ struct ComposeArgs {
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_scan(int K, int V, int C, int dtype, bool carry, const ScanArgs &a,
                        hipStream_t s);
+// segment 0 of every sequence emitted (h_in, o, h_out), segments 1 .. R-1 carried
+hipError_t launch_scan_head(int K, int V, int C, int dtype, const ScanArgs &a, const float *h_in, void *o,
+                            float *h_out, hipStream_t s);
 hipError_t launch_prepare(int K, int V, int C, int dtype, const PrepArgs &a, hipStream_t s);
 bool mfma_prepare_available(int K, int V, int C, int dtype);
 hipError_t launch_prepare_mfma(const PrepArgs &a, hipStream_t s);

@@ -90,26 +90,34 @@ template <> struct Lds<true> {
     float kdec[2][C];       // exp(G_C - G_r) (folded into the kT tile)
 };
 
+// What one workgroup works on: a chain (its tokens and first chunk), a head,
+// the state slot of its incoming state (emitting) or of its pair (carrying),
+// and whether it writes the final state (emitting, last segment).
+struct ScanUnit {
+    ChainSpan sp;
+    int h;
+    int64_t slot;
+    bool final_state;
+};
+
+// Workgroup id -> (unit, column half): the two halves of a unit are 8 ids apart,
+// so that round-robin dispatch puts them on one XCD.
+__device__ __forceinline__ int unit_of_block(int bid) { return ((bid >> 4) << 3) | (bid & 7); }
+__device__ __forceinline__ int half_of_block(int bid) { return (bid >> 3) & 1; }
+
 template <bool EMIT, bool WY>
-__global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_units) {
+__device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const ScanUnit &u, int cg) {
     constexpr int CPW = EMIT ? 16 : 32;   // state columns per consumer wave
     constexpr int NCT = CPW / 16;
-    __shared__ Lds<WY> sm;
     auto kslot = [](int64_t j) { return WY ? (int)(j & 1) : (int)(j % 3); };
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
 
-    const int bid = blockIdx.x;
-    const int cg = (bid >> 3) & 1;
-    const int unit = ((bid >> 4) << 3) | (bid & 7);
-    if (unit >= n_units) return;
     const int H = a.H;
-    const int h = unit % H;
-    const int chain = unit / H;
-    const ChainSpan sp = chain_span(a.ct, chain, C);
-    const int N = a.ct.n_seqs;
-    const int64_t slot = ((int64_t)sp.seg * N + sp.seq) * H + h;
+    const int h = u.h;
+    const ChainSpan sp = u.sp;
+    const int64_t slot = u.slot;
     const int64_t n_chunks = (sp.t1 - sp.t0 + C - 1) / C;
     const int64_t rowK = (int64_t)H * K;   // element stride between tokens of q, k
     const int64_t rowV = (int64_t)H * V;
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
         }
         // chain end: final state (emit, last segment) or the pair (M_r, U_r) (carry)
         if (EMIT) {
-            if (a.h_out && sp.seg == a.ct.n_seg - 1) {
+            if (a.h_out && u.final_state) {
                 const int64_t so = (int64_t)sp.seq * H + h;
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
@@ -600,6 +608,55 @@ __global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_unit
     }
 }
 
+template <bool EMIT, bool WY>
+__global__ __launch_bounds__(NT, 1) void scan_mfma_kernel(ScanArgs a, int n_units) {
+    __shared__ Lds<WY> sm;
+    const int unit = unit_of_block(blockIdx.x);
+    if (unit >= n_units) return;
+    ScanUnit u;
+    u.h = unit % a.H;
+    u.sp = chain_span(a.ct, unit / a.H, C);
+    u.slot = ((int64_t)u.sp.seg * a.ct.n_seqs + u.sp.seq) * a.H + u.h;
+    u.final_state = u.sp.seg == a.ct.n_seg - 1;
+    scan_body<EMIT, WY>(sm, a, u, half_of_block(blockIdx.x));
+}
+
+// One launch for segment 0 of every sequence emitted (from h_in, outputs o,
+// final state h_out) beside segments 1 .. R-1 carried (pairs in slots 0 .. R-2
+// of M_out, U_out).  a holds the chain table of all R segments and the
+// carrying pass's outputs; the first emit_blocks workgroups emit.
+template <bool WY>
+__global__ __launch_bounds__(NT, 1) void scan_mfma_head_kernel(ScanArgs a, const float *h_in, void *o, float *h_out,
+                                                               int emit_blocks) {
+    __shared__ Lds<WY> sm;
+    const int R = a.ct.n_seg, N = a.ct.n_seqs, H = a.H;
+    const bool emitting = (int)blockIdx.x < emit_blocks;
+    const int bid = emitting ? (int)blockIdx.x : (int)blockIdx.x - emit_blocks;
+    const int unit = unit_of_block(bid);
+    ScanUnit u;
+    u.h = unit % H;
+    if (emitting) {
+        if (unit >= N * H) return;
+        const int seq = unit / H;
+        u.sp = chain_span(a.ct, seq * R, C);
+        u.slot = (int64_t)seq * H + u.h;
+        u.final_state = true;
+        ScanArgs e = a;
+        e.h_in = h_in;
+        e.o = o;
+        e.h_out = h_out;
+        e.M_out = e.U_out = nullptr;
+        scan_body<true, WY>(sm, e, u, half_of_block(bid));
+    } else {
+        if (unit >= N * (R - 1) * H) return;
+        const int c = unit / H, seq = c / (R - 1), seg = 1 + c % (R - 1);
+        u.sp = chain_span(a.ct, seq * R + seg, C);
+        u.slot = ((int64_t)(seg - 1) * N + seq) * H + u.h;
+        u.final_state = false;
+        scan_body<false, WY>(sm, a, u, half_of_block(bid));
+    }
+}
+
 }  // namespace
 
 bool mfma_scan_available(int K_, int V_, int C_, int dtype) {
@@ -620,6 +677,21 @@ hipError_t launch_scan_mfma(int K_, int V_, int C_, int dtype, bool carry, const
     else if (carry) hipLaunchKernelGGL((scan_mfma_kernel<false, false>), g, b, 0, s, a, (int)units);
     else if (wy) hipLaunchKernelGGL((scan_mfma_kernel<true, true>), g, b, 0, s, a, (int)units);
     else hipLaunchKernelGGL((scan_mfma_kernel<true, false>), g, b, 0, s, a, (int)units);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan_head_mfma(int K_, int V_, int C_, int dtype, const ScanArgs &a, const float *h_in, void *o,
+                                 float *h_out, hipStream_t s, bool *handled) {
+    *handled = false;
+    if (!mfma_scan_available(K_, V_, C_, dtype)) return hipSuccess;
+    *handled = true;
+    const int64_t N = a.ct.n_seqs, R = a.ct.n_seg;
+    const int64_t emit_units = N * a.H, carry_units = N * (R - 1) * a.H;
+    if (emit_units == 0) return hipSuccess;
+    const int64_t emit_blocks = ((emit_units + 7) / 8) * 16, carry_blocks = ((carry_units + 7) / 8) * 16;
+    const dim3 g((unsigned)(emit_blocks + carry_blocks)), b(NT);
+    if (a.wy_w) hipLaunchKernelGGL((scan_mfma_head_kernel<true>), g, b, 0, s, a, h_in, o, h_out, (int)emit_blocks);
+    else hipLaunchKernelGGL((scan_mfma_head_kernel<false>), g, b, 0, s, a, h_in, o, h_out, (int)emit_blocks);
     return hipGetLastError();
 }
 

@@ -119,6 +119,30 @@ def scan_emit(q, k, v, g, beta, h_in=None, wy=None, chunk_size=64, cu_seqlens=No
     return o, h_out
 
 
+def scan_head_carry(q, k, v, g, beta, h_in=None, wy=None, chunk_size=64, n_segments=2, seg_starts=None,
+                    out=None):
+    """Segment 0 emitted, segments 1 .. R-1 carried (``gdn_scan`` with
+    GDN_SCAN_HEAD_EMIT_CARRY): returns (o, h1, M [R-1,B,H,K,K], U [R-1,B,H,K,V]).
+    o holds segment 0's outputs (other tokens untouched when ``out`` is given),
+    h1 [B,H,K,V] is segment 0's final state, the state entering segment 1."""
+    B, S, H, K, V = _check_inputs(q, k, v, g, beta)
+    dev = k.device
+    p = problem_for(k, v, chunk_size, None, n_segments, seg_starts)
+    _b.gdn_validate(p)
+    if h_in is not None:
+        _need(h_in, "h_in", (B, H, K, V), torch.float32, dev)
+    if wy is not None:
+        _need(wy, "wy", (_b.gdn_wy_workspace_bytes(p) // k.element_size(),), k.dtype, dev)
+    o = out if out is not None else torch.empty((B, S, H, V), dtype=k.dtype, device=dev)
+    _need(o, "o", (B, S, H, V), k.dtype, dev)
+    h1 = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+    M = torch.empty((n_segments - 1, B, H, K, K), dtype=torch.float32, device=dev)
+    U = torch.empty((n_segments - 1, B, H, K, V), dtype=torch.float32, device=dev)
+    _b.gdn_scan(p, _b.GDN_SCAN_HEAD_EMIT_CARRY, _addr(q), _addr(k), _addr(v), _addr(g), _addr(beta),
+                _addr(wy), _addr(h_in), _addr(o), _addr(h1), _addr(M), _addr(U), _stream(dev))
+    return o, h1, M, U
+
+
 def scan_carry(k, v, g, beta, wy=None, chunk_size=64, n_segments=1, seg_starts=None):
     """Carrying zero-state scan (``gdn_scan`` with GDN_SCAN_CARRY): returns
     (M [R,B,H,K,K], U [R,B,H,K,V]) with h_end = M h_start + U per segment."""
@@ -181,18 +205,7 @@ def segment_bounds(S, chunk_size, n_segments, seg_starts=None):
     return [(r * nc // n_segments) * chunk_size for r in range(n_segments)] + [S]
 
 
-_side = {}
-
-
-def _side_stream(dev):
-    s = _side.get(dev)
-    if s is None:
-        s = torch.cuda.Stream(device=dev)   # default priority
-        _side[dev] = s
-    return s
-
-
-def _untimed(_name, fn, _stream=None):
+def _untimed(_name, fn):
     return fn()
 
 
@@ -202,11 +215,11 @@ def forward_segmented(q, k, v, g, beta, h0=None, chunk_size=64, n_segments=2, se
     redundant pieces: segment 0 starts from the true initial state, so it needs
     no carried M and is emitted directly (its final state is the state entering
     segment 1); the last segment is emitted from its incoming state, so it needs
-    no carrying pass.  The emitting pass of segment 0 runs on a second stream
-    beside the carrying pass of segments 1 .. R-2; then the segment scan seeded
-    with segment 0's final state, then the emitting pass of segments 1 .. R-1.
+    no carrying pass.  One launch emits segment 0 beside the carrying pass of
+    segments 1 .. R-2 (GDN_SCAN_HEAD_EMIT_CARRY); then the segment scan seeded
+    with segment 0's final state; then the emitting pass of segments 1 .. R-1.
 
-    ``timer(name, fn, stream)`` wraps each launch (for per-kernel timing)."""
+    ``timer(name, fn)`` wraps each launch (for per-kernel timing)."""
     B, S, H, K, V = _check_inputs(q, k, v, g, beta)
     if B != 1:
         raise ValueError("forward_segmented takes one sequence (B == 1)")
@@ -218,33 +231,26 @@ def forward_segmented(q, k, v, g, beta, h0=None, chunk_size=64, n_segments=2, se
     bnd = segment_bounds(S, chunk_size, R, seg_starts)
     s1, sl = bnd[1], bnd[R - 1]
     o = torch.empty((B, S, H, V), dtype=k.dtype, device=dev)
-    main, side = torch.cuda.current_stream(dev), _side_stream(dev)
-    sl0 = slice(0, s1)
-    side.wait_stream(main)
-    with torch.cuda.stream(side):
-        _, h1 = timer("scan_emit_first", lambda: scan_emit(
-            q[:, sl0], k[:, sl0], v[:, sl0], g[:, sl0], beta[:, sl0], h_in=h0,
-            chunk_size=chunk_size, out=o[:, sl0]), side)
     if R > 2:
-        mid = slice(s1, sl)
-        M, U = timer("scan_carry", lambda: scan_carry(
-            k[:, mid], v[:, mid], g[:, mid], beta[:, mid], chunk_size=chunk_size,
-            n_segments=R - 2, seg_starts=[b - s1 for b in bnd[1:R - 1]]), main)
-    main.wait_stream(side)
-    h1.record_stream(main)
-    if R > 2:
+        head = slice(0, sl)
+        _, h1, M, U = timer("scan_head_carry", lambda: scan_head_carry(
+            q[:, head], k[:, head], v[:, head], g[:, head], beta[:, head], h_in=h0,
+            chunk_size=chunk_size, n_segments=R - 1, seg_starts=bnd[:R - 1], out=o[:, head]))
         # states entering segments 1 .. R-1: the scan's outputs, then its final state
         h_all = torch.empty((R - 1, B, H, K, V), dtype=torch.float32, device=dev)
         timer("segment_compose", lambda: _b.gdn_segment_compose(
             R - 2, B, H, K, V, _addr(M), _addr(U), _addr(h1), _addr(h_all), _addr(h_all[R - 2]),
-            _stream(dev)), main)
+            _stream(dev)))
     else:
-        h_all = h1
+        first = slice(0, s1)
+        _, h_all = timer("scan_emit_first", lambda: scan_emit(
+            q[:, first], k[:, first], v[:, first], g[:, first], beta[:, first], h_in=h0,
+            chunk_size=chunk_size, out=o[:, first]))
     rest = slice(s1, S)
     _, hT = timer("scan_emit", lambda: scan_emit(
         q[:, rest], k[:, rest], v[:, rest], g[:, rest], beta[:, rest], h_in=h_all,
         chunk_size=chunk_size, n_segments=R - 1, seg_starts=[b - s1 for b in bnd[1:R]],
-        output_final_state=output_final_state, out=o[:, rest]), main)
+        output_final_state=output_final_state, out=o[:, rest]))
     return o, hT
 
 

@@ -56,7 +56,8 @@ typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 
 typedef enum gdn_scan_mode {
     GDN_SCAN_EMIT = 0,   /* outputs o and the final state                           */
-    GDN_SCAN_CARRY = 1   /* zero-state pass per segment emitting (M_r, U_r), no o   */
+    GDN_SCAN_CARRY = 1,  /* zero-state pass per segment emitting (M_r, U_r), no o   */
+    GDN_SCAN_HEAD_EMIT_CARRY = 2  /* segment 0 emitted, segments 1 .. R-1 carried  */
 } gdn_scan_mode;
 
 #define GDN_MAX_SEQS 256
@@ -135,6 +136,15 @@ gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
  * GDN_SCAN_CARRY: for every segment, a zero-state pass carrying the composed
  *   transition: writes M_out [R,N,H,K,K] and U_out [R,N,H,K,V] with
  *   h_end = M_r h_start + U_r.  q, o, h_in, h_out are ignored.
+ * GDN_SCAN_HEAD_EMIT_CARRY (batch mode, R >= 2): phase 1 of the segment pass
+ *   without its redundant piece.  Segment 0's incoming state is known, so it
+ *   is emitted as in GDN_SCAN_EMIT from h_in [N,H,K,V] (NULL = zero): o for its
+ *   tokens (the rest of o is not written) and its final state, the state
+ *   entering segment 1, to h_out [N,H,K,V] (nullable).  Segments 1 .. R-1 are
+ *   carried as in GDN_SCAN_CARRY into M_out [R-1,N,H,K,K] and
+ *   U_out [R-1,N,H,K,V] (slot r-1 for segment r).  On the matrix-core path
+ *   (bf16, K = V = 128, C = 64) this is one launch.  GDN_EINVAL for packed
+ *   problems or R < 2.
  */
 gdn_status gdn_scan(const gdn_problem *p, int32_t mode,
                     const void *q, const void *k, const void *v,

@@ -303,6 +303,38 @@ def test_carry_pairs_match_transition(wl):
         assert em <= TOL[x.dtype] and eu <= TOL[x.dtype]
 
 
+@pytest.mark.parametrize("shape,B", [("f32", 1), ("bf16", 1), ("bf16", 2)])
+def test_head_emit_carry_matches_separate_passes(shape, B):
+    """GDN_SCAN_HEAD_EMIT_CARRY (one launch on the matrix-core path, two generic
+    launches otherwise) against the emitting pass of segment 0 and the carrying
+    pass of the rest, element for element, and segment 0's final state against
+    the oracle.  Ragged last chunk, three segments, nonzero initial state."""
+    K, C, dt = (32, 16, "f32") if shape == "f32" else (128, 64, "bf16")
+    S = 5 * C + 9
+    x = make_inputs(41, B, S, 2, K, K, C, dt, 0.02, decay="slow", name=f"head-{shape}-B{B}")
+    d = device_inputs(x)
+    R = 3
+    bnd = gdn.segment_bounds(S, C, R)
+    s1 = bnd[1]
+    o, h1, M, U = gdn.scan_head_carry(d["q"], d["k"], d["v"], d["g"], d["beta"], h_in=d["h0"], chunk_size=C,
+                                      n_segments=R)
+    head = {n: d[n][:, :s1].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    tail = {n: d[n][:, s1:].contiguous() for n in ("k", "v", "g", "beta")}
+    o_e, h1_e = gdn.scan_emit(head["q"], head["k"], head["v"], head["g"], head["beta"], h_in=d["h0"],
+                              chunk_size=C)
+    M_c, U_c = gdn.scan_carry(tail["k"], tail["v"], tail["g"], tail["beta"], chunk_size=C, n_segments=R - 1,
+                              seg_starts=[b - s1 for b in bnd[1:R]])
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :s1], o_e)
+    assert torch.equal(h1, h1_e)
+    assert torch.equal(M, M_c) and torch.equal(U, U_c)
+    _, h1_ref = oracle.forward(x.q[:, :s1], x.k[:, :s1], x.v[:, :s1], x.g[:, :s1], x.beta[:, :s1], h0=x.h0,
+                               want_o=False)
+    err = rel_err(h1.cpu().numpy(), h1_ref)
+    say(f"  head emit + carry {shape} B={B}: err(h1)={err:.3e}")
+    assert err <= TOL[dt]
+
+
 def test_segment_compose_matches_oracle_scan():
     rng = np.random.default_rng(21)
     R, N, H, K, V = 5, 2, 3, 128, 128

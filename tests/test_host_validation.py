@@ -117,6 +117,20 @@ def test_scan_rejects_bad_mode_and_missing_carry_outputs():
     assert _scan_status(prob(), mode=b.GDN_SCAN_CARRY, M=FAKE) == b.GDN_EINVAL
 
 
+def test_head_emit_carry_mode_rules():
+    """GDN_SCAN_HEAD_EMIT_CARRY needs batch mode, at least two segments, the
+    carried pairs and the emitting pass's q and o."""
+    H = b.GDN_SCAN_HEAD_EMIT_CARRY
+    full = dict(M=FAKE, U=FAKE)
+    assert _scan_status(prob(n_segments=1), mode=H, **full) == b.GDN_EINVAL
+    assert _scan_status(prob(S=100, cu_seqlens=[0, 30, 100]), mode=H, **full) == b.GDN_EINVAL
+    assert _scan_status(prob(n_segments=3), mode=H) == b.GDN_EINVAL
+    assert _scan_status(prob(n_segments=3), mode=H, M=FAKE) == b.GDN_EINVAL
+    assert _scan_status(prob(n_segments=3), mode=H, q=None, **full) == b.GDN_EINVAL
+    assert _scan_status(prob(n_segments=3), mode=H, o=None, **full) == b.GDN_EINVAL
+    assert _scan_status(prob(n_segments=3), mode=H, h_out=FAKE + 4, **full) == b.GDN_EINVAL
+
+
 def test_scan_rejects_state_alias_with_segments():
     p = prob(n_segments=4)
     assert _scan_status(p, h_in=FAKE, h_out=FAKE) == b.GDN_EINVAL
