@@ -310,20 +310,26 @@ def main():
         del q, k, v, g, beta, h0
         torch.cuda.empty_cache()
 
+        # the 4k sequence and the packed batch: one emitting scan over whole
+        # sequences, and the piece schedule (long sequences cut into pieces that
+        # run as parallel chains; the cut chosen by plan_pieces)
         for wl, name in ((1, "seq4k_h16"), (3, "packed8_32k")):
-            log(f"bench: {name}")
             y = workload(wl)
             t = lambda a, dt=None: (torch.from_numpy(a).to(dt) if dt else torch.from_numpy(a)).to(dev)
             yq, yk, yv = t(y.q, bf), t(y.k, bf), t(y.v, bf)
             yg, yb, yh = t(y.g), t(y.beta), t(y.h0)
-            cu = y.cu_seqlens
+            cu = y.cu_seqlens if y.cu_seqlens is not None else np.array([0, y.q.shape[1]], dtype=np.int32)
+            chunks = tuple(-(-(int(cu[n + 1]) - int(cu[n])) // 64) for n in range(len(cu) - 1))
+            m = gdn.plan_pieces(chunks, y.q.shape[2], torch.cuda.get_device_properties(dev).multi_processor_count)
+            for tag, mm in (("", 0), ("_pieces", m)):
+                log(f"bench: {name}{tag} (max_piece_chunks {mm})")
 
-            def fwd(timer, yq=yq, yk=yk, yv=yv, yg=yg, yb=yb, yh=yh, cu=cu):
-                tm = timer.around if timer else (lambda _n, f: f())
-                return tm("scan_emit", lambda: gdn.scan_emit(yq, yk, yv, yg, yb, h_in=yh,
-                                                             chunk_size=64, cu_seqlens=cu))
-            ms2, _ = time_steps(torch, fwd, steps2, 2)
-            extra[name] = {"tokens_per_s": y.real_tokens / (ms2 * 1e-3), "ms": ms2}
+                def fwd(timer, yq=yq, yk=yk, yv=yv, yg=yg, yb=yb, yh=yh, cu=cu, mm=mm):
+                    return gdn.forward_packed(yq, yk, yv, yg, yb, cu, h0=yh, chunk_size=64, max_piece_chunks=mm,
+                                              timer=timer.around if timer else None)
+                ms2, _ = time_steps(torch, fwd, steps2, 2)
+                extra[name + tag] = {"tokens_per_s": y.real_tokens / (ms2 * 1e-3), "ms": ms2, "max_piece_chunks": mm,
+                                     "pieces": gdn.num_pieces(yk, yv, 64, cu, mm)}
             del yq, yk, yv, yg, yb, yh
 
         log("bench: decode")

@@ -5,9 +5,11 @@ ABI of ``include/gdn.h``); ``binding`` mirrors that ABI with ctypes and
 ``ops`` wraps it for torch tensors.  Importing this package does not load the
 library; the first call does, and raises if it has not been built.
 """
-from .ops import (chunk_prepare, decode_step, forward, forward_segmented, problem_for, scan_carry,
-                  scan_emit, scan_head_carry, segment_bounds, segment_compose, split_wy)
+from .ops import (chunk_prepare, decode_step, forward, forward_packed, forward_segmented, num_pieces,
+                  piece_compose, plan_pieces, problem_for, scan_carry, scan_emit, scan_head_carry,
+                  scan_tail_emit, segment_bounds, segment_compose, split_wy)
 
-__all__ = ["chunk_prepare", "decode_step", "forward", "forward_segmented", "problem_for",
-           "scan_carry", "scan_emit", "scan_head_carry", "segment_bounds", "segment_compose", "split_wy"]
+__all__ = ["chunk_prepare", "decode_step", "forward", "forward_packed", "forward_segmented", "num_pieces",
+           "piece_compose", "plan_pieces", "problem_for", "scan_carry", "scan_emit", "scan_head_carry",
+           "scan_tail_emit", "segment_bounds", "segment_compose", "split_wy"]
 __version__ = "0.1.0"

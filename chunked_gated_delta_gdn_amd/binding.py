@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EORDER, GDN_ELAUNCH = range(5)
 GDN_F32, GDN_BF16 = 0, 1
-GDN_SCAN_EMIT, GDN_SCAN_CARRY, GDN_SCAN_HEAD_EMIT_CARRY = 0, 1, 2
+GDN_SCAN_EMIT, GDN_SCAN_CARRY, GDN_SCAN_HEAD_EMIT_CARRY, GDN_SCAN_TAIL_EMIT = 0, 1, 2, 3
 GDN_MAX_SEQS, GDN_MAX_SEGMENTS = 256, 64
 
 _i32 = ctypes.c_int32
@@ -30,14 +30,17 @@ class GdnProblem(ctypes.Structure):
         ("cu_seqlens", ctypes.POINTER(_i32)),
         ("n_segments", _i32),
         ("seg_starts", ctypes.POINTER(_i32)),
+        ("max_piece_chunks", _i32),
     ]
 
 
-def make_problem(B, S, H, K, V, C, dtype, cu_seqlens=None, n_segments=1, seg_starts=None):
+def make_problem(B, S, H, K, V, C, dtype, cu_seqlens=None, n_segments=1, seg_starts=None,
+                 max_piece_chunks=0):
     """Build a ``GdnProblem``; the host arrays it points to are kept alive on it."""
     p = GdnProblem()
     p.B, p.S, p.H, p.K, p.V, p.C, p.dtype = B, S, H, K, V, C, dtype
     p.n_segments = n_segments
+    p.max_piece_chunks = max_piece_chunks
     if cu_seqlens is not None:
         cu = [int(x) for x in cu_seqlens]
         arr = (_i32 * len(cu))(*cu)
@@ -77,11 +80,13 @@ def library():
         P = ctypes.POINTER(GdnProblem)
         sig = {
             "gdn_validate": (_i32, [P]),
+            "gdn_num_pieces": (_i32, [P]),
             "gdn_wy_workspace_bytes": (ctypes.c_size_t, [P]),
             "gdn_segment_workspace_bytes": (ctypes.c_size_t, [P]),
             "gdn_chunk_prepare": (_i32, [P, _vp, _vp, _vp, _vp, _vp, _vp]),
             "gdn_scan": (_i32, [P, _i32] + [_vp] * 12),
             "gdn_segment_compose": (_i32, [_i32] * 5 + [_vp] * 6),
+            "gdn_piece_compose": (_i32, [P, _i32] + [_vp] * 6),
             "gdn_decode_step": (_i32, [_i32] * 5 + [_vp] * 8),
             "gdn_scan_backend": (_i32, [P]),
             "gdn_status_string": (ctypes.c_char_p, [_i32]),
@@ -115,6 +120,11 @@ def gdn_validate(problem, raise_on_error=True):
     return st
 
 
+def gdn_num_pieces(problem):
+    """Pieces of a packed problem (segments B * R of a batch one); -1 if invalid."""
+    return int(library().gdn_num_pieces(ctypes.byref(problem)))
+
+
 def gdn_wy_workspace_bytes(problem):
     return int(library().gdn_wy_workspace_bytes(ctypes.byref(problem)))
 
@@ -136,6 +146,11 @@ def gdn_scan(problem, mode, q, k, v, g, beta, wy, h_in, o, h_out, M_out, U_out, 
 def gdn_segment_compose(R, N, H, K, V, M, U, h0, h_in, h_final, stream=0):
     _check(library().gdn_segment_compose(R, N, H, K, V, M, U, h0, h_in, h_final, stream),
            "gdn_segment_compose")
+
+
+def gdn_piece_compose(problem, first, M, U, h_seed, h_in, h_final, stream=0):
+    _check(library().gdn_piece_compose(ctypes.byref(problem), first, M, U, h_seed, h_in, h_final, stream),
+           "gdn_piece_compose")
 
 
 def gdn_decode_step(B, H, K, V, dtype, q, k, v, g, beta, state, o, stream=0):

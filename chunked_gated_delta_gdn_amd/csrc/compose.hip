@@ -2,6 +2,9 @@
 // context parallelism to the Gated Delta Net", section "Implementation",
 // phase 2):  h_in[0] = h0,  h_in[r+1] = M[r] h_in[r] + U[r],
 // h_final = M[R-1] h_in[R-1] + U[R-1].
+// Batch mode walks the R segments of a (sequence, head) with state rows
+// [R, N, H]; packed mode walks the pieces of one sequence (rows [P, H]) from
+// its piece `first` on.
 //
 // The columns of the state are independent under h <- M h + U, so one
 // workgroup owns a 16-column strip of one (sequence, head) state and walks
@@ -22,6 +25,19 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kStrip = 16;
 
+// Steps r0 .. r1-1 of the (sequence, head) pair nh, and the state row of step r.
+struct Steps {
+    int r0, r1;
+};
+__device__ __forceinline__ Steps compose_steps(const ComposeArgs &a, int64_t nh) {
+    if (!a.packed) return {0, a.R};
+    const int n = (int)(nh / a.H);
+    return {a.seq_first[n] + a.first, a.seq_first[n + 1]};
+}
+__device__ __forceinline__ int64_t compose_row(const ComposeArgs &a, int r, int64_t nh) {
+    return a.packed ? (int64_t)r * a.H + nh % a.H : (int64_t)r * a.N * a.H + nh;
+}
+
 template <int K, int V>
 __global__ __launch_bounds__(kThreads) void compose_kernel(ComposeArgs a) {
     constexpr int KP = K + 1;
@@ -35,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void compose_kernel(ComposeArgs a) {
     const int tid = threadIdx.x;
     const int strip = blockIdx.x % NS;
     const int64_t nh = blockIdx.x / NS;        // (n, h) flattened
-    const int64_t NH = (int64_t)a.N * a.H;
+    const Steps st = compose_steps(a, nh);
     const int j = tid % kStrip, rg = tid / kStrip;
     const int c0 = strip * kStrip;
 
@@ -45,13 +61,13 @@ __global__ __launch_bounds__(kThreads) void compose_kernel(ComposeArgs a) {
     }
     __syncthreads();
 
-    for (int r = 0; r < a.R; ++r) {
-        const int64_t slot = (int64_t)r * NH + nh;
+    for (int r = st.r0; r < st.r1; ++r) {
+        const int64_t slot = compose_row(a, r, nh);
         for (int e = tid; e < K * kStrip; e += kThreads) {
             const int i = e / kStrip, jj = e % kStrip;
             a.h_in[(slot * K + i) * V + c0 + jj] = sh[e];
         }
-        if (r == a.R - 1 && !a.h_final) break;
+        if (r == st.r1 - 1 && !a.h_final) break;
         const float *Mr = a.M + slot * K * K;
         for (int e = tid; e < K * K; e += kThreads) sM[(e / K) * KP + e % K] = Mr[e];
         __syncthreads();
@@ -93,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void compose_mfma_kernel(ComposeArgs a) {
     const int li = lane & 15, lg = lane >> 4;
     const int strip = blockIdx.x % NS;
     const int64_t nh = blockIdx.x / NS;
-    const int64_t NH = (int64_t)a.N * a.H;
+    const Steps st = compose_steps(a, nh);
     const int c0 = strip * kStrip;
 
     for (int e = tid; e < K * kStrip; e += kThreads) {
@@ -102,13 +118,13 @@ __global__ __launch_bounds__(kThreads) void compose_mfma_kernel(ComposeArgs a) {
     }
     __syncthreads();
     int cur = 0;
-    for (int r = 0; r < a.R; ++r) {
-        const int64_t slot = (int64_t)r * NH + nh;
+    for (int r = st.r0; r < st.r1; ++r) {
+        const int64_t slot = compose_row(a, r, nh);
         for (int e = tid; e < K * kStrip; e += kThreads) {
             const int i = e / kStrip, jj = e % kStrip;
             a.h_in[(slot * K + i) * V + c0 + jj] = hT[cur][jj * LD + i];
         }
-        if (r == a.R - 1 && !a.h_final) break;
+        if (r == st.r1 - 1 && !a.h_final) break;
         const float *Mr = a.M + slot * K * K;
         f32x4 ma[2][8];
 #pragma unroll

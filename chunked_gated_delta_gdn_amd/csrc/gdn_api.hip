@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -33,6 +35,22 @@ hipError_t launch_scan_head(int K, int V, int C, int dtype, const ScanArgs &a, c
     bool handled = false;
     hipError_t e = launch_scan_head_mfma(K, V, C, dtype, a, h_in, o, h_out, s, &handled);
     if (handled) return e;
+    if (a.ct.packed) {
+        // two launches over the emitting and the carrying items
+        ScanArgs e_args = a, c_args = a;
+        e_args.ct.n_items = c_args.ct.n_items = 0;
+        for (int i = 0; i < a.ct.n_items; ++i) {
+            ScanArgs &dst = (a.ct.item[i] >> 8) == kItemCarry ? c_args : e_args;
+            dst.ct.item[dst.ct.n_items++] = a.ct.item[i];
+        }
+        e_args.n_chains = e_args.ct.n_items;
+        c_args.n_chains = c_args.ct.n_items;
+        if (e_args.n_chains > 0) {
+            e = launch_scan_generic(K, V, C, dtype, false, e_args, s);
+            if (e != hipSuccess) return e;
+        }
+        return c_args.n_chains > 0 ? launch_scan_generic(K, V, C, dtype, true, c_args, s) : hipSuccess;
+    }
     // two launches: the head segments emitted, then the others carried, each over
     // a chain table restricted to its segments (token offsets stay absolute)
     const int R = a.ct.n_seg;
@@ -74,9 +92,11 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Resolved {
     int N = 0;            // sequences (B or n_seqs)
-    int R = 1;            // segments per sequence
+    int R = 1;            // segments per sequence (batch mode)
+    int P = 0;            // pieces (packed mode), N * R (batch mode)
     int64_t T = 0;        // tokens on the flattened axis
     int64_t n_chunks = 0; // chunks over all sequences
+    int16_t seq_first[GDN_MAX_SEQS + 1];   // packed mode: first piece of each sequence
     ChainTable ct;
 };
 
@@ -91,6 +111,9 @@ gdn_status resolve(const gdn_problem *p, Resolved &out) {
     if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
         return fail(GDN_EUNSUPPORTED, "dtype %d not supported", p->dtype);
     if (p->n_seqs < 0) return fail(GDN_EINVAL, "n_seqs %d < 0", p->n_seqs);
+    if (p->max_piece_chunks < 0) return fail(GDN_EINVAL, "max_piece_chunks %d < 0", p->max_piece_chunks);
+    if (p->n_seqs == 0 && p->max_piece_chunks != 0)
+        return fail(GDN_EINVAL, "max_piece_chunks applies to packed problems only (use segments)");
     memset(&out.ct, 0, sizeof(out.ct));
     const int C = p->C;
     if (p->n_seqs > 0) {
@@ -99,29 +122,48 @@ gdn_status resolve(const gdn_problem *p, Resolved &out) {
             return fail(GDN_EUNSUPPORTED, "%d sequences > GDN_MAX_SEQS", p->n_seqs);
         if (!p->cu_seqlens) return fail(GDN_EINVAL, "cu_seqlens is NULL in packed mode");
         if (p->n_segments != 1)
-            return fail(GDN_EUNSUPPORTED, "segments are not supported in packed mode");
+            return fail(GDN_EUNSUPPORTED, "segments are not supported in packed mode (use max_piece_chunks)");
         const int32_t *cu = p->cu_seqlens;
         if (cu[0] != 0) return fail(GDN_EORDER, "cu_seqlens[0] = %d, must be 0", cu[0]);
-        int64_t chunks = 0;
-        for (int n = 0; n < p->n_seqs; ++n) {
+        for (int n = 0; n < p->n_seqs; ++n)
             if (cu[n + 1] < cu[n])
                 return fail(GDN_EORDER, "cu_seqlens decreases at %d (%d -> %d)", n, cu[n],
                             cu[n + 1]);
-            out.ct.seq_start[n] = cu[n];
-            out.ct.chunk_start[n] = (int32_t)chunks;
-            chunks += cdiv(cu[n + 1] - cu[n], C);
-        }
         if (cu[p->n_seqs] != p->S)
             return fail(GDN_EINVAL, "cu_seqlens[n_seqs] = %d != S = %d", cu[p->n_seqs], p->S);
-        out.ct.seq_start[p->n_seqs] = cu[p->n_seqs];
-        out.ct.chunk_start[p->n_seqs] = (int32_t)chunks;
+        // the chains are the pieces: a sequence of nc > m chunks becomes
+        // R_n = ceil(nc / m) pieces, piece s starting at chunk s * nc / R_n
+        const int64_t m = p->max_piece_chunks;
+        int64_t chunks = 0;
+        int P = 0;
+        for (int n = 0; n < p->n_seqs; ++n) {
+            const int64_t nc = cdiv(cu[n + 1] - cu[n], C);
+            const int64_t Rn = (m > 0 && nc > m) ? cdiv(nc, m) : 1;
+            if (P + Rn > GDN_MAX_SEQS)
+                return fail(GDN_EUNSUPPORTED, "more than GDN_MAX_SEQS = %d pieces (max_piece_chunks %d)",
+                            GDN_MAX_SEQS, p->max_piece_chunks);
+            out.seq_first[n] = (int16_t)P;
+            for (int64_t sgm = 0; sgm < Rn; ++sgm) {
+                const int64_t c0 = sgm * nc / Rn;
+                out.ct.seq_start[P] = (int32_t)(cu[n] + c0 * C);
+                out.ct.chunk_start[P] = (int32_t)(chunks + c0);
+                out.ct.piece_seq[P] = (uint8_t)n;
+                out.ct.piece_last[P] = sgm == Rn - 1;
+                ++P;
+            }
+            chunks += nc;
+        }
+        out.seq_first[p->n_seqs] = (int16_t)P;
+        out.ct.seq_start[P] = cu[p->n_seqs];
+        out.ct.chunk_start[P] = (int32_t)chunks;
         out.ct.packed = 1;
-        out.ct.n_seqs = p->n_seqs;
+        out.ct.n_seqs = P;
         out.ct.n_seg = 1;
         out.ct.seg_start[0] = 0;
         out.ct.seg_start[1] = 0x3fffffff;
         out.N = p->n_seqs;
         out.R = 1;
+        out.P = P;
         out.n_chunks = chunks;
     } else {
         const int R = p->n_segments;
@@ -156,10 +198,11 @@ gdn_status resolve(const gdn_problem *p, Resolved &out) {
         out.ct.n_seg = R;
         out.N = p->B;
         out.R = R;
+        out.P = p->B * R;
         out.n_chunks = (int64_t)p->B * nc;
     }
     out.T = p->n_seqs > 0 ? (int64_t)p->S : (int64_t)p->B * p->S;
-    const int64_t wgs = (int64_t)out.N * out.R * p->H * (p->K + p->V);
+    const int64_t wgs = (int64_t)out.P * p->H * (p->K + p->V);
     if (wgs > 0x7fffffffLL || out.n_chunks * p->H > 0x7fffffffLL)
         return fail(GDN_EUNSUPPORTED, "problem too large for one launch");
     return GDN_OK;
@@ -190,6 +233,32 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     return pa < pb + nb && pb < pa + na;
 }
 
+// Packed mode: the work items of a gdn_scan launch in r.ct.item, longest piece
+// first (so that the longest chains are dispatched first).  Counts the
+// emitting and carrying items.
+void packed_items(Resolved &r, int32_t mode, int &n_emit, int &n_carry) {
+    ChainTable &ct = r.ct;
+    n_emit = n_carry = 0;
+    int n = 0;
+    for (int p = 0; p < r.P; ++p) {
+        const bool first = p == r.seq_first[ct.piece_seq[p]];
+        int kind;
+        if (mode == GDN_SCAN_EMIT) kind = kItemEmit;
+        else if (mode == GDN_SCAN_CARRY) kind = kItemCarry;
+        else if (mode == GDN_SCAN_HEAD_EMIT_CARRY) kind = first ? kItemEmitFirst : ct.piece_last[p] ? -1 : kItemCarry;
+        else kind = first ? -1 : kItemEmit;   // GDN_SCAN_TAIL_EMIT
+        if (kind < 0) continue;
+        ct.item[n++] = (uint16_t)(p | kind << 8);
+        if (kind == kItemCarry) ++n_carry;
+        else ++n_emit;
+    }
+    ct.n_items = n;
+    std::stable_sort(ct.item, ct.item + n, [&](uint16_t x, uint16_t y) {
+        const int px = x & 0xff, py = y & 0xff;
+        return ct.chunk_start[px + 1] - ct.chunk_start[px] > ct.chunk_start[py + 1] - ct.chunk_start[py];
+    });
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,6 +267,12 @@ gdn_status gdn_validate(const gdn_problem *p) {
     g_err[0] = 0;
     Resolved r;
     return resolve(p, r);
+}
+
+int32_t gdn_num_pieces(const gdn_problem *p) {
+    Resolved r;
+    if (resolve(p, r) != GDN_OK) return -1;
+    return r.P;
 }
 
 size_t gdn_wy_workspace_bytes(const gdn_problem *p) {
@@ -209,7 +284,7 @@ size_t gdn_wy_workspace_bytes(const gdn_problem *p) {
 size_t gdn_segment_workspace_bytes(const gdn_problem *p) {
     Resolved r;
     if (resolve(p, r) != GDN_OK) return 0;
-    return (size_t)r.R * r.N * p->H * p->K * (size_t)(p->K + p->V) * sizeof(float);
+    return (size_t)r.P * p->H * p->K * (size_t)(p->K + p->V) * sizeof(float);
 }
 
 gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
@@ -239,13 +314,15 @@ gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
                     "gdn_chunk_prepare");
 }
 
-// GDN_SCAN_HEAD_EMIT_CARRY: segment 0 of every sequence emitted, the others carried,
-// in one launch on the matrix-core path.
-static gdn_status scan_head(const gdn_problem *p, const Resolved &r, const void *q, const void *k, const void *v,
+// GDN_SCAN_HEAD_EMIT_CARRY: segment 0 (first piece) of every sequence emitted, the
+// others carried, in one launch on the matrix-core path.
+static gdn_status scan_head(const gdn_problem *p, Resolved &r, const void *q, const void *k, const void *v,
                             const float *g, const float *beta, const void *wy, const float *h_in, void *o,
                             float *h_out, float *M_out, float *U_out, void *stream) {
-    if (r.ct.packed || r.R < 2)
-        return fail(GDN_EINVAL, "GDN_SCAN_HEAD_EMIT_CARRY needs batch mode and n_segments >= 2 (got %d)", r.R);
+    if (!r.ct.packed && r.R < 2)
+        return fail(GDN_EINVAL, "GDN_SCAN_HEAD_EMIT_CARRY needs n_segments >= 2 in batch mode (got %d)", r.R);
+    int n_emit = 0, n_carry = 1;
+    if (r.ct.packed) packed_items(r, GDN_SCAN_HEAD_EMIT_CARRY, n_emit, n_carry);
     const bool any = r.T > 0;
     GDN_TRY(check_ptr(q, "q", any));
     GDN_TRY(check_ptr(k, "k", any));
@@ -256,8 +333,8 @@ static gdn_status scan_head(const gdn_problem *p, const Resolved &r, const void 
     GDN_TRY(check_ptr(o, "o", any));
     GDN_TRY(check_ptr(h_in, "h_in", false));
     GDN_TRY(check_ptr(h_out, "h_out", false));
-    GDN_TRY(check_ptr(M_out, "M_out", true));
-    GDN_TRY(check_ptr(U_out, "U_out", true));
+    GDN_TRY(check_ptr(M_out, "M_out", n_carry > 0));
+    GDN_TRY(check_ptr(U_out, "U_out", n_carry > 0));
     ScanArgs a;
     a.q = q;
     a.k = k;
@@ -275,6 +352,14 @@ static gdn_status scan_head(const gdn_problem *p, const Resolved &r, const void 
     a.H = p->H;
     a.n_chains = r.N * (r.R - 1);
     a.ct = r.ct;
+    if (r.ct.packed) {
+        // the items say which pieces emit and which carry; every pointer rides in a
+        a.h_in = h_in;
+        a.o = o;
+        a.h_out = h_out;
+        a.n_chains = r.ct.n_items;
+        if (a.n_chains == 0) return GDN_OK;
+    }
     (void)hipGetLastError();
     return launched(launch_scan_head(p->K, p->V, p->C, p->dtype, a, h_in, o, h_out, (hipStream_t)stream),
                     "gdn_scan");
@@ -287,11 +372,16 @@ gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const voi
     g_err[0] = 0;
     Resolved r;
     GDN_TRY(resolve(p, r));
-    if (mode != GDN_SCAN_EMIT && mode != GDN_SCAN_CARRY && mode != GDN_SCAN_HEAD_EMIT_CARRY)
+    if (mode != GDN_SCAN_EMIT && mode != GDN_SCAN_CARRY && mode != GDN_SCAN_HEAD_EMIT_CARRY &&
+        mode != GDN_SCAN_TAIL_EMIT)
         return fail(GDN_EINVAL, "unknown scan mode %d", mode);
     if (mode == GDN_SCAN_HEAD_EMIT_CARRY) return scan_head(p, r, q, k, v, g, beta, wy, h_in, o, h_out, M_out, U_out,
                                                            stream);
+    if (mode == GDN_SCAN_TAIL_EMIT && !r.ct.packed)
+        return fail(GDN_EINVAL, "GDN_SCAN_TAIL_EMIT needs a packed problem (batch callers slice the tensors)");
     const bool carry = mode == GDN_SCAN_CARRY;
+    int n_emit = 0, n_carry = 0;
+    if (r.ct.packed) packed_items(r, mode, n_emit, n_carry);
     const bool any = r.T > 0;
     GDN_TRY(check_ptr(k, "k", any));
     GDN_TRY(check_ptr(v, "v", any));
@@ -306,10 +396,11 @@ gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const voi
         GDN_TRY(check_ptr(o, "o", any));
         GDN_TRY(check_ptr(h_in, "h_in", false));
         GDN_TRY(check_ptr(h_out, "h_out", false));
-        if (h_out && h_in && r.R > 1) {
+        // h_in rows: [R, N] segments (batch) or [P] pieces (packed)
+        if (h_out && h_in && r.P > r.N) {
             const size_t state = (size_t)p->H * p->K * p->V * sizeof(float);
-            if (overlaps(h_in, state * r.R * r.N, h_out, state * r.N))
-                return fail(GDN_EINVAL, "h_out may alias h_in only with one segment");
+            if (overlaps(h_in, state * r.P, h_out, state * r.N))
+                return fail(GDN_EINVAL, "h_out may alias h_in only with one segment (piece) per sequence");
         }
     }
     ScanArgs a;
@@ -328,8 +419,9 @@ gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const voi
     a.M_out = carry ? M_out : nullptr;
     a.U_out = carry ? U_out : nullptr;
     a.H = p->H;
-    a.n_chains = r.N * r.R;
+    a.n_chains = r.ct.packed ? r.ct.n_items : r.N * r.R;
     a.ct = r.ct;
+    if (a.n_chains == 0) return GDN_OK;
     (void)hipGetLastError();
     return launched(launch_scan(p->K, p->V, p->C, p->dtype, carry, a, (hipStream_t)stream),
                     "gdn_scan");
@@ -359,6 +451,7 @@ gdn_status gdn_segment_compose(int32_t R, int32_t N, int32_t H, int32_t K, int32
         overlaps(h_final, nh * sz_state, U, R * nh * sz_state))
         return fail(GDN_EINVAL, "h_in / h_final must not alias the inputs or each other");
     ComposeArgs a;
+    memset(&a, 0, sizeof(a));
     a.M = M;
     a.U = U;
     a.h0 = h0;
@@ -369,6 +462,50 @@ gdn_status gdn_segment_compose(int32_t R, int32_t N, int32_t H, int32_t K, int32
     a.H = H;
     (void)hipGetLastError();
     return launched(launch_compose(K, V, a, (hipStream_t)stream), "gdn_segment_compose");
+}
+
+gdn_status gdn_piece_compose(const gdn_problem *p, int32_t first, const float *M, const float *U,
+                             const float *h_seed, float *h_in, float *h_final, void *stream) {
+    g_err[0] = 0;
+    Resolved r;
+    GDN_TRY(resolve(p, r));
+    if (!r.ct.packed) return fail(GDN_EINVAL, "gdn_piece_compose needs a packed problem (use gdn_segment_compose)");
+    if (first != 0 && first != 1) return fail(GDN_EINVAL, "first = %d, must be 0 or 1", first);
+    if (r.N == 0) return GDN_OK;
+    // which buffers some sequence touches
+    bool writes_in = false, reads_mu = false;
+    for (int n = 0; n < r.N; ++n) {
+        const int steps = r.seq_first[n + 1] - r.seq_first[n] - first;
+        writes_in |= steps >= 1;
+        reads_mu |= steps >= (h_final ? 1 : 2);
+    }
+    if (!writes_in && !h_final) return GDN_OK;   // nothing to do
+    GDN_TRY(check_ptr(M, "M", reads_mu));
+    GDN_TRY(check_ptr(U, "U", reads_mu));
+    GDN_TRY(check_ptr(h_seed, "h_seed", false));
+    GDN_TRY(check_ptr(h_in, "h_in", writes_in));
+    GDN_TRY(check_ptr(h_final, "h_final", false));
+    const size_t state = (size_t)p->H * p->K * p->V * sizeof(float);
+    const size_t sz_in = r.P * state, sz_seq = r.N * state, sz_m = (size_t)r.P * p->H * p->K * p->K * sizeof(float);
+    if (overlaps(h_in, sz_in, M, sz_m) || overlaps(h_in, sz_in, U, sz_in) || overlaps(h_in, sz_in, h_seed, sz_seq) ||
+        overlaps(h_final, sz_seq, h_in, sz_in) || overlaps(h_final, sz_seq, M, sz_m) ||
+        overlaps(h_final, sz_seq, U, sz_in))
+        return fail(GDN_EINVAL, "h_in / h_final must not alias the inputs or each other");
+    ComposeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.M = M;
+    a.U = U;
+    a.h0 = h_seed;
+    a.h_in = h_in;
+    a.h_final = h_final;
+    a.R = 0;
+    a.N = r.N;
+    a.H = p->H;
+    a.packed = 1;
+    a.first = first;
+    for (int n = 0; n <= r.N; ++n) a.seq_first[n] = r.seq_first[n];
+    (void)hipGetLastError();
+    return launched(launch_compose(p->K, p->V, a, (hipStream_t)stream), "gdn_piece_compose");
 }
 
 gdn_status gdn_decode_step(int32_t B, int32_t H, int32_t K, int32_t V, int32_t dtype,
@@ -423,6 +560,6 @@ const char *gdn_status_string(int32_t status) {
 
 const char *gdn_last_error(void) { return g_err; }
 
-int32_t gdn_version(void) { return 100; }
+int32_t gdn_version(void) { return 110; }
 
 }  // extern "C"

@@ -8,14 +8,25 @@
 
 namespace gdn {
 
+// What a packed-mode scan launch does with one piece.
+enum ItemKind : int {
+    kItemEmit = 0,       // emit from h_in[piece]; the sequence's last piece writes h_out[sequence]
+    kItemEmitFirst = 1,  // emit from h_in[sequence]; writes h_out[sequence]
+    kItemCarry = 2,      // zero-state pass into M_out, U_out [piece]
+};
+
 // Where every chain (one sequence segment) lives on the flattened token axis.
 // Passed by value as a kernel argument.
 //   batch mode:  sequence n owns tokens [n*seq_len, (n+1)*seq_len)
-//   packed mode: sequence n owns tokens [seq_start[n], seq_start[n+1])
+//   packed mode: the chains are the pieces of the sequences (n_seg == 1):
+//                piece p owns tokens [seq_start[p], seq_start[p+1]), and
+//                n_seqs counts pieces
 // Segment r of a sequence starts seg_start[r] tokens after the sequence start
 // and ends at seg_start[r+1] (seg_start[n_seg] is a large sentinel clipped to
 // the sequence end).  Chunks are counted per sequence: chunk j of sequence n
 // starts at token start(n) + j*C and has global index chunk_base(n) + j.
+// (Pieces start on chunk boundaries of their sequence, so a piece's chunk
+// numbering is its sequence's.)
 struct ChainTable {
     int32_t n_seqs;
     int32_t n_seg;
@@ -24,6 +35,11 @@ struct ChainTable {
     int32_t seq_start[GDN_MAX_SEQS + 1];
     int32_t chunk_start[GDN_MAX_SEQS + 1];
     int32_t seg_start[GDN_MAX_SEGMENTS + 1];
+    // packed mode: the launch's work items, longest first
+    int32_t n_items;
+    uint16_t item[GDN_MAX_SEQS];        // piece | ItemKind << 8
+    uint8_t piece_seq[GDN_MAX_SEQS];    // sequence of each piece
+    uint8_t piece_last[GDN_MAX_SEQS];   // 1 for the last piece of its sequence
 };
 
 struct ChainSpan {
@@ -54,6 +70,41 @@ __host__ __device__ inline ChainSpan chain_span(const ChainTable &ct, int chain,
     return s;
 }
 
+// One (chain, head) unit of a scan launch: its tokens and its state rows
+// (row indices of [.., H, K, *] state arrays, head included).
+struct UnitRef {
+    ChainSpan sp;
+    int64_t slot;       // emit: h_in row; carry: M_out / U_out row
+    int64_t out_slot;   // emit: h_out row
+    bool final_state;   // emit: writes h_out
+    bool carry;
+};
+
+// Batch mode: chain = seq * n_seg + seg; h_in, M_out, U_out are [R, N, H].
+__host__ __device__ inline UnitRef batch_unit(const ChainTable &ct, int chain, int h, int H, int C, bool carry) {
+    UnitRef u;
+    u.sp = chain_span(ct, chain, C);
+    u.slot = ((int64_t)u.sp.seg * ct.n_seqs + u.sp.seq) * H + h;
+    u.out_slot = (int64_t)u.sp.seq * H + h;
+    u.final_state = u.sp.seg == ct.n_seg - 1;
+    u.carry = carry;
+    return u;
+}
+
+// Packed mode: item i of the launch.
+__host__ __device__ inline UnitRef packed_unit(const ChainTable &ct, int i, int h, int H, int C) {
+    const int code = ct.item[i];
+    const int p = code & 0xff, kind = code >> 8;
+    const int n = ct.piece_seq[p];
+    UnitRef u;
+    u.sp = chain_span(ct, p, C);
+    u.slot = (int64_t)(kind == kItemEmitFirst ? n : p) * H + h;
+    u.out_slot = (int64_t)n * H + h;
+    u.final_state = kind == kItemEmitFirst || ct.piece_last[p] != 0;
+    u.carry = kind == kItemCarry;
+    return u;
+}
+
 struct ScanArgs {
     const void *q, *k, *v;
     const float *g, *beta;
@@ -63,9 +114,11 @@ struct ScanArgs {
     float *h_out;
     float *M_out, *U_out;
     int32_t H;
-    int32_t n_chains;
+    int32_t n_chains;   // batch mode: chains; packed mode: ct.n_items
     ChainTable ct;
 };
+// kernel arguments stay within the 4 KiB the runtime passes
+static_assert(sizeof(ScanArgs) + 64 <= 4096, "scan kernel arguments too large");
 
 struct PrepArgs {
     const void *k, *v;
@@ -88,6 +141,10 @@ struct ComposeArgs {
     const float *M, *U, *h0;
     float *h_in, *h_final;
     int32_t R, N, H;
+    // packed mode: sequence n's pieces are seq_first[n] .. seq_first[n+1]-1;
+    // the scan starts at piece `first` of each; state rows are [P, H]
+    int32_t packed, first;
+    int16_t seq_first[GDN_MAX_SEQS + 1];
 };
 
 // Launchers (return the hipError_t of the launch).

@@ -132,12 +132,13 @@ __global__ __launch_bounds__(kThreads) void scan_generic(ScanArgs a) {
     const int H = a.H;
     const int h = bid % H;
     const int chain = bid / H;
-    const ChainSpan sp = chain_span(a.ct, chain, C);
-    const int N = a.ct.n_seqs;
+    const UnitRef ur = a.ct.packed ? packed_unit(a.ct, chain, h, H, C) : batch_unit(a.ct, chain, h, H, C, CARRY);
+    if (ur.carry != CARRY) return;   // an item of the other kind (the host never lists one)
+    const ChainSpan sp = ur.sp;
     const int col0 = cg * NCOL;
     const bool is_M = CARRY && col0 < K;
     const int hc0 = CARRY ? col0 - K : col0;
-    const int64_t slot = ((int64_t)sp.seg * N + sp.seq) * H + h;   // [R,N,H] index
+    const int64_t slot = ur.slot;   // state row of h_in (emit) or M_out / U_out (carry)
     const bool active = tid < NCOL;
 
     float x[K];
@@ -249,8 +250,8 @@ __global__ __launch_bounds__(kThreads) void scan_generic(ScanArgs a) {
 #pragma unroll
                 for (int i = 0; i < K; ++i) a.U_out[(slot * K + i) * V + hc0 + tid] = x[i];
             }
-        } else if (a.h_out && sp.seg == a.ct.n_seg - 1) {
-            const int64_t so = (int64_t)sp.seq * H + h;
+        } else if (a.h_out && ur.final_state) {
+            const int64_t so = ur.out_slot;
 #pragma unroll
             for (int i = 0; i < K; ++i) a.h_out[(so * K + i) * V + hc0 + tid] = x[i];
         }

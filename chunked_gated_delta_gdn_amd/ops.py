@@ -6,15 +6,19 @@ chains the entry points exactly as the three-phase pass of the MaxText PR "Add
 context parallelism to the Gated Delta Net" (section "Implementation")
 describes: one segment runs a single emitting scan; several segments run the
 carrying scan (phase 1), the exclusive segment scan (phase 2) and the emitting
-scan from the true incoming states (phase 3).
+scan from the true incoming states (phase 3).  Packed batches run the same
+pass over pieces of their long sequences (``forward_packed``).
 """
+import functools
+import heapq
+
 import torch
 
 from . import binding as _b
 
 __all__ = ["problem_for", "chunk_prepare", "scan_emit", "scan_carry", "segment_compose",
-           "segment_bounds", "forward_segmented",
-           "decode_step", "forward"]
+           "segment_bounds", "forward_segmented", "num_pieces", "scan_tail_emit", "piece_compose",
+           "plan_pieces", "forward_packed", "decode_step", "forward"]
 
 
 def _dtype_code(t):
@@ -47,12 +51,20 @@ def _need(t, name, shape, dtype, device):
     return t
 
 
-def problem_for(k, v, chunk_size, cu_seqlens=None, n_segments=1, seg_starts=None):
+def problem_for(k, v, chunk_size, cu_seqlens=None, n_segments=1, seg_starts=None, max_piece_chunks=0):
     """The ``gdn_problem`` of batch tensors k [B,S,H,K], v [B,S,H,V]."""
     B, S, H, K = k.shape
     V = v.shape[-1]
     return _b.make_problem(B, S, H, K, V, chunk_size, _dtype_code(k), cu_seqlens=cu_seqlens,
-                           n_segments=n_segments, seg_starts=seg_starts)
+                           n_segments=n_segments, seg_starts=seg_starts,
+                           max_piece_chunks=max_piece_chunks)
+
+
+def num_pieces(k, v, chunk_size, cu_seqlens, max_piece_chunks):
+    """Pieces P of a packed problem (``gdn_num_pieces``)."""
+    p = problem_for(k, v, chunk_size, cu_seqlens, max_piece_chunks=max_piece_chunks)
+    _b.gdn_validate(p)
+    return _b.gdn_num_pieces(p)
 
 
 def _n_seqs(k, cu_seqlens):
@@ -96,18 +108,22 @@ def split_wy(wy, k, v, chunk_size, cu_seqlens=None):
 
 
 def scan_emit(q, k, v, g, beta, h_in=None, wy=None, chunk_size=64, cu_seqlens=None,
-              n_segments=1, seg_starts=None, output_final_state=True, out=None):
+              n_segments=1, seg_starts=None, output_final_state=True, out=None, max_piece_chunks=0):
     """Emitting scan (``gdn_scan`` with GDN_SCAN_EMIT): returns (o, h_out).
 
     h_in is [N,H,K,V] for one segment, or [R,N,H,K,V] (the state entering each
-    segment) for R segments; None means zero state everywhere."""
+    segment) for R segments, or [P,H,K,V] (per piece) for a packed problem cut
+    into pieces; None means zero state everywhere."""
     B, S, H, K, V = _check_inputs(q, k, v, g, beta)
     dev = k.device
     N = _n_seqs(k, cu_seqlens)
-    p = problem_for(k, v, chunk_size, cu_seqlens, n_segments, seg_starts)
+    p = problem_for(k, v, chunk_size, cu_seqlens, n_segments, seg_starts, max_piece_chunks)
     _b.gdn_validate(p)
     if h_in is not None:
-        shape = (N, H, K, V) if n_segments == 1 else (n_segments, N, H, K, V)
+        if cu_seqlens is not None:
+            shape = (_b.gdn_num_pieces(p), H, K, V)
+        else:
+            shape = (N, H, K, V) if n_segments == 1 else (n_segments, N, H, K, V)
         _need(h_in, "h_in", shape, torch.float32, dev)
     if wy is not None:
         _need(wy, "wy", (_b.gdn_wy_workspace_bytes(p) // k.element_size(),), k.dtype, dev)
@@ -120,40 +136,53 @@ def scan_emit(q, k, v, g, beta, h_in=None, wy=None, chunk_size=64, cu_seqlens=No
 
 
 def scan_head_carry(q, k, v, g, beta, h_in=None, wy=None, chunk_size=64, n_segments=2, seg_starts=None,
-                    out=None):
+                    out=None, cu_seqlens=None, max_piece_chunks=0, h_out=None):
     """Segment 0 emitted, segments 1 .. R-1 carried (``gdn_scan`` with
     GDN_SCAN_HEAD_EMIT_CARRY): returns (o, h1, M [R-1,B,H,K,K], U [R-1,B,H,K,V]).
     o holds segment 0's outputs (other tokens untouched when ``out`` is given),
-    h1 [B,H,K,V] is segment 0's final state, the state entering segment 1."""
+    h1 [B,H,K,V] is segment 0's final state, the state entering segment 1.
+
+    Packed problems (cu_seqlens, max_piece_chunks): the first piece of every
+    sequence is emitted from h_in [N,H,K,V] and the middle pieces carried;
+    returns (o, h1 [N,H,K,V], M [P,H,K,K], U [P,H,K,V]) with the rows of
+    pieces that are not carried left unwritten."""
     B, S, H, K, V = _check_inputs(q, k, v, g, beta)
     dev = k.device
-    p = problem_for(k, v, chunk_size, None, n_segments, seg_starts)
+    packed = cu_seqlens is not None
+    N = _n_seqs(k, cu_seqlens)
+    p = problem_for(k, v, chunk_size, cu_seqlens, 1 if packed else n_segments, None if packed else seg_starts,
+                    max_piece_chunks)
     _b.gdn_validate(p)
     if h_in is not None:
-        _need(h_in, "h_in", (B, H, K, V), torch.float32, dev)
+        _need(h_in, "h_in", (N, H, K, V), torch.float32, dev)
     if wy is not None:
         _need(wy, "wy", (_b.gdn_wy_workspace_bytes(p) // k.element_size(),), k.dtype, dev)
     o = out if out is not None else torch.empty((B, S, H, V), dtype=k.dtype, device=dev)
     _need(o, "o", (B, S, H, V), k.dtype, dev)
-    h1 = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
-    M = torch.empty((n_segments - 1, B, H, K, K), dtype=torch.float32, device=dev)
-    U = torch.empty((n_segments - 1, B, H, K, V), dtype=torch.float32, device=dev)
+    h1 = h_out if h_out is not None else torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    _need(h1, "h_out", (N, H, K, V), torch.float32, dev)
+    lead = (_b.gdn_num_pieces(p),) if packed else (n_segments - 1, B)
+    M = torch.empty(lead + (H, K, K), dtype=torch.float32, device=dev)
+    U = torch.empty(lead + (H, K, V), dtype=torch.float32, device=dev)
     _b.gdn_scan(p, _b.GDN_SCAN_HEAD_EMIT_CARRY, _addr(q), _addr(k), _addr(v), _addr(g), _addr(beta),
                 _addr(wy), _addr(h_in), _addr(o), _addr(h1), _addr(M), _addr(U), _stream(dev))
     return o, h1, M, U
 
 
-def scan_carry(k, v, g, beta, wy=None, chunk_size=64, n_segments=1, seg_starts=None):
+def scan_carry(k, v, g, beta, wy=None, chunk_size=64, n_segments=1, seg_starts=None, cu_seqlens=None,
+               max_piece_chunks=0):
     """Carrying zero-state scan (``gdn_scan`` with GDN_SCAN_CARRY): returns
-    (M [R,B,H,K,K], U [R,B,H,K,V]) with h_end = M h_start + U per segment."""
+    (M [R,B,H,K,K], U [R,B,H,K,V]) with h_end = M h_start + U per segment, or
+    (M [P,H,K,K], U [P,H,K,V]) per piece of a packed problem."""
     B, S, H, K, V = _check_inputs(None, k, v, g, beta)
     dev = k.device
-    p = problem_for(k, v, chunk_size, None, n_segments, seg_starts)
+    p = problem_for(k, v, chunk_size, cu_seqlens, n_segments, seg_starts, max_piece_chunks)
     _b.gdn_validate(p)
     if wy is not None:
         _need(wy, "wy", (_b.gdn_wy_workspace_bytes(p) // k.element_size(),), k.dtype, dev)
-    M = torch.empty((n_segments, B, H, K, K), dtype=torch.float32, device=dev)
-    U = torch.empty((n_segments, B, H, K, V), dtype=torch.float32, device=dev)
+    lead = (_b.gdn_num_pieces(p),) if cu_seqlens is not None else (n_segments, B)
+    M = torch.empty(lead + (H, K, K), dtype=torch.float32, device=dev)
+    U = torch.empty(lead + (H, K, V), dtype=torch.float32, device=dev)
     _b.gdn_scan(p, _b.GDN_SCAN_CARRY, None, _addr(k), _addr(v), _addr(g), _addr(beta),
                 _addr(wy), None, None, None, _addr(M), _addr(U), _stream(dev))
     return M, U
@@ -174,6 +203,166 @@ def segment_compose(M, U, h0=None, want_final=False):
     _b.gdn_segment_compose(R, N, H, K, V, _addr(M), _addr(U), _addr(h0), _addr(h_in),
                            _addr(h_final), _stream(dev))
     return h_in, h_final
+
+
+def scan_tail_emit(q, k, v, g, beta, h_in, cu_seqlens, max_piece_chunks, wy=None, chunk_size=64,
+                   out=None, h_out=None):
+    """Pieces 1 .. R_n-1 of every sequence of a packed problem emitted from
+    h_in [P,H,K,V] (``gdn_scan`` with GDN_SCAN_TAIL_EMIT): returns (o, h_out).
+    Tokens of first pieces in o, and h_out rows of one-piece sequences, are not
+    written (pass ``out`` / ``h_out`` holding them)."""
+    B, S, H, K, V = _check_inputs(q, k, v, g, beta)
+    dev = k.device
+    N = _n_seqs(k, cu_seqlens)
+    p = problem_for(k, v, chunk_size, cu_seqlens, max_piece_chunks=max_piece_chunks)
+    _b.gdn_validate(p)
+    if h_in is not None:
+        _need(h_in, "h_in", (_b.gdn_num_pieces(p), H, K, V), torch.float32, dev)
+    if wy is not None:
+        _need(wy, "wy", (_b.gdn_wy_workspace_bytes(p) // k.element_size(),), k.dtype, dev)
+    o = out if out is not None else torch.empty((B, S, H, V), dtype=k.dtype, device=dev)
+    _need(o, "o", (B, S, H, V), k.dtype, dev)
+    if h_out is None:
+        h_out = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    _need(h_out, "h_out", (N, H, K, V), torch.float32, dev)
+    _b.gdn_scan(p, _b.GDN_SCAN_TAIL_EMIT, _addr(q), _addr(k), _addr(v), _addr(g), _addr(beta),
+                _addr(wy), _addr(h_in), _addr(o), _addr(h_out), None, None, _stream(dev))
+    return o, h_out
+
+
+def piece_compose(k, v, M, U, cu_seqlens, max_piece_chunks, chunk_size=64, first=0, h_seed=None,
+                  want_final=False):
+    """Per-sequence scan over the pieces of a packed problem
+    (``gdn_piece_compose``): returns (h_in [P,H,K,V], h_final [N,H,K,V] or None).
+    Rows of h_in before piece ``first`` of each sequence are not written."""
+    B, S, H, K = k.shape
+    V = v.shape[-1]
+    dev = M.device
+    N = _n_seqs(k, cu_seqlens)
+    p = problem_for(k, v, chunk_size, cu_seqlens, max_piece_chunks=max_piece_chunks)
+    _b.gdn_validate(p)
+    P = _b.gdn_num_pieces(p)
+    _need(M, "M", (P, H, K, K), torch.float32, dev)
+    _need(U, "U", (P, H, K, V), torch.float32, dev)
+    if h_seed is not None:
+        _need(h_seed, "h_seed", (N, H, K, V), torch.float32, dev)
+    h_in = torch.empty((P, H, K, V), dtype=torch.float32, device=dev)
+    h_final = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if want_final else None
+    _b.gdn_piece_compose(p, first, _addr(M), _addr(U), _addr(h_seed), _addr(h_in), _addr(h_final),
+                         _stream(dev))
+    return h_in, h_final
+
+
+def _lpt_makespan(items, n_cu):
+    """Finish time of list scheduling (longest first) of `items` = [(length,
+    count)] workgroups on n_cu compute units, one workgroup per unit."""
+    free = [0] * n_cu
+    for length, count in sorted(items, reverse=True):
+        if length == 0:
+            continue
+        for _ in range(count):
+            heapq.heapreplace(free, free[0] + length)
+    return max(free)
+
+
+def _piece_chunks(nc, m):
+    """Chunk counts of the pieces of a sequence of nc chunks (the library's split)."""
+    if m <= 0 or nc <= m:
+        return [nc]
+    R = -(-nc // m)
+    return [(s + 1) * nc // R - s * nc // R for s in range(R)]
+
+
+@functools.lru_cache(maxsize=256)
+def plan_pieces(chunks, heads, n_cu, overhead=12, max_pieces=_b.GDN_MAX_SEQS):
+    """max_piece_chunks for a packed batch whose sequences have ``chunks``
+    chunks (a tuple), or 0 when cutting pieces does not pay.
+
+    Cost model: every (piece, head) runs as two workgroups, one per compute
+    unit, for as many chunk steps as the piece has chunks; the emitting and
+    carrying steps cost about the same; a launch takes the longest-first list
+    schedule's makespan.  One piece per sequence is one launch; pieces take
+    two launches (first pieces emitted with the middle ones carried; then the
+    rest emitted) plus ``overhead`` chunk steps for the compose and the extra
+    launch.  Candidates are the caps that split the longest sequence into
+    2 .. 32 pieces."""
+    w = 2 * heads
+    best, best_cost = 0, _lpt_makespan([(c, w) for c in chunks], n_cu)
+    top = max(chunks, default=0)
+    for r in range(2, 33):
+        m = -(-top // r)
+        if m < 1:
+            break
+        first, tail = [], []
+        n_pieces = 0
+        for c in chunks:
+            pcs = _piece_chunks(c, m)
+            n_pieces += len(pcs)
+            first.append((pcs[0], w))
+            first += [(x, w) for x in pcs[1:-1]]
+            tail += [(x, w) for x in pcs[1:]]
+        if n_pieces > max_pieces:
+            break
+        cost = _lpt_makespan(first, n_cu) + _lpt_makespan(tail, n_cu) + overhead
+        if cost < best_cost:
+            best, best_cost = m, cost
+    return best
+
+
+def forward_packed(q, k, v, g, beta, cu_seqlens, h0=None, chunk_size=64, max_piece_chunks=None,
+                   wy=None, output_final_state=True, timer=None):
+    """Packed batch with long sequences cut into pieces: the segment pass
+    without redundant work over pieces (first pieces emitted beside the
+    carried middle ones, the per-sequence scan from the first pieces' final
+    states, then the other pieces emitted).  ``max_piece_chunks=None`` picks
+    the cut with ``plan_pieces``; a cut that leaves every sequence whole runs
+    one emitting scan.  Returns (o, final states or None).
+
+    One problem description, one validation and two allocations serve the
+    three launches, so that short workloads are not bound by host work."""
+    timer = timer or _untimed
+    B, S, H, K, V = _check_inputs(q, k, v, g, beta)
+    dev = k.device
+    cu = [int(x) for x in cu_seqlens]
+    N = len(cu) - 1
+    if max_piece_chunks is None:
+        chunks = tuple(-(-(cu[n + 1] - cu[n]) // chunk_size) for n in range(N))
+        max_piece_chunks = plan_pieces(chunks, H, _n_cu(dev))
+    p = problem_for(k, v, chunk_size, cu, max_piece_chunks=max_piece_chunks)
+    _b.gdn_validate(p)
+    P = _b.gdn_num_pieces(p)
+    if h0 is not None:
+        _need(h0, "h0", (N, H, K, V), torch.float32, dev)
+    if wy is not None:
+        _need(wy, "wy", (_b.gdn_wy_workspace_bytes(p) // k.element_size(),), k.dtype, dev)
+    st = _stream(dev)
+    args = (_addr(q), _addr(k), _addr(v), _addr(g), _addr(beta), _addr(wy))
+    o = torch.empty((B, S, H, V), dtype=k.dtype, device=dev)
+    if P == N:
+        hT = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
+        timer("scan_emit", lambda: _b.gdn_scan(p, _b.GDN_SCAN_EMIT, *args, _addr(h0), _addr(o), _addr(hT),
+                                               None, None, st))
+        return o, hT
+    # one fp32 buffer: M [P,H,K,K], U [P,H,K,V], h_in [P,H,K,V], final states [N,H,K,V]
+    nm, ns = P * H * K * K, P * H * K * V
+    buf = torch.empty(nm + 2 * ns + N * H * K * V, dtype=torch.float32, device=dev)
+    M, U, h_in, hT = buf[:nm], buf[nm:nm + ns], buf[nm + ns:nm + 2 * ns], buf[nm + 2 * ns:]
+    timer("scan_head_carry", lambda: _b.gdn_scan(p, _b.GDN_SCAN_HEAD_EMIT_CARRY, *args, _addr(h0), _addr(o),
+                                                 _addr(hT), _addr(M), _addr(U), st))
+    timer("piece_compose", lambda: _b.gdn_piece_compose(p, 1, _addr(M), _addr(U), _addr(hT), _addr(h_in), None,
+                                                        st))
+    timer("scan_tail_emit", lambda: _b.gdn_scan(p, _b.GDN_SCAN_TAIL_EMIT, *args, _addr(h_in), _addr(o),
+                                                _addr(hT), None, None, st))
+    return o, (hT.view(N, H, K, V) if output_final_state else None)
+
+
+@functools.lru_cache(maxsize=16)
+def _n_cu_of(index):
+    return torch.cuda.get_device_properties(index).multi_processor_count
+
+
+def _n_cu(dev):
+    return _n_cu_of(dev.index if dev.index is not None else torch.cuda.current_device())
 
 
 def decode_step(q, k, v, g, beta, state, out=None):
@@ -255,16 +444,40 @@ def forward_segmented(q, k, v, g, beta, h0=None, chunk_size=64, n_segments=2, se
 
 
 def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segments=1,
-            seg_starts=None, reuse_wy=False, output_final_state=True, schedule="auto"):
+            seg_starts=None, reuse_wy=False, output_final_state=True, schedule="auto",
+            max_piece_chunks=None):
     """Chunked gated delta rule forward: returns (o, final state or None).
 
     n_segments > 1 runs the three-phase segment pass; reuse_wy prepares the WY
     factors once (``gdn_chunk_prepare``) and hands them to both scans instead of
     recomputing them inside each scan.  schedule="auto" uses forward_segmented
     for one sequence with recomputed WY factors, "plain" always runs the full
-    carrying pass over every segment."""
+    carrying pass over every segment.
+
+    Packed batches (cu_seqlens) take max_piece_chunks instead of segments:
+    None lets schedule="auto" choose the cut (``plan_pieces``; no cut when the
+    WY factors are reused or the schedule is "plain"), 0 keeps every sequence
+    whole; "auto" runs ``forward_packed``, "plain" the carrying pass over every
+    piece, ``gdn_piece_compose`` from the initial states, and the emitting
+    pass over every piece."""
     if schedule not in ("auto", "plain"):
         raise ValueError(f"unknown schedule {schedule!r}")
+    if cu_seqlens is not None:
+        if n_segments != 1:
+            raise ValueError("packed batches take max_piece_chunks, not segments")
+        wy = chunk_prepare(k, v, g, beta, chunk_size, cu_seqlens) if reuse_wy else None
+        if schedule == "auto":
+            m = max_piece_chunks if max_piece_chunks is not None else (0 if reuse_wy else None)
+            return forward_packed(q, k, v, g, beta, cu_seqlens, h0=h0, chunk_size=chunk_size,
+                                  max_piece_chunks=m, wy=wy, output_final_state=output_final_state)
+        m = max_piece_chunks or 0
+        if m == 0:
+            return scan_emit(q, k, v, g, beta, h_in=h0, wy=wy, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
+                             output_final_state=output_final_state)
+        M, U = scan_carry(k, v, g, beta, wy=wy, chunk_size=chunk_size, cu_seqlens=cu_seqlens, max_piece_chunks=m)
+        h_in, _ = piece_compose(k, v, M, U, cu_seqlens, m, chunk_size, first=0, h_seed=h0)
+        return scan_emit(q, k, v, g, beta, h_in=h_in, wy=wy, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
+                         output_final_state=output_final_state, max_piece_chunks=m)
     if (schedule == "auto" and n_segments > 1 and cu_seqlens is None and not reuse_wy
             and k.shape[0] == 1):
         return forward_segmented(q, k, v, g, beta, h0=h0, chunk_size=chunk_size,
@@ -274,8 +487,6 @@ def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segment
     if n_segments == 1:
         return scan_emit(q, k, v, g, beta, h_in=h0, wy=wy, chunk_size=chunk_size,
                          cu_seqlens=cu_seqlens, output_final_state=output_final_state)
-    if cu_seqlens is not None:
-        raise ValueError("segments are not supported together with cu_seqlens")
     M, U = scan_carry(k, v, g, beta, wy=wy, chunk_size=chunk_size, n_segments=n_segments,
                       seg_starts=seg_starts)
     h_in, _ = segment_compose(M, U, h0)

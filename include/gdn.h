@@ -57,7 +57,8 @@ typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 typedef enum gdn_scan_mode {
     GDN_SCAN_EMIT = 0,   /* outputs o and the final state                           */
     GDN_SCAN_CARRY = 1,  /* zero-state pass per segment emitting (M_r, U_r), no o   */
-    GDN_SCAN_HEAD_EMIT_CARRY = 2  /* segment 0 emitted, segments 1 .. R-1 carried  */
+    GDN_SCAN_HEAD_EMIT_CARRY = 2, /* segment 0 emitted, segments 1 .. R-1 carried */
+    GDN_SCAN_TAIL_EMIT = 3        /* packed pieces: every piece but the first emitted */
 } gdn_scan_mode;
 
 #define GDN_MAX_SEQS 256
@@ -83,6 +84,18 @@ typedef enum gdn_scan_mode {
  *   contiguous, in-order slices (MaxText PR, section "Limitation").
  *   seg_starts == NULL splits the chunks as evenly as possible.
  *   Packed mode requires n_segments == 1.
+ *
+ * Pieces (packed mode only): the segments of a packed batch, sized per
+ *   sequence so that one long sequence does not set the time of the whole
+ *   batch (its chunks are sequential; the segment pass of the MaxText PR,
+ *   section "Implementation", turns them into parallel chains).  With
+ *   max_piece_chunks = m > 0, a sequence of c > m chunks is cut into
+ *   R_n = ceil(c / m) pieces, piece s starting at chunk floor(s * c / R_n) of
+ *   the sequence; every other sequence is one piece.  m == 0 makes every
+ *   sequence one piece.  Pieces are numbered in token order; their count P
+ *   (gdn_num_pieces) must not exceed GDN_MAX_SEQS.  Per-piece buffers are
+ *   [P,H,...]; sequence n's pieces are consecutive.  Batch mode requires
+ *   max_piece_chunks == 0.
  */
 typedef struct gdn_problem {
     int32_t B, S, H, K, V, C;
@@ -91,10 +104,15 @@ typedef struct gdn_problem {
     const int32_t *cu_seqlens;    /* host pointer, n_seqs + 1 entries (packed mode) */
     int32_t n_segments;           /* R >= 1                                          */
     const int32_t *seg_starts;    /* host pointer, R entries, or NULL                */
+    int32_t max_piece_chunks;     /* packed mode: longest piece in chunks, 0 = none  */
 } gdn_problem;
 
 /* Check a problem description without touching the GPU. */
 gdn_status gdn_validate(const gdn_problem *p);
+
+/* Number of pieces P of a packed problem (n_seqs when max_piece_chunks == 0);
+ * the number of segments B * R of a batch problem; -1 if p is invalid. */
+int32_t gdn_num_pieces(const gdn_problem *p);
 
 /* Bytes of the WY workspace written by gdn_chunk_prepare: for every chunk
  * (batch: B * ceil(S/C); packed: sum over sequences of ceil(len/C)) and head,
@@ -105,7 +123,8 @@ size_t gdn_wy_workspace_bytes(const gdn_problem *p);
 /* Bytes of the segment transition pairs M [R,N,H,K,K] plus U [R,N,H,K,V]
  * (fp32; N = B or n_seqs): R*N*H*K*(K+V)*4, independent of S -- the
  * sequence-length-independent cross-rank payload of the MaxText PR
- * ("Measured results", "Tests").  Returns 0 for an invalid problem. */
+ * ("Measured results", "Tests").  Packed problems: P*H*K*(K+V)*4 for the P
+ * pieces.  Returns 0 for an invalid problem. */
 size_t gdn_segment_workspace_bytes(const gdn_problem *p);
 
 /*
@@ -143,8 +162,27 @@ gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
  *   entering segment 1, to h_out [N,H,K,V] (nullable).  Segments 1 .. R-1 are
  *   carried as in GDN_SCAN_CARRY into M_out [R-1,N,H,K,K] and
  *   U_out [R-1,N,H,K,V] (slot r-1 for segment r).  On the matrix-core path
- *   (bf16, K = V = 128, C = 64) this is one launch.  GDN_EINVAL for packed
- *   problems or R < 2.
+ *   (bf16, K = V = 128, C = 64) this is one launch.  GDN_EINVAL for batch
+ *   problems with R < 2.
+ *
+ * Packed problems work on pieces (P of them, see gdn_problem):
+ *   GDN_SCAN_EMIT and GDN_SCAN_CARRY run every piece, with h_in, M_out and
+ *   U_out indexed by piece ([P,H,...]); the last piece of sequence n writes
+ *   h_out[n] ([N,H,K,V]).
+ *   GDN_SCAN_HEAD_EMIT_CARRY emits the first piece of every sequence from
+ *   h_in[n] ([N,H,K,V], NULL = zero) and writes the state at its end to
+ *   h_out[n] (the final state when the sequence is one piece), and carries
+ *   pieces 1 .. R_n-2 of every sequence into M_out, U_out [P,H,...] (slot =
+ *   piece); the last piece of a sequence of R_n >= 2 pieces is not run.
+ *   GDN_SCAN_TAIL_EMIT emits pieces 1 .. R_n-1 of every sequence from
+ *   h_in [P,H,K,V] (slot = piece; the first pieces' slots are not read) and
+ *   writes each such sequence's final state to h_out[n]; one-piece sequences
+ *   are not touched.  GDN_EINVAL for batch problems (slice the tensors
+ *   instead).
+ *   Together: HEAD_EMIT_CARRY, gdn_piece_compose(first = 1), TAIL_EMIT is the
+ *   segment pass without redundant work; CARRY, gdn_piece_compose(first = 0),
+ *   EMIT is the plain one.
+ *   Work items are ordered longest first, so long pieces start first.
  */
 gdn_status gdn_scan(const gdn_problem *p, int32_t mode,
                     const void *q, const void *k, const void *v,
@@ -163,6 +201,24 @@ gdn_status gdn_scan(const gdn_problem *p, int32_t mode,
 gdn_status gdn_segment_compose(int32_t R, int32_t N, int32_t H, int32_t K, int32_t V,
                                const float *M, const float *U, const float *h0,
                                float *h_in, float *h_final, void *stream);
+
+/*
+ * gdn_piece_compose -- the prefix scan of gdn_segment_compose run per
+ * sequence of a packed problem over its pieces (pieces f_n .. f_n+R_n-1 of
+ * sequence n, see gdn_problem), starting at piece `first` (0 or 1) of each:
+ *   x = h_seed[n] (NULL = zero);  for s = first .. R_n-1:
+ *     h_in[f_n+s] = x;  x = M[f_n+s] x + U[f_n+s] (skipped for s = R_n-1
+ *     unless h_final);
+ *   h_final[n] = x (nullable; h_seed[n] when first >= R_n).
+ * first = 0 seeds every sequence with its initial state (after
+ * GDN_SCAN_CARRY); first = 1 seeds it with the state after its first piece
+ * (h_out of GDN_SCAN_HEAD_EMIT_CARRY), reading M, U of pieces 1 .. R_n-2 only.
+ * M [P,H,K,K], U and h_in [P,H,K,V], h_seed and h_final [N,H,K,V], fp32.
+ * h_in and h_final must not alias the inputs or each other.  GDN_EINVAL for
+ * batch problems (use gdn_segment_compose).
+ */
+gdn_status gdn_piece_compose(const gdn_problem *p, int32_t first, const float *M, const float *U,
+                             const float *h_seed, float *h_in, float *h_final, void *stream);
 
 /*
  * gdn_decode_step -- one token per sequence, in place on the fp32 state

@@ -34,11 +34,13 @@ def device_inputs(x):
                 beta=to_dev(x.beta), h0=None if x.h0 is None else to_dev(x.h0))
 
 
-def run_forward(x, n_segments=1, seg_starts=None, reuse_wy=False, h0=True, schedule="auto"):
+def run_forward(x, n_segments=1, seg_starts=None, reuse_wy=False, h0=True, schedule="auto",
+                max_piece_chunks=None):
     d = device_inputs(x)
     o, hT = gdn.forward(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"] if h0 else None,
                         chunk_size=x.C, cu_seqlens=x.cu_seqlens, n_segments=n_segments,
-                        seg_starts=seg_starts, reuse_wy=reuse_wy, schedule=schedule)
+                        seg_starts=seg_starts, reuse_wy=reuse_wy, schedule=schedule,
+                        max_piece_chunks=max_piece_chunks)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), hT.cpu().numpy()
 

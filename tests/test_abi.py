@@ -47,9 +47,18 @@ def test_status_strings_and_version():
     assert b.gdn_version() >= 100
 
 
-def test_problem_struct_layout_matches_c():
+def test_problem_struct_layout_matches_c(tmp_path):
+    """The ctypes mirror of gdn_problem has the C compiler's size and offsets."""
     import ctypes
-    assert ctypes.sizeof(b.GdnProblem) == 56
-    assert b.GdnProblem.cu_seqlens.offset == 32
-    assert b.GdnProblem.n_segments.offset == 40
-    assert b.GdnProblem.seg_starts.offset == 48
+    fields = [f[0] for f in b.GdnProblem._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"gdn.h\"\nint main(void) {\n"
+                   + '  printf("%zu\\n", sizeof(gdn_problem));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(gdn_problem, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(b.GdnProblem)
+    assert got[1:] == [getattr(b.GdnProblem, f).offset for f in fields]

@@ -123,12 +123,64 @@ def test_head_emit_carry_mode_rules():
     H = b.GDN_SCAN_HEAD_EMIT_CARRY
     full = dict(M=FAKE, U=FAKE)
     assert _scan_status(prob(n_segments=1), mode=H, **full) == b.GDN_EINVAL
-    assert _scan_status(prob(S=100, cu_seqlens=[0, 30, 100]), mode=H, **full) == b.GDN_EINVAL
+    # packed: the carried middle pieces need M and U
+    assert _scan_status(prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=1), mode=H) == b.GDN_EINVAL
     assert _scan_status(prob(n_segments=3), mode=H) == b.GDN_EINVAL
     assert _scan_status(prob(n_segments=3), mode=H, M=FAKE) == b.GDN_EINVAL
     assert _scan_status(prob(n_segments=3), mode=H, q=None, **full) == b.GDN_EINVAL
     assert _scan_status(prob(n_segments=3), mode=H, o=None, **full) == b.GDN_EINVAL
     assert _scan_status(prob(n_segments=3), mode=H, h_out=FAKE + 4, **full) == b.GDN_EINVAL
+
+
+def test_packed_piece_rules():
+    """Pieces: packed problems only, a non-negative cap, at most GDN_MAX_SEQS of
+    them; the tail mode is packed-only and its states are per piece."""
+    assert status(prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=-1)) == b.GDN_EINVAL
+    assert status(prob(max_piece_chunks=2)) == b.GDN_EINVAL
+    assert status(prob(S=16 * 300, cu_seqlens=[0, 16 * 300], max_piece_chunks=1)) == b.GDN_EUNSUPPORTED
+    assert status(prob(S=16 * 300, cu_seqlens=[0, 16 * 300], max_piece_chunks=2)) == b.GDN_OK
+    assert status(prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=1, n_segments=2)) == b.GDN_EUNSUPPORTED
+    T = b.GDN_SCAN_TAIL_EMIT
+    assert _scan_status(prob(n_segments=2), mode=T, h_in=FAKE) == b.GDN_EINVAL
+    # per-piece h_in spans P > N states: h_out may not alias it
+    pk = prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=2)
+    assert _scan_status(pk, mode=T, h_in=FAKE, h_out=FAKE) == b.GDN_EINVAL
+    assert _scan_status(pk, mode=b.GDN_SCAN_EMIT, h_in=FAKE, h_out=FAKE) == b.GDN_EINVAL
+
+
+@pytest.mark.parametrize("cu,m,expect", [([0, 30, 30, 100], 0, 3), ([0, 30, 30, 100], 2, 5),
+                                          ([0, 30, 30, 100], 5, 3), ([0, 30, 30, 100], 4, 4),
+                                          ([0, 256], 3, 6), ([0, 0], 1, 1)])
+def test_num_pieces(cu, m, expect):
+    """Chunks per sequence at C = 16: [0,30,30,100] -> 2, 0, 5; a sequence of
+    c > m chunks makes ceil(c / m) pieces, every other sequence one."""
+    p = prob(S=cu[-1], cu_seqlens=cu, max_piece_chunks=m)
+    assert b.gdn_num_pieces(p) == expect
+    assert b.gdn_segment_workspace_bytes(p) == expect * 2 * 32 * 64 * 4
+
+
+def test_num_pieces_batch_and_invalid():
+    assert b.gdn_num_pieces(prob(B=3, n_segments=4)) == 12
+    assert b.gdn_num_pieces(prob(B=0)) == -1
+
+
+def test_piece_compose_validation():
+    import ctypes
+    lib = b.library()
+    pk = prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=2)
+    ref = ctypes.byref
+    assert lib.gdn_piece_compose(ref(prob(n_segments=2)), 0, FAKE, FAKE, None, FAKE, None, None) == b.GDN_EINVAL
+    assert lib.gdn_piece_compose(ref(pk), 2, FAKE, FAKE, None, FAKE, None, None) == b.GDN_EINVAL
+    assert lib.gdn_piece_compose(ref(pk), 0, None, FAKE, None, FAKE, None, None) == b.GDN_EINVAL
+    assert lib.gdn_piece_compose(ref(pk), 0, FAKE, FAKE, None, None, None, None) == b.GDN_EINVAL
+    # h_in aliasing M, h_final aliasing h_in
+    assert lib.gdn_piece_compose(ref(pk), 0, FAKE, FAKE + (1 << 30), None, FAKE, None, None) == b.GDN_EINVAL
+    assert lib.gdn_piece_compose(ref(pk), 0, FAKE, FAKE + (1 << 30), None, FAKE + (1 << 31), FAKE + (1 << 31),
+                                 None) == b.GDN_EINVAL
+    # first = 1 with every sequence one piece long reads nothing and writes no h_in
+    one = prob(S=100, cu_seqlens=[0, 30, 100])
+    assert lib.gdn_piece_compose(ref(pk), 1, None, None, None, None, None, None) == b.GDN_EINVAL
+    assert lib.gdn_piece_compose(ref(one), 1, None, None, None, None, None, None) == b.GDN_OK
 
 
 def test_scan_rejects_state_alias_with_segments():
