@@ -148,6 +148,15 @@ def time_steps(torch, step, steps, warmup, only=None):
     return start.elapsed_time(end) / steps, timer.avg_ms()
 
 
+def time_with_breakdown(torch, step, steps, warmup):
+    """Mean ms per step with no events inside the timed steps (events around
+    each launch cost a short multi-launch step a large share), then the mean
+    HIP-event time of each named kernel from a separate pass of up to 10 steps."""
+    ms, _ = time_steps(torch, step, steps, warmup, only=set())
+    _, kern = time_steps(torch, step, min(steps, 10), 1)
+    return ms, kern
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -263,7 +272,7 @@ def main():
             tm = timer.around if timer else (lambda _n, f: f())
             return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h0, chunk_size=C))
         steps2 = max(3, args.steps // 4)
-        ms1, k1 = time_steps(torch, mono, steps2, 2)
+        ms1, k1 = time_with_breakdown(torch, mono, steps2, 2)
         extra["monolithic_64k"] = {"tokens_per_s": tokens / (ms1 * 1e-3), "ms": ms1}
 
         # the plain three-phase pass: carrying pass over every segment, scan, emitting
@@ -275,7 +284,7 @@ def main():
             return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h_in, chunk_size=C,
                                                          n_segments=R))
         if R > 1:
-            ms_pl, k_pl = time_steps(torch, plain, steps2, 2)
+            ms_pl, k_pl = time_with_breakdown(torch, plain, steps2, 2)
             extra["segmented_64k_plain_schedule"] = {"tokens_per_s": tokens / (ms_pl * 1e-3),
                                                      "ms": ms_pl, "kernels_ms": k_pl}
 
@@ -290,7 +299,7 @@ def main():
             return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h_in, wy=wy,
                                                          chunk_size=C, n_segments=R))
         if R > 1:
-            ms_w, k_w = time_steps(torch, seg_wy, steps2, 2)
+            ms_w, k_w = time_with_breakdown(torch, seg_wy, steps2, 2)
             extra["segmented_64k_wy_reused"] = {"tokens_per_s": tokens / (ms_w * 1e-3), "ms": ms_w,
                                                 "kernels_ms": k_w}
 
@@ -299,7 +308,7 @@ def main():
         def prep(timer):
             tm = timer.around if timer else (lambda _n, f: f())
             return tm("chunk_prepare", lambda: gdn.chunk_prepare(k, v, g, beta, chunk_size=C))
-        ms_p, k_p = time_steps(torch, prep, steps2, 2)
+        ms_p, k_p = time_with_breakdown(torch, prep, steps2, 2)
         prep_bytes = th * ((K + V) * 2 + 8 + (K + V) * 2)
         t_p = k_p["chunk_prepare"] * 1e-3
         extra["chunk_prepare_64k"] = {
@@ -327,9 +336,9 @@ def main():
                 def fwd(timer, yq=yq, yk=yk, yv=yv, yg=yg, yb=yb, yh=yh, cu=cu, mm=mm):
                     return gdn.forward_packed(yq, yk, yv, yg, yb, cu, h0=yh, chunk_size=64, max_piece_chunks=mm,
                                               timer=timer.around if timer else None)
-                ms2, _ = time_steps(torch, fwd, steps2, 2)
+                ms2, k2 = time_with_breakdown(torch, fwd, steps2, 2)
                 extra[name + tag] = {"tokens_per_s": y.real_tokens / (ms2 * 1e-3), "ms": ms2, "max_piece_chunks": mm,
-                                     "pieces": gdn.num_pieces(yk, yv, 64, cu, mm)}
+                                     "pieces": gdn.num_pieces(yk, yv, 64, cu, mm), "kernels_ms": k2}
             del yq, yk, yv, yg, yb, yh
 
         log("bench: decode")
@@ -347,7 +356,7 @@ def main():
                         dq[s_], dk[s_], dv[s_], dg[s_], db[s_], state, out=dout))
                 else:
                     gdn.decode_step(dq[s_], dk[s_], dv[s_], dg[s_], db[s_], state, out=dout)
-        ms3, k3 = time_steps(torch, dec, 2, 1)
+        ms3, k3 = time_with_breakdown(torch, dec, 2, 1)
         step_bytes = 2 * 256 * 32 * 128 * 128 * 4 + 256 * 32 * ((2 * 128 + 128) * 2 + 128 * 2 + 8)
         t_step = k3["decode_step"] * 1e-3
         extra["decode_b256_h32"] = {

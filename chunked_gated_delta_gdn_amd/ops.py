@@ -455,13 +455,26 @@ def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segment
     carrying pass over every segment.
 
     Packed batches (cu_seqlens) take max_piece_chunks instead of segments:
-    None lets schedule="auto" choose the cut (``plan_pieces``; no cut when the
-    WY factors are reused or the schedule is "plain"), 0 keeps every sequence
-    whole; "auto" runs ``forward_packed``, "plain" the carrying pass over every
-    piece, ``gdn_piece_compose`` from the initial states, and the emitting
-    pass over every piece."""
+    None or "auto" lets schedule="auto" choose the cut (``plan_pieces``; no cut
+    when the WY factors are reused or the schedule is "plain"), 0 keeps every
+    sequence whole; "auto" runs ``forward_packed``, "plain" the carrying pass
+    over every piece, ``gdn_piece_compose`` from the initial states, and the
+    emitting pass over every piece.  A batch [B,S,H,*] given max_piece_chunks
+    ("auto" or a number) runs as the packed batch of its B sequences."""
     if schedule not in ("auto", "plain"):
         raise ValueError(f"unknown schedule {schedule!r}")
+    if cu_seqlens is None and max_piece_chunks is not None:
+        if n_segments != 1:
+            raise ValueError("pieces replace segments: pass n_segments=1 with max_piece_chunks")
+        B, S, H = k.shape[:3]
+        flat = lambda t: t.reshape((1, B * S) + tuple(t.shape[2:]))
+        o, hT = forward(flat(q), flat(k), flat(v), flat(g), flat(beta), h0=h0, chunk_size=chunk_size,
+                        cu_seqlens=[b * S for b in range(B + 1)], reuse_wy=reuse_wy,
+                        output_final_state=output_final_state, schedule=schedule,
+                        max_piece_chunks=max_piece_chunks)
+        return o.view(B, S, H, v.shape[-1]), hT
+    if max_piece_chunks == "auto":
+        max_piece_chunks = None
     if cu_seqlens is not None:
         if n_segments != 1:
             raise ValueError("packed batches take max_piece_chunks, not segments")

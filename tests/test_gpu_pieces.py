@@ -130,3 +130,14 @@ def test_packed_config_plans_pieces_and_matches_oracle():
     heads = [0, 13, 30]
     o_ref, h_ref = oracle_forward(x, heads=heads)
     check(x, o[0][:, heads], hT[:, heads], o_ref, h_ref, f"planned m={m}, heads {heads}")
+
+
+@pytest.mark.parametrize("m", ["auto", 2])
+def test_batch_given_pieces_runs_as_packed(m):
+    """A [B,S,H,*] batch with max_piece_chunks runs as the packed batch of its
+    B sequences: same results as the oracle per sequence."""
+    x = make_inputs(37, 2, 300, 2, 32, 32, 16, "f32", 0.1, "slow", name="batch-pieces")
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, max_piece_chunks=m)
+    assert o.shape == (2, 300, 2, 32)
+    check(x, o, hT, o_ref, h_ref, f"batch m={m}")
