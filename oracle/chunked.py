@@ -11,7 +11,8 @@ and the low-rank composition of M from the same page, section
 
 The page leaves gamma, k_tilde, w, u, q_g and attn_i undefined.  The reading
 taken here (the unique one that makes the equations reproduce the token
-recurrence in ``recurrence.py``; derived in the design doc) is, for a chunk of L
+recurrence in ``recurrence.py`` at every chunk size, which the tests check
+against it) is, for a chunk of L
 tokens with local indices r, s and within-chunk cumulative log-decay
 G_r = g_1 + ... + g_r:
 
