@@ -432,6 +432,29 @@ def test_beta_zero_is_pure_decay(dtype):
     assert rel_err(o[0], o_cf) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n_segments", [1, 3])
+def test_mixed_degenerate_tokens(dtype, n_segments):
+    """Scattered degenerate tokens inside chunks: beta = 0 (no write; the
+    matrix-core path folds beta in as the exponent -log2(beta) = +inf), g = 0
+    (no decay), g = -40 (a hard reset of the state), and zero keys or zero
+    queries.  Nothing may turn into NaN and the result follows the oracle."""
+    K = 32 if dtype == "f32" else 128
+    C = 16 if dtype == "f32" else 64
+    S = 5 * C + 7
+    x = make_inputs(26, 1, S, 2, K, K, C, dtype, 0.05, decay="slow", name="degenerate")
+    rng = np.random.default_rng(26)
+    pick = lambda frac: rng.random((1, S, 2)) < frac
+    x.beta[pick(0.2)] = 0.0
+    x.g[pick(0.2)] = 0.0
+    x.g[pick(0.03)] = -40.0
+    x.k[pick(0.05)] = 0
+    x.q[pick(0.05)] = 0
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, n_segments=n_segments)
+    check(x, o, hT, o_ref, h_ref, what=f"degenerate tokens R={n_segments}")
+
+
 def test_no_decay_4k():
     """g = 0 (alpha = 1) over 4k tokens, 4 segments: no forgetting at all."""
     x = workload(1, H=4, decay="none")
