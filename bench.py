@@ -49,6 +49,17 @@ def bytes_per_token_head(K, V, s_in, s_out):
     return (2 * K + V) * s_in + V * s_out + 8
 
 
+def step_roofline(tokens, heads, ms, C=64, K=128, V=128, elem=2):
+    """Whole-step rates of a forward over `tokens` real tokens and `heads` heads:
+    canonical FLOPs against the bf16 MFMA peak and algorithmic bytes (states
+    excluded) against HBM, each over the whole step's time."""
+    t = ms * 1e-3
+    fl = tokens * heads * flops_per_token_head(C, K, V)
+    by = tokens * heads * bytes_per_token_head(K, V, elem, elem)
+    return {"useful_tflops": fl / t / 1e12, "mfma_frac": fl / t / 1e12 / PEAK_BF16_TFLOPS,
+            "hbm_frac": by / t / 1e9 / PEAK_HBM_GBS}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +272,7 @@ def main():
         "roofline": roof,
         "kernels_ms": kern,   # dominant kernel from the timed steps, the rest from the second pass
         "useful_tflops": useful / (ms * 1e-3) / 1e12,
+        "step_roofline": step_roofline(tokens, H, ms, C, K, V),
         "scan_backend": "mfma" if backend == 1 else "valu",
     }
     del seg_step
@@ -273,7 +285,8 @@ def main():
             return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h0, chunk_size=C))
         steps2 = max(3, args.steps // 4)
         ms1, k1 = time_with_breakdown(torch, mono, steps2, 2)
-        extra["monolithic_64k"] = {"tokens_per_s": tokens / (ms1 * 1e-3), "ms": ms1}
+        extra["monolithic_64k"] = {"tokens_per_s": tokens / (ms1 * 1e-3), "ms": ms1,
+                                   "step_roofline": step_roofline(tokens, H, ms1)}
 
         # the plain three-phase pass: carrying pass over every segment, scan, emitting
         # pass over every segment
@@ -286,6 +299,7 @@ def main():
         if R > 1:
             ms_pl, k_pl = time_with_breakdown(torch, plain, steps2, 2)
             extra["segmented_64k_plain_schedule"] = {"tokens_per_s": tokens / (ms_pl * 1e-3),
+                                                     "step_roofline": step_roofline(tokens, H, ms_pl),
                                                      "ms": ms_pl, "kernels_ms": k_pl}
 
         # the same three-phase pass with the WY factors prepared once and reused by
@@ -301,6 +315,7 @@ def main():
         if R > 1:
             ms_w, k_w = time_with_breakdown(torch, seg_wy, steps2, 2)
             extra["segmented_64k_wy_reused"] = {"tokens_per_s": tokens / (ms_w * 1e-3), "ms": ms_w,
+                                                "step_roofline": step_roofline(tokens, H, ms_w),
                                                 "kernels_ms": k_w}
 
         # per-chunk WY preparation (gdn_chunk_prepare) of the same workload: an HBM
@@ -338,6 +353,7 @@ def main():
                                               timer=timer.around if timer else None)
                 ms2, k2 = time_with_breakdown(torch, fwd, steps2, 2)
                 extra[name + tag] = {"tokens_per_s": y.real_tokens / (ms2 * 1e-3), "ms": ms2, "max_piece_chunks": mm,
+                                     "step_roofline": step_roofline(y.real_tokens, y.q.shape[2], ms2),
                                      "pieces": gdn.num_pieces(yk, yv, 64, cu, mm), "kernels_ms": k2}
             del yq, yk, yv, yg, yb, yh
 
