@@ -318,6 +318,19 @@ def main():
                                                 "step_roofline": step_roofline(tokens, H, ms_w),
                                                 "kernels_ms": k_w}
 
+        # grouped key heads: the same step with q and k on H/2 heads (value head h reads
+        # key head h // 2), as in models whose linear attention has fewer key heads
+        if R > 1 and H % 2 == 0:
+            qg, kg = q[:, :, : H // 2].contiguous(), k[:, :, : H // 2].contiguous()
+
+            def grouped(timer):
+                tm = timer.around if timer else (lambda _n, f: f())
+                return gdn.forward_segmented(qg, kg, v, g, beta, h0=h0, chunk_size=C, n_segments=R, timer=tm)
+            ms_g, k_g = time_with_breakdown(torch, grouped, steps2, 2)
+            extra[f"segmented_64k_hqk{H // 2}"] = {"tokens_per_s": tokens / (ms_g * 1e-3), "ms": ms_g,
+                                                  "step_roofline": step_roofline(tokens, H, ms_g), "kernels_ms": k_g}
+            del qg, kg
+
         # per-chunk WY preparation (gdn_chunk_prepare) of the same workload: an HBM
         # stream of k, v, g, beta in and w, u out
         def prep(timer):

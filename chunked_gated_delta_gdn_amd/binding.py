@@ -31,16 +31,18 @@ class GdnProblem(ctypes.Structure):
         ("n_segments", _i32),
         ("seg_starts", ctypes.POINTER(_i32)),
         ("max_piece_chunks", _i32),
+        ("H_qk", _i32),
     ]
 
 
 def make_problem(B, S, H, K, V, C, dtype, cu_seqlens=None, n_segments=1, seg_starts=None,
-                 max_piece_chunks=0):
+                 max_piece_chunks=0, H_qk=0):
     """Build a ``GdnProblem``; the host arrays it points to are kept alive on it."""
     p = GdnProblem()
     p.B, p.S, p.H, p.K, p.V, p.C, p.dtype = B, S, H, K, V, C, dtype
     p.n_segments = n_segments
     p.max_piece_chunks = max_piece_chunks
+    p.H_qk = H_qk
     if cu_seqlens is not None:
         cu = [int(x) for x in cu_seqlens]
         arr = (_i32 * len(cu))(*cu)
@@ -87,7 +89,7 @@ def library():
             "gdn_scan": (_i32, [P, _i32] + [_vp] * 12),
             "gdn_segment_compose": (_i32, [_i32] * 5 + [_vp] * 6),
             "gdn_piece_compose": (_i32, [P, _i32] + [_vp] * 6),
-            "gdn_decode_step": (_i32, [_i32] * 5 + [_vp] * 8),
+            "gdn_decode_step": (_i32, [_i32] * 6 + [_vp] * 8),
             "gdn_scan_backend": (_i32, [P]),
             "gdn_status_string": (ctypes.c_char_p, [_i32]),
             "gdn_last_error": (ctypes.c_char_p, []),
@@ -153,8 +155,8 @@ def gdn_piece_compose(problem, first, M, U, h_seed, h_in, h_final, stream=0):
            "gdn_piece_compose")
 
 
-def gdn_decode_step(B, H, K, V, dtype, q, k, v, g, beta, state, o, stream=0):
-    _check(library().gdn_decode_step(B, H, K, V, dtype, q, k, v, g, beta, state, o, stream),
+def gdn_decode_step(B, H, H_qk, K, V, dtype, q, k, v, g, beta, state, o, stream=0):
+    _check(library().gdn_decode_step(B, H, H_qk, K, V, dtype, q, k, v, g, beta, state, o, stream),
            "gdn_decode_step")
 
 

@@ -57,9 +57,11 @@ __global__ __launch_bounds__((threads_for<K, V>())) void decode_step_kernel(Deco
     const int64_t bh = blockIdx.x;
     const int cg = tid % CG, rs = tid / CG;
 
+    // q, k of the key head this value head reads (grouped order)
+    const int64_t bhk = (bh / a.H) * a.Hk + (bh % a.H) / (a.H / a.Hk);
     for (int i = tid; i < K; i += kThreads) {
-        sk[i] = Elem<T>::load(a.k, bh * K + i);
-        sq[i] = Elem<T>::load(a.q, bh * K + i);
+        sk[i] = Elem<T>::load(a.k, bhk * K + i);
+        sq[i] = Elem<T>::load(a.q, bhk * K + i);
     }
     const float alpha = expf(a.g[bh]);
     const float beta = a.beta[bh];

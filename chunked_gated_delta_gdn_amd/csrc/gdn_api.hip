@@ -111,6 +111,8 @@ gdn_status resolve(const gdn_problem *p, Resolved &out) {
     if (p->dtype != GDN_F32 && p->dtype != GDN_BF16)
         return fail(GDN_EUNSUPPORTED, "dtype %d not supported", p->dtype);
     if (p->n_seqs < 0) return fail(GDN_EINVAL, "n_seqs %d < 0", p->n_seqs);
+    if (p->H_qk < 0 || p->H_qk > p->H || (p->H_qk > 0 && p->H % p->H_qk != 0))
+        return fail(GDN_EINVAL, "H_qk = %d must divide H = %d (0 means H)", p->H_qk, p->H);
     if (p->max_piece_chunks < 0) return fail(GDN_EINVAL, "max_piece_chunks %d < 0", p->max_piece_chunks);
     if (p->n_seqs == 0 && p->max_piece_chunks != 0)
         return fail(GDN_EINVAL, "max_piece_chunks applies to packed problems only (use segments)");
@@ -307,6 +309,7 @@ gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
     a.wy_w = wy;
     a.wy_u = static_cast<char *>(wy) + (size_t)r.n_chunks * p->H * p->C * p->K * elem_size(p->dtype);
     a.H = p->H;
+    a.Hk = p->H_qk > 0 ? p->H_qk : p->H;
     a.n_chunks = r.n_chunks;
     a.ct = r.ct;
     (void)hipGetLastError();
@@ -350,6 +353,7 @@ static gdn_status scan_head(const gdn_problem *p, Resolved &r, const void *q, co
     a.M_out = M_out;
     a.U_out = U_out;
     a.H = p->H;
+    a.Hk = p->H_qk > 0 ? p->H_qk : p->H;
     a.n_chains = r.N * (r.R - 1);
     a.ct = r.ct;
     if (r.ct.packed) {
@@ -419,6 +423,7 @@ gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const voi
     a.M_out = carry ? M_out : nullptr;
     a.U_out = carry ? U_out : nullptr;
     a.H = p->H;
+    a.Hk = p->H_qk > 0 ? p->H_qk : p->H;
     a.n_chains = r.ct.packed ? r.ct.n_items : r.N * r.R;
     a.ct = r.ct;
     if (a.n_chains == 0) return GDN_OK;
@@ -508,12 +513,14 @@ gdn_status gdn_piece_compose(const gdn_problem *p, int32_t first, const float *M
     return launched(launch_compose(p->K, p->V, a, (hipStream_t)stream), "gdn_piece_compose");
 }
 
-gdn_status gdn_decode_step(int32_t B, int32_t H, int32_t K, int32_t V, int32_t dtype,
+gdn_status gdn_decode_step(int32_t B, int32_t H, int32_t H_qk, int32_t K, int32_t V, int32_t dtype,
                            const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *state, void *o, void *stream) {
     g_err[0] = 0;
     if (B < 0 || H < 1 || K < 1 || V < 1)
         return fail(GDN_EINVAL, "bad sizes B=%d H=%d K=%d V=%d", B, H, K, V);
+    if (H_qk < 1 || H_qk > H || H % H_qk != 0)
+        return fail(GDN_EINVAL, "H_qk = %d must divide H = %d", H_qk, H);
     if (!((K == 32 && V == 32) || (K == 128 && V == 128)))
         return fail(GDN_EUNSUPPORTED, "(K,V)=(%d,%d) not built", K, V);
     if (dtype != GDN_F32 && dtype != GDN_BF16)
@@ -537,6 +544,7 @@ gdn_status gdn_decode_step(int32_t B, int32_t H, int32_t K, int32_t V, int32_t d
     a.o = o;
     a.B = B;
     a.H = H;
+    a.Hk = H_qk;
     (void)hipGetLastError();
     return launched(launch_decode(K, V, dtype, a, (hipStream_t)stream), "gdn_decode_step");
 }

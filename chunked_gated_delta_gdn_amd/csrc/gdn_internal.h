@@ -113,7 +113,8 @@ struct ScanArgs {
     void *o;
     float *h_out;
     float *M_out, *U_out;
-    int32_t H;
+    int32_t H;          // value heads (state heads)
+    int32_t Hk;         // heads of q and k: value head h reads key head h / (H / Hk)
     int32_t n_chains;   // batch mode: chains; packed mode: ct.n_items
     ChainTable ct;
 };
@@ -124,7 +125,7 @@ struct PrepArgs {
     const void *k, *v;
     const float *g, *beta;
     void *wy_w, *wy_u;
-    int32_t H;
+    int32_t H, Hk;      // value heads; heads of k (value head h reads key head h / (H / Hk))
     int64_t n_chunks;
     ChainTable ct;
 };
@@ -134,7 +135,7 @@ struct DecodeArgs {
     const float *g, *beta;
     float *state;
     void *o;
-    int32_t B, H;
+    int32_t B, H, Hk;   // value heads H; q, k have Hk heads (value head h reads key head h / (H / Hk))
 };
 
 struct ComposeArgs {

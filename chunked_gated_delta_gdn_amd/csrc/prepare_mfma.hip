@@ -102,11 +102,12 @@ __global__ __launch_bounds__(NTP) void prepare_mfma_kernel(PrepArgs a) {
         tend = (n + 1) * a.ct.seq_len;
     }
     const int L = (int)((tend - tc) < C ? (tend - tc) : C);
-    const int64_t rowK = (int64_t)H * K, rowV = (int64_t)H * V;
+    const int64_t rowK = (int64_t)a.Hk * K, rowV = (int64_t)H * V;
+    const int hk = h / (H / a.Hk);   // key head of this value head (grouped order)
 
     {
         uint4 tk[4], tv[4];
-        load_quarter(tk, static_cast<const bf16 *>(a.k) + tc * rowK + h * K, (uint32_t)(rowK * 2), L, lane, wv);
+        load_quarter(tk, static_cast<const bf16 *>(a.k) + tc * rowK + hk * K, (uint32_t)(rowK * 2), L, lane, wv);
         load_quarter(tv, static_cast<const bf16 *>(a.v) + tc * rowV + h * V, (uint32_t)(rowV * 2), L, lane, wv);
         if (wv == 0) {
             const uint32_t go = min((uint32_t)lane, (uint32_t)(L - 1)) * (uint32_t)(4 * H);

@@ -139,6 +139,7 @@ __global__ __launch_bounds__(kThreads) void scan_generic(ScanArgs a) {
     const bool is_M = CARRY && col0 < K;
     const int hc0 = CARRY ? col0 - K : col0;
     const int64_t slot = ur.slot;   // state row of h_in (emit) or M_out / U_out (carry)
+    const int hk = h / (H / a.Hk);  // key head of this value head (grouped order)
     const bool active = tid < NCOL;
 
     float x[K];
@@ -160,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void scan_generic(ScanArgs a) {
         const int L = (int)((sp.t1 - tc) < C ? (sp.t1 - tc) : C);
         const int64_t chunk = sp.chunk0 + j;
 
-        load_rows<T, K, C>(sk, KP, a.k, tc, L, H, h, K, 0, K);
-        if (EMIT) load_rows<T, K, C>(sq, KP, a.q, tc, L, H, h, K, 0, K);
+        load_rows<T, K, C>(sk, KP, a.k, tc, L, a.Hk, hk, K, 0, K);
+        if (EMIT) load_rows<T, K, C>(sq, KP, a.q, tc, L, a.Hk, hk, K, 0, K);
         if (WY_IN) {
             for (int e = tid; e < C * K; e += kThreads) {
                 const int r = e / K, i = e % K;
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void prepare_generic(PrepArgs a) {
     }
     const int L = (int)((tend - tc) < C ? (tend - tc) : C);
 
-    load_rows<T, K, C>(sk, KP, a.k, tc, L, H, h, K, 0, K);
+    load_rows<T, K, C>(sk, KP, a.k, tc, L, a.Hk, h / (H / a.Hk), K, 0, K);
     load_rows<T, K, C>(su, V, a.v, tc, L, H, h, V, 0, V);
     load_decay<C>(sG, sb, a.g, a.beta, tc, L, H, h);
     __syncthreads();

@@ -130,7 +130,8 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
     const ChainSpan sp = u.sp;
     const int64_t slot = u.slot;
     const int64_t n_chunks = (sp.t1 - sp.t0 + C - 1) / C;
-    const int64_t rowK = (int64_t)H * K;   // element stride between tokens of q, k
+    const int hk = h / (H / a.Hk);          // key head of this value head (grouped order)
+    const int64_t rowK = (int64_t)a.Hk * K; // element stride between tokens of q, k
     const int64_t rowV = (int64_t)H * V;
     const uint32_t row_bytes_k = (uint32_t)(rowK * 2), row_bytes_v = (uint32_t)(rowV * 2);
 
@@ -423,7 +424,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
         float gA, bA, gB, bB;
         auto issue = [&](uint4 (&t)[16], float &gv_, float &bv_, int64_t j) {
             const int L = chunk_len(j);
-            load_rows(t, gk + tok(j, 0) * rowK + h * K, row_bytes_k, L, lane);
+            load_rows(t, gk + tok(j, 0) * rowK + hk * K, row_bytes_k, L, lane);
             const int64_t t0 = tok(j, 0) * H + h;
             const uint32_t go = min((uint32_t)lane, (uint32_t)(L - 1)) * (uint32_t)(4 * H);
             gv_ = bload4f(rsrc(a.g + t0), go);
@@ -470,7 +471,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
         }
         uint4 qA_[16], qB_[16];
         auto issue = [&](uint4 (&t)[16], int64_t j) {
-            load_rows(t, gq + tok(j, 0) * rowK + h * K, row_bytes_k, chunk_len(j), lane);
+            load_rows(t, gq + tok(j, 0) * rowK + hk * K, row_bytes_k, chunk_len(j), lane);
         };
         auto work = [&](const uint4 (&qraw)[16], int64_t jn) {
             const int b2 = (int)(jn & 1), b3 = kslot(jn);

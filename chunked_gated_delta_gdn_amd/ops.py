@@ -52,12 +52,13 @@ def _need(t, name, shape, dtype, device):
 
 
 def problem_for(k, v, chunk_size, cu_seqlens=None, n_segments=1, seg_starts=None, max_piece_chunks=0):
-    """The ``gdn_problem`` of batch tensors k [B,S,H,K], v [B,S,H,V]."""
-    B, S, H, K = k.shape
-    V = v.shape[-1]
+    """The ``gdn_problem`` of batch tensors k [B,S,H_qk,K], v [B,S,H,V] (H_qk
+    key heads for H value heads, H a multiple of H_qk)."""
+    B, S, Hk, K = k.shape
+    H, V = v.shape[2], v.shape[3]
     return _b.make_problem(B, S, H, K, V, chunk_size, _dtype_code(k), cu_seqlens=cu_seqlens,
                            n_segments=n_segments, seg_starts=seg_starts,
-                           max_piece_chunks=max_piece_chunks)
+                           max_piece_chunks=max_piece_chunks, H_qk=0 if Hk == H else Hk)
 
 
 def num_pieces(k, v, chunk_size, cu_seqlens, max_piece_chunks):
@@ -72,12 +73,19 @@ def _n_seqs(k, cu_seqlens):
 
 
 def _check_inputs(q, k, v, g, beta):
+    """Shapes q, k [B,S,H_qk,K]; v [B,S,H,V]; g, beta [B,S,H] (H a multiple of
+    H_qk: value head h reads key head h // (H // H_qk)).  Returns B, S, H, K, V
+    with H the value (state) heads."""
     dev = k.device
-    B, S, H, K = k.shape
-    V = v.shape[-1]
+    B, S, Hk, K = k.shape
+    if v.dim() != 4 or v.shape[:2] != k.shape[:2]:
+        raise ValueError(f"v has shape {tuple(v.shape)}, expected [B,S,H,V] with B,S of k {tuple(k.shape)}")
+    H, V = v.shape[2], v.shape[3]
+    if Hk < 1 or H % Hk != 0:
+        raise ValueError(f"value heads {H} are not a multiple of key heads {Hk}")
     if q is not None:
-        _need(q, "q", (B, S, H, K), k.dtype, dev)
-    _need(k, "k", (B, S, H, K), k.dtype, dev)
+        _need(q, "q", (B, S, Hk, K), k.dtype, dev)
+    _need(k, "k", (B, S, Hk, K), k.dtype, dev)
     _need(v, "v", (B, S, H, V), k.dtype, dev)
     _need(g, "g", (B, S, H), torch.float32, dev)
     _need(beta, "beta", (B, S, H), torch.float32, dev)
@@ -99,8 +107,8 @@ def chunk_prepare(k, v, g, beta, chunk_size=64, cu_seqlens=None):
 
 
 def split_wy(wy, k, v, chunk_size, cu_seqlens=None):
-    """Views (w [n_chunks,H,C,K], u [n_chunks,H,C,V]) of a WY workspace."""
-    H, K, V = k.shape[2], k.shape[3], v.shape[3]
+    """Views (w [n_chunks,H,C,K], u [n_chunks,H,C,V]) of a WY workspace (H value heads)."""
+    H, K, V = v.shape[2], k.shape[3], v.shape[3]
     n_chunks = wy.numel() // (H * chunk_size * (K + V))
     w = wy[: n_chunks * H * chunk_size * K].view(n_chunks, H, chunk_size, K)
     u = wy[n_chunks * H * chunk_size * K:].view(n_chunks, H, chunk_size, V)
@@ -235,8 +243,8 @@ def piece_compose(k, v, M, U, cu_seqlens, max_piece_chunks, chunk_size=64, first
     """Per-sequence scan over the pieces of a packed problem
     (``gdn_piece_compose``): returns (h_in [P,H,K,V], h_final [N,H,K,V] or None).
     Rows of h_in before piece ``first`` of each sequence are not written."""
-    B, S, H, K = k.shape
-    V = v.shape[-1]
+    K = k.shape[3]
+    H, V = v.shape[2], v.shape[3]
     dev = M.device
     N = _n_seqs(k, cu_seqlens)
     p = problem_for(k, v, chunk_size, cu_seqlens, max_piece_chunks=max_piece_chunks)
@@ -368,19 +376,21 @@ def _n_cu(dev):
 def decode_step(q, k, v, g, beta, state, out=None):
     """One recurrent step (``gdn_decode_step``), updating ``state`` in place.
 
-    q, k [B,H,K]; v [B,H,V]; g, beta [B,H] fp32; state [B,H,K,V] fp32.
-    Returns o [B,H,V]."""
-    B, H, K = k.shape
-    V = v.shape[-1]
+    q, k [B,H_qk,K]; v [B,H,V]; g, beta [B,H] fp32; state [B,H,K,V] fp32 (H a
+    multiple of H_qk).  Returns o [B,H,V]."""
+    B, Hk, K = k.shape
+    H, V = v.shape[1], v.shape[2]
     dev = k.device
-    _need(q, "q", (B, H, K), k.dtype, dev)
+    if Hk < 1 or H % Hk != 0:
+        raise ValueError(f"value heads {H} are not a multiple of key heads {Hk}")
+    _need(q, "q", (B, Hk, K), k.dtype, dev)
     _need(v, "v", (B, H, V), k.dtype, dev)
     _need(g, "g", (B, H), torch.float32, dev)
     _need(beta, "beta", (B, H), torch.float32, dev)
     _need(state, "state", (B, H, K, V), torch.float32, dev)
     o = out if out is not None else torch.empty((B, H, V), dtype=k.dtype, device=dev)
     _need(o, "o", (B, H, V), k.dtype, dev)
-    _b.gdn_decode_step(B, H, K, V, _dtype_code(k), _addr(q), _addr(k), _addr(v), _addr(g),
+    _b.gdn_decode_step(B, H, Hk, K, V, _dtype_code(k), _addr(q), _addr(k), _addr(v), _addr(g),
                        _addr(beta), _addr(state), _addr(o), _stream(dev))
     return o
 
@@ -466,7 +476,7 @@ def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segment
     if cu_seqlens is None and max_piece_chunks is not None:
         if n_segments != 1:
             raise ValueError("pieces replace segments: pass n_segments=1 with max_piece_chunks")
-        B, S, H = k.shape[:3]
+        B, S, H = v.shape[:3]
         flat = lambda t: t.reshape((1, B * S) + tuple(t.shape[2:]))
         o, hT = forward(flat(q), flat(k), flat(v), flat(g), flat(beta), h0=h0, chunk_size=chunk_size,
                         cu_seqlens=[b * S for b in range(B + 1)], reuse_wy=reuse_wy,

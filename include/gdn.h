@@ -77,6 +77,14 @@ typedef enum gdn_scan_mode {
  *   masked exactly like padding (g = 0, q = k = v = 0, beta = 0), which the
  *   MaxText PR ("Implementation") shows is a no-op for the recurrence.
  *
+ * Grouped heads: q and k may have H_qk heads for the H value heads (v, o,
+ *   g, beta and every state have H), H a multiple of H_qk; value head h reads
+ *   key head h / (H / H_qk), each key head serving H / H_qk consecutive value
+ *   heads (the separate key and value head counts of "RFC(qwen35): TP Phase
+ *   2", section "Partition Contract"; the grouped order of the Ulysses
+ *   context-parallelism page).  q, k are then [B,S,H_qk,K] ([S,H_qk,K]
+ *   packed).  H_qk == 0 means H_qk = H.  Anything else is GDN_EINVAL.
+ *
  * Segments (batch mode only): every sequence is cut into n_segments
  *   contiguous, in-order pieces starting at seg_starts[r] (relative to the
  *   sequence start).  seg_starts[0] == 0, strictly increasing, multiples of
@@ -105,6 +113,7 @@ typedef struct gdn_problem {
     int32_t n_segments;           /* R >= 1                                          */
     const int32_t *seg_starts;    /* host pointer, R entries, or NULL                */
     int32_t max_piece_chunks;     /* packed mode: longest piece in chunks, 0 = none  */
+    int32_t H_qk;                 /* heads of q and k; 0 = H (see grouped heads)     */
 } gdn_problem;
 
 /* Check a problem description without touching the GPU. */
@@ -224,10 +233,11 @@ gdn_status gdn_piece_compose(const gdn_problem *p, int32_t first, const float *M
  * gdn_decode_step -- one token per sequence, in place on the fp32 state
  * (the per-token recurrence above; the "GDR decode kernel" of
  * "RFC(qwen35): TP Phase 2", section "Kernel Work", state [H_v,K,V] f32).
- * q, k [B,H,K]; v, o [B,H,V] in `dtype`; g, beta [B,H] fp32;
- * state [B,H,K,V] fp32, read and written once.
+ * q, k [B,H_qk,K]; v, o [B,H,V] in `dtype`; g, beta [B,H] fp32;
+ * state [B,H,K,V] fp32, read and written once.  H_qk divides H (grouped heads
+ * as in gdn_problem; pass H_qk = H for one key head per value head).
  */
-gdn_status gdn_decode_step(int32_t B, int32_t H, int32_t K, int32_t V, int32_t dtype,
+gdn_status gdn_decode_step(int32_t B, int32_t H, int32_t H_qk, int32_t K, int32_t V, int32_t dtype,
                            const void *q, const void *k, const void *v,
                            const float *g, const float *beta, float *state, void *o,
                            void *stream);

@@ -17,6 +17,9 @@ Contents (every function cites the passage of the pages it follows):
   recurrence, and the oracle for the WY factors w, u.
 * ``segments``    -- the exclusive prefix scan over (M_r, U_r) (same page,
   section "Implementation", phase 2).
+* ``heads``       -- grouped key heads ("RFC(qwen35): TP Phase 2", section
+  "Partition Contract"; grouped order from the Ulysses page): the ungrouped
+  definition on q, k with each key head repeated in place.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, hand-worked fixtures under
@@ -29,9 +32,10 @@ from .recurrence import (forward, forward_packed, decode_step, transition_pair,
 from .chunked import (chunk_wy, chunked_forward, chunk_transition,
                       lowrank_segment_pair)
 from .segments import exclusive_scan
+from .heads import expand_key_heads
 
 __all__ = [
     "forward", "forward_packed", "decode_step", "transition_pair", "load_library",
     "chunk_wy", "chunked_forward", "chunk_transition", "lowrank_segment_pair",
-    "exclusive_scan",
+    "exclusive_scan", "expand_key_heads",
 ]

@@ -141,3 +141,30 @@ def test_batch_given_pieces_runs_as_packed(m):
     o, hT = run_forward(x, max_piece_chunks=m)
     assert o.shape == (2, 300, 2, 32)
     check(x, o, hT, o_ref, h_ref, f"batch m={m}")
+
+
+@pytest.mark.parametrize("dtype,K,C", [("f32", 32, 16), ("bf16", 128, 64)])
+def test_mixed_prefill_and_decode_batch(dtype, K, C):
+    """A packed batch mixing prefills and one-token decode requests, each
+    request with its own state: the decode requests' outputs and states equal
+    gdn_decode_step on the same token and state (to the tolerance: the chunked
+    and the single-token kernels round differently), and every sequence follows
+    the oracle."""
+    lens = [5 * C + 3, 1, 2 * C, 1, 1, 3 * C + 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = packed(45, cu, 2, K, C, dtype, h0_std=0.05)
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x)
+    check(x, o[0], hT, o_ref, h_ref, "mixed prefill/decode")
+    d = device_inputs(x)
+    dt = d["k"].dtype
+    for n, L in enumerate(lens):
+        if L != 1:
+            continue
+        t = int(cu[n])
+        state = d["h0"][n:n + 1].clone()
+        tok = {n_: d[n_][0, t:t + 1].clone() for n_ in ("q", "k", "v", "g", "beta")}   # aligned copies
+        od = gdn.decode_step(tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"], state)
+        torch.cuda.synchronize()
+        assert rel_err(o[0, t], od[0].float().cpu().numpy()) <= TOL[dtype]
+        assert rel_err(hT[n], state[0].cpu().numpy()) <= TOL[dtype]

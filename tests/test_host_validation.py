@@ -202,8 +202,19 @@ def test_compose_and_decode_validation():
     # h_in aliasing M is refused
     assert lib.gdn_segment_compose(2, 1, 1, 32, 32, FAKE, FAKE + (1 << 20), None, FAKE, None,
                                    None) == b.GDN_EINVAL
-    assert lib.gdn_decode_step(4, 2, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EUNSUPPORTED
-    assert lib.gdn_decode_step(4, 2, 32, 32, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EUNSUPPORTED
-    assert lib.gdn_decode_step(4, 2, 32, 32, 0, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EINVAL
-    assert lib.gdn_decode_step(4, 0, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EINVAL
-    assert lib.gdn_decode_step(0, 2, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_OK
+    assert lib.gdn_decode_step(4, 2, 2, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EUNSUPPORTED
+    assert lib.gdn_decode_step(4, 2, 2, 32, 32, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EUNSUPPORTED
+    assert lib.gdn_decode_step(4, 2, 2, 32, 32, 0, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EINVAL
+    assert lib.gdn_decode_step(4, 0, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EINVAL
+    assert lib.gdn_decode_step(0, 2, 2, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_OK
+    # grouped heads: H_qk must divide H
+    for hq in (0, 4, 12, -1):
+        assert lib.gdn_decode_step(4, 6, hq, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.GDN_EINVAL
+
+
+@pytest.mark.parametrize("hq,ok", [(0, True), (1, True), (2, True), (4, True), (3, False), (8, False), (-1, False)])
+def test_grouped_heads_rules(hq, ok):
+    """q, k may have H_qk heads for H = 4 value heads when H_qk divides H
+    (0 means H_qk = H)."""
+    st = status(prob(H=4, H_qk=hq))
+    assert st == (b.GDN_OK if ok else b.GDN_EINVAL)

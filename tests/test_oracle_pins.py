@@ -353,3 +353,27 @@ def test_c_oracle_indexing_against_exact_arithmetic():
                                        atol=1e-15)
             np.testing.assert_allclose(hT[b, hh], np.array(he, dtype=np.float64), rtol=1e-14,
                                        atol=1e-15)
+
+
+def test_grouped_key_heads_order_and_meaning():
+    """Grouped key heads ("RFC(qwen35): TP Phase 2", section "Partition
+    Contract"; grouped order from the Ulysses page's examples at cp = 4 and 8):
+    each key head serves consecutive value heads, [kv0, kv0, kv1, kv1] and not
+    the tiled [kv0, kv1, kv0, kv1]; one key head per value head is the identity;
+    two value heads reading one key head with equal v, g, beta give equal results."""
+    labels = np.arange(2).reshape(1, 2, 1)
+    assert oracle.expand_key_heads(labels, 4)[0, :, 0].tolist() == [0, 0, 1, 1]
+    assert oracle.expand_key_heads(labels, 8)[0, :, 0].tolist() == [0] * 4 + [1] * 4
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal((1, 20, 2, 4)), rng.standard_normal((1, 20, 2, 4))
+    assert np.array_equal(oracle.expand_key_heads(q, 2), q)
+    with pytest.raises(ValueError):
+        oracle.expand_key_heads(q, 3)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = np.repeat(rng.standard_normal((1, 20, 1, 4)), 4, axis=2)
+    g = np.repeat(-np.abs(rng.standard_normal((1, 20, 1))), 4, axis=2) * 0.1
+    beta = np.repeat(rng.random((1, 20, 1)), 4, axis=2)
+    o, h = oracle.forward(oracle.expand_key_heads(q, 4), oracle.expand_key_heads(k, 4), v, g, beta)
+    assert np.array_equal(o[:, :, 0], o[:, :, 1]) and np.array_equal(o[:, :, 2], o[:, :, 3])
+    assert not np.allclose(o[:, :, 1], o[:, :, 2])
+    assert np.array_equal(h[:, 0], h[:, 1])
