@@ -283,7 +283,7 @@ def main():
         def mono(timer):
             tm = timer.around if timer else (lambda _n, f: f())
             return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h0, chunk_size=C))
-        steps2 = max(3, args.steps // 4)
+        steps2 = max(5, args.steps // 2)
         ms1, k1 = time_with_breakdown(torch, mono, steps2, 2)
         extra["monolithic_64k"] = {"tokens_per_s": tokens / (ms1 * 1e-3), "ms": ms1,
                                    "step_roofline": step_roofline(tokens, H, ms1)}
