@@ -17,6 +17,10 @@ Contents (every function cites the passage of the pages it follows):
   recurrence, and the oracle for the WY factors w, u.
 * ``segments``    -- the exclusive prefix scan over (M_r, U_r) (same page,
   section "Implementation", phase 2).
+* ``layers``      -- the depthwise causal conv before the core and the gated
+  RMSNorm after it (MaxText PR, section "Implementation"; "RFC(qwen35): TP
+  Phase 2", sections "Partition Contract" and "Execution Contract"); readings in its
+  header.
 * ``heads``       -- grouped key heads ("RFC(qwen35): TP Phase 2", section
   "Partition Contract"; grouped order from the Ulysses page): the ungrouped
   definition on q, k with each key head repeated in place.
@@ -33,9 +37,10 @@ from .chunked import (chunk_wy, chunked_forward, chunk_transition,
                       lowrank_segment_pair)
 from .segments import exclusive_scan
 from .heads import expand_key_heads
+from .layers import silu, causal_conv1d, causal_conv1d_packed, gated_rmsnorm
 
 __all__ = [
     "forward", "forward_packed", "decode_step", "transition_pair", "load_library",
     "chunk_wy", "chunked_forward", "chunk_transition", "lowrank_segment_pair",
-    "exclusive_scan", "expand_key_heads",
+    "exclusive_scan", "expand_key_heads", "silu", "causal_conv1d", "causal_conv1d_packed", "gated_rmsnorm",
 ]

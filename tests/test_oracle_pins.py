@@ -377,3 +377,67 @@ def test_grouped_key_heads_order_and_meaning():
     assert np.array_equal(o[:, :, 0], o[:, :, 1]) and np.array_equal(o[:, :, 2], o[:, :, 3])
     assert not np.allclose(o[:, :, 1], o[:, :, 2])
     assert np.array_equal(h[:, 0], h[:, 1])
+
+
+# ---- the steps beside the core: depthwise causal conv and gated RMSNorm -------------------
+
+def _conv_case(seed, T=11, D=6, W=4):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((T, D)), rng.standard_normal((D, W)), rng.standard_normal((D, W - 1))
+
+
+def test_causal_conv_identity_and_shift_taps():
+    """Taps (0,..,0,1) pass x through; taps (1,0,..,0) delay it by W-1 tokens,
+    the first W-1 outputs coming from the state; the new state is the last W-1
+    positions."""
+    x, _, st = _conv_case(1)
+    ident = np.zeros((6, 4)); ident[:, 3] = 1
+    y, s2 = oracle.causal_conv1d(x, ident, st, activation="none")
+    assert np.array_equal(y, x) and np.array_equal(s2, x[-3:].T)
+    shift = np.zeros((6, 4)); shift[:, 0] = 1
+    y, _ = oracle.causal_conv1d(x, shift, st, activation="none")
+    assert np.array_equal(y[:3], st.T) and np.array_equal(y[3:], x[:-3])
+    y0, _ = oracle.causal_conv1d(x, shift, None, activation="none")
+    assert np.array_equal(y0[:3], np.zeros((3, 6)))
+
+
+def test_causal_conv_matches_numpy_convolve():
+    """Each channel against numpy's full convolution with the reversed taps
+    (a library routine), state prepended."""
+    x, w, st = _conv_case(2)
+    y, _ = oracle.causal_conv1d(x, w, st, activation="none")
+    for c in range(6):
+        full = np.convolve(np.concatenate([st[c], x[:, c]]), w[c, ::-1], mode="full")
+        np.testing.assert_allclose(y[:, c], full[3:3 + 11], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("cut", [0, 1, 2, 3, 7, 11])
+def test_causal_conv_streams_through_its_state(cut):
+    """Convolving [a | b] equals convolving a, then b from a's final state, also
+    when a is shorter than the W-1 tokens the state holds (decode steps)."""
+    x, w, st = _conv_case(3)
+    y, s_end = oracle.causal_conv1d(x, w, st)
+    ya, sa = oracle.causal_conv1d(x[:cut], w, st)
+    yb, sb = oracle.causal_conv1d(x[cut:], w, sa)
+    np.testing.assert_allclose(np.concatenate([ya, yb]), y, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(sb, s_end, rtol=0, atol=0)
+
+
+def test_silu_and_gated_rmsnorm_closed_forms():
+    """SiLU(u) = u * sigmoid(u) (scipy's expit); RMSNorm of c*1 is sign(c) as
+    eps -> 0; it is invariant to positive scaling; with eps = 0 it equals
+    o * sqrt(V) / ||o||; the gate multiplies elementwise by SiLU(z)."""
+    from scipy.special import expit
+    u = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(oracle.silu(u), u * expit(u), rtol=1e-14, atol=1e-300)
+    assert oracle.silu(0.0) == 0.0
+    V = 8
+    one = np.ones(V)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(-3.0 * one, one, eps=0.0), -one, rtol=1e-15)
+    rng = np.random.default_rng(4)
+    o, w, z = rng.standard_normal((5, V)), rng.standard_normal(V), rng.standard_normal((5, V))
+    np.testing.assert_allclose(oracle.gated_rmsnorm(7.5 * o, w, eps=0.0), oracle.gated_rmsnorm(o, w, eps=0.0),
+                               rtol=1e-13)
+    ref = o * np.sqrt(V) / np.linalg.norm(o, axis=-1, keepdims=True) * w
+    np.testing.assert_allclose(oracle.gated_rmsnorm(o, w, eps=0.0), ref, rtol=1e-13)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(o, w, z, eps=0.0), ref * z * expit(z), rtol=1e-13)
