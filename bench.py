@@ -370,6 +370,47 @@ def main():
                                      "pieces": gdn.num_pieces(yk, yv, 64, cu, mm), "kernels_ms": k2}
             del yq, yk, yv, yg, yb, yh
 
+        # the steps beside the core at the 64k workload's size: the depthwise causal conv
+        # over the q, k, v channels (16 key heads and 32 value heads of 128: 8,192
+        # channels; 4 taps, SiLU, with the conv state) and the gated RMSNorm of the
+        # 32 x 128 outputs of every token; both stream HBM once
+        log("bench: causal conv1d and gated rmsnorm")
+        gen = torch.Generator(device=dev).manual_seed(7)
+        Tn, Dc, Wc = 65536, 2 * 16 * 128 + 32 * 128, 4
+        xc = torch.randn((1, Tn, Dc), device=dev, generator=gen).to(bf)
+        wc = (torch.randn((Dc, Wc), device=dev, generator=gen) * 0.5).to(bf)
+        sc = torch.randn((1, Dc, Wc - 1), device=dev, generator=gen).to(bf)
+
+        def conv(timer):
+            tm = timer.around if timer else (lambda _n, f: f())
+            return tm("causal_conv1d", lambda: gdn.causal_conv1d(xc, wc, sc))
+        ms_c, k_c = time_with_breakdown(torch, conv, steps2, 2)
+        conv_bytes = Tn * Dc * 2 * 2 + Dc * Wc * 2 + 2 * Dc * (Wc - 1) * 2
+        t_c = k_c["causal_conv1d"] * 1e-3
+        extra["causal_conv1d_64k"] = {
+            "tokens_per_s": Tn / (ms_c * 1e-3), "ms": ms_c, "channels": Dc, "taps": Wc,
+            "roofline": {"bound": "hbm", "achieved": conv_bytes / t_c / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": conv_bytes / t_c / 1e9 / PEAK_HBM_GBS},
+        }
+        del xc, wc, sc
+        on = torch.randn((Tn, H, V), device=dev, generator=gen).to(bf)
+        zn = torch.randn((Tn, H, V), device=dev, generator=gen).to(bf)
+        wn = torch.randn((V,), device=dev, generator=gen)
+
+        def norm(timer):
+            tm = timer.around if timer else (lambda _n, f: f())
+            return tm("gated_rmsnorm", lambda: gdn.gated_rmsnorm(on, wn, zn))
+        ms_n, k_n = time_with_breakdown(torch, norm, steps2, 2)
+        norm_bytes = Tn * H * V * 2 * 3 + V * 4
+        t_n = k_n["gated_rmsnorm"] * 1e-3
+        extra["gated_rmsnorm_64k"] = {
+            "tokens_per_s": Tn / (ms_n * 1e-3), "ms": ms_n,
+            "roofline": {"bound": "hbm", "achieved": norm_bytes / t_n / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": norm_bytes / t_n / 1e9 / PEAK_HBM_GBS},
+        }
+        del on, zn, wn
+        torch.cuda.empty_cache()
+
         log("bench: decode")
         nsteps = 128
         d = make_decode_inputs(4, 256, 32, 128, 128, nsteps, dtype="bf16")

@@ -91,6 +91,8 @@ def library():
             "gdn_piece_compose": (_i32, [P, _i32] + [_vp] * 6),
             "gdn_decode_step": (_i32, [_i32] * 6 + [_vp] * 8),
             "gdn_scan_backend": (_i32, [P]),
+            "gdn_causal_conv1d": (_i32, [_i32] * 6 + [ctypes.POINTER(_i32), _i32] + [_vp] * 6),
+            "gdn_gated_rmsnorm": (_i32, [ctypes.c_int64, _i32, _i32, ctypes.c_float] + [_vp] * 5),
             "gdn_status_string": (ctypes.c_char_p, [_i32]),
             "gdn_last_error": (ctypes.c_char_p, []),
             "gdn_version": (_i32, []),
@@ -158,6 +160,22 @@ def gdn_piece_compose(problem, first, M, U, h_seed, h_in, h_final, stream=0):
 def gdn_decode_step(B, H, H_qk, K, V, dtype, q, k, v, g, beta, state, o, stream=0):
     _check(library().gdn_decode_step(B, H, H_qk, K, V, dtype, q, k, v, g, beta, state, o, stream),
            "gdn_decode_step")
+
+
+def gdn_causal_conv1d(B, S, D, W, dtype, activation, cu_seqlens, x, weight, state_in, state_out, y, stream=0):
+    """cu_seqlens: a host sequence of n_seqs + 1 offsets, or None (batch mode)."""
+    if cu_seqlens is None:
+        cu, n = None, 0
+    else:
+        vals = [int(c) for c in cu_seqlens]
+        cu, n = (_i32 * len(vals))(*vals), len(vals) - 1
+    _check(library().gdn_causal_conv1d(B, S, D, W, dtype, activation,
+                                       ctypes.cast(cu, ctypes.POINTER(_i32)) if cu is not None else None, n,
+                                       x, weight, state_in, state_out, y, stream), "gdn_causal_conv1d")
+
+
+def gdn_gated_rmsnorm(rows, V, dtype, eps, o, z, weight, y, stream=0):
+    _check(library().gdn_gated_rmsnorm(rows, V, dtype, eps, o, z, weight, y, stream), "gdn_gated_rmsnorm")
 
 
 def gdn_scan_backend(problem):

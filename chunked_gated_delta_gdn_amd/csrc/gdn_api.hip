@@ -549,6 +549,98 @@ gdn_status gdn_decode_step(int32_t B, int32_t H, int32_t H_qk, int32_t K, int32_
     return launched(launch_decode(K, V, dtype, a, (hipStream_t)stream), "gdn_decode_step");
 }
 
+gdn_status gdn_causal_conv1d(int32_t B, int32_t S, int32_t D, int32_t W, int32_t dtype, int32_t activation,
+                             const int32_t *cu_seqlens, int32_t n_seqs, const void *x, const void *weight,
+                             const void *state_in, void *state_out, void *y, void *stream) {
+    g_err[0] = 0;
+    if (B < 0 || S < 0 || D < 1 || W < 1 || W > 8)
+        return fail(GDN_EINVAL, "bad sizes B=%d S=%d D=%d W=%d (1 <= W <= 8)", B, S, D, W);
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_EUNSUPPORTED, "dtype %d not supported", dtype);
+    if (activation != 0 && activation != 1) return fail(GDN_EINVAL, "activation %d (0 or 1)", activation);
+    if ((int64_t)D > 65535LL * 256) return fail(GDN_EUNSUPPORTED, "D = %d too large", D);
+    ConvArgs a;
+    memset(&a, 0, sizeof(a));
+    if (cu_seqlens) {
+        if (B != 1) return fail(GDN_EINVAL, "packed mode needs B == 1 (got %d)", B);
+        if (n_seqs < 1 || n_seqs > GDN_MAX_SEQS) return fail(GDN_EINVAL, "n_seqs %d not in 1 .. GDN_MAX_SEQS", n_seqs);
+        if (cu_seqlens[0] != 0) return fail(GDN_EORDER, "cu_seqlens[0] = %d, must be 0", cu_seqlens[0]);
+        for (int n = 0; n < n_seqs; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n])
+                return fail(GDN_EORDER, "cu_seqlens decreases at %d (%d -> %d)", n, cu_seqlens[n], cu_seqlens[n + 1]);
+        if (cu_seqlens[n_seqs] != S) return fail(GDN_EINVAL, "cu_seqlens[n_seqs] = %d != S = %d", cu_seqlens[n_seqs], S);
+        for (int n = 0; n <= n_seqs; ++n) a.start[n] = cu_seqlens[n];
+        a.packed = 1;
+        a.N = n_seqs;
+        a.T = S;
+    } else {
+        if ((int64_t)B > GDN_MAX_SEQS * 1024LL) return fail(GDN_EUNSUPPORTED, "B = %d too large", B);
+        a.N = B;
+        a.T = (int64_t)B * S;
+    }
+    const int N = a.N;
+    if (N == 0) return GDN_OK;
+    const bool any = a.T > 0;
+    GDN_TRY(check_ptr(x, "x", any));
+    GDN_TRY(check_ptr(y, "y", any));
+    GDN_TRY(check_ptr(weight, "weight", any || state_out));
+    GDN_TRY(check_ptr(state_in, "state_in", false));
+    GDN_TRY(check_ptr(state_out, "state_out", false));
+    const size_t es = dtype == GDN_F32 ? 4 : 2;
+    const size_t xbytes = (size_t)a.T * D * es, sbytes = (size_t)N * D * (W - 1) * es;
+    if (overlaps(x, xbytes, y, xbytes)) return fail(GDN_EINVAL, "y must not overlap x");
+    if (state_out && state_in && overlaps(state_in, sbytes, state_out, sbytes)) {
+        // a sequence spread over two token blocks (of 8 tokens or more, laid out
+        // per sequence or along the token axis in blocks of 64) would read its
+        // state in one block while another block writes it
+        for (int n = 0; n < N; ++n) {
+            const int64_t s0 = a.packed ? a.start[n] : (int64_t)n * S, s1 = a.packed ? a.start[n + 1] : s0 + S;
+            if (s1 - s0 > 8 || (s1 > s0 && s0 / 64 != (s1 - 1) / 64))
+                return fail(GDN_EINVAL, "state_out may alias state_in only when every sequence has at most 8 tokens "
+                                        "within one multiple of 64 (sequence %d spans %lld .. %lld)",
+                            n, (long long)s0, (long long)s1);
+        }
+    }
+    a.x = x;
+    a.weight = weight;
+    a.state_in = state_in;
+    a.state_out = state_out;
+    a.y = y;
+    a.D = D;
+    a.W = W;
+    a.S = S;
+    a.activation = activation;
+    if (!any && !state_out) return GDN_OK;
+    (void)hipGetLastError();
+    return launched(launch_causal_conv(dtype, a, (hipStream_t)stream), "gdn_causal_conv1d");
+}
+
+gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t V, int32_t dtype, float eps, const void *o, const void *z,
+                             const float *weight, void *y, void *stream) {
+    g_err[0] = 0;
+    if (rows < 0 || V < 1 || V > 256) return fail(GDN_EINVAL, "bad sizes rows=%lld V=%d (1 <= V <= 256)",
+                                                  (long long)rows, V);
+    if (!(eps >= 0.f)) return fail(GDN_EINVAL, "eps must be >= 0");
+    if (dtype != GDN_F32 && dtype != GDN_BF16) return fail(GDN_EUNSUPPORTED, "dtype %d not supported", dtype);
+    if (rows == 0) return GDN_OK;
+    GDN_TRY(check_ptr(o, "o", true));
+    GDN_TRY(check_ptr(z, "z", false));
+    GDN_TRY(check_ptr(weight, "weight", true));
+    GDN_TRY(check_ptr(y, "y", true));
+    const size_t bytes = (size_t)rows * V * (dtype == GDN_F32 ? 4 : 2);
+    if (y != o && overlaps(o, bytes, y, bytes)) return fail(GDN_EINVAL, "y must be o or not overlap it");
+    if (z && overlaps(z, bytes, y, bytes)) return fail(GDN_EINVAL, "y must not overlap z");
+    NormArgs a;
+    a.o = o;
+    a.z = z;
+    a.weight = weight;
+    a.y = y;
+    a.rows = rows;
+    a.V = V;
+    a.eps = eps;
+    (void)hipGetLastError();
+    return launched(launch_gated_rmsnorm(dtype, a, (hipStream_t)stream), "gdn_gated_rmsnorm");
+}
+
 int32_t gdn_scan_backend(const gdn_problem *p) {
     Resolved r;
     if (resolve(p, r) != GDN_OK) return -1;

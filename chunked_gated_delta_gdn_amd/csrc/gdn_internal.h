@@ -148,6 +148,30 @@ struct ComposeArgs {
     int16_t seq_first[GDN_MAX_SEQS + 1];
 };
 
+// Depthwise causal convolution: x, y [T, D]; weight [D, W]; states [N, D, W-1].
+struct ConvArgs {
+    const void *x, *weight, *state_in;
+    void *state_out, *y;
+    int64_t T;                 // tokens
+    int32_t D, W;              // channels, taps
+    int32_t S, N, packed;      // batch: N sequences of S tokens; packed: offsets in start
+    int32_t activation;        // 0: none, 1: SiLU
+    int32_t start[GDN_MAX_SEQS + 1];
+    // the 8-channel kernel's token blocks, laid out per sequence (set by its launcher)
+    int64_t n_blocks;
+    int32_t block_start[GDN_MAX_SEQS + 1];
+};
+
+// Gated RMSNorm over rows of V: y = o / sqrt(mean(o^2) + eps) * weight * SiLU(z).
+struct NormArgs {
+    const void *o, *z;         // z nullable (no gate)
+    const float *weight;       // [V]
+    void *y;
+    int64_t rows;
+    int32_t V;
+    float eps;
+};
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_scan(int K, int V, int C, int dtype, bool carry, const ScanArgs &a,
                        hipStream_t s);
@@ -159,6 +183,8 @@ bool mfma_prepare_available(int K, int V, int C, int dtype);
 hipError_t launch_prepare_mfma(const PrepArgs &a, hipStream_t s);
 hipError_t launch_decode(int K, int V, int dtype, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_compose(int K, int V, const ComposeArgs &a, hipStream_t s);
+hipError_t launch_causal_conv(int dtype, const ConvArgs &a, hipStream_t s);
+hipError_t launch_gated_rmsnorm(int dtype, const NormArgs &a, hipStream_t s);
 
 bool shape_supported(int K, int V, int C);
 

@@ -18,7 +18,7 @@ from . import binding as _b
 
 __all__ = ["problem_for", "chunk_prepare", "scan_emit", "scan_carry", "segment_compose",
            "segment_bounds", "forward_segmented", "num_pieces", "scan_tail_emit", "piece_compose",
-           "plan_pieces", "forward_packed", "decode_step", "forward"]
+           "plan_pieces", "forward_packed", "decode_step", "forward", "causal_conv1d", "gated_rmsnorm"]
 
 
 def _dtype_code(t):
@@ -393,6 +393,49 @@ def decode_step(q, k, v, g, beta, state, out=None):
     _b.gdn_decode_step(B, H, Hk, K, V, _dtype_code(k), _addr(q), _addr(k), _addr(v), _addr(g),
                        _addr(beta), _addr(state), _addr(o), _stream(dev))
     return o
+
+
+def causal_conv1d(x, weight, state=None, cu_seqlens=None, activation="silu", want_state=True, state_out=None):
+    """Depthwise causal convolution before the core (``gdn_causal_conv1d``).
+
+    x [B,S,D] (or [1,T,D] with cu_seqlens), weight [D,W], state [N,D,W-1] or
+    None (zeros), all in x's dtype.  Returns (y like x, the state after each
+    sequence [N,D,W-1] or None).  ``state_out`` may be ``state`` itself for
+    one-token steps (decode)."""
+    dev = x.device
+    B, S, D = x.shape
+    W = weight.shape[-1]
+    N = B if cu_seqlens is None else len(cu_seqlens) - 1
+    _need(x, "x", (B, S, D), x.dtype, dev)
+    _need(weight, "weight", (D, W), x.dtype, dev)
+    if state is not None:
+        _need(state, "state", (N, D, W - 1), x.dtype, dev)
+    if state_out is None and want_state:
+        state_out = torch.empty((N, D, W - 1), dtype=x.dtype, device=dev)
+    if state_out is not None:
+        _need(state_out, "state_out", (N, D, W - 1), x.dtype, dev)
+    act = {"silu": 1, "none": 0, None: 0}[activation]
+    y = torch.empty_like(x)
+    _b.gdn_causal_conv1d(B, S, D, W, _dtype_code(x), act, cu_seqlens, _addr(x), _addr(weight), _addr(state),
+                         _addr(state_out), _addr(y), _stream(dev))
+    return y, state_out
+
+
+def gated_rmsnorm(o, weight, z=None, eps=1e-6, out=None):
+    """Gated RMSNorm after the core (``gdn_gated_rmsnorm``): each vector of the
+    last axis of o (V elements) becomes o / sqrt(mean(o^2) + eps) * weight *
+    SiLU(z).  weight [V] fp32; z like o or None; ``out`` may be o."""
+    dev = o.device
+    V = o.shape[-1]
+    _need(o, "o", tuple(o.shape), o.dtype, dev)
+    _need(weight, "weight", (V,), torch.float32, dev)
+    if z is not None:
+        _need(z, "z", tuple(o.shape), o.dtype, dev)
+    y = out if out is not None else torch.empty_like(o)
+    _need(y, "out", tuple(o.shape), o.dtype, dev)
+    _b.gdn_gated_rmsnorm(o.numel() // V, V, _dtype_code(o), float(eps), _addr(o), _addr(z), _addr(weight),
+                         _addr(y), _stream(dev))
+    return y
 
 
 def segment_bounds(S, chunk_size, n_segments, seg_starts=None):

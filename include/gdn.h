@@ -242,6 +242,39 @@ gdn_status gdn_decode_step(int32_t B, int32_t H, int32_t H_qk, int32_t K, int32_
                            const float *g, const float *beta, float *state, void *o,
                            void *stream);
 
+/*
+ * gdn_causal_conv1d -- the depthwise causal convolution over the q, k, v
+ * channels before the core (MaxText PR, section "Implementation": a causal
+ * conv1d whose shard halo is W-1 tokens; "RFC(qwen35): TP Phase 2", section
+ * "Partition Contract": a conv state of qkv_dim x (W-1) per request):
+ *   y[t,c] = act( sum_{i<W} weight[c,i] * x~[t-(W-1)+i, c] ),
+ * x~ being the sequence's tokens preceded by its state (the W-1 previous
+ * tokens, oldest first; zeros when state_in is NULL); act is the identity
+ * (activation 0) or SiLU(u) = u / (1 + e^-u) (activation 1).  state_out
+ * (nullable) receives the last W-1 positions of x~, so a sequence can be
+ * continued token by token (decode) or chunk by chunk.
+ * Batch (cu_seqlens NULL): B sequences of S tokens, x, y [B,S,D].  Packed:
+ * B == 1, n_seqs sequences at offsets cu_seqlens (host, n_seqs + 1 entries,
+ * first 0, non-decreasing, last S), x, y [S,D].  weight [D,W]; states
+ * [N,D,W-1] (N = B or n_seqs); all in `dtype`, accumulation in fp32.
+ * 1 <= W <= 8.  y must not overlap x.  state_out may alias state_in only when
+ * every sequence has at most 8 tokens and none crosses a multiple of 64 on the
+ * token axis (one-token decode batches always qualify); otherwise GDN_EINVAL.
+ */
+gdn_status gdn_causal_conv1d(int32_t B, int32_t S, int32_t D, int32_t W, int32_t dtype, int32_t activation,
+                             const int32_t *cu_seqlens, int32_t n_seqs, const void *x, const void *weight,
+                             const void *state_in, void *state_out, void *y, void *stream);
+
+/*
+ * gdn_gated_rmsnorm -- the gated RMSNorm after the core ("RFC(qwen35): TP
+ * Phase 2", section "Execution Contract"), per row of V elements:
+ *   y = o / sqrt(mean(o^2) + eps) * weight * SiLU(z).
+ * o, z, y [rows, V] in `dtype` (z nullable: no gate), weight [V] fp32,
+ * 1 <= V <= 256, eps >= 0; accumulation in fp32.  y may alias o.
+ */
+gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t V, int32_t dtype, float eps, const void *o, const void *z,
+                             const float *weight, void *y, void *stream);
+
 /* Which units run gdn_scan for this problem: 1 = matrix cores (bf16 MFMA
  * kernel), 0 = fp32 vector ALU kernel, -1 = invalid problem.  Lets callers
  * and benchmarks name the roofline that bounds the call. */

@@ -218,3 +218,30 @@ def test_grouped_heads_rules(hq, ok):
     (0 means H_qk = H)."""
     st = status(prob(H=4, H_qk=hq))
     assert st == (b.GDN_OK if ok else b.GDN_EINVAL)
+
+
+def test_conv_and_norm_validation():
+    import ctypes
+    lib = b.library()
+    conv = lambda *a: lib.gdn_causal_conv1d(*a)
+    assert conv(2, 16, 8, 0, b.GDN_F32, 1, None, 0, FAKE, FAKE, None, None, FAKE + (1 << 20), None) == b.GDN_EINVAL
+    assert conv(2, 16, 8, 9, b.GDN_F32, 1, None, 0, FAKE, FAKE, None, None, FAKE + (1 << 20), None) == b.GDN_EINVAL
+    assert conv(2, 16, 8, 4, 7, 1, None, 0, FAKE, FAKE, None, None, FAKE + (1 << 20), None) == b.GDN_EUNSUPPORTED
+    assert conv(2, 16, 8, 4, b.GDN_F32, 2, None, 0, FAKE, FAKE, None, None, FAKE + (1 << 20), None) == b.GDN_EINVAL
+    assert conv(2, 16, 8, 4, b.GDN_F32, 1, None, 0, FAKE, FAKE, None, None, FAKE, None) == b.GDN_EINVAL   # y == x
+    assert conv(2, 16, 8, 4, b.GDN_F32, 1, None, 0, None, FAKE, None, None, FAKE + (1 << 20), None) == b.GDN_EINVAL
+    cu = (ctypes.c_int32 * 3)(0, 20, 10)
+    assert conv(1, 10, 8, 4, b.GDN_F32, 1, cu, 2, FAKE, FAKE, None, None, FAKE + (1 << 20), None) == b.GDN_EORDER
+    cu = (ctypes.c_int32 * 3)(0, 5, 12)
+    assert conv(2, 12, 8, 4, b.GDN_F32, 1, cu, 2, FAKE, FAKE, None, None, FAKE + (1 << 20), None) == b.GDN_EINVAL
+    # in-place state with a sequence crossing token 64
+    assert conv(1, 100, 8, 4, b.GDN_F32, 1, None, 0, FAKE, FAKE, FAKE + (2 << 20), FAKE + (2 << 20),
+                FAKE + (1 << 20), None) == b.GDN_EINVAL
+    norm = lib.gdn_gated_rmsnorm
+    assert norm(4, 0, b.GDN_F32, 1e-6, FAKE, None, FAKE, FAKE, None) == b.GDN_EINVAL
+    assert norm(4, 257, b.GDN_F32, 1e-6, FAKE, None, FAKE, FAKE, None) == b.GDN_EINVAL
+    assert norm(4, 128, b.GDN_F32, -1.0, FAKE, None, FAKE, FAKE, None) == b.GDN_EINVAL
+    assert norm(4, 128, 5, 1e-6, FAKE, None, FAKE, FAKE, None) == b.GDN_EUNSUPPORTED
+    assert norm(4, 128, b.GDN_F32, 1e-6, FAKE, None, None, FAKE, None) == b.GDN_EINVAL
+    assert norm(4, 128, b.GDN_F32, 1e-6, FAKE, None, FAKE, FAKE + 16, None) == b.GDN_EINVAL   # partial overlap
+    assert norm(0, 128, b.GDN_F32, 1e-6, None, None, None, None, None) == b.GDN_OK
