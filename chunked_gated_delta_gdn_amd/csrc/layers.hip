@@ -20,6 +20,9 @@
 namespace gdn {
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kConvThreads = 256;   // channels per workgroup
 constexpr int kConvTokens = 64;     // tokens per thread (one token block)
 constexpr int kMaxTaps = 8;
@@ -154,10 +157,11 @@ template <> struct Vec8<bf16_t> {
         }
     }
     static __device__ __forceinline__ void store(void *p, int64_t i, const float (&v)[8]) {
+        // two values per v_cvt_pk_bf16_f32 (round to nearest even)
         uint32_t w[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            w[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
+            w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v[2 * k], v[2 * k + 1]}, bf16x2));
         *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p) + i) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 };
