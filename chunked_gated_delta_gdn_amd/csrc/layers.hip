@@ -256,10 +256,21 @@ __global__ __launch_bounds__(kConvThreads) void causal_conv8_kernel(ConvArgs a) 
     for (int u = 0; u < TB; ++u)
         if (u < nt) raw_load(xs[u], a.x, (t0 + u) * D + c);
     float w[8][MT];
+    if (MT == 4 && W == 4) {
+        // the 8 channels' 32 taps are contiguous: 4 accesses of 8 values
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+        for (int q = 0; q < 4; ++q) {
+            float t8[8];
+            Vec8<T>::load(a.weight, c * 4 + 8 * q, t8);
 #pragma unroll
-        for (int i = 0; i < MT; ++i) w[k][i] = i < W ? Elem<T>::load(a.weight, (c + k) * W + i) : 0.f;
+            for (int e = 0; e < 8; ++e) w[2 * q + e / 4][e % 4] = t8[e];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int i = 0; i < MT; ++i) w[k][i] = i < W ? Elem<T>::load(a.weight, (c + k) * W + i) : 0.f;
+    }
     // the tap on the current token, picked without a run-time array index (which
     // would put w in scratch memory)
     float wl[8];
