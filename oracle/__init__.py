@@ -21,20 +21,26 @@ Contents (every function cites the passage of the pages it follows):
   RMSNorm after it (MaxText PR, section "Implementation"; "RFC(qwen35): TP
   Phase 2", sections "Partition Contract" and "Execution Contract"); readings in its
   header.
+* ``backward``    -- reverse mode: the chain rule applied to the token
+  recurrence (the vector-Jacobian product for given dl/do, dl/dhT), fp64 in
+  C; ``chunked.chunked_backward`` is the same gradient taken through the
+  chunk equations, an independent second derivation.
 * ``heads``       -- grouped key heads ("RFC(qwen35): TP Phase 2", section
   "Partition Contract"; grouped order from the Ulysses page): the ungrouped
   definition on q, k with each key head repeated in place.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, hand-worked fixtures under
-``tests/golden/`` and the independent chunked algorithm.  The only thing left
+``tests/golden/`` and the independent chunked algorithm; the backward pass
+also against central finite differences of the forward.  The only thing left
 unpinned is the bf16 tolerance margin of the GPU comparison, which the pages
 do not print.
 """
 from .recurrence import (forward, forward_packed, decode_step, transition_pair,
                          load_library)
 from .chunked import (chunk_wy, chunked_forward, chunk_transition,
-                      lowrank_segment_pair)
+                      lowrank_segment_pair, chunked_backward)
+from .backward import backward, backward_packed
 from .segments import exclusive_scan
 from .heads import expand_key_heads
 from .layers import silu, causal_conv1d, causal_conv1d_packed, gated_rmsnorm
@@ -42,5 +48,6 @@ from .layers import silu, causal_conv1d, causal_conv1d_packed, gated_rmsnorm
 __all__ = [
     "forward", "forward_packed", "decode_step", "transition_pair", "load_library",
     "chunk_wy", "chunked_forward", "chunk_transition", "lowrank_segment_pair",
+    "chunked_backward", "backward", "backward_packed",
     "exclusive_scan", "expand_key_heads", "silu", "causal_conv1d", "causal_conv1d_packed", "gated_rmsnorm",
 ]

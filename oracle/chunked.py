@@ -44,7 +44,7 @@ def _chunk_terms(q, k, v, g, beta):
     u = solve_triangular(I_A, beta[:, None] * v, lower=True, unit_diagonal=True)
     gamma = np.exp(G[-1]) if L else 1.0
     k_tilde = np.exp(G[-1] - G)[:, None] * k if L else k
-    terms = dict(G=G, A=A, w=w, u=u, gamma=gamma, k_tilde=k_tilde)
+    terms = dict(G=G, A=A, w=w, u=u, gamma=gamma, k_tilde=k_tilde, decay=decay)
     if q is not None:
         terms["q_g"] = np.exp(G)[:, None] * q
         terms["attn"] = np.where(causal, decay * (q @ k.T), 0.0)
@@ -129,3 +129,85 @@ def lowrank_segment_pair(k, v, g, beta, C):
                 uu = t["gamma"] * uu + t["k_tilde"].T @ (t["u"] - t["w"] @ uu)
             M[b, hh], U[b, hh] = m, uu
     return M, U
+
+
+def chunked_backward(q, k, v, g, beta, C, h0, do, dhT=None):
+    """Gradients of the chunked form, batch layout: (dq, dk, dv, dg, dbeta, dh0).
+
+    The chain rule taken through the chunk equations above rather than through
+    the token recurrence, so it checks the chunk algebra of a backward pass
+    against ``backward.backward``.  A forward sweep keeps the state h_c at the
+    start of every chunk; a reverse sweep carries dh (dl/dh at the chunk's end)
+    and, per chunk, with D = Dec (the causal decay ratios exp(G_r - G_s)),
+    Kb = diag(beta exp(G)) K and Vb = diag(beta) V (so w = T Kb, u = T Vb):
+
+        delta  = u - w h_c
+        ddelta = attn^T do + k_tilde dh           (o and h_out both read delta)
+        dh_c   = gamma dh + q_g^T do - w^T ddelta
+        dattn  = causal(do delta^T);  dq_g = do h_c^T;  dk_tilde = delta dh^T
+        dw     = -ddelta h_c^T;       du = ddelta
+        dT     = du Vb^T + dw Kb^T;   dVb = T^T du;  dKb = T^T dw
+        dA     = -strict_lower(T^T dT T^T)        (T = (I + A)^{-1})
+
+    then every chunk quantity hands its gradient to q, k, v, beta and the
+    cumulative decay G; dg is the reverse cumulative sum of dG in the chunk.
+    """
+    q, k, v, g, beta, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, beta, do))
+    B, S, H, K = k.shape
+    V = v.shape[-1]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dg, dbeta = np.zeros_like(g), np.zeros_like(beta)
+    dh0 = np.zeros((B, H, K, V))
+    spans = _chunks(S, C)
+    for b in range(B):
+        for hh in range(H):
+            h = np.zeros((K, V)) if h0 is None else np.array(h0[b, hh], dtype=np.float64)
+            starts, terms = [], []
+            for c0, c1 in spans:
+                t = _chunk_terms(q[b, c0:c1, hh], k[b, c0:c1, hh], v[b, c0:c1, hh],
+                                 g[b, c0:c1, hh], beta[b, c0:c1, hh])
+                starts.append(h)
+                terms.append(t)
+                h = t["gamma"] * h + t["k_tilde"].T @ (t["u"] - t["w"] @ h)
+            dh = np.zeros((K, V)) if dhT is None else np.array(dhT[b, hh], dtype=np.float64)
+            for (c0, c1), hc, t in reversed(list(zip(spans, starts, terms))):
+                qq, kk, vv = q[b, c0:c1, hh], k[b, c0:c1, hh], v[b, c0:c1, hh]
+                bb, dd = beta[b, c0:c1, hh], do[b, c0:c1, hh]
+                L = c1 - c0
+                G, D, A = t["G"], t["decay"], t["A"]
+                eG = np.exp(G)
+                T = np.linalg.inv(np.eye(L) + A)
+                Kb, Vb = (bb * eG)[:, None] * kk, bb[:, None] * vv
+                delta = t["u"] - t["w"] @ hc
+                ddelta = t["attn"].T @ dd + t["k_tilde"] @ dh
+                dh_c = t["gamma"] * dh + t["q_g"].T @ dd - t["w"].T @ ddelta
+                causal = np.tril(np.ones((L, L), dtype=bool), 0)
+                dattn = np.where(causal, dd @ delta.T, 0.0)
+                dq_g = dd @ hc.T
+                dk_tilde = delta @ dh.T
+                dw = -ddelta @ hc.T
+                dT = ddelta @ Vb.T + dw @ Kb.T
+                dVb, dKb = T.T @ ddelta, T.T @ dw
+                dA = np.tril(-(T.T @ dT @ T.T), -1)
+                dKK = dA * bb[:, None] * D                       # A = beta_r D (K K^T)
+                P = dattn * D                                    # attn = D (Q K^T)
+                dq_ = eG[:, None] * dq_g + P @ kk
+                dk_ = (P.T @ qq + np.exp(G[-1] - G)[:, None] * dk_tilde
+                       + (bb * eG)[:, None] * dKb + dKK @ kk + dKK.T @ kk)
+                dv_ = bb[:, None] * dVb
+                db_ = (dVb * vv).sum(1) + (dKb * eG[:, None] * kk).sum(1) + (dA * D * (kk @ kk.T)).sum(1)
+                dG = (dq_g * t["q_g"]).sum(1)
+                ea = dattn * t["attn"]
+                dG += ea.sum(1) - ea.sum(0)
+                ek = (dk_tilde * t["k_tilde"]).sum(1)
+                dG -= ek
+                dG += (dKb * Kb).sum(1)
+                eA = dA * A
+                dG += eA.sum(1) - eA.sum(0)
+                dG[-1] += ek.sum() + t["gamma"] * (hc * dh).sum()
+                dq[b, c0:c1, hh], dk[b, c0:c1, hh], dv[b, c0:c1, hh] = dq_, dk_, dv_
+                dbeta[b, c0:c1, hh] = db_
+                dg[b, c0:c1, hh] = np.cumsum(dG[::-1])[::-1]
+                dh = dh_c
+            dh0[b, hh] = dh
+    return dq, dk, dv, dg, dbeta, dh0
