@@ -11,7 +11,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = ["gdn_api.hip", "scan_generic.hip", "scan_mfma.hip", "prepare_mfma.hip", "decode.hip",
-           "compose.hip", "layers.hip"]
+           "compose.hip", "layers.hip", "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -91,6 +91,8 @@ def library():
             "gdn_piece_compose": (_i32, [P, _i32] + [_vp] * 6),
             "gdn_decode_step": (_i32, [_i32] * 6 + [_vp] * 8),
             "gdn_scan_backend": (_i32, [P]),
+            "gdn_backward_workspace_bytes": (ctypes.c_size_t, [P]),
+            "gdn_backward": (_i32, [P] + [_vp] * 15 + [ctypes.c_size_t, _vp]),
             "gdn_causal_conv1d": (_i32, [_i32] * 6 + [ctypes.POINTER(_i32), _i32] + [_vp] * 6),
             "gdn_gated_rmsnorm": (_i32, [ctypes.c_int64, _i32, _i32, ctypes.c_float] + [_vp] * 5),
             "gdn_status_string": (ctypes.c_char_p, [_i32]),
@@ -176,6 +178,17 @@ def gdn_causal_conv1d(B, S, D, W, dtype, activation, cu_seqlens, x, weight, stat
 
 def gdn_gated_rmsnorm(rows, V, dtype, eps, o, z, weight, y, stream=0):
     _check(library().gdn_gated_rmsnorm(rows, V, dtype, eps, o, z, weight, y, stream), "gdn_gated_rmsnorm")
+
+
+def gdn_backward_workspace_bytes(problem):
+    return int(library().gdn_backward_workspace_bytes(ctypes.byref(problem)))
+
+
+def gdn_backward(problem, q, k, v, g, beta, h0, dout, dhT, dq, dk, dv, dg, dbeta, dh0,
+                 workspace, workspace_bytes, stream=0):
+    _check(library().gdn_backward(ctypes.byref(problem), q, k, v, g, beta, h0, dout, dhT, dq, dk,
+                                  dv, dg, dbeta, dh0, workspace, workspace_bytes, stream),
+           "gdn_backward")
 
 
 def gdn_scan_backend(problem):

@@ -641,6 +641,112 @@ gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t V, int32_t dtype, float eps, 
     return launched(launch_gated_rmsnorm(dtype, a, (hipStream_t)stream), "gdn_gated_rmsnorm");
 }
 
+// Workspace of the backward pass, per (chunk, head), fp32: T, attn, Ak
+// (C x C), w (C x K), u, delta, ddelta (C x V), state, dstate (K x V).
+static size_t backward_ws_per_chunk(const gdn_problem *p) {
+    return sizeof(float) * ((size_t)3 * p->C * p->C + (size_t)p->C * p->K + (size_t)3 * p->C * p->V +
+                            (size_t)2 * p->K * p->V);
+}
+
+static gdn_status backward_problem(const gdn_problem *p, Resolved &r) {
+    GDN_TRY(resolve(p, r));
+    if (p->n_seqs == 0 && p->n_segments != 1)
+        return fail(GDN_EUNSUPPORTED, "the backward pass runs whole sequences (n_segments must be 1)");
+    if (p->max_piece_chunks != 0)
+        return fail(GDN_EUNSUPPORTED, "the backward pass runs whole sequences (max_piece_chunks must be 0)");
+    if (p->H_qk != 0 && p->H_qk != p->H)
+        return fail(GDN_EUNSUPPORTED, "grouped key heads (H_qk = %d < H = %d) have no backward pass",
+                    p->H_qk, p->H);
+    return GDN_OK;
+}
+
+size_t gdn_backward_workspace_bytes(const gdn_problem *p) {
+    Resolved r;
+    if (backward_problem(p, r) != GDN_OK) return 0;
+    return (size_t)r.n_chunks * p->H * backward_ws_per_chunk(p);
+}
+
+gdn_status gdn_backward(const gdn_problem *p, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, const float *h0, const void *dout,
+                        const float *dhT, void *dq, void *dk, void *dv, float *dg, float *dbeta,
+                        float *dh0, void *workspace, size_t workspace_bytes, void *stream) {
+    g_err[0] = 0;
+    Resolved r;
+    GDN_TRY(backward_problem(p, r));
+    const bool any = r.T > 0;
+    GDN_TRY(check_ptr(q, "q", any));
+    GDN_TRY(check_ptr(k, "k", any));
+    GDN_TRY(check_ptr(v, "v", any));
+    GDN_TRY(check_ptr(g, "g", any));
+    GDN_TRY(check_ptr(beta, "beta", any));
+    GDN_TRY(check_ptr(h0, "h0", false));
+    GDN_TRY(check_ptr(dout, "dout", any));
+    GDN_TRY(check_ptr(dhT, "dhT", false));
+    GDN_TRY(check_ptr(dq, "dq", any));
+    GDN_TRY(check_ptr(dk, "dk", any));
+    GDN_TRY(check_ptr(dv, "dv", any));
+    GDN_TRY(check_ptr(dg, "dg", any));
+    GDN_TRY(check_ptr(dbeta, "dbeta", any));
+    GDN_TRY(check_ptr(dh0, "dh0", false));
+    const size_t need = (size_t)r.n_chunks * p->H * backward_ws_per_chunk(p);
+    GDN_TRY(check_ptr(workspace, "workspace", need > 0));
+    if (workspace_bytes < need)
+        return fail(GDN_EINVAL, "backward workspace %zu bytes < %zu needed", workspace_bytes, need);
+    const size_t es = elem_size(p->dtype);
+    const size_t nqk = (size_t)r.T * p->H * p->K * es, nv = (size_t)r.T * p->H * p->V * es;
+    const size_t ngb = (size_t)r.T * p->H * sizeof(float);
+    const size_t nst = (size_t)r.N * p->H * p->K * p->V * sizeof(float);
+    const struct { const void *ptr; size_t n; } ins[] = {
+        {q, nqk}, {k, nqk}, {v, nv}, {g, ngb}, {beta, ngb}, {h0, nst}, {dout, nv}, {dhT, nst},
+        {workspace, need}};
+    const struct { const void *ptr; size_t n; const char *name; } outs[] = {
+        {dq, nqk, "dq"}, {dk, nqk, "dk"}, {dv, nv, "dv"}, {dg, ngb, "dg"}, {dbeta, ngb, "dbeta"},
+        {dh0, nst, "dh0"}};
+    for (const auto &o : outs) {
+        for (const auto &in : ins)
+            if (overlaps(o.ptr, o.n, in.ptr, in.n))
+                return fail(GDN_EINVAL, "%s overlaps an input or the workspace", o.name);
+        for (const auto &o2 : outs)
+            if (&o2 != &o && overlaps(o.ptr, o.n, o2.ptr, o2.n))
+                return fail(GDN_EINVAL, "%s overlaps another output", o.name);
+    }
+    if (!any && !dh0) return GDN_OK;
+    // (with no tokens only the reverse scan runs: it writes dh0 = dhT, or 0)
+    BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.g = g;
+    a.beta = beta;
+    a.h0 = h0;
+    a.dhT = dhT;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dg = dg;
+    a.dbeta = dbeta;
+    a.dh0 = dh0;
+    const size_t CH = (size_t)r.n_chunks * p->H;
+    float *ws = static_cast<float *>(workspace);
+    const size_t CC = (size_t)p->C * p->C;
+    a.T = ws;
+    a.attn = a.T + CH * CC;
+    a.Ak = a.attn + CH * CC;
+    a.w = a.Ak + CH * CC;
+    a.u = a.w + CH * p->C * p->K;
+    a.d = a.u + CH * p->C * p->V;
+    a.dd = a.d + CH * p->C * p->V;
+    a.hs = a.dd + CH * p->C * p->V;
+    a.dhs = a.hs + CH * p->K * p->V;
+    a.H = p->H;
+    a.n_chunks = r.n_chunks;
+    a.ct = r.ct;
+    (void)hipGetLastError();
+    return launched(launch_backward(p->K, p->V, p->C, p->dtype, a, r.P, (hipStream_t)stream),
+                    "gdn_backward");
+}
+
 int32_t gdn_scan_backend(const gdn_problem *p) {
     Resolved r;
     if (resolve(p, r) != GDN_OK) return -1;
@@ -660,6 +766,6 @@ const char *gdn_status_string(int32_t status) {
 
 const char *gdn_last_error(void) { return g_err; }
 
-int32_t gdn_version(void) { return 110; }
+int32_t gdn_version(void) { return 120; }
 
 }  // extern "C"

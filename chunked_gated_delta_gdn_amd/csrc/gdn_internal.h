@@ -172,6 +172,22 @@ struct NormArgs {
     float eps;
 };
 
+// Backward pass.  Gradients in the layouts of their inputs; the fp32
+// workspace holds, per (chunk, head): T = (I + A)^{-1}, attn and the decayed
+// Gram Dec (.) K K^T (C x C each), w (C x K), u, delta, ddelta (C x V), and
+// the state and its gradient at the chunk's start and end (V x K, transposed).
+struct BwdArgs {
+    const void *q, *k, *v, *dout;
+    const float *g, *beta, *h0, *dhT;
+    void *dq, *dk, *dv;
+    float *dg, *dbeta, *dh0;
+    float *T, *attn, *Ak, *w, *u, *hs, *dhs, *d, *dd;
+    int32_t H;
+    int64_t n_chunks;
+    ChainTable ct;
+};
+static_assert(sizeof(BwdArgs) + 64 <= 4096, "backward kernel arguments too large");
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_scan(int K, int V, int C, int dtype, bool carry, const ScanArgs &a,
                        hipStream_t s);
@@ -185,6 +201,9 @@ hipError_t launch_decode(int K, int V, int dtype, const DecodeArgs &a, hipStream
 hipError_t launch_compose(int K, int V, const ComposeArgs &a, hipStream_t s);
 hipError_t launch_causal_conv(int dtype, const ConvArgs &a, hipStream_t s);
 hipError_t launch_gated_rmsnorm(int dtype, const NormArgs &a, hipStream_t s);
+// the four backward launches; n_chains = sequences
+hipError_t launch_backward(int K, int V, int C, int dtype, const BwdArgs &a, int n_chains,
+                           hipStream_t s);
 
 bool shape_supported(int K, int V, int C);
 

@@ -18,7 +18,8 @@ from . import binding as _b
 
 __all__ = ["problem_for", "chunk_prepare", "scan_emit", "scan_carry", "segment_compose",
            "segment_bounds", "forward_segmented", "num_pieces", "scan_tail_emit", "piece_compose",
-           "plan_pieces", "forward_packed", "decode_step", "forward", "causal_conv1d", "gated_rmsnorm"]
+           "plan_pieces", "forward_packed", "decode_step", "forward", "causal_conv1d", "gated_rmsnorm",
+           "backward", "chunk_gated_delta_rule"]
 
 
 def _dtype_code(t):
@@ -559,3 +560,59 @@ def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segment
     return scan_emit(q, k, v, g, beta, h_in=h_in, wy=wy, chunk_size=chunk_size,
                      n_segments=n_segments, seg_starts=seg_starts,
                      output_final_state=output_final_state)
+
+
+def backward(q, k, v, g, beta, do, h0=None, dhT=None, chunk_size=64, cu_seqlens=None, want_dh0=True):
+    """Gradients through the forward pass (``gdn_backward``).
+
+    q, k [B,S,H,K]; v, do [B,S,H,V] (fp32 or bf16); g, beta [B,S,H] fp32;
+    h0, dhT [N,H,K,V] fp32 or None (zero).  Packed batches pass B == 1 and
+    cu_seqlens.  Returns (dq, dk, dv, dg, dbeta, dh0 or None), each in the
+    layout and dtype of its input (dh0 fp32)."""
+    B, S, H, K, V = _check_inputs(q, k, v, g, beta)
+    if k.shape[2] != H:
+        raise ValueError("grouped key heads have no backward pass")
+    dev = k.device
+    N = _n_seqs(k, cu_seqlens)
+    _need(do, "do", (B, S, H, V), k.dtype, dev)
+    if h0 is not None:
+        _need(h0, "h0", (N, H, K, V), torch.float32, dev)
+    if dhT is not None:
+        _need(dhT, "dhT", (N, H, K, V), torch.float32, dev)
+    p = problem_for(k, v, chunk_size, cu_seqlens)
+    _b.gdn_validate(p)
+    nbytes = _b.gdn_backward_workspace_bytes(p)
+    ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg, dbeta = torch.empty_like(g), torch.empty_like(beta)
+    dh0 = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if want_dh0 else None
+    _b.gdn_backward(p, _addr(q), _addr(k), _addr(v), _addr(g), _addr(beta), _addr(h0), _addr(do),
+                    _addr(dhT), _addr(dq), _addr(dk), _addr(dv), _addr(dg), _addr(dbeta), _addr(dh0),
+                    _addr(ws), nbytes, _stream(dev))
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+class _ChunkGatedDeltaRule(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, h0, chunk_size, cu_seqlens):
+        o, hT = forward(q, k, v, g, beta, h0=h0, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
+                        max_piece_chunks=0 if cu_seqlens is not None else None)
+        ctx.save_for_backward(q, k, v, g, beta, h0)
+        ctx.chunk_size, ctx.cu_seqlens = chunk_size, cu_seqlens
+        return o, hT
+
+    @staticmethod
+    def backward(ctx, do, dhT):
+        q, k, v, g, beta, h0 = ctx.saved_tensors
+        dq, dk, dv, dg, dbeta, dh0 = backward(
+            q, k, v, g, beta, do.contiguous(), h0=h0,
+            dhT=None if dhT is None else dhT.contiguous(), chunk_size=ctx.chunk_size,
+            cu_seqlens=ctx.cu_seqlens, want_dh0=h0 is not None and ctx.needs_input_grad[5])
+        return dq, dk, dv, dg, dbeta, dh0, None, None
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None):
+    """Differentiable forward: (o, final state), with ``backward`` as its
+    gradient (torch.autograd).  Shapes as ``forward``; one key head per value
+    head."""
+    return _ChunkGatedDeltaRule.apply(q, k, v, g, beta, h0, chunk_size, cu_seqlens)

@@ -275,6 +275,28 @@ gdn_status gdn_causal_conv1d(int32_t B, int32_t S, int32_t D, int32_t W, int32_t
 gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t V, int32_t dtype, float eps, const void *o, const void *z,
                              const float *weight, void *y, void *stream);
 
+/*
+ * gdn_backward -- gradients of a loss l(o, hT) through the forward of the
+ * problem (batch or packed; n_segments == 1, max_piece_chunks == 0, H_qk == H
+ * or 0), given dout = dl/do [same layout as o, `dtype`] and dhT = dl/dhT
+ * ([N,H,K,V] fp32, nullable = zero).  The MaxText PR "Add context
+ * parallelism to the Gated Delta Net" tests a backward pass against the
+ * single-device recurrence (section "Tests") without printing one; this is
+ * the chain rule through the chunk equations of its section "Why".
+ * Outputs, each in the layout of its input: dq, dk, dv in `dtype`; dg,
+ * dbeta fp32; dh0 [N,H,K,V] fp32 (nullable: not written; written whether or
+ * not h0 is given).  h0 nullable (zero state).  Every output is fully
+ * written for the real tokens; none may overlap an input.  workspace: caller
+ * owned device memory of gdn_backward_workspace_bytes(p) bytes, 16-byte
+ * aligned (contents undefined on return).  Arithmetic is fp32 throughout.
+ * Errors as gdn_scan; nothing is written on failure.
+ */
+size_t gdn_backward_workspace_bytes(const gdn_problem *p);
+gdn_status gdn_backward(const gdn_problem *p, const void *q, const void *k, const void *v,
+                        const float *g, const float *beta, const float *h0, const void *dout,
+                        const float *dhT, void *dq, void *dk, void *dv, float *dg, float *dbeta,
+                        float *dh0, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Which units run gdn_scan for this problem: 1 = matrix cores (bf16 MFMA
  * kernel), 0 = fp32 vector ALU kernel, -1 = invalid problem.  Lets callers
  * and benchmarks name the roofline that bounds the call. */

@@ -1,0 +1,125 @@
+"""GPU parity of the backward pass (``gdn_backward`` through the C ABI).
+
+The HIP kernels take the chain rule through the chunk equations of the
+MaxText PR "Add context parallelism to the Gated Delta Net" (section "Why");
+the oracle takes it through the token recurrence (``oracle.backward``), which
+is pinned by finite differences.  Every gradient is compared element by
+element, normwise, to the forward tolerances: 1e-4 for fp32 inputs and 2e-2
+for bf16 inputs (the kernels compute in fp32; bf16 enters through the inputs
+and the rounding of dq, dk, dv).  Cases span several chunks, ragged tails,
+both built shapes, packed streams with an empty sequence, absent h0 / dhT
+and the autograd wrapper.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import chunked_gated_delta_gdn_amd as gdn
+from workloads import make_inputs, make_packed_inputs, make_cotangents
+from gpu_util import TOL, DEV, say, to_dev, tdt, rel_err
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def oracle_grads(x, do, dhT, h0=True):
+    h0a = x.h0 if h0 else None
+    if x.cu_seqlens is not None:
+        return oracle.backward_packed(x.cu_seqlens, x.q[0], x.k[0], x.v[0], x.g[0], x.beta[0],
+                                      h0a, do[0], dhT)
+    return oracle.backward(x.q, x.k, x.v, x.g, x.beta, h0a, do, dhT)
+
+
+def gpu_grads(x, do, dhT, h0=True):
+    dt = tdt(x.dtype)
+    cu = None if x.cu_seqlens is None else [int(c) for c in x.cu_seqlens]
+    out = gdn.backward(to_dev(x.q, dt), to_dev(x.k, dt), to_dev(x.v, dt), to_dev(x.g),
+                       to_dev(x.beta), to_dev(do, dt),
+                       h0=to_dev(x.h0) if (h0 and x.h0 is not None) else None,
+                       dhT=None if dhT is None else to_dev(dhT), chunk_size=x.C, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy() for t in out]
+
+
+def check(x, do, dhT, h0=True, tag=""):
+    say(f"backward {tag}: {x.name} dtype={x.dtype} shape={x.k.shape} C={x.C}")
+    got = gpu_grads(x, do, dhT, h0)
+    ref = oracle_grads(x, do, dhT, h0)
+    if x.cu_seqlens is not None:
+        got = [g_[0] if i < 5 else g_ for i, g_ in enumerate(got)]
+    errs = {n: rel_err(g_, r) for n, g_, r in zip(NAMES, got, ref)}
+    say(f"  errors {errs}")
+    for n in NAMES:
+        assert errs[n] <= TOL[x.dtype], (n, errs[n])
+    return got, ref
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,S,H,K,C", [(2, 37, 2, 32, 16), (1, 200, 2, 128, 64), (2, 64, 1, 128, 64)])
+def test_backward_batch(dtype, B, S, H, K, C):
+    x = make_inputs(31, B, S, H, K, K, C, dtype, h0_std=0.02, name=f"bwd{B}x{S}")
+    do, dhT = make_cotangents(32, x)
+    check(x, do, dhT)
+
+
+@pytest.mark.parametrize("decay", ["slow", "none"])
+def test_backward_long_memory(decay):
+    # slow decay keeps every chunk's state and its gradient alive across the sequence
+    x = make_inputs(33, 1, 300, 2, 128, 128, 64, "f32", h0_std=0.5, decay=decay, name=f"bwd-{decay}")
+    do, dhT = make_cotangents(34, x)
+    check(x, do, dhT)
+
+
+def test_backward_without_h0_or_dhT():
+    x = make_inputs(35, 1, 150, 2, 128, 128, 64, "bf16", h0_std=0.0, name="bwd-zero-state")
+    do, _ = make_cotangents(36, x, dhT_std=0.0)
+    got, _ = check(x, do, None, h0=False)
+    assert np.isfinite(got[5]).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_packed(dtype):
+    x = make_packed_inputs(37, 4, 520, 2, 128, 128, 64, dtype, h0_std=0.02, median=120,
+                           pad_to_chunk=False, name="bwd-packed")
+    # an empty sequence in the middle: dl/dh0 of it must be dl/dhT
+    cu = [int(c) for c in x.cu_seqlens]
+    x.cu_seqlens = np.array(cu[:2] + [cu[1]] + cu[2:], dtype=np.int32)
+    x.h0 = np.concatenate([x.h0[:1], np.full_like(x.h0[:1], 0.3), x.h0[1:]])
+    x.meta = {}
+    do, dhT = make_cotangents(38, x)
+    got, ref = check(x, do, dhT)
+    np.testing.assert_array_equal(got[5][1], dhT[1])
+
+
+def test_backward_packed_small_shape_ragged():
+    x = make_packed_inputs(39, 3, 90, 3, 32, 32, 16, "f32", h0_std=0.1, median=30,
+                           pad_to_chunk=False, name="bwd-packed-small")
+    do, dhT = make_cotangents(40, x)
+    check(x, do, dhT)
+
+
+def test_backward_no_tokens_passes_dhT_through():
+    x = make_inputs(41, 2, 0, 2, 32, 32, 16, "f32", h0_std=0.1, name="bwd-empty")
+    dhT = np.random.default_rng(42).standard_normal((2, 2, 32, 32)).astype(np.float32)
+    do = np.zeros(x.v.shape, dtype=np.float32)
+    say("backward: S = 0")
+    got = gpu_grads(x, do, dhT)
+    np.testing.assert_array_equal(got[5], dhT)
+
+
+def test_autograd_wrapper():
+    x = make_inputs(43, 1, 130, 2, 128, 128, 64, "f32", h0_std=0.02, name="bwd-autograd")
+    do, dhT = make_cotangents(44, x)
+    say("backward: autograd wrapper")
+    q, k, v = (to_dev(a).requires_grad_() for a in (x.q, x.k, x.v))
+    g, beta, h0 = (to_dev(a).requires_grad_() for a in (x.g, x.beta, x.h0))
+    o, hT = gdn.chunk_gated_delta_rule(q, k, v, g, beta, h0, chunk_size=64)
+    loss = (o * to_dev(do)).sum() + (hT * to_dev(dhT)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = oracle_grads(x, do, dhT)
+    for n, t, r in zip(NAMES, (q, k, v, g, beta, h0), ref):
+        e = rel_err(t.grad.cpu().numpy(), r)
+        assert e <= TOL["f32"], (n, e)

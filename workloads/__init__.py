@@ -26,7 +26,7 @@ import numpy as np
 
 __all__ = ["GdnInputs", "DecodeInputs", "round_bf16", "bf16_bits", "make_inputs",
            "packed_lengths", "make_packed_inputs", "workload", "make_decode_inputs",
-           "WORKLOADS"]
+           "WORKLOADS", "make_cotangents"]
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -176,6 +176,25 @@ def make_packed_inputs(seed, n_seqs, total, H, K, V, C, dtype="bf16", h0_std=0.0
         h0 = rng.standard_normal((n_seqs, H, K, V), dtype=np.float32) * np.float32(h0_std)
     return GdnInputs(q, k, v, g, beta, h0, dtype, C, cu_seqlens=cu, real_tokens=int(lens.sum()),
                      name=name, meta={"lengths": lens.tolist()})
+
+
+def make_cotangents(seed, x, dhT_std=1.0):
+    """Seeded loss gradients for a backward pass over workload ``x``:
+    dl/do ~ N(0,1) in the layout of v (rounded to bf16 for bf16 workloads,
+    zero on padded positions of a packed stream) and dl/dhT ~ N(0, dhT_std^2)
+    [N,H,K,V] fp32 (None when dhT_std is 0)."""
+    rng = np.random.default_rng(seed)
+    do = rng.standard_normal(x.v.shape, dtype=np.float32)
+    if x.dtype == "bf16":
+        do = round_bf16(do)
+    if x.cu_seqlens is not None and "lengths" in x.meta:
+        for n, ln in enumerate(x.meta["lengths"]):
+            do[:, int(x.cu_seqlens[n]) + int(ln):int(x.cu_seqlens[n + 1])] = 0
+    N = x.B if x.cu_seqlens is None else len(x.cu_seqlens) - 1
+    dhT = None
+    if dhT_std > 0:
+        dhT = rng.standard_normal((N, x.H, x.K, x.V), dtype=np.float32) * np.float32(dhT_std)
+    return do, dhT
 
 
 @dataclass
