@@ -33,8 +33,6 @@
 namespace gdn {
 namespace {
 
-constexpr int kBT = 256;
-
 struct ChunkLoc {
     int64_t tc;   // first token of the chunk
     int L;        // real tokens in it (rows L .. C-1 are padding)
@@ -63,10 +61,11 @@ __device__ __forceinline__ ChunkLoc locate_chunk(const ChainTable &ct, int64_t c
     return l;
 }
 
-// Within-chunk cumulative log-decay of rows 0 .. C-1 (padding rows add 0).
+// Within-chunk cumulative log-decay G of rows 0 .. C-1 (padding rows add 0)
+// and the row factors sEg[r] = exp(G_r), sEk[r] = exp(G_{C-1} - G_r).
 template <int C>
-__device__ __forceinline__ void load_cumdecay(float *sG, const float *g, int64_t tc, int L, int H,
-                                              int h) {
+__device__ __forceinline__ void load_cumdecay(float *sG, float *sEg, float *sEk, const float *g,
+                                              int64_t tc, int L, int H, int h) {
     if (threadIdx.x < C) sG[threadIdx.x] = threadIdx.x < L ? g[(tc + threadIdx.x) * H + h] : 0.f;
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -75,6 +74,11 @@ __device__ __forceinline__ void load_cumdecay(float *sG, const float *g, int64_t
             acc += sG[r];
             sG[r] = acc;
         }
+    }
+    __syncthreads();
+    if (threadIdx.x < C) {
+        sEg[threadIdx.x] = expf(sG[threadIdx.x]);
+        sEk[threadIdx.x] = expf(sG[C - 1] - sG[threadIdx.x]);
     }
     __syncthreads();
 }
@@ -90,12 +94,12 @@ __device__ __forceinline__ void add_row(float *dst, int row, float x) {
 }
 
 // ---------------------------------------------------------------- 1. prep
-template <typename T, int K, int V, int C>
-__global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
+template <typename T, int K, int V, int C, int NT>
+__global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
     constexpr int KP = K + 1, CP = C + 1;
     __shared__ float sk[C * KP], sq[C * KP];
     __shared__ float sA[C * CP], sT[C * CP];
-    __shared__ float sG[C], sb[C], sbg[C];
+    __shared__ float sG[C], sEg[C], sEk[C], sb[C], sbg[C];
     const int tid = threadIdx.x, H = a.H;
     const int h = blockIdx.x % H;
     const int64_t chunk = blockIdx.x / H;
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
     const int64_t rowK = (int64_t)H * K, rowV = (int64_t)H * V;
     const int64_t ch = chunk * H + h;
 
-    for (int e = tid; e < C * K; e += kBT) {
+    for (int e = tid; e < C * K; e += NT) {
         const int r = e / K, i = e % K;
         const bool ok = r < cl.L;
         const int64_t x = (cl.tc + r) * rowK + h * K + i;
@@ -111,11 +115,11 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
         sq[r * KP + i] = ok ? Elem<T>::load(a.q, x) : 0.f;
     }
     if (tid < C) sb[tid] = tid < cl.L ? a.beta[(cl.tc + tid) * H + h] : 0.f;
-    load_cumdecay<C>(sG, a.g, cl.tc, cl.L, H, h);
-    if (tid < C) sbg[tid] = sb[tid] * expf(sG[tid]);
+    load_cumdecay<C>(sG, sEg, sEk, a.g, cl.tc, cl.L, H, h);
+    if (tid < C) sbg[tid] = sb[tid] * sEg[tid];
 
     float *Ak = a.Ak + ch * C * C, *attn = a.attn + ch * C * C;
-    for (int e = tid; e < C * C; e += kBT) {
+    for (int e = tid; e < C * C; e += NT) {
         const int r = e / C, s = e % C;
         float kk = 0.f, qk = 0.f, dec = 0.f;
         if (s <= r) {
@@ -143,14 +147,14 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
     }
     __syncthreads();
     float *To = a.T + ch * C * C, *w = a.w + ch * C * K, *u = a.u + ch * C * V;
-    for (int e = tid; e < C * C; e += kBT) To[e] = sT[(e / C) * CP + e % C];
-    for (int e = tid; e < C * K; e += kBT) {
+    for (int e = tid; e < C * C; e += NT) To[e] = sT[(e / C) * CP + e % C];
+    for (int e = tid; e < C * K; e += NT) {
         const int r = e / K, i = e % K;
         float acc = 0.f;
         for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * CP + s], sbg[s] * sk[s * KP + i], acc);
         w[e] = acc;
     }
-    for (int e = tid; e < C * V; e += kBT) {
+    for (int e = tid; e < C * V; e += NT) {
         const int r = e / V, j = e % V;
         float acc = 0.f;
         for (int s = 0; s <= r && s < cl.L; ++s)
@@ -160,12 +164,12 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- 2. states
-template <typename T, int K, int V, int C, int NCOL>
-__global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdArgs a) {
-    constexpr int KP = K + 1, NP = NCOL + 1, NG = V / NCOL, EPT = K * NCOL / kBT;
-    static_assert(V % NCOL == 0 && (K * NCOL) % kBT == 0, "column groups");
+template <typename T, int K, int V, int C, int NCOL, int NT>
+__global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
+    constexpr int KP = K + 1, NP = NCOL + 1, NG = V / NCOL, EPT = K * NCOL / NT;
+    static_assert(V % NCOL == 0 && (K * NCOL) % NT == 0, "column groups");
     __shared__ float sw[C * KP], sk[C * KP], sh[K * NP], sd[C * NP];
-    __shared__ float sG[C];
+    __shared__ float sG[C], sEg[C], sEk[C];
     const int tid = threadIdx.x, H = a.H;
     const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
     const int j0 = cg * NCOL;
@@ -176,7 +180,7 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdArgs a) {
     float hr[EPT];
 #pragma unroll
     for (int m = 0; m < EPT; ++m) {
-        const int e = tid + kBT * m, i = e % K, jj = e / K;
+        const int e = tid + NT * m, i = e % K, jj = e / K;
         hr[m] = a.h0 ? a.h0[((int64_t)n * H + h) * KV + (int64_t)i * V + j0 + jj] : 0.f;
     }
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
@@ -187,22 +191,22 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdArgs a) {
         float *hs = a.hs + ch * KV;
 #pragma unroll
         for (int m = 0; m < EPT; ++m) {
-            const int e = tid + kBT * m, i = e % K, jj = e / K;
+            const int e = tid + NT * m, i = e % K, jj = e / K;
             hs[(int64_t)(j0 + jj) * K + i] = hr[m];
             sh[i * NP + jj] = hr[m];
         }
-        load_cumdecay<C>(sG, a.g, tc, L, H, h);
-        const float Gl = sG[C - 1];
+        load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);
+        const float gamma = sEg[C - 1];
         const float *w = a.w + ch * C * K;
-        for (int e = tid; e < C * K; e += kBT) {
+        for (int e = tid; e < C * K; e += NT) {
             const int r = e / K, i = e % K;
             sw[r * KP + i] = w[e];
-            sk[r * KP + i] = r < L ? expf(Gl - sG[r]) * Elem<T>::load(a.k, (tc + r) * rowK + h * K + i) : 0.f;
+            sk[r * KP + i] = r < L ? sEk[r] * Elem<T>::load(a.k, (tc + r) * rowK + h * K + i) : 0.f;
         }
         __syncthreads();
         const float *u = a.u + ch * C * V;
         float *d = a.d + ch * C * V;
-        for (int o = tid; o < C * NCOL; o += kBT) {
+        for (int o = tid; o < C * NCOL; o += NT) {
             const int r = o / NCOL, jj = o % NCOL;
             float acc = u[r * V + j0 + jj];
             for (int i = 0; i < K; ++i) acc = fmaf(-sw[r * KP + i], sh[i * NP + jj], acc);
@@ -210,10 +214,9 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdArgs a) {
             d[r * V + j0 + jj] = acc;
         }
         __syncthreads();
-        const float gamma = expf(Gl);
 #pragma unroll
         for (int m = 0; m < EPT; ++m) {
-            const int e = tid + kBT * m, i = e % K, jj = e / K;
+            const int e = tid + NT * m, i = e % K, jj = e / K;
             float acc = gamma * hr[m];
             for (int r = 0; r < C; ++r) acc = fmaf(sk[r * KP + i], sd[r * NP + jj], acc);
             hr[m] = acc;
@@ -223,13 +226,13 @@ __global__ __launch_bounds__(kBT) void bwd_states_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- 3. dstates
-template <typename T, int K, int V, int C, int NCOL>
-__global__ __launch_bounds__(kBT) void bwd_dstates_kernel(BwdArgs a) {
-    constexpr int KP = K + 1, CP = C + 1, NP = NCOL + 1, NG = V / NCOL, EPT = K * NCOL / kBT;
-    static_assert(V % NCOL == 0 && (K * NCOL) % kBT == 0, "column groups");
+template <typename T, int K, int V, int C, int NCOL, int NT>
+__global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
+    constexpr int KP = K + 1, CP = C + 1, NP = NCOL + 1, NG = V / NCOL, EPT = K * NCOL / NT;
+    static_assert(V % NCOL == 0 && (K * NCOL) % NT == 0, "column groups");
     __shared__ float sw[C * KP], sk[C * KP], sq[C * KP], sa[C * CP];
     __shared__ float sdh[K * NP], sdo[C * NP], sdd[C * NP];
-    __shared__ float sG[C];
+    __shared__ float sG[C], sEg[C], sEk[C];
     const int tid = threadIdx.x, H = a.H;
     const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
     const int j0 = cg * NCOL;
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kBT) void bwd_dstates_kernel(BwdArgs a) {
     float dh[EPT];
 #pragma unroll
     for (int m = 0; m < EPT; ++m) {
-        const int e = tid + kBT * m, i = e % K, jj = e / K;
+        const int e = tid + NT * m, i = e % K, jj = e / K;
         dh[m] = a.dhT ? a.dhT[((int64_t)n * H + h) * KV + (int64_t)i * V + j0 + jj] : 0.f;
     }
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
@@ -251,29 +254,29 @@ __global__ __launch_bounds__(kBT) void bwd_dstates_kernel(BwdArgs a) {
         float *dhs = a.dhs + ch * KV;
 #pragma unroll
         for (int m = 0; m < EPT; ++m) {
-            const int e = tid + kBT * m, i = e % K, jj = e / K;
+            const int e = tid + NT * m, i = e % K, jj = e / K;
             dhs[(int64_t)(j0 + jj) * K + i] = dh[m];
             sdh[i * NP + jj] = dh[m];
         }
-        load_cumdecay<C>(sG, a.g, tc, L, H, h);
-        const float Gl = sG[C - 1];
+        load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);
+        const float gamma = sEg[C - 1];
         const float *w = a.w + ch * C * K, *attn = a.attn + ch * C * C;
-        for (int e = tid; e < C * K; e += kBT) {
+        for (int e = tid; e < C * K; e += NT) {
             const int r = e / K, i = e % K;
             const bool ok = r < L;
             const int64_t x = (tc + r) * rowK + h * K + i;
             sw[r * KP + i] = w[e];
-            sk[r * KP + i] = ok ? expf(Gl - sG[r]) * Elem<T>::load(a.k, x) : 0.f;
-            sq[r * KP + i] = ok ? expf(sG[r]) * Elem<T>::load(a.q, x) : 0.f;
+            sk[r * KP + i] = ok ? sEk[r] * Elem<T>::load(a.k, x) : 0.f;
+            sq[r * KP + i] = ok ? sEg[r] * Elem<T>::load(a.q, x) : 0.f;
         }
-        for (int e = tid; e < C * C; e += kBT) sa[(e / C) * CP + e % C] = attn[e];
-        for (int e = tid; e < C * NCOL; e += kBT) {
+        for (int e = tid; e < C * C; e += NT) sa[(e / C) * CP + e % C] = attn[e];
+        for (int e = tid; e < C * NCOL; e += NT) {
             const int r = e / NCOL, jj = e % NCOL;
             sdo[r * NP + jj] = r < L ? Elem<T>::load(a.dout, (tc + r) * rowV + h * V + j0 + jj) : 0.f;
         }
         __syncthreads();
         float *dd = a.dd + ch * C * V;
-        for (int o = tid; o < C * NCOL; o += kBT) {
+        for (int o = tid; o < C * NCOL; o += NT) {
             const int r = o / NCOL, jj = o % NCOL;
             float acc = 0.f;
             for (int t = r; t < C; ++t) acc = fmaf(sa[t * CP + r], sdo[t * NP + jj], acc);
@@ -282,10 +285,9 @@ __global__ __launch_bounds__(kBT) void bwd_dstates_kernel(BwdArgs a) {
             dd[r * V + j0 + jj] = acc;
         }
         __syncthreads();
-        const float gamma = expf(Gl);
 #pragma unroll
         for (int m = 0; m < EPT; ++m) {
-            const int e = tid + kBT * m, i = e % K, jj = e / K;
+            const int e = tid + NT * m, i = e % K, jj = e / K;
             float acc = gamma * dh[m];
             for (int r = 0; r < C; ++r) {
                 acc = fmaf(sq[r * KP + i], sdo[r * NP + jj], acc);
@@ -298,18 +300,18 @@ __global__ __launch_bounds__(kBT) void bwd_dstates_kernel(BwdArgs a) {
     if (a.dh0) {
 #pragma unroll
         for (int m = 0; m < EPT; ++m) {
-            const int e = tid + kBT * m, i = e % K, jj = e / K;
+            const int e = tid + NT * m, i = e % K, jj = e / K;
             a.dh0[((int64_t)n * H + h) * KV + (int64_t)i * V + j0 + jj] = dh[m];
         }
     }
 }
 
 // ---------------------------------------------------------------- 4. grads
-template <typename T, int K, int V, int C>
-__global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs a) {
+template <typename T, int K, int V, int C, int NT>
+__global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     constexpr int VP = V + 1, CP = C + 1;
-    static_assert((C * C) % kBT == 0 && (C * K) % kBT == 0 && (C * V) % kBT == 0 &&
-                  (K * C) % kBT == 0, "uniform trip counts (add_row needs whole waves)");
+    static_assert((C * C) % NT == 0 && (C * K) % NT == 0 && (C * V) % NT == 0 &&
+                  (K * C) % NT == 0, "uniform trip counts (add_row needs whole waves)");
     static_assert(C * CP <= C * VP, "Z fits where delta was");
     __shared__ float bDZ[C * VP];               // delta (read by dattn), then Z = dT T^T
     __shared__ float bdD[C * VP];               // ddelta
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs a) {
     __shared__ float bY[C * CP];                // dT^T, then dA
     __shared__ float bW[K * CP];                // dw^T
     float *const bD = bDZ, *const bZ = bDZ;
-    __shared__ float sG[C], sb[C], sdG[C], sdb[C];
+    __shared__ float sG[C], sEg[C], sEk[C], sb[C], sdG[C], sdb[C];
     const int tid = threadIdx.x, H = a.H;
     const int h = blockIdx.x % H;
     const int64_t chunk = blockIdx.x / H;
@@ -338,50 +340,53 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs a) {
 
     {
         const float *d = a.d + ch * C * V, *dd = a.dd + ch * C * V, *Tm = a.T + ch * C * C;
-        for (int e = tid; e < C * V; e += kBT) {
+        for (int e = tid; e < C * V; e += NT) {
             bD[(e / V) * VP + e % V] = d[e];
             bdD[(e / V) * VP + e % V] = dd[e];
         }
-        for (int e = tid; e < C * C; e += kBT) bT[(e / C) * CP + e % C] = Tm[e];
+        for (int e = tid; e < C * C; e += NT) bT[(e / C) * CP + e % C] = Tm[e];
         if (tid < C) {
             sb[tid] = tid < L ? a.beta[(tc + tid) * H + h] : 0.f;
             sdG[tid] = 0.f;
             sdb[tid] = 0.f;
         }
     }
-    load_cumdecay<C>(sG, a.g, tc, L, H, h);   // (synchronises)
-    const float Gl = sG[C - 1];
+    load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);   // (synchronises)
 
     // dattn[r][s] = causal(do delta^T);  dw^T[i][r] = -(h ddelta^T)[i][r]
-    for (int o = tid; o < C * C; o += kBT) {
+    for (int o = tid; o < C * C; o += NT) {
         const int r = o / C, s = o % C;
         float acc = 0.f;
         if (s <= r && r < L)
+#pragma unroll 8
             for (int j = 0; j < V; ++j) acc = fmaf(dox(r, j), bD[s * VP + j], acc);
         bX[r * CP + s] = acc;
     }
-    for (int o = tid; o < K * C; o += kBT) {
+    for (int o = tid; o < K * C; o += NT) {
         const int i = o / C, r = o % C;
         float acc = 0.f;
+#pragma unroll 8
         for (int j = 0; j < V; ++j) acc = fmaf(-hsT[(int64_t)j * K + i], bdD[r * VP + j], acc);
         bW[i * CP + r] = acc;
     }
     __syncthreads();
     // dT^T[s][r] = (Vb ddelta^T)[s][r] + (Kb dw^T)[s][r]
-    for (int o = tid; o < C * C; o += kBT) {
+    for (int o = tid; o < C * C; o += NT) {
         const int s = o / C, r = o % C;
         float acc = 0.f;
         if (s < L) {
             float av = 0.f, ak = 0.f;
+#pragma unroll 8
             for (int j = 0; j < V; ++j) av = fmaf(vx(s, j), bdD[r * VP + j], av);
+#pragma unroll 8
             for (int i = 0; i < K; ++i) ak = fmaf(kx(s, i), bW[i * CP + r], ak);
-            acc = sb[s] * (av + expf(sG[s]) * ak);
+            acc = sb[s] * (av + sEg[s] * ak);
         }
         bY[s * CP + r] = acc;
     }
     __syncthreads();
     // Z = dT T^T
-    for (int o = tid; o < C * C; o += kBT) {
+    for (int o = tid; o < C * C; o += NT) {
         const int r = o / C, s = o % C;
         float acc = 0.f;
         for (int p = 0; p < C; ++p) acc = fmaf(bY[p * CP + r], bT[s * CP + p], acc);
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs a) {
     }
     __syncthreads();
     // dA = -strict_lower(T^T Z)   (T[p][r] = 0 for p < r)
-    for (int o = tid; o < C * C; o += kBT) {
+    for (int o = tid; o < C * C; o += NT) {
         const int r = o / C, s = o % C;
         float acc = 0.f;
         if (s < r)
@@ -399,7 +404,7 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs a) {
     __syncthreads();
 
     // dv = diag(beta) T^T ddelta;  dbeta += (T^T ddelta) . v
-    for (int o = tid; o < C * V; o += kBT) {
+    for (int o = tid; o < C * V; o += NT) {
         const int r = o / V, j = o % V;
         float dvb = 0.f;
         for (int p = r; p < C; ++p) dvb = fmaf(bT[p * CP + r], bdD[p * VP + j], dvb);
@@ -410,32 +415,54 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs a) {
         }
         add_row<V>(sdb, r, part);
     }
+    // attn and A through the decay: dG_r += e, dG_s -= e;  dbeta from A
+    for (int o = tid; o < C * C; o += NT) {
+        const int r = o / C, s = o % C;
+        float ea = 0.f, eA = 0.f;
+        if (s <= r) ea = bX[r * CP + s] * attn[o];
+        if (s < r) eA = bY[r * CP + s] * Ak[o];
+        const float e = ea + sb[r] * eA;
+        if (e != 0.f) atomicAdd(&sdG[s], -e);
+        add_row<C>(sdG, r, e);
+        add_row<C>(sdb, r, eA);
+    }
+    __syncthreads();
+    // fold the decay in once: bX <- dattn (.) D,  bY <- dA (.) beta_r D  (= dKK)
+    for (int o = tid; o < C * C; o += NT) {
+        const int r = o / C, s = o % C;
+        if (s <= r) {
+            const float dec = expf(sG[r] - sG[s]);
+            bX[r * CP + s] *= dec;
+            bY[r * CP + s] *= sb[r] * dec;
+        }
+    }
+    __syncthreads();
     // dq and dk, one element each
-    for (int o = tid; o < C * K; o += kBT) {
+    for (int o = tid; o < C * K; o += NT) {
         const int r = o / K, i = o % K;
         float pg = 0.f, pd = 0.f, pk = 0.f;
         if (r < L) {
-            const float eG = expf(sG[r]), er = expf(Gl - sG[r]), br = sb[r];
+            const float eG = sEg[r], er = sEk[r], br = sb[r];
             // q_g: dq_g = do h^T;  attn (row r): sum_s dattn[r][s] D[r][s] k_s
             float dqg = 0.f, qa = 0.f;
+#pragma unroll 8
             for (int j = 0; j < V; ++j) dqg = fmaf(dox(r, j), hsT[(int64_t)j * K + i], dqg);
-            for (int s = 0; s <= r; ++s) qa = fmaf(bX[r * CP + s] * expf(sG[r] - sG[s]), kx(s, i), qa);
+            for (int s = 0; s <= r; ++s) qa = fmaf(bX[r * CP + s], kx(s, i), qa);
             Elem<T>::store(a.dq, (tc + r) * rowK + h * K + i, eG * dqg + qa);
             // k as a key of attn (column r): sum_t dattn[t][r] D[t][r] q_t
             float ka = 0.f;
-            for (int t = r; t < L; ++t) ka = fmaf(bX[t * CP + r] * expf(sG[t] - sG[r]), qx(t, i), ka);
+            for (int t = r; t < L; ++t) ka = fmaf(bX[t * CP + r], qx(t, i), ka);
             // k_tilde: dk_tilde = delta dh^T (delta from the workspace: its LDS copy is gone)
             float dkt = 0.f;
+#pragma unroll 8
             for (int j = 0; j < V; ++j) dkt = fmaf(dws[r * V + j], dhsT[(int64_t)j * K + i], dkt);
             // Kb: dKb = T^T dw
             float dkb = 0.f;
             for (int p = r; p < C; ++p) dkb = fmaf(bT[p * CP + r], bW[i * CP + p], dkb);
-            // A (both operands): dKK[r][p] = dA[r][p] beta_r D[r][p] (p < r), its transpose
+            // A (both operands): dKK k, dKK^T k
             float kaa = 0.f;
-            for (int p = 0; p < r; ++p)
-                kaa = fmaf(bY[r * CP + p] * br * expf(sG[r] - sG[p]), kx(p, i), kaa);
-            for (int p = r + 1; p < L; ++p)
-                kaa = fmaf(bY[p * CP + r] * sb[p] * expf(sG[p] - sG[r]), kx(p, i), kaa);
+            for (int p = 0; p < r; ++p) kaa = fmaf(bY[r * CP + p], kx(p, i), kaa);
+            for (int p = r + 1; p < L; ++p) kaa = fmaf(bY[p * CP + r], kx(p, i), kaa);
             const float kri = kx(r, i);
             Elem<T>::store(a.dk, (tc + r) * rowK + h * K + i, ka + er * dkt + br * eG * dkb + kaa);
             pg = eG * dqg * qx(r, i) - er * dkt * kri + br * eG * dkb * kri;
@@ -446,22 +473,12 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs a) {
         add_row<K>(sdG, C - 1, pd);
         add_row<K>(sdb, r, pk);
     }
-    // attn and A through the decay: dG_r += e, dG_s -= e;  dbeta from A
-    for (int o = tid; o < C * C; o += kBT) {
-        const int r = o / C, s = o % C;
-        float ea = 0.f, eA = 0.f;
-        if (s <= r) ea = bX[r * CP + s] * attn[o];
-        if (s < r) eA = bY[r * CP + s] * Ak[o];
-        const float e = ea + sb[r] * eA;
-        if (e != 0.f) atomicAdd(&sdG[s], -e);
-        add_row<C>(sdG, r, e);
-        add_row<C>(sdb, r, eA);
-    }
     // gamma: dG_last += gamma <h, dh>
     {
         float x = 0.f;
-        for (int e = tid; e < K * V; e += kBT) x = fmaf(hsT[e], dhsT[e], x);
-        add_row<64>(sdG, C - 1, expf(Gl) * x);
+#pragma unroll 4
+        for (int e = tid; e < K * V; e += NT) x = fmaf(hsT[e], dhsT[e], x);
+        add_row<64>(sdG, C - 1, sEg[C - 1] * x);
     }
     __syncthreads();
     if (tid == 0) {
@@ -476,25 +493,25 @@ __global__ __launch_bounds__(kBT) void bwd_grads_kernel(BwdArgs a) {
     }
 }
 
-template <typename T, int K, int V, int C, int NCOL>
+template <typename T, int K, int V, int C, int NCOL, int NT>
 hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
     const unsigned chunk_grid = (unsigned)(a.n_chunks * a.H);
     const unsigned chain_grid = (unsigned)((int64_t)n_chains * a.H * (V / NCOL));
     if (chunk_grid > 0) {
-        hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C>), dim3(chunk_grid), dim3(kBT), 0, s, a);
+        hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C, NT>), dim3(chunk_grid), dim3(NT), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (chain_grid > 0) {
-        hipLaunchKernelGGL((bwd_states_kernel<T, K, V, C, NCOL>), dim3(chain_grid), dim3(kBT), 0, s, a);
+        hipLaunchKernelGGL((bwd_states_kernel<T, K, V, C, NCOL, NT>), dim3(chain_grid), dim3(NT), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_dstates_kernel<T, K, V, C, NCOL>), dim3(chain_grid), dim3(kBT), 0, s, a);
+        hipLaunchKernelGGL((bwd_dstates_kernel<T, K, V, C, NCOL, NT>), dim3(chain_grid), dim3(NT), 0, s, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (chunk_grid > 0) {
-        hipLaunchKernelGGL((bwd_grads_kernel<T, K, V, C>), dim3(chunk_grid), dim3(kBT), 0, s, a);
+        hipLaunchKernelGGL((bwd_grads_kernel<T, K, V, C, NT>), dim3(chunk_grid), dim3(NT), 0, s, a);
         return hipGetLastError();
     }
     return hipSuccess;
@@ -504,12 +521,20 @@ hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
 
 hipError_t launch_backward(int K, int V, int C, int dtype, const BwdArgs &a, int n_chains,
                            hipStream_t s) {
-    if (K == 128 && V == 128 && C == 64)
-        return dtype == GDN_F32 ? launch_all<float, 128, 128, 64, 16>(a, n_chains, s)
-                                : launch_all<bf16_t, 128, 128, 64, 16>(a, n_chains, s);
+    // The two state scans run one workgroup per (chain, head, column group)
+    // for the whole sequence: narrower groups when that still fits one
+    // workgroup per compute unit, so that small problems fill the chip.
+    if (K == 128 && V == 128 && C == 64) {
+        const bool narrow = (int64_t)n_chains * a.H * (V / 8) <= 256;
+        if (dtype == GDN_F32)
+            return narrow ? launch_all<float, 128, 128, 64, 8, 512>(a, n_chains, s)
+                          : launch_all<float, 128, 128, 64, 16, 512>(a, n_chains, s);
+        return narrow ? launch_all<bf16_t, 128, 128, 64, 8, 512>(a, n_chains, s)
+                      : launch_all<bf16_t, 128, 128, 64, 16, 512>(a, n_chains, s);
+    }
     if (K == 32 && V == 32 && C == 16)
-        return dtype == GDN_F32 ? launch_all<float, 32, 32, 16, 8>(a, n_chains, s)
-                                : launch_all<bf16_t, 32, 32, 16, 8>(a, n_chains, s);
+        return dtype == GDN_F32 ? launch_all<float, 32, 32, 16, 8, 256>(a, n_chains, s)
+                                : launch_all<bf16_t, 32, 32, 16, 8, 256>(a, n_chains, s);
     return hipErrorInvalidValue;
 }
 
