@@ -44,6 +44,15 @@ def carry_flops_per_token_head(C, K, V):
     return 2 * C * K + 2 * C * (K + V) + 4 * K * (K + V)
 
 
+def bwd_flops_per_token_head(C, K, V):
+    """Dense work of the backward kernels (masked triangles counted dense, as in
+    the forward): the Grams, T applied to [Kb | Vb], both state scans (delta and
+    the state update; ddelta and the state-gradient update), and per chunk
+    dattn, dw, dT, T^T dT T^T, dv, dq and the four parts of dk.  Per chunk-head
+    18 C^2 K + 10 C^2 V + 16 C K V + 4 C^3 multiply-adds x 2, over C tokens."""
+    return 2 * (9 * C * K + 5 * C * V + 8 * K * V + 2 * C * C)
+
+
 def bytes_per_token_head(K, V, s_in, s_out):
     """q, k, v in, o out, g and beta fp32."""
     return (2 * K + V) * s_in + V * s_out + 8
@@ -437,6 +446,34 @@ def main():
                          "frac": step_bytes / t_step / 1e9 / PEAK_HBM_GBS},
         }
         del dq, dk, dv, dg, db, state
+        torch.cuda.empty_cache()
+
+        # the backward pass (gradients of a loss through the forward): the 4k sequence
+        # and the 64k workload.  Its four kernels run fp32 on the vector ALU, so the
+        # roofline is the fp32 vector peak against their dense work.
+        log("bench: backward")
+        for name, wl in (("backward_seq4k_h16", 1), ("backward_64k_h32", 2)):
+            y = x if wl == 2 else workload(wl)
+            t = lambda a, dt=None: (torch.from_numpy(a).to(dt) if dt else torch.from_numpy(a)).to(dev)
+            bq, bk, bv, bg, bb, bh = t(y.q, bf), t(y.k, bf), t(y.v, bf), t(y.g), t(y.beta), t(y.h0)
+            gen = torch.Generator(device=dev).manual_seed(11)
+            bdo = torch.randn(bv.shape, device=dev, generator=gen).to(bf)
+            bdh = torch.randn(bh.shape, device=dev, generator=gen)
+            Sb, Hb = bq.shape[1], bq.shape[2]
+
+            def bwd(timer):
+                tm = timer.around if timer else (lambda _n, f: f())
+                return tm("backward", lambda: gdn.backward(bq, bk, bv, bg, bb, bdo, h0=bh, dhT=bdh))
+            ms_b, k_b = time_with_breakdown(torch, bwd, max(3, steps2 // 2), 1)
+            fl = Sb * Hb * bwd_flops_per_token_head(C, K, V)
+            t_b = k_b["backward"] * 1e-3
+            extra[name] = {
+                "tokens_per_s": Sb / (ms_b * 1e-3), "ms": ms_b,
+                "roofline": {"bound": "alu", "achieved": fl / t_b / 1e12, "peak": PEAK_F32_VALU_TFLOPS,
+                             "unit": "TFLOP/s", "frac": fl / t_b / 1e12 / PEAK_F32_VALU_TFLOPS},
+            }
+            del bq, bk, bv, bg, bb, bh, bdo, bdh
+            torch.cuda.empty_cache()
     result["extra"] = extra
 
     # ---------------------------------------------------------------- CPU oracle baseline

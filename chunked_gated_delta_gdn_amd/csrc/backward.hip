@@ -62,24 +62,31 @@ __device__ __forceinline__ ChunkLoc locate_chunk(const ChainTable &ct, int64_t c
 }
 
 // Within-chunk cumulative log-decay G of rows 0 .. C-1 (padding rows add 0)
-// and the row factors sEg[r] = exp(G_r), sEk[r] = exp(G_{C-1} - G_r).
+// and the row factors sEg[r] = exp(G_r), sEk[r] = exp(G_{C-1} - G_r), from
+// lane r's own g (0 past the chunk).  Called by the 64 lanes of wave 0.
+template <int C>
+__device__ __forceinline__ void chunk_decay(float x, float *sG, float *sEg, float *sEk) {
+    static_assert(C <= 64, "one wave scans the chunk");
+    const int lane = threadIdx.x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    const float Gl = __shfl(x, C - 1);
+    if (lane < C) {
+        sG[lane] = x;
+        sEg[lane] = expf(x);
+        sEk[lane] = expf(Gl - x);
+    }
+}
+
 template <int C>
 __device__ __forceinline__ void load_cumdecay(float *sG, float *sEg, float *sEk, const float *g,
                                               int64_t tc, int L, int H, int h) {
-    if (threadIdx.x < C) sG[threadIdx.x] = threadIdx.x < L ? g[(tc + threadIdx.x) * H + h] : 0.f;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float acc = 0.f;
-        for (int r = 0; r < C; ++r) {
-            acc += sG[r];
-            sG[r] = acc;
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x < C) {
-        sEg[threadIdx.x] = expf(sG[threadIdx.x]);
-        sEk[threadIdx.x] = expf(sG[C - 1] - sG[threadIdx.x]);
-    }
+    if (threadIdx.x < 64)
+        chunk_decay<C>(threadIdx.x < C && threadIdx.x < L ? g[(tc + threadIdx.x) * H + h] : 0.f,
+                       sG, sEg, sEk);
     __syncthreads();
 }
 
@@ -99,6 +106,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
     constexpr int KP = K + 1, CP = C + 1;
     __shared__ float sk[C * KP], sq[C * KP];
     __shared__ float sA[C * CP], sT[C * CP];
+    __shared__ float sv[C * V];   // Vb = diag(beta) V
     __shared__ float sG[C], sEg[C], sEk[C], sb[C], sbg[C];
     const int tid = threadIdx.x, H = a.H;
     const int h = blockIdx.x % H;
@@ -117,6 +125,10 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
     if (tid < C) sb[tid] = tid < cl.L ? a.beta[(cl.tc + tid) * H + h] : 0.f;
     load_cumdecay<C>(sG, sEg, sEk, a.g, cl.tc, cl.L, H, h);
     if (tid < C) sbg[tid] = sb[tid] * sEg[tid];
+    for (int e = tid; e < C * V; e += NT) {
+        const int r = e / V, j = e % V;
+        sv[e] = r < cl.L ? sb[r] * Elem<T>::load(a.v, (cl.tc + r) * rowV + h * V + j) : 0.f;
+    }
 
     float *Ak = a.Ak + ch * C * C, *attn = a.attn + ch * C * C;
     for (int e = tid; e < C * C; e += NT) {
@@ -135,17 +147,22 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
         attn[e] = dec * qk;
     }
     __syncthreads();
-    // T = (I + A)^{-1} by forward substitution, one column per thread
-    if (tid < C) {
-        const int c = tid;
+    // T = (I + A)^{-1} by forward substitution, row by row: column c belongs to
+    // the PARTS consecutive lanes c * PARTS .., each summing every PARTS-th term
+    {
+        constexpr int PARTS = NT / C;
+        static_assert(PARTS * C == NT && (PARTS & (PARTS - 1)) == 0 && PARTS <= 64, "solve lanes");
+        const int c = tid / PARTS, part = tid % PARTS;
         for (int r = 0; r < C; ++r) {
-            float x = r == c ? 1.f : 0.f;
+            float x = 0.f;
             if (r > c)
-                for (int s = c; s < r; ++s) x = fmaf(-sA[r * CP + s], sT[s * CP + c], x);
-            sT[r * CP + c] = x;
+                for (int s = c + part; s < r; s += PARTS) x = fmaf(-sA[r * CP + s], sT[s * CP + c], x);
+#pragma unroll
+            for (int off = PARTS / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+            if (part == 0) sT[r * CP + c] = r == c ? 1.f : (r > c ? x : 0.f);
+            __syncthreads();
         }
     }
-    __syncthreads();
     float *To = a.T + ch * C * C, *w = a.w + ch * C * K, *u = a.u + ch * C * V;
     for (int e = tid; e < C * C; e += NT) To[e] = sT[(e / C) * CP + e % C];
     for (int e = tid; e < C * K; e += NT) {
@@ -157,17 +174,23 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
     for (int e = tid; e < C * V; e += NT) {
         const int r = e / V, j = e % V;
         float acc = 0.f;
-        for (int s = 0; s <= r && s < cl.L; ++s)
-            acc = fmaf(sT[r * CP + s], sb[s] * Elem<T>::load(a.v, (cl.tc + s) * rowV + h * V + j), acc);
+        for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * CP + s], sv[s * V + j], acc);
         u[e] = acc;
     }
 }
 
 // ---------------------------------------------------------------- 2. states
+// A chunk's operands in registers, loaded one chunk ahead of their use.
+template <int C, int NT>
+__device__ __forceinline__ void chunk_rows(int64_t t0, int64_t t1, int64_t c, int &L, int64_t &tc) {
+    tc = t0 + c * C;
+    L = (int)((t1 - tc) < C ? (t1 - tc) : C);
+}
+
 template <typename T, int K, int V, int C, int NCOL, int NT>
 __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
-    constexpr int KP = K + 1, NP = NCOL + 1, NG = V / NCOL, EPT = K * NCOL / NT;
-    static_assert(V % NCOL == 0 && (K * NCOL) % NT == 0, "column groups");
+    constexpr int KP = K + 1, NP = NCOL + 1, NG = V / NCOL, EPT = K * NCOL / NT, LPT = C * K / NT;
+    static_assert(V % NCOL == 0 && (K * NCOL) % NT == 0 && (C * K) % NT == 0, "column groups");
     __shared__ float sw[C * KP], sk[C * KP], sh[K * NP], sd[C * NP];
     __shared__ float sG[C], sEg[C], sEk[C];
     const int tid = threadIdx.x, H = a.H;
@@ -184,9 +207,23 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
         hr[m] = a.h0 ? a.h0[((int64_t)n * H + h) * KV + (int64_t)i * V + j0 + jj] : 0.f;
     }
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
+    // w, raw k and g of the next chunk, fetched while the current one computes
+    float pw[LPT], pk[LPT], pg = 0.f;
+    auto fetch = [&](int64_t c) {
+        int L;
+        int64_t tc;
+        chunk_rows<C, NT>(sp.t0, sp.t1, c, L, tc);
+        const float *w = a.w + ((sp.chunk0 + c) * H + h) * C * K;
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) {
+            const int e = tid + NT * m, r = e / K, i = e % K;
+            pw[m] = w[e];
+            pk[m] = r < L ? Elem<T>::load(a.k, (tc + r) * rowK + h * K + i) : 0.f;
+        }
+        pg = tid < C && tid < L ? a.g[(tc + tid) * H + h] : 0.f;
+    };
+    if (nch > 0) fetch(0);
     for (int64_t c = 0; c < nch; ++c) {
-        const int64_t tc = sp.t0 + c * C;
-        const int L = (int)((sp.t1 - tc) < C ? (sp.t1 - tc) : C);
         const int64_t ch = (sp.chunk0 + c) * H + h;
         float *hs = a.hs + ch * KV;
 #pragma unroll
@@ -195,22 +232,25 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
             hs[(int64_t)(j0 + jj) * K + i] = hr[m];
             sh[i * NP + jj] = hr[m];
         }
-        load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);
-        const float gamma = sEg[C - 1];
-        const float *w = a.w + ch * C * K;
-        for (int e = tid; e < C * K; e += NT) {
-            const int r = e / K, i = e % K;
-            sw[r * KP + i] = w[e];
-            sk[r * KP + i] = r < L ? sEk[r] * Elem<T>::load(a.k, (tc + r) * rowK + h * K + i) : 0.f;
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) {
+            const int e = tid + NT * m, r = e / K, i = e % K;
+            sw[r * KP + i] = pw[m];
+            sk[r * KP + i] = pk[m];
         }
+        if (tid < 64) chunk_decay<C>(pg, sG, sEg, sEk);
         __syncthreads();
+        if (c + 1 < nch) fetch(c + 1);
+        const float gamma = sEg[C - 1];
         const float *u = a.u + ch * C * V;
         float *d = a.d + ch * C * V;
+        // delta = u - w h (own columns); k_tilde^T delta = k^T (exp(G_C - G) delta)
         for (int o = tid; o < C * NCOL; o += NT) {
             const int r = o / NCOL, jj = o % NCOL;
             float acc = u[r * V + j0 + jj];
+#pragma unroll 8
             for (int i = 0; i < K; ++i) acc = fmaf(-sw[r * KP + i], sh[i * NP + jj], acc);
-            sd[r * NP + jj] = acc;
+            sd[r * NP + jj] = sEk[r] * acc;
             d[r * V + j0 + jj] = acc;
         }
         __syncthreads();
@@ -218,6 +258,7 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
         for (int m = 0; m < EPT; ++m) {
             const int e = tid + NT * m, i = e % K, jj = e / K;
             float acc = gamma * hr[m];
+#pragma unroll 8
             for (int r = 0; r < C; ++r) acc = fmaf(sk[r * KP + i], sd[r * NP + jj], acc);
             hr[m] = acc;
         }
@@ -229,9 +270,11 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
 template <typename T, int K, int V, int C, int NCOL, int NT>
 __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
     constexpr int KP = K + 1, CP = C + 1, NP = NCOL + 1, NG = V / NCOL, EPT = K * NCOL / NT;
-    static_assert(V % NCOL == 0 && (K * NCOL) % NT == 0, "column groups");
+    constexpr int LPT = C * K / NT, APT = C * C / NT, DPT = (C * NCOL + NT - 1) / NT;
+    static_assert(V % NCOL == 0 && (K * NCOL) % NT == 0 && (C * K) % NT == 0 && (C * C) % NT == 0,
+                  "column groups");
     __shared__ float sw[C * KP], sk[C * KP], sq[C * KP], sa[C * CP];
-    __shared__ float sdh[K * NP], sdo[C * NP], sdd[C * NP];
+    __shared__ float sdh[K * NP], sdo[C * NP], sdoG[C * NP], sdd[C * NP];
     __shared__ float sG[C], sEg[C], sEk[C];
     const int tid = threadIdx.x, H = a.H;
     const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
@@ -247,9 +290,34 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
         dh[m] = a.dhT ? a.dhT[((int64_t)n * H + h) * KV + (int64_t)i * V + j0 + jj] : 0.f;
     }
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
+    // the next chunk's (in reverse order) w, raw k and q, attn, do columns and g
+    float pw[LPT], pk[LPT], pq[LPT], pa[APT], pd[DPT], pg = 0.f;
+    auto fetch = [&](int64_t c) {
+        int L;
+        int64_t tc;
+        chunk_rows<C, NT>(sp.t0, sp.t1, c, L, tc);
+        const int64_t ch = (sp.chunk0 + c) * H + h;
+        const float *w = a.w + ch * C * K, *attn = a.attn + ch * C * C;
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) {
+            const int e = tid + NT * m, r = e / K, i = e % K;
+            const bool ok = r < L;
+            const int64_t x = (tc + r) * rowK + h * K + i;
+            pw[m] = w[e];
+            pk[m] = ok ? Elem<T>::load(a.k, x) : 0.f;
+            pq[m] = ok ? Elem<T>::load(a.q, x) : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < APT; ++m) pa[m] = attn[tid + NT * m];
+#pragma unroll
+        for (int m = 0; m < DPT; ++m) {
+            const int e = tid + NT * m, r = e / NCOL, jj = e % NCOL;
+            pd[m] = e < C * NCOL && r < L ? Elem<T>::load(a.dout, (tc + r) * rowV + h * V + j0 + jj) : 0.f;
+        }
+        pg = tid < C && tid < L ? a.g[(tc + tid) * H + h] : 0.f;
+    };
+    if (nch > 0) fetch(nch - 1);
     for (int64_t c = nch - 1; c >= 0; --c) {
-        const int64_t tc = sp.t0 + c * C;
-        const int L = (int)((sp.t1 - tc) < C ? (sp.t1 - tc) : C);
         const int64_t ch = (sp.chunk0 + c) * H + h;
         float *dhs = a.dhs + ch * KV;
 #pragma unroll
@@ -258,30 +326,39 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
             dhs[(int64_t)(j0 + jj) * K + i] = dh[m];
             sdh[i * NP + jj] = dh[m];
         }
-        load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);
-        const float gamma = sEg[C - 1];
-        const float *w = a.w + ch * C * K, *attn = a.attn + ch * C * C;
-        for (int e = tid; e < C * K; e += NT) {
-            const int r = e / K, i = e % K;
-            const bool ok = r < L;
-            const int64_t x = (tc + r) * rowK + h * K + i;
-            sw[r * KP + i] = w[e];
-            sk[r * KP + i] = ok ? sEk[r] * Elem<T>::load(a.k, x) : 0.f;
-            sq[r * KP + i] = ok ? sEg[r] * Elem<T>::load(a.q, x) : 0.f;
+#pragma unroll
+        for (int m = 0; m < LPT; ++m) {
+            const int e = tid + NT * m, r = e / K, i = e % K;
+            sw[r * KP + i] = pw[m];
+            sk[r * KP + i] = pk[m];
+            sq[r * KP + i] = pq[m];
         }
-        for (int e = tid; e < C * C; e += NT) sa[(e / C) * CP + e % C] = attn[e];
-        for (int e = tid; e < C * NCOL; e += NT) {
-            const int r = e / NCOL, jj = e % NCOL;
-            sdo[r * NP + jj] = r < L ? Elem<T>::load(a.dout, (tc + r) * rowV + h * V + j0 + jj) : 0.f;
+#pragma unroll
+        for (int m = 0; m < APT; ++m) {
+            const int e = tid + NT * m;
+            sa[(e / C) * CP + e % C] = pa[m];
         }
+#pragma unroll
+        for (int m = 0; m < DPT; ++m) {
+            const int e = tid + NT * m;
+            if (e < C * NCOL) sdo[(e / NCOL) * NP + e % NCOL] = pd[m];
+        }
+        if (tid < 64) chunk_decay<C>(pg, sG, sEg, sEk);
         __syncthreads();
+        if (c > 0) fetch(c - 1);
+        const float gamma = sEg[C - 1];
         float *dd = a.dd + ch * C * V;
+        // ddelta = attn^T do + k_tilde dh;  also exp(G) do for the q_g^T do term
         for (int o = tid; o < C * NCOL; o += NT) {
             const int r = o / NCOL, jj = o % NCOL;
-            float acc = 0.f;
+            float acc = 0.f, acck = 0.f;
+#pragma unroll 8
             for (int t = r; t < C; ++t) acc = fmaf(sa[t * CP + r], sdo[t * NP + jj], acc);
-            for (int i = 0; i < K; ++i) acc = fmaf(sk[r * KP + i], sdh[i * NP + jj], acc);
+#pragma unroll 8
+            for (int i = 0; i < K; ++i) acck = fmaf(sk[r * KP + i], sdh[i * NP + jj], acck);
+            acc = fmaf(sEk[r], acck, acc);
             sdd[r * NP + jj] = acc;
+            sdoG[r * NP + jj] = sEg[r] * sdo[r * NP + jj];
             dd[r * V + j0 + jj] = acc;
         }
         __syncthreads();
@@ -289,8 +366,9 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
         for (int m = 0; m < EPT; ++m) {
             const int e = tid + NT * m, i = e % K, jj = e / K;
             float acc = gamma * dh[m];
+#pragma unroll 8
             for (int r = 0; r < C; ++r) {
-                acc = fmaf(sq[r * KP + i], sdo[r * NP + jj], acc);
+                acc = fmaf(sq[r * KP + i], sdoG[r * NP + jj], acc);
                 acc = fmaf(-sw[r * KP + i], sdd[r * NP + jj], acc);
             }
             dh[m] = acc;
@@ -353,36 +431,87 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     }
     load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);   // (synchronises)
 
-    // dattn[r][s] = causal(do delta^T);  dw^T[i][r] = -(h ddelta^T)[i][r]
-    for (int o = tid; o < C * C; o += NT) {
-        const int r = o / C, s = o % C;
-        float acc = 0.f;
-        if (s <= r && r < L)
-#pragma unroll 8
-            for (int j = 0; j < V; ++j) acc = fmaf(dox(r, j), bD[s * VP + j], acc);
-        bX[r * CP + s] = acc;
+    // Products with register tiles: a thread owns TR rows x TW consecutive
+    // columns of the output, so each operand it loads feeds several FMAs.
+    // C x C outputs: tiles of CR rows x CW columns.
+    constexpr int CW = C >= 64 ? 4 : 1;
+    constexpr int CG = C / CW;                       // column groups of a row
+    constexpr int CR = (C * C) / (NT * CW);
+    static_assert(CR >= 1 && CR * CW * NT == C * C && CG <= 64, "C x C tiles");
+    // dattn[r][s] = causal(do delta^T)
+    {
+        const int s0 = (tid % CG) * CW, r0 = (tid / CG) * CR;
+        float acc[CR][CW] = {};
+        for (int j = 0; j < V; ++j) {
+            float y[CW], x[CR];
+#pragma unroll
+            for (int n = 0; n < CW; ++n) y[n] = bD[(s0 + n) * VP + j];
+#pragma unroll
+            for (int m = 0; m < CR; ++m) x[m] = r0 + m < L ? dox(r0 + m, j) : 0.f;
+#pragma unroll
+            for (int m = 0; m < CR; ++m)
+#pragma unroll
+                for (int n = 0; n < CW; ++n) acc[m][n] = fmaf(x[m], y[n], acc[m][n]);
+        }
+#pragma unroll
+        for (int m = 0; m < CR; ++m)
+#pragma unroll
+            for (int n = 0; n < CW; ++n) bX[(r0 + m) * CP + s0 + n] = s0 + n <= r0 + m ? acc[m][n] : 0.f;
     }
-    for (int o = tid; o < K * C; o += NT) {
-        const int i = o / C, r = o % C;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int j = 0; j < V; ++j) acc = fmaf(-hsT[(int64_t)j * K + i], bdD[r * VP + j], acc);
-        bW[i * CP + r] = acc;
+    // dw^T[i][r] = -(h ddelta^T)[i][r]: K x C outputs, tiles of KR rows x CW columns
+    {
+        constexpr int KR = (K * C) / (NT * CW);
+        static_assert(KR >= 1 && KR * CW * NT == K * C, "K x C tiles");
+        const int c0 = (tid % CG) * CW, i0 = (tid / CG) * KR;
+        float acc[KR][CW] = {};
+        for (int j = 0; j < V; ++j) {
+            float y[CW], x[KR];
+#pragma unroll
+            for (int n = 0; n < CW; ++n) y[n] = bdD[(c0 + n) * VP + j];
+#pragma unroll
+            for (int m = 0; m < KR; ++m) x[m] = hsT[(int64_t)j * K + i0 + m];
+#pragma unroll
+            for (int m = 0; m < KR; ++m)
+#pragma unroll
+                for (int n = 0; n < CW; ++n) acc[m][n] = fmaf(x[m], y[n], acc[m][n]);
+        }
+#pragma unroll
+        for (int m = 0; m < KR; ++m)
+#pragma unroll
+            for (int n = 0; n < CW; ++n) bW[(i0 + m) * CP + c0 + n] = -acc[m][n];
     }
     __syncthreads();
-    // dT^T[s][r] = (Vb ddelta^T)[s][r] + (Kb dw^T)[s][r]
-    for (int o = tid; o < C * C; o += NT) {
-        const int s = o / C, r = o % C;
-        float acc = 0.f;
-        if (s < L) {
-            float av = 0.f, ak = 0.f;
-#pragma unroll 8
-            for (int j = 0; j < V; ++j) av = fmaf(vx(s, j), bdD[r * VP + j], av);
-#pragma unroll 8
-            for (int i = 0; i < K; ++i) ak = fmaf(kx(s, i), bW[i * CP + r], ak);
-            acc = sb[s] * (av + sEg[s] * ak);
+    // dT^T[s][r] = beta_s ((V ddelta^T)[s][r] + exp(G_s) (K dw^T)[s][r])
+    {
+        const int r0 = (tid % CG) * CW, s0 = (tid / CG) * CR;
+        float av[CR][CW] = {}, ak[CR][CW] = {};
+        for (int j = 0; j < V; ++j) {
+            float y[CW], x[CR];
+#pragma unroll
+            for (int n = 0; n < CW; ++n) y[n] = bdD[(r0 + n) * VP + j];
+#pragma unroll
+            for (int m = 0; m < CR; ++m) x[m] = s0 + m < L ? vx(s0 + m, j) : 0.f;
+#pragma unroll
+            for (int m = 0; m < CR; ++m)
+#pragma unroll
+                for (int n = 0; n < CW; ++n) av[m][n] = fmaf(x[m], y[n], av[m][n]);
         }
-        bY[s * CP + r] = acc;
+        for (int i = 0; i < K; ++i) {
+            float y[CW], x[CR];
+#pragma unroll
+            for (int n = 0; n < CW; ++n) y[n] = bW[i * CP + r0 + n];
+#pragma unroll
+            for (int m = 0; m < CR; ++m) x[m] = s0 + m < L ? kx(s0 + m, i) : 0.f;
+#pragma unroll
+            for (int m = 0; m < CR; ++m)
+#pragma unroll
+                for (int n = 0; n < CW; ++n) ak[m][n] = fmaf(x[m], y[n], ak[m][n]);
+        }
+#pragma unroll
+        for (int m = 0; m < CR; ++m)
+#pragma unroll
+            for (int n = 0; n < CW; ++n)
+                bY[(s0 + m) * CP + r0 + n] = sb[s0 + m] * (av[m][n] + sEg[s0 + m] * ak[m][n]);
     }
     __syncthreads();
     // Z = dT T^T
@@ -437,41 +566,80 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
-    // dq and dk, one element each
-    for (int o = tid; o < C * K; o += NT) {
-        const int r = o / K, i = o % K;
-        float pg = 0.f, pd = 0.f, pk = 0.f;
-        if (r < L) {
-            const float eG = sEg[r], er = sEk[r], br = sb[r];
-            // q_g: dq_g = do h^T;  attn (row r): sum_s dattn[r][s] D[r][s] k_s
-            float dqg = 0.f, qa = 0.f;
-#pragma unroll 8
-            for (int j = 0; j < V; ++j) dqg = fmaf(dox(r, j), hsT[(int64_t)j * K + i], dqg);
-            for (int s = 0; s <= r; ++s) qa = fmaf(bX[r * CP + s], kx(s, i), qa);
-            Elem<T>::store(a.dq, (tc + r) * rowK + h * K + i, eG * dqg + qa);
-            // k as a key of attn (column r): sum_t dattn[t][r] D[t][r] q_t
-            float ka = 0.f;
-            for (int t = r; t < L; ++t) ka = fmaf(bX[t * CP + r], qx(t, i), ka);
-            // k_tilde: dk_tilde = delta dh^T (delta from the workspace: its LDS copy is gone)
-            float dkt = 0.f;
-#pragma unroll 8
-            for (int j = 0; j < V; ++j) dkt = fmaf(dws[r * V + j], dhsT[(int64_t)j * K + i], dkt);
-            // Kb: dKb = T^T dw
-            float dkb = 0.f;
-            for (int p = r; p < C; ++p) dkb = fmaf(bT[p * CP + r], bW[i * CP + p], dkb);
-            // A (both operands): dKK k, dKK^T k
-            float kaa = 0.f;
-            for (int p = 0; p < r; ++p) kaa = fmaf(bY[r * CP + p], kx(p, i), kaa);
-            for (int p = r + 1; p < L; ++p) kaa = fmaf(bY[p * CP + r], kx(p, i), kaa);
-            const float kri = kx(r, i);
-            Elem<T>::store(a.dk, (tc + r) * rowK + h * K + i, ka + er * dkt + br * eG * dkb + kaa);
-            pg = eG * dqg * qx(r, i) - er * dkt * kri + br * eG * dkb * kri;
-            pd = er * dkt * kri;
-            pk = eG * dkb * kri;
+    // dq and dk: C x K outputs, tiles of QR rows x QW consecutive columns
+    {
+        constexpr int QW = K >= 128 ? 4 : 2;
+        constexpr int QG = K / QW;                   // column groups of a row
+        constexpr int QR = (C * K) / (NT * QW);
+        static_assert(QR >= 1 && QR * QW * NT == C * K && QG <= 64, "C x K tiles");
+        const int i0 = (tid % QG) * QW, r0 = (tid / QG) * QR;
+        // over the chunk's tokens p (rows p >= L hold zeros in every factor):
+        //   qa  = (dattn D) k          dkr = (dattn D)^T q + (dKK + dKK^T) k
+        //   dkb = T^T dw
+        float qa[QR][QW] = {}, dkr[QR][QW] = {}, dkb[QR][QW] = {};
+        for (int p = 0; p < L; ++p) {
+            float kp[QW], qp[QW], wp[QW];
+#pragma unroll
+            for (int n = 0; n < QW; ++n) {
+                kp[n] = kx(p, i0 + n);
+                qp[n] = qx(p, i0 + n);
+                wp[n] = bW[(i0 + n) * CP + p];
+            }
+#pragma unroll
+            for (int m = 0; m < QR; ++m) {
+                const int r = r0 + m;
+                const float xa = bX[r * CP + p], xat = bX[p * CP + r];
+                const float xy = bY[r * CP + p] + bY[p * CP + r], xt = bT[p * CP + r];
+#pragma unroll
+                for (int n = 0; n < QW; ++n) {
+                    qa[m][n] = fmaf(xa, kp[n], qa[m][n]);
+                    dkr[m][n] = fmaf(xat, qp[n], fmaf(xy, kp[n], dkr[m][n]));
+                    dkb[m][n] = fmaf(xt, wp[n], dkb[m][n]);
+                }
+            }
         }
-        add_row<K>(sdG, r, pg);
-        add_row<K>(sdG, C - 1, pd);
-        add_row<K>(sdb, r, pk);
+        //   dqg = do h^T               dkt = delta dh^T   (the k_tilde gradient)
+        float dqg[QR][QW] = {}, dkt[QR][QW] = {};
+        for (int j = 0; j < V; ++j) {
+            float hp[QW], dhp[QW];
+#pragma unroll
+            for (int n = 0; n < QW; ++n) {
+                hp[n] = hsT[(int64_t)j * K + i0 + n];
+                dhp[n] = dhsT[(int64_t)j * K + i0 + n];
+            }
+#pragma unroll
+            for (int m = 0; m < QR; ++m) {
+                const int r = r0 + m;
+                const float xo = r < L ? dox(r, j) : 0.f, xd = dws[r * V + j];
+#pragma unroll
+                for (int n = 0; n < QW; ++n) {
+                    dqg[m][n] = fmaf(xo, hp[n], dqg[m][n]);
+                    dkt[m][n] = fmaf(xd, dhp[n], dkt[m][n]);
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < QR; ++m) {
+            const int r = r0 + m;
+            float pg = 0.f, pd = 0.f, pk = 0.f;
+            if (r < L) {
+                const float eG = sEg[r], er = sEk[r], br = sb[r];
+#pragma unroll
+                for (int n = 0; n < QW; ++n) {
+                    const int i = i0 + n;
+                    const float kri = kx(r, i), qri = qx(r, i);
+                    Elem<T>::store(a.dq, (tc + r) * rowK + h * K + i, eG * dqg[m][n] + qa[m][n]);
+                    Elem<T>::store(a.dk, (tc + r) * rowK + h * K + i,
+                                   dkr[m][n] + er * dkt[m][n] + br * eG * dkb[m][n]);
+                    pg += eG * dqg[m][n] * qri - er * dkt[m][n] * kri + br * eG * dkb[m][n] * kri;
+                    pd += er * dkt[m][n] * kri;
+                    pk += eG * dkb[m][n] * kri;
+                }
+            }
+            add_row<QG>(sdG, r, pg);
+            add_row<QG>(sdG, C - 1, pd);
+            add_row<QG>(sdb, r, pk);
+        }
     }
     // gamma: dG_last += gamma <h, dh>
     {
