@@ -245,3 +245,37 @@ def test_conv_and_norm_validation():
     assert norm(4, 128, b.GDN_F32, 1e-6, FAKE, None, None, FAKE, None) == b.GDN_EINVAL
     assert norm(4, 128, b.GDN_F32, 1e-6, FAKE, None, FAKE, FAKE + 16, None) == b.GDN_EINVAL   # partial overlap
     assert norm(0, 128, b.GDN_F32, 1e-6, None, None, None, None, None) == b.GDN_OK
+
+
+def test_backward_validation():
+    """gdn_backward: whole sequences, one key head per value head, every buffer
+    distinct, the workspace sized by gdn_backward_workspace_bytes."""
+    import ctypes
+    lib = b.library()
+    ref = ctypes.byref
+    p = prob()                                    # B1 S256 H2 K32 V32 C16 fp32
+    ws = b.gdn_backward_workspace_bytes(p)
+    assert ws == 16 * 2 * 4 * (3 * 16 * 16 + 16 * 32 + 3 * 16 * 32 + 2 * 32 * 32)
+    assert b.gdn_backward_workspace_bytes(prob(n_segments=2)) == 0
+    assert b.gdn_backward_workspace_bytes(prob(H=4, H_qk=2)) == 0
+    step = 1 << 24                                # distinct fake buffers, 16 MiB apart
+    buf = [FAKE + i * step for i in range(16)]
+
+    def call(pp, **over):
+        names = ["q", "k", "v", "g", "beta", "h0", "dout", "dhT", "dq", "dk", "dv", "dg", "dbeta", "dh0",
+                 "ws"]
+        a = dict(zip(names, buf))
+        a.update(over)
+        return lib.gdn_backward(ref(pp), *[a[n] for n in names], over.get("ws_bytes", ws), None)
+
+    assert call(prob(n_segments=2)) == b.GDN_EUNSUPPORTED
+    assert call(prob(H=4, H_qk=2)) == b.GDN_EUNSUPPORTED
+    assert call(prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=2)) == b.GDN_EUNSUPPORTED
+    assert call(p, ws_bytes=ws - 1) == b.GDN_EINVAL
+    assert call(p, q=None) == b.GDN_EINVAL
+    assert call(p, dout=None) == b.GDN_EINVAL
+    assert call(p, dg=buf[1] + 4) == b.GDN_EINVAL          # misaligned
+    assert call(p, dq=buf[0]) == b.GDN_EINVAL              # dq overlaps q
+    assert call(p, dk=buf[14]) == b.GDN_EINVAL             # dk overlaps the workspace
+    assert call(p, dv=buf[8]) == b.GDN_EINVAL              # dv overlaps dq
+    assert call(prob(K=64, V=64, C=16)) == b.GDN_EUNSUPPORTED
