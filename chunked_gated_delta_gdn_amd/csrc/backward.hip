@@ -112,13 +112,14 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
     const int h = blockIdx.x % H;
     const int64_t chunk = blockIdx.x / H;
     const ChunkLoc cl = locate_chunk(a.ct, chunk, C);
-    const int64_t rowK = (int64_t)H * K, rowV = (int64_t)H * V;
+    const int64_t rowK = (int64_t)a.Hk * K, rowV = (int64_t)H * V;
+    const int hk = h / (H / a.Hk);   // key head of this value head (grouped order)
     const int64_t ch = chunk * H + h;
 
     for (int e = tid; e < C * K; e += NT) {
         const int r = e / K, i = e % K;
         const bool ok = r < cl.L;
-        const int64_t x = (cl.tc + r) * rowK + h * K + i;
+        const int64_t x = (cl.tc + r) * rowK + hk * K + i;
         sk[r * KP + i] = ok ? Elem<T>::load(a.k, x) : 0.f;
         sq[r * KP + i] = ok ? Elem<T>::load(a.q, x) : 0.f;
     }
@@ -197,7 +198,8 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
     const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
     const int j0 = cg * NCOL;
     const ChainSpan sp = chain_span(a.ct, n, C);
-    const int64_t rowK = (int64_t)H * K;
+    const int64_t rowK = (int64_t)a.Hk * K;
+    const int hk = h / (H / a.Hk);
     const int64_t KV = (int64_t)K * V;
 
     float hr[EPT];
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
         for (int m = 0; m < LPT; ++m) {
             const int e = tid + NT * m, r = e / K, i = e % K;
             pw[m] = w[e];
-            pk[m] = r < L ? Elem<T>::load(a.k, (tc + r) * rowK + h * K + i) : 0.f;
+            pk[m] = r < L ? Elem<T>::load(a.k, (tc + r) * rowK + hk * K + i) : 0.f;
         }
         pg = tid < C && tid < L ? a.g[(tc + tid) * H + h] : 0.f;
     };
@@ -280,7 +282,8 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
     const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
     const int j0 = cg * NCOL;
     const ChainSpan sp = chain_span(a.ct, n, C);
-    const int64_t rowK = (int64_t)H * K, rowV = (int64_t)H * V;
+    const int64_t rowK = (int64_t)a.Hk * K, rowV = (int64_t)H * V;
+    const int hk = h / (H / a.Hk);
     const int64_t KV = (int64_t)K * V;
 
     float dh[EPT];
@@ -302,7 +305,7 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
         for (int m = 0; m < LPT; ++m) {
             const int e = tid + NT * m, r = e / K, i = e % K;
             const bool ok = r < L;
-            const int64_t x = (tc + r) * rowK + h * K + i;
+            const int64_t x = (tc + r) * rowK + hk * K + i;
             pw[m] = w[e];
             pk[m] = ok ? Elem<T>::load(a.k, x) : 0.f;
             pq[m] = ok ? Elem<T>::load(a.q, x) : 0.f;
@@ -405,14 +408,21 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     const ChunkLoc cl = locate_chunk(a.ct, chunk, C);
     const int L = cl.L;
     const int64_t tc = cl.tc;
-    const int64_t rowK = (int64_t)H * K, rowV = (int64_t)H * V;
+    const int64_t rowK = (int64_t)a.Hk * K, rowV = (int64_t)H * V;
+    const int hk = h / (H / a.Hk);
     const int64_t ch = chunk * H + h;
     const int64_t KV = (int64_t)K * V;
     const float *hsT = a.hs + ch * KV, *dhsT = a.dhs + ch * KV;   // [V][K]
     const float *attn = a.attn + ch * C * C, *Ak = a.Ak + ch * C * C;
     const float *dws = a.d + ch * C * V;
-    auto qx = [&](int r, int i) { return Elem<T>::load(a.q, (tc + r) * rowK + h * K + i); };
-    auto kx = [&](int r, int i) { return Elem<T>::load(a.k, (tc + r) * rowK + h * K + i); };
+    auto qx = [&](int r, int i) { return Elem<T>::load(a.q, (tc + r) * rowK + hk * K + i); };
+    auto kx = [&](int r, int i) { return Elem<T>::load(a.k, (tc + r) * rowK + hk * K + i); };
+    // dq, dk of this value head: the outputs themselves, or (grouped key heads)
+    // fp32 rows [T, H, K] that a second kernel sums over each key head's group
+    auto put_qk = [&](void *out, float *acc, int r, int i, float x) {
+        if (acc) acc[((tc + r) * H + h) * K + i] = x;
+        else Elem<T>::store(out, (tc + r) * rowK + hk * K + i, x);
+    };
     auto vx = [&](int r, int j) { return Elem<T>::load(a.v, (tc + r) * rowV + h * V + j); };
     auto dox = [&](int r, int j) { return Elem<T>::load(a.dout, (tc + r) * rowV + h * V + j); };
 
@@ -628,9 +638,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
                 for (int n = 0; n < QW; ++n) {
                     const int i = i0 + n;
                     const float kri = kx(r, i), qri = qx(r, i);
-                    Elem<T>::store(a.dq, (tc + r) * rowK + h * K + i, eG * dqg[m][n] + qa[m][n]);
-                    Elem<T>::store(a.dk, (tc + r) * rowK + h * K + i,
-                                   dkr[m][n] + er * dkt[m][n] + br * eG * dkb[m][n]);
+                    put_qk(a.dq, a.dq_acc, r, i, eG * dqg[m][n] + qa[m][n]);
+                    put_qk(a.dk, a.dk_acc, r, i, dkr[m][n] + er * dkt[m][n] + br * eG * dkb[m][n]);
                     pg += eG * dqg[m][n] * qri - er * dkt[m][n] * kri + br * eG * dkb[m][n] * kri;
                     pd += er * dkt[m][n] * kri;
                     pk += eG * dkb[m][n] * kri;
@@ -661,6 +670,22 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- 5. grouped key heads
+// A key head serves G = H / Hk value heads, so its dq, dk are the sums of
+// theirs: out[t][hk][i] = sum_g acc[t][hk G + g][i].
+template <typename T, int K>
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float *acc, void *out, int64_t n, int H, int Hk) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    const int G = H / Hk;
+    const int i = (int)(e % K);
+    const int64_t th = e / K;               // t * Hk + hk
+    const float *src = acc + (th * G) * K + i;
+    float x = 0.f;
+    for (int g = 0; g < G; ++g) x += src[(int64_t)g * K];
+    Elem<T>::store(out, e, x);
+}
+
 template <typename T, int K, int V, int C, int NCOL, int NT>
 hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
     const unsigned chunk_grid = (unsigned)(a.n_chunks * a.H);
@@ -680,6 +705,12 @@ hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
     }
     if (chunk_grid > 0) {
         hipLaunchKernelGGL((bwd_grads_kernel<T, K, V, C, NT>), dim3(chunk_grid), dim3(NT), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || !a.dq_acc) return e;
+        const int64_t n = a.tokens * a.Hk * K;
+        const unsigned grid = (unsigned)((n + 255) / 256);
+        hipLaunchKernelGGL((bwd_group_sum_kernel<T, K>), dim3(grid), dim3(256), 0, s, a.dq_acc, a.dq, n, a.H, a.Hk);
+        hipLaunchKernelGGL((bwd_group_sum_kernel<T, K>), dim3(grid), dim3(256), 0, s, a.dk_acc, a.dk, n, a.H, a.Hk);
         return hipGetLastError();
     }
     return hipSuccess;

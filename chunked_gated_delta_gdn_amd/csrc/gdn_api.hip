@@ -654,16 +654,22 @@ static gdn_status backward_problem(const gdn_problem *p, Resolved &r) {
         return fail(GDN_EUNSUPPORTED, "the backward pass runs whole sequences (n_segments must be 1)");
     if (p->max_piece_chunks != 0)
         return fail(GDN_EUNSUPPORTED, "the backward pass runs whole sequences (max_piece_chunks must be 0)");
-    if (p->H_qk != 0 && p->H_qk != p->H)
-        return fail(GDN_EUNSUPPORTED, "grouped key heads (H_qk = %d < H = %d) have no backward pass",
-                    p->H_qk, p->H);
     return GDN_OK;
+}
+
+static bool grouped(const gdn_problem *p) { return p->H_qk != 0 && p->H_qk != p->H; }
+
+// per-chunk-head workspace, then (grouped key heads) dq, dk of every value head
+static size_t backward_ws_bytes(const gdn_problem *p, const Resolved &r) {
+    size_t n = (size_t)r.n_chunks * p->H * backward_ws_per_chunk(p);
+    if (grouped(p)) n += 2 * (size_t)r.T * p->H * p->K * sizeof(float);
+    return n;
 }
 
 size_t gdn_backward_workspace_bytes(const gdn_problem *p) {
     Resolved r;
     if (backward_problem(p, r) != GDN_OK) return 0;
-    return (size_t)r.n_chunks * p->H * backward_ws_per_chunk(p);
+    return backward_ws_bytes(p, r);
 }
 
 gdn_status gdn_backward(const gdn_problem *p, const void *q, const void *k, const void *v,
@@ -688,12 +694,13 @@ gdn_status gdn_backward(const gdn_problem *p, const void *q, const void *k, cons
     GDN_TRY(check_ptr(dg, "dg", any));
     GDN_TRY(check_ptr(dbeta, "dbeta", any));
     GDN_TRY(check_ptr(dh0, "dh0", false));
-    const size_t need = (size_t)r.n_chunks * p->H * backward_ws_per_chunk(p);
+    const size_t need = backward_ws_bytes(p, r);
     GDN_TRY(check_ptr(workspace, "workspace", need > 0));
     if (workspace_bytes < need)
         return fail(GDN_EINVAL, "backward workspace %zu bytes < %zu needed", workspace_bytes, need);
     const size_t es = elem_size(p->dtype);
-    const size_t nqk = (size_t)r.T * p->H * p->K * es, nv = (size_t)r.T * p->H * p->V * es;
+    const int Hk = p->H_qk > 0 ? p->H_qk : p->H;
+    const size_t nqk = (size_t)r.T * Hk * p->K * es, nv = (size_t)r.T * p->H * p->V * es;
     const size_t ngb = (size_t)r.T * p->H * sizeof(float);
     const size_t nst = (size_t)r.N * p->H * p->K * p->V * sizeof(float);
     const struct { const void *ptr; size_t n; } ins[] = {
@@ -739,7 +746,14 @@ gdn_status gdn_backward(const gdn_problem *p, const void *q, const void *k, cons
     a.dd = a.d + CH * p->C * p->V;
     a.hs = a.dd + CH * p->C * p->V;
     a.dhs = a.hs + CH * p->K * p->V;
+    a.dq_acc = a.dk_acc = nullptr;
+    if (grouped(p)) {
+        a.dq_acc = a.dhs + CH * p->K * p->V;
+        a.dk_acc = a.dq_acc + (size_t)r.T * p->H * p->K;
+    }
     a.H = p->H;
+    a.Hk = Hk;
+    a.tokens = r.T;
     a.n_chunks = r.n_chunks;
     a.ct = r.ct;
     (void)hipGetLastError();

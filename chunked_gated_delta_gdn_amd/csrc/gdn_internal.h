@@ -182,8 +182,9 @@ struct BwdArgs {
     void *dq, *dk, *dv;
     float *dg, *dbeta, *dh0;
     float *T, *attn, *Ak, *w, *u, *hs, *dhs, *d, *dd;
-    int32_t H;
-    int64_t n_chunks;
+    float *dq_acc, *dk_acc;   // grouped key heads: per value head dq, dk [T, H, K]; else NULL
+    int32_t H, Hk;            // value heads; heads of q and k (value head h reads key head h / (H / Hk))
+    int64_t n_chunks, tokens; // chunks over all sequences; tokens
     ChainTable ct;
 };
 static_assert(sizeof(BwdArgs) + 64 <= 4096, "backward kernel arguments too large");

@@ -565,13 +565,11 @@ def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segment
 def backward(q, k, v, g, beta, do, h0=None, dhT=None, chunk_size=64, cu_seqlens=None, want_dh0=True):
     """Gradients through the forward pass (``gdn_backward``).
 
-    q, k [B,S,H,K]; v, do [B,S,H,V] (fp32 or bf16); g, beta [B,S,H] fp32;
+    q, k [B,S,H_qk,K]; v, do [B,S,H,V] (fp32 or bf16); g, beta [B,S,H] fp32;
     h0, dhT [N,H,K,V] fp32 or None (zero).  Packed batches pass B == 1 and
     cu_seqlens.  Returns (dq, dk, dv, dg, dbeta, dh0 or None), each in the
     layout and dtype of its input (dh0 fp32)."""
     B, S, H, K, V = _check_inputs(q, k, v, g, beta)
-    if k.shape[2] != H:
-        raise ValueError("grouped key heads have no backward pass")
     dev = k.device
     N = _n_seqs(k, cu_seqlens)
     _need(do, "do", (B, S, H, V), k.dtype, dev)
@@ -613,6 +611,6 @@ class _ChunkGatedDeltaRule(torch.autograd.Function):
 
 def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None):
     """Differentiable forward: (o, final state), with ``backward`` as its
-    gradient (torch.autograd).  Shapes as ``forward``; one key head per value
-    head."""
+    gradient (torch.autograd).  Shapes as ``forward`` (q, k may have fewer heads
+    than v: grouped key heads)."""
     return _ChunkGatedDeltaRule.apply(q, k, v, g, beta, h0, chunk_size, cu_seqlens)

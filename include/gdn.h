@@ -277,12 +277,15 @@ gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t V, int32_t dtype, float eps, 
 
 /*
  * gdn_backward -- gradients of a loss l(o, hT) through the forward of the
- * problem (batch or packed; n_segments == 1, max_piece_chunks == 0, H_qk == H
- * or 0), given dout = dl/do [same layout as o, `dtype`] and dhT = dl/dhT
+ * problem (batch or packed, grouped key heads included; n_segments == 1 and
+ * max_piece_chunks == 0: a sequence runs as one chain), given
+ * dout = dl/do [same layout as o, `dtype`] and dhT = dl/dhT
  * ([N,H,K,V] fp32, nullable = zero).  The MaxText PR "Add context
  * parallelism to the Gated Delta Net" tests a backward pass against the
  * single-device recurrence (section "Tests") without printing one; this is
  * the chain rule through the chunk equations of its section "Why".
+ * With grouped key heads dq, dk of a key head are the sums over the value
+ * heads that read it.
  * Outputs, each in the layout of its input: dq, dk, dv in `dtype`; dg,
  * dbeta fp32; dh0 [N,H,K,V] fp32 (nullable: not written; written whether or
  * not h0 is given).  h0 nullable (zero state).  Every output is fully

@@ -8,8 +8,11 @@ element, normwise, to the forward tolerances: 1e-4 for fp32 inputs and 2e-2
 for bf16 inputs (the kernels compute in fp32; bf16 enters through the inputs
 and the rounding of dq, dk, dv).  Cases span several chunks, ragged tails,
 both built shapes, packed streams with an empty sequence, absent h0 / dhT
-and the autograd wrapper.
+the autograd wrapper and grouped key heads (whose dq, dk are the sums over
+the value heads that read them: the chain rule through repeating a key head).
 """
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -123,3 +126,34 @@ def test_autograd_wrapper():
     for n, t, r in zip(NAMES, (q, k, v, g, beta, h0), ref):
         e = rel_err(t.grad.cpu().numpy(), r)
         assert e <= TOL["f32"], (n, e)
+
+
+@pytest.mark.parametrize("dtype,H,Hk,packed", [("f32", 4, 2, False), ("bf16", 4, 1, False),
+                                              ("f32", 6, 3, True)])
+def test_backward_grouped_key_heads(dtype, H, Hk, packed):
+    if packed:
+        x = make_packed_inputs(45, 3, 260, H, 128, 128, 64, dtype, h0_std=0.02, median=80,
+                               pad_to_chunk=False, name="bwd-grouped-packed")
+        x.meta = {}
+    else:
+        x = make_inputs(45, 2, 150, H, 128, 128, 64, dtype, h0_std=0.02, name="bwd-grouped")
+    do, dhT = make_cotangents(46, x)
+    G = H // Hk
+    qg = np.ascontiguousarray(x.q[:, :, ::G])      # key head j = the head that value heads jG .. jG+G-1 read
+    kg = np.ascontiguousarray(x.k[:, :, ::G])
+    xe = copy.copy(x)
+    xe.q, xe.k = oracle.expand_key_heads(qg, H), oracle.expand_key_heads(kg, H)
+    say(f"backward grouped {dtype} H={H} Hk={Hk} packed={packed}")
+    ref = list(oracle_grads(xe, do, dhT))
+    for i in (0, 1):   # repeat -> sum over the group
+        r = ref[i]
+        ref[i] = r.reshape(r.shape[:-2] + (Hk, G, r.shape[-1])).sum(-2)
+    xg = copy.copy(x)
+    xg.q, xg.k = qg, kg
+    got = gpu_grads(xg, do, dhT)
+    if packed:
+        got = [g_[0] if i < 5 else g_ for i, g_ in enumerate(got)]
+    errs = {n: rel_err(g_, r) for n, g_, r in zip(NAMES, got, ref)}
+    say(f"  errors {errs}")
+    for n in NAMES:
+        assert errs[n] <= TOL[dtype], (n, errs[n])

@@ -248,8 +248,8 @@ def test_conv_and_norm_validation():
 
 
 def test_backward_validation():
-    """gdn_backward: whole sequences, one key head per value head, every buffer
-    distinct, the workspace sized by gdn_backward_workspace_bytes."""
+    """gdn_backward: whole sequences, every buffer distinct, the workspace sized
+    by gdn_backward_workspace_bytes."""
     import ctypes
     lib = b.library()
     ref = ctypes.byref
@@ -257,7 +257,9 @@ def test_backward_validation():
     ws = b.gdn_backward_workspace_bytes(p)
     assert ws == 16 * 2 * 4 * (3 * 16 * 16 + 16 * 32 + 3 * 16 * 32 + 2 * 32 * 32)
     assert b.gdn_backward_workspace_bytes(prob(n_segments=2)) == 0
-    assert b.gdn_backward_workspace_bytes(prob(H=4, H_qk=2)) == 0
+    # grouped key heads add fp32 dq, dk rows of every value head
+    wg = b.gdn_backward_workspace_bytes(prob(H=4, H_qk=2))
+    assert wg == 2 * ws + 2 * 256 * 4 * 32 * 4
     step = 1 << 24                                # distinct fake buffers, 16 MiB apart
     buf = [FAKE + i * step for i in range(16)]
 
@@ -269,7 +271,7 @@ def test_backward_validation():
         return lib.gdn_backward(ref(pp), *[a[n] for n in names], over.get("ws_bytes", ws), None)
 
     assert call(prob(n_segments=2)) == b.GDN_EUNSUPPORTED
-    assert call(prob(H=4, H_qk=2)) == b.GDN_EUNSUPPORTED
+    assert call(prob(H=4, H_qk=2), ws_bytes=wg - 1) == b.GDN_EINVAL
     assert call(prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=2)) == b.GDN_EUNSUPPORTED
     assert call(p, ws_bytes=ws - 1) == b.GDN_EINVAL
     assert call(p, q=None) == b.GDN_EINVAL
