@@ -387,6 +387,250 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- 2b/3b. the scans on fp32 matrix cores
+// K = V = 128, C = 64, a 16-column strip per workgroup of 8 waves.  The
+// products are v_mfma_f32_16x16x4_f32 tiles (fp32 in, fp32 accumulate, so the
+// arithmetic class is that of the vector kernels above).  For one product
+// D += A B, lane (li, lg) = (lane & 15, lane >> 4) gives A[li][k] and B[k][li]
+// with k = 4 (4 q + lg) + e at step (q, e), so that its operands for one q are
+// 16-byte runs of a row of A and of a row of B^T; it holds D[4 lg + e][li].
+// Wave wv owns rows 16 wv .. 16 wv + 15 of the strip (of the state, or of its
+// gradient) in that layout.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 lds4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+template <typename T>
+__global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
+    constexpr int K = 128, V = 128, C = 64, NCOL = 16, NT = 512, NG = V / NCOL;
+    constexpr int LDK = K + 4, LDC = C + 4, KPT = C * K / NT;
+    __shared__ __attribute__((aligned(16))) float hT[NCOL * LDK];   // state strip [column][row]
+    __shared__ __attribute__((aligned(16))) float kT[K * LDC];      // raw k [i][r]
+    __shared__ __attribute__((aligned(16))) float dT[NCOL * LDC];   // exp(G_C - G_r) delta [column][r]
+    __shared__ float sG[C], sEg[C], sEk[C];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+    const int H = a.H;
+    const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
+    const int j0 = cg * NCOL;
+    const ChainSpan sp = chain_span(a.ct, n, C);
+    const int64_t rowK = (int64_t)a.Hk * K;
+    const int hk = h / (H / a.Hk);
+    const int64_t KV = (int64_t)K * V;
+    const int row0 = 16 * wv + 4 * lg;   // this lane's rows of the strip: row0 .. row0 + 3
+
+    f32x4 hacc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        hacc[e] = a.h0 ? a.h0[((int64_t)n * H + h) * KV + (int64_t)(row0 + e) * V + j0 + li] : 0.f;
+    const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
+    // next chunk: w rows (A operands of delta, waves 0-3), u seeds, raw k, g
+    f32x4 pw[8];
+    float pu[4], pk[KPT], pg = 0.f;
+    auto fetch = [&](int64_t c) {
+        int L;
+        int64_t tc;
+        chunk_rows<C, NT>(sp.t0, sp.t1, c, L, tc);
+        const int64_t ch = (sp.chunk0 + c) * H + h;
+        if (wv < 4) {
+            const float *w = a.w + ch * C * K + (16 * wv + li) * K;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) pw[q] = *reinterpret_cast<const f32x4 *>(w + 4 * (4 * q + lg));
+            const float *u = a.u + ch * C * V;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pu[e] = u[(row0 + e) * V + j0 + li];
+        }
+#pragma unroll
+        for (int m = 0; m < KPT; ++m) {
+            const int e = tid + NT * m, r = e / K, i = e % K;
+            pk[m] = r < L ? Elem<T>::load(a.k, (tc + r) * rowK + hk * K + i) : 0.f;
+        }
+        pg = tid < C && tid < L ? a.g[(tc + tid) * H + h] : 0.f;
+    };
+    if (nch > 0) fetch(0);
+    for (int64_t c = 0; c < nch; ++c) {
+        const int64_t ch = (sp.chunk0 + c) * H + h;
+        *reinterpret_cast<f32x4 *>(a.hs + ch * KV + (int64_t)(j0 + li) * K + row0) = hacc;
+        *reinterpret_cast<f32x4 *>(&hT[li * LDK + row0]) = hacc;
+#pragma unroll
+        for (int m = 0; m < KPT; ++m) {
+            const int e = tid + NT * m;
+            kT[(e % K) * LDC + e / K] = pk[m];
+        }
+        if (tid < 64) chunk_decay<C>(pg, sG, sEg, sEk);
+        __syncthreads();
+        f32x4 wc[8];
+        float uc[4];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) wc[q] = pw[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) uc[e] = pu[e];
+        if (c + 1 < nch) fetch(c + 1);
+        if (wv < 4) {
+            // delta rows 16 wv .. of the strip: u - w h
+            f32x4 acc = {uc[0], uc[1], uc[2], uc[3]};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const f32x4 hb = lds4(&hT[li * LDK + 4 * (4 * q + lg)]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(-wc[q][e], hb[e], acc, 0, 0, 0);
+            }
+            float *d = a.d + ch * C * V;
+            f32x4 sc;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d[(row0 + e) * V + j0 + li] = acc[e];
+                sc[e] = sEk[row0 + e] * acc[e];
+            }
+            *reinterpret_cast<f32x4 *>(&dT[li * LDC + row0]) = sc;
+        }
+        __syncthreads();
+        // h <- gamma h + k^T (exp(G_C - G) delta)
+        hacc *= sEg[C - 1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 ka = lds4(&kT[(16 * wv + li) * LDC + 4 * (4 * q + lg)]);
+            const f32x4 db = lds4(&dT[li * LDC + 4 * (4 * q + lg)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], db[e], hacc, 0, 0, 0);
+        }
+        __syncthreads();
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
+    constexpr int K = 128, V = 128, C = 64, NCOL = 16, NT = 512, NG = V / NCOL;
+    constexpr int LDK = K + 4, LDC = C + 4, KPT = C * K / NT, APT = C * C / NT, DPT = C * NCOL / NT;
+    __shared__ __attribute__((aligned(16))) float dhT[NCOL * LDK];   // gradient strip [column][row]
+    __shared__ __attribute__((aligned(16))) float sk[C * LDK];       // raw k [r][i]
+    __shared__ __attribute__((aligned(16))) float qT[K * LDC];       // raw q [i][r]
+    __shared__ __attribute__((aligned(16))) float wT[K * LDC];       // w [i][r]
+    __shared__ __attribute__((aligned(16))) float aT[C * LDC];       // attn^T [r][t]
+    __shared__ __attribute__((aligned(16))) float doT[NCOL * LDC];   // do strip [column][t]
+    __shared__ __attribute__((aligned(16))) float doGT[NCOL * LDC];  // exp(G_t) do [column][t]
+    __shared__ __attribute__((aligned(16))) float ddT[NCOL * LDC];   // ddelta [column][r]
+    __shared__ float sG[C], sEg[C], sEk[C];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+    const int H = a.H;
+    const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
+    const int j0 = cg * NCOL;
+    const ChainSpan sp = chain_span(a.ct, n, C);
+    const int64_t rowK = (int64_t)a.Hk * K, rowV = (int64_t)H * V;
+    const int hk = h / (H / a.Hk);
+    const int64_t KV = (int64_t)K * V;
+    const int row0 = 16 * wv + 4 * lg;
+
+    f32x4 dacc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        dacc[e] = a.dhT ? a.dhT[((int64_t)n * H + h) * KV + (int64_t)(row0 + e) * V + j0 + li] : 0.f;
+    const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
+    float pk[KPT], pq[KPT], pw[KPT], pa[APT], pd[DPT], pg = 0.f;
+    auto fetch = [&](int64_t c) {
+        int L;
+        int64_t tc;
+        chunk_rows<C, NT>(sp.t0, sp.t1, c, L, tc);
+        const int64_t ch = (sp.chunk0 + c) * H + h;
+        const float *w = a.w + ch * C * K, *attn = a.attn + ch * C * C;
+#pragma unroll
+        for (int m = 0; m < KPT; ++m) {
+            const int e = tid + NT * m, r = e / K, i = e % K;
+            const bool ok = r < L;
+            const int64_t x = (tc + r) * rowK + hk * K + i;
+            pk[m] = ok ? Elem<T>::load(a.k, x) : 0.f;
+            pq[m] = ok ? Elem<T>::load(a.q, x) : 0.f;
+            pw[m] = w[e];
+        }
+#pragma unroll
+        for (int m = 0; m < APT; ++m) pa[m] = attn[tid + NT * m];
+#pragma unroll
+        for (int m = 0; m < DPT; ++m) {
+            const int e = tid + NT * m, t = e / NCOL, jj = e % NCOL;
+            pd[m] = t < L ? Elem<T>::load(a.dout, (tc + t) * rowV + h * V + j0 + jj) : 0.f;
+        }
+        pg = tid < C && tid < L ? a.g[(tc + tid) * H + h] : 0.f;
+    };
+    if (nch > 0) fetch(nch - 1);
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int64_t ch = (sp.chunk0 + c) * H + h;
+        *reinterpret_cast<f32x4 *>(a.dhs + ch * KV + (int64_t)(j0 + li) * K + row0) = dacc;
+        *reinterpret_cast<f32x4 *>(&dhT[li * LDK + row0]) = dacc;
+#pragma unroll
+        for (int m = 0; m < KPT; ++m) {
+            const int e = tid + NT * m, r = e / K, i = e % K;
+            sk[r * LDK + i] = pk[m];
+            qT[i * LDC + r] = pq[m];
+            wT[i * LDC + r] = pw[m];
+        }
+#pragma unroll
+        for (int m = 0; m < APT; ++m) {
+            const int e = tid + NT * m;
+            aT[(e % C) * LDC + e / C] = pa[m];
+        }
+#pragma unroll
+        for (int m = 0; m < DPT; ++m) {
+            const int e = tid + NT * m;
+            doT[(e % NCOL) * LDC + e / NCOL] = pd[m];
+        }
+        if (tid < 64) chunk_decay<C>(pg, sG, sEg, sEk);
+        __syncthreads();
+        if (c > 0) fetch(c - 1);
+        if (wv < 4) {
+            // ddelta rows 16 wv ..: attn^T do + exp(G_C - G_r) k dh
+            f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 aa = lds4(&aT[(16 * wv + li) * LDC + 4 * (4 * q + lg)]);
+                const f32x4 bb = lds4(&doT[li * LDC + 4 * (4 * q + lg)]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(aa[e], bb[e], acc1, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const f32x4 ka = lds4(&sk[(16 * wv + li) * LDK + 4 * (4 * q + lg)]);
+                const f32x4 hb = lds4(&dhT[li * LDK + 4 * (4 * q + lg)]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], hb[e], acc2, 0, 0, 0);
+            }
+            float *dd = a.dd + ch * C * V;
+            f32x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v4[e] = fmaf(sEk[row0 + e], acc2[e], acc1[e]);
+                dd[(row0 + e) * V + j0 + li] = v4[e];
+            }
+            *reinterpret_cast<f32x4 *>(&ddT[li * LDC + row0]) = v4;
+        } else {
+            for (int e = tid - 256; e < NCOL * C; e += 256) {
+                const int jj = e / C, t = e % C;
+                doGT[jj * LDC + t] = sEg[t] * doT[jj * LDC + t];
+            }
+        }
+        __syncthreads();
+        // dh <- gamma dh + q^T (exp(G) do) - w^T ddelta
+        dacc *= sEg[C - 1];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int kk = 4 * (4 * q + lg);
+            const f32x4 qa = lds4(&qT[(16 * wv + li) * LDC + kk]);
+            const f32x4 ob = lds4(&doGT[li * LDC + kk]);
+            const f32x4 wa = lds4(&wT[(16 * wv + li) * LDC + kk]);
+            const f32x4 db = lds4(&ddT[li * LDC + kk]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[e], ob[e], dacc, 0, 0, 0);
+                dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(-wa[e], db[e], dacc, 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    if (a.dh0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            a.dh0[((int64_t)n * H + h) * KV + (int64_t)(row0 + e) * V + j0 + li] = dacc[e];
+    }
+}
+
 // ---------------------------------------------------------------- 4. grads
 template <typename T, int K, int V, int C, int NT>
 __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
@@ -696,10 +940,18 @@ hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (chain_grid > 0) {
-        hipLaunchKernelGGL((bwd_states_kernel<T, K, V, C, NCOL, NT>), dim3(chain_grid), dim3(NT), 0, s, a);
+        if constexpr (K == 128 && V == 128 && C == 64 && NCOL == 16 && NT == 512) {
+            hipLaunchKernelGGL((bwd_states_mfma_kernel<T>), dim3(chain_grid), dim3(NT), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((bwd_states_kernel<T, K, V, C, NCOL, NT>), dim3(chain_grid), dim3(NT), 0, s, a);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_dstates_kernel<T, K, V, C, NCOL, NT>), dim3(chain_grid), dim3(NT), 0, s, a);
+        if constexpr (K == 128 && V == 128 && C == 64 && NCOL == 16 && NT == 512) {
+            hipLaunchKernelGGL((bwd_dstates_mfma_kernel<T>), dim3(chain_grid), dim3(NT), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((bwd_dstates_kernel<T, K, V, C, NCOL, NT>), dim3(chain_grid), dim3(NT), 0, s, a);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -720,17 +972,11 @@ hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
 
 hipError_t launch_backward(int K, int V, int C, int dtype, const BwdArgs &a, int n_chains,
                            hipStream_t s) {
-    // The two state scans run one workgroup per (chain, head, column group)
-    // for the whole sequence: narrower groups when that still fits one
-    // workgroup per compute unit, so that small problems fill the chip.
-    if (K == 128 && V == 128 && C == 64) {
-        const bool narrow = (int64_t)n_chains * a.H * (V / 8) <= 256;
-        if (dtype == GDN_F32)
-            return narrow ? launch_all<float, 128, 128, 64, 8, 512>(a, n_chains, s)
-                          : launch_all<float, 128, 128, 64, 16, 512>(a, n_chains, s);
-        return narrow ? launch_all<bf16_t, 128, 128, 64, 8, 512>(a, n_chains, s)
-                      : launch_all<bf16_t, 128, 128, 64, 16, 512>(a, n_chains, s);
-    }
+    // The two state scans run one workgroup per (chain, head, 16-column strip)
+    // for the whole sequence, on the fp32 matrix cores at K = V = 128.
+    if (K == 128 && V == 128 && C == 64)
+        return dtype == GDN_F32 ? launch_all<float, 128, 128, 64, 16, 512>(a, n_chains, s)
+                                : launch_all<bf16_t, 128, 128, 64, 16, 512>(a, n_chains, s);
     if (K == 32 && V == 32 && C == 16)
         return dtype == GDN_F32 ? launch_all<float, 32, 32, 16, 8, 256>(a, n_chains, s)
                                 : launch_all<bf16_t, 32, 32, 16, 8, 256>(a, n_chains, s);
