@@ -685,89 +685,160 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     }
     load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);   // (synchronises)
 
+    if constexpr (K == 128 && V == 128 && C == 64 && NT == 512) {
+        // fp32 matrix-core tiles (layout as in the state scans)
+        const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        // dattn = causal(do delta^T): 4 x 4 tiles of C x C, wave wv owns two
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tile = 2 * wv + u, tr = tile >> 2, tcol = tile & 3;
+            const int r = 16 * tr + li, sc = 16 * tcol + li;   // A row, B column
+            f32x4 acc = z4;
+            for (int q = 0; q < 8; ++q) {
+                const int j0q = 4 * (4 * q + lg);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ao = r < L ? dox(r, j0q + e) : 0.f;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, bD[sc * VP + j0q + e], acc, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 16 * tr + 4 * lg + e;
+                bX[rr * CP + sc] = sc <= rr ? acc[e] : 0.f;
+            }
+        }
+        // dw^T = -(h ddelta^T): 8 x 4 tiles of K x C, wave wv owns row tile wv
+        {
+            const int i = 16 * wv + li;   // A row
+            f32x4 acc[4] = {z4, z4, z4, z4};
+            for (int q = 0; q < 8; ++q) {
+                const int j0q = 4 * (4 * q + lg);
+                float ha[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ha[e] = hsT[(int64_t)(j0q + e) * K + i];
+#pragma unroll
+                for (int tcol = 0; tcol < 4; ++tcol) {
+                    const int rc = 16 * tcol + li;   // B column
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[tcol] = __builtin_amdgcn_mfma_f32_16x16x4f32(ha[e], bdD[rc * VP + j0q + e], acc[tcol], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int tcol = 0; tcol < 4; ++tcol)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bW[(16 * wv + 4 * lg + e) * CP + 16 * tcol + li] = -acc[tcol][e];
+        }
+        __syncthreads();
+        // dT^T[s][r] = beta_s ((V ddelta^T)[s][r] + exp(G_s) (K dw^T)[s][r]): two tiles per wave
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tile = 2 * wv + u, ts = tile >> 2, tcol = tile & 3;
+            const int sr = 16 * ts + li, rc = 16 * tcol + li;   // A row, B column
+            f32x4 av = z4, ak = z4;
+            for (int q = 0; q < 8; ++q) {
+                const int j0q = 4 * (4 * q + lg);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = sr < L;
+                    av = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? vx(sr, j0q + e) : 0.f, bdD[rc * VP + j0q + e], av, 0, 0, 0);
+                    ak = __builtin_amdgcn_mfma_f32_16x16x4f32(ok ? kx(sr, j0q + e) : 0.f, bW[(j0q + e) * CP + rc], ak, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ss = 16 * ts + 4 * lg + e;
+                bY[ss * CP + rc] = sb[ss] * (av[e] + sEg[ss] * ak[e]);
+            }
+        }
+        __syncthreads();
+    } else {
     // Products with register tiles: a thread owns TR rows x TW consecutive
-    // columns of the output, so each operand it loads feeds several FMAs.
-    // C x C outputs: tiles of CR rows x CW columns.
-    constexpr int CW = C >= 64 ? 4 : 1;
-    constexpr int CG = C / CW;                       // column groups of a row
-    constexpr int CR = (C * C) / (NT * CW);
-    static_assert(CR >= 1 && CR * CW * NT == C * C && CG <= 64, "C x C tiles");
-    // dattn[r][s] = causal(do delta^T)
-    {
-        const int s0 = (tid % CG) * CW, r0 = (tid / CG) * CR;
-        float acc[CR][CW] = {};
-        for (int j = 0; j < V; ++j) {
-            float y[CW], x[CR];
-#pragma unroll
-            for (int n = 0; n < CW; ++n) y[n] = bD[(s0 + n) * VP + j];
-#pragma unroll
-            for (int m = 0; m < CR; ++m) x[m] = r0 + m < L ? dox(r0 + m, j) : 0.f;
-#pragma unroll
+        // columns of the output, so each operand it loads feeds several FMAs.
+        // C x C outputs: tiles of CR rows x CW columns.
+        constexpr int CW = C >= 64 ? 4 : 1;
+        constexpr int CG = C / CW;                       // column groups of a row
+        constexpr int CR = (C * C) / (NT * CW);
+        static_assert(CR >= 1 && CR * CW * NT == C * C && CG <= 64, "C x C tiles");
+        // dattn[r][s] = causal(do delta^T)
+        {
+            const int s0 = (tid % CG) * CW, r0 = (tid / CG) * CR;
+            float acc[CR][CW] = {};
+            for (int j = 0; j < V; ++j) {
+                float y[CW], x[CR];
+    #pragma unroll
+                for (int n = 0; n < CW; ++n) y[n] = bD[(s0 + n) * VP + j];
+    #pragma unroll
+                for (int m = 0; m < CR; ++m) x[m] = r0 + m < L ? dox(r0 + m, j) : 0.f;
+    #pragma unroll
+                for (int m = 0; m < CR; ++m)
+    #pragma unroll
+                    for (int n = 0; n < CW; ++n) acc[m][n] = fmaf(x[m], y[n], acc[m][n]);
+            }
+    #pragma unroll
             for (int m = 0; m < CR; ++m)
-#pragma unroll
-                for (int n = 0; n < CW; ++n) acc[m][n] = fmaf(x[m], y[n], acc[m][n]);
+    #pragma unroll
+                for (int n = 0; n < CW; ++n) bX[(r0 + m) * CP + s0 + n] = s0 + n <= r0 + m ? acc[m][n] : 0.f;
         }
-#pragma unroll
-        for (int m = 0; m < CR; ++m)
-#pragma unroll
-            for (int n = 0; n < CW; ++n) bX[(r0 + m) * CP + s0 + n] = s0 + n <= r0 + m ? acc[m][n] : 0.f;
-    }
-    // dw^T[i][r] = -(h ddelta^T)[i][r]: K x C outputs, tiles of KR rows x CW columns
-    {
-        constexpr int KR = (K * C) / (NT * CW);
-        static_assert(KR >= 1 && KR * CW * NT == K * C, "K x C tiles");
-        const int c0 = (tid % CG) * CW, i0 = (tid / CG) * KR;
-        float acc[KR][CW] = {};
-        for (int j = 0; j < V; ++j) {
-            float y[CW], x[KR];
-#pragma unroll
-            for (int n = 0; n < CW; ++n) y[n] = bdD[(c0 + n) * VP + j];
-#pragma unroll
-            for (int m = 0; m < KR; ++m) x[m] = hsT[(int64_t)j * K + i0 + m];
-#pragma unroll
+        // dw^T[i][r] = -(h ddelta^T)[i][r]: K x C outputs, tiles of KR rows x CW columns
+        {
+            constexpr int KR = (K * C) / (NT * CW);
+            static_assert(KR >= 1 && KR * CW * NT == K * C, "K x C tiles");
+            const int c0 = (tid % CG) * CW, i0 = (tid / CG) * KR;
+            float acc[KR][CW] = {};
+            for (int j = 0; j < V; ++j) {
+                float y[CW], x[KR];
+    #pragma unroll
+                for (int n = 0; n < CW; ++n) y[n] = bdD[(c0 + n) * VP + j];
+    #pragma unroll
+                for (int m = 0; m < KR; ++m) x[m] = hsT[(int64_t)j * K + i0 + m];
+    #pragma unroll
+                for (int m = 0; m < KR; ++m)
+    #pragma unroll
+                    for (int n = 0; n < CW; ++n) acc[m][n] = fmaf(x[m], y[n], acc[m][n]);
+            }
+    #pragma unroll
             for (int m = 0; m < KR; ++m)
-#pragma unroll
-                for (int n = 0; n < CW; ++n) acc[m][n] = fmaf(x[m], y[n], acc[m][n]);
+    #pragma unroll
+                for (int n = 0; n < CW; ++n) bW[(i0 + m) * CP + c0 + n] = -acc[m][n];
         }
-#pragma unroll
-        for (int m = 0; m < KR; ++m)
-#pragma unroll
-            for (int n = 0; n < CW; ++n) bW[(i0 + m) * CP + c0 + n] = -acc[m][n];
-    }
-    __syncthreads();
-    // dT^T[s][r] = beta_s ((V ddelta^T)[s][r] + exp(G_s) (K dw^T)[s][r])
-    {
-        const int r0 = (tid % CG) * CW, s0 = (tid / CG) * CR;
-        float av[CR][CW] = {}, ak[CR][CW] = {};
-        for (int j = 0; j < V; ++j) {
-            float y[CW], x[CR];
-#pragma unroll
-            for (int n = 0; n < CW; ++n) y[n] = bdD[(r0 + n) * VP + j];
-#pragma unroll
-            for (int m = 0; m < CR; ++m) x[m] = s0 + m < L ? vx(s0 + m, j) : 0.f;
-#pragma unroll
+        __syncthreads();
+        // dT^T[s][r] = beta_s ((V ddelta^T)[s][r] + exp(G_s) (K dw^T)[s][r])
+        {
+            const int r0 = (tid % CG) * CW, s0 = (tid / CG) * CR;
+            float av[CR][CW] = {}, ak[CR][CW] = {};
+            for (int j = 0; j < V; ++j) {
+                float y[CW], x[CR];
+    #pragma unroll
+                for (int n = 0; n < CW; ++n) y[n] = bdD[(r0 + n) * VP + j];
+    #pragma unroll
+                for (int m = 0; m < CR; ++m) x[m] = s0 + m < L ? vx(s0 + m, j) : 0.f;
+    #pragma unroll
+                for (int m = 0; m < CR; ++m)
+    #pragma unroll
+                    for (int n = 0; n < CW; ++n) av[m][n] = fmaf(x[m], y[n], av[m][n]);
+            }
+            for (int i = 0; i < K; ++i) {
+                float y[CW], x[CR];
+    #pragma unroll
+                for (int n = 0; n < CW; ++n) y[n] = bW[i * CP + r0 + n];
+    #pragma unroll
+                for (int m = 0; m < CR; ++m) x[m] = s0 + m < L ? kx(s0 + m, i) : 0.f;
+    #pragma unroll
+                for (int m = 0; m < CR; ++m)
+    #pragma unroll
+                    for (int n = 0; n < CW; ++n) ak[m][n] = fmaf(x[m], y[n], ak[m][n]);
+            }
+    #pragma unroll
             for (int m = 0; m < CR; ++m)
-#pragma unroll
-                for (int n = 0; n < CW; ++n) av[m][n] = fmaf(x[m], y[n], av[m][n]);
+    #pragma unroll
+                for (int n = 0; n < CW; ++n)
+                    bY[(s0 + m) * CP + r0 + n] = sb[s0 + m] * (av[m][n] + sEg[s0 + m] * ak[m][n]);
         }
-        for (int i = 0; i < K; ++i) {
-            float y[CW], x[CR];
-#pragma unroll
-            for (int n = 0; n < CW; ++n) y[n] = bW[i * CP + r0 + n];
-#pragma unroll
-            for (int m = 0; m < CR; ++m) x[m] = s0 + m < L ? kx(s0 + m, i) : 0.f;
-#pragma unroll
-            for (int m = 0; m < CR; ++m)
-#pragma unroll
-                for (int n = 0; n < CW; ++n) ak[m][n] = fmaf(x[m], y[n], ak[m][n]);
-        }
-#pragma unroll
-        for (int m = 0; m < CR; ++m)
-#pragma unroll
-            for (int n = 0; n < CW; ++n)
-                bY[(s0 + m) * CP + r0 + n] = sb[s0 + m] * (av[m][n] + sEg[s0 + m] * ak[m][n]);
+        __syncthreads();
     }
-    __syncthreads();
     // Z = dT T^T
     for (int o = tid; o < C * C; o += NT) {
         const int r = o / C, s = o % C;
@@ -786,17 +857,50 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // dv = diag(beta) T^T ddelta;  dbeta += (T^T ddelta) . v
-    for (int o = tid; o < C * V; o += NT) {
-        const int r = o / V, j = o % V;
-        float dvb = 0.f;
-        for (int p = r; p < C; ++p) dvb = fmaf(bT[p * CP + r], bdD[p * VP + j], dvb);
-        float part = 0.f;
-        if (r < L) {
-            Elem<T>::store(a.dv, (tc + r) * rowV + h * V + j, sb[r] * dvb);
-            part = dvb * vx(r, j);
+    if constexpr (K == 128 && V == 128 && C == 64 && NT == 512) {
+        // dv = diag(beta) T^T ddelta, dbeta += (T^T ddelta) . v: 4 x 8 tiles of C x V,
+        // wave wv owns column tile wv
+        const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+        const int j = 16 * wv + li;   // B column
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[4] = {z4, z4, z4, z4};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int p0 = 4 * (4 * q + lg);
+            float bb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bb[e] = bdD[(p0 + e) * VP + j];
+#pragma unroll
+            for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(bT[(p0 + e) * CP + 16 * tr + li], bb[e], acc[tr], 0, 0, 0);
         }
-        add_row<V>(sdb, r, part);
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tr + 4 * lg + e;
+                float part = 0.f;
+                if (r < L) {
+                    Elem<T>::store(a.dv, (tc + r) * rowV + h * V + j, sb[r] * acc[tr][e]);
+                    part = acc[tr][e] * vx(r, j);
+                }
+                add_row<16>(sdb, r, part);
+            }
+    } else {
+    // dv = diag(beta) T^T ddelta;  dbeta += (T^T ddelta) . v
+        for (int o = tid; o < C * V; o += NT) {
+            const int r = o / V, j = o % V;
+            float dvb = 0.f;
+            for (int p = r; p < C; ++p) dvb = fmaf(bT[p * CP + r], bdD[p * VP + j], dvb);
+            float part = 0.f;
+            if (r < L) {
+                Elem<T>::store(a.dv, (tc + r) * rowV + h * V + j, sb[r] * dvb);
+                part = dvb * vx(r, j);
+            }
+            add_row<V>(sdb, r, part);
+        }
     }
     // attn and A through the decay: dG_r += e, dG_s -= e;  dbeta from A
     for (int o = tid; o < C * C; o += NT) {
@@ -820,8 +924,88 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
-    // dq and dk: C x K outputs, tiles of QR rows x QW consecutive columns
+    if constexpr (K == 128 && C == 64 && NT == 512) {
+        // dq and dk on the fp32 matrix cores: 16 x 16 output tiles, wave wv owns
+        // column tile 16 wv and the four row tiles.  Operand and accumulator
+        // layout as in the state scans: lane (li, lg) gives A[li][k], B[k][li]
+        // with k = 4 (4 q + lg) + e, and holds D[4 lg + e][li].
+        const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+        const int i = 16 * wv + li;
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 dqg[4], dkt[4], qa[4], dkr[4], dkb[4];
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr) dqg[tr] = dkt[tr] = qa[tr] = dkr[tr] = dkb[tr] = z4;
+        // over V:  dqg = do h^T,  dkt = delta dh^T  (the k_tilde gradient)
+        for (int q = 0; q < 8; ++q) {
+            const int j0q = 4 * (4 * q + lg);
+            float hb[4], dhb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hb[e] = hsT[(int64_t)(j0q + e) * K + i];
+                dhb[e] = dhsT[(int64_t)(j0q + e) * K + i];
+            }
+#pragma unroll
+            for (int tr = 0; tr < 4; ++tr) {
+                const int r = 16 * tr + li;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ao = r < L ? dox(r, j0q + e) : 0.f;
+                    dqg[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao, hb[e], dqg[tr], 0, 0, 0);
+                    dkt[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(dws[r * V + j0q + e], dhb[e], dkt[tr], 0, 0, 0);
+                }
+            }
+        }
+        // over the chunk's tokens p (zero past L in every B operand):
+        //   qa = (dattn D) k,  dkr = (dattn D)^T q + (dKK + dKK^T) k,  dkb = T^T dw
+        for (int q = 0; q < 4; ++q) {
+            const int p0 = 4 * (4 * q + lg);
+            float kb[4], qb[4], wb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int p = p0 + e;
+                kb[e] = p < L ? kx(p, i) : 0.f;
+                qb[e] = p < L ? qx(p, i) : 0.f;
+                wb[e] = bW[i * CP + p];
+            }
+#pragma unroll
+            for (int tr = 0; tr < 4; ++tr) {
+                const int r = 16 * tr + li;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int p = p0 + e;
+                    const float xa = bX[r * CP + p], xat = bX[p * CP + r];
+                    const float xy = bY[r * CP + p] + bY[p * CP + r], xt = bT[p * CP + r];
+                    qa[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, kb[e], qa[tr], 0, 0, 0);
+                    dkr[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(xat, qb[e], dkr[tr], 0, 0, 0);
+                    dkr[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(xy, kb[e], dkr[tr], 0, 0, 0);
+                    dkb[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt, wb[e], dkb[tr], 0, 0, 0);
+                }
+            }
+        }
+        // lane holds rows 16 tr + 4 lg + e of column i
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tr + 4 * lg + e;
+                float pg = 0.f, pd = 0.f, pk = 0.f;
+                if (r < L) {
+                    const float eG = sEg[r], er = sEk[r], br = sb[r];
+                    const float kri = kx(r, i), qri = qx(r, i);
+                    put_qk(a.dq, a.dq_acc, r, i, eG * dqg[tr][e] + qa[tr][e]);
+                    put_qk(a.dk, a.dk_acc, r, i, dkr[tr][e] + er * dkt[tr][e] + br * eG * dkb[tr][e]);
+                    pg = eG * dqg[tr][e] * qri - er * dkt[tr][e] * kri + br * eG * dkb[tr][e] * kri;
+                    pd = er * dkt[tr][e] * kri;
+                    pk = eG * dkb[tr][e] * kri;
+                }
+                add_row<16>(sdG, r, pg);
+                add_row<16>(sdG, C - 1, pd);
+                add_row<16>(sdb, r, pk);
+            }
+        }
+    } else
     {
+        // dq and dk: C x K outputs, tiles of QR rows x QW consecutive columns
         constexpr int QW = K >= 128 ? 4 : 2;
         constexpr int QG = K / QW;                   // column groups of a row
         constexpr int QR = (C * K) / (NT * QW);
