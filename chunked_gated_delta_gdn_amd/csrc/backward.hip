@@ -100,6 +100,10 @@ __device__ __forceinline__ void add_row(float *dst, int row, float x) {
     if ((threadIdx.x & (W - 1)) == 0) atomicAdd(&dst[row], x);
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 lds4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
 // ---------------------------------------------------------------- 1. prep
 template <typename T, int K, int V, int C, int NT>
 __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
@@ -132,20 +136,52 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
     }
 
     float *Ak = a.Ak + ch * C * C, *attn = a.attn + ch * C * C;
-    for (int e = tid; e < C * C; e += NT) {
-        const int r = e / C, s = e % C;
-        float kk = 0.f, qk = 0.f, dec = 0.f;
-        if (s <= r) {
-            for (int i = 0; i < K; ++i) {
-                kk = fmaf(sk[r * KP + i], sk[s * KP + i], kk);
-                qk = fmaf(sq[r * KP + i], sk[s * KP + i], qk);
+    if constexpr (K == 128 && V == 128 && C == 64 && NT == 512) {
+        // the Grams K K^T and Q K^T as fp32 matrix-core tiles, two of the 4 x 4
+        // per wave (lane (li, lg) gives A[li][k], B[k][li], k = 4 (4 q + lg) + e;
+        // it holds D[4 lg + e][li])
+        const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+#pragma unroll
+        for (int u2 = 0; u2 < 2; ++u2) {
+            const int tile = 2 * wv + u2, tr = tile >> 2, tcol = tile & 3;
+            const int r = 16 * tr + li, sc = 16 * tcol + li;
+            f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qk = kk;
+            for (int q = 0; q < 8; ++q) {
+                const int i0 = 4 * (4 * q + lg);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float bk = sk[sc * KP + i0 + e];
+                    kk = __builtin_amdgcn_mfma_f32_16x16x4f32(sk[r * KP + i0 + e], bk, kk, 0, 0, 0);
+                    qk = __builtin_amdgcn_mfma_f32_16x16x4f32(sq[r * KP + i0 + e], bk, qk, 0, 0, 0);
+                }
             }
-            dec = expf(sG[r] - sG[s]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 16 * tr + 4 * lg + e;
+                const float dec = sc <= rr ? expf(sG[rr] - sG[sc]) : 0.f;
+                const float ak = sc < rr ? dec * kk[e] : 0.f;
+                sA[rr * CP + sc] = sb[rr] * ak;   // A itself
+                Ak[rr * C + sc] = ak;
+                attn[rr * C + sc] = dec * qk[e];
+            }
         }
-        const float ak = s < r ? dec * kk : 0.f;
-        sA[r * CP + s] = sb[r] * ak;   // A itself
-        Ak[e] = ak;
-        attn[e] = dec * qk;
+    } else {
+    float *Ak = a.Ak + ch * C * C, *attn = a.attn + ch * C * C;
+        for (int e = tid; e < C * C; e += NT) {
+            const int r = e / C, s = e % C;
+            float kk = 0.f, qk = 0.f, dec = 0.f;
+            if (s <= r) {
+                for (int i = 0; i < K; ++i) {
+                    kk = fmaf(sk[r * KP + i], sk[s * KP + i], kk);
+                    qk = fmaf(sq[r * KP + i], sk[s * KP + i], qk);
+                }
+                dec = expf(sG[r] - sG[s]);
+            }
+            const float ak = s < r ? dec * kk : 0.f;
+            sA[r * CP + s] = sb[r] * ak;   // A itself
+            Ak[e] = ak;
+            attn[e] = dec * qk;
+        }
     }
     __syncthreads();
     // T = (I + A)^{-1} by forward substitution, row by row: column c belongs to
@@ -166,17 +202,52 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
     }
     float *To = a.T + ch * C * C, *w = a.w + ch * C * K, *u = a.u + ch * C * V;
     for (int e = tid; e < C * C; e += NT) To[e] = sT[(e / C) * CP + e % C];
+    if constexpr (K == 128 && V == 128 && C == 64 && NT == 512) {
+        // w = T diag(beta exp(G)) K and u = T diag(beta) V: wave wv owns column
+        // tile wv of both and the four row tiles
+        const int lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+        const int col = 16 * wv + li;
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        f32x4 aw[4] = {z4, z4, z4, z4}, au[4] = {z4, z4, z4, z4};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int s0 = 4 * (4 * q + lg);
+            float bw[4], bu[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bw[e] = sbg[s0 + e] * sk[(s0 + e) * KP + col];
+                bu[e] = sv[(s0 + e) * V + col];
+            }
+#pragma unroll
+            for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ta = sT[(16 * tr + li) * CP + s0 + e];
+                    aw[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta, bw[e], aw[tr], 0, 0, 0);
+                    au[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta, bu[e], au[tr], 0, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tr + 4 * lg + e;
+                w[r * K + col] = aw[tr][e];
+                u[r * V + col] = au[tr][e];
+            }
+    } else {
     for (int e = tid; e < C * K; e += NT) {
-        const int r = e / K, i = e % K;
-        float acc = 0.f;
-        for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * CP + s], sbg[s] * sk[s * KP + i], acc);
-        w[e] = acc;
-    }
-    for (int e = tid; e < C * V; e += NT) {
-        const int r = e / V, j = e % V;
-        float acc = 0.f;
-        for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * CP + s], sv[s * V + j], acc);
-        u[e] = acc;
+            const int r = e / K, i = e % K;
+            float acc = 0.f;
+            for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * CP + s], sbg[s] * sk[s * KP + i], acc);
+            w[e] = acc;
+        }
+        for (int e = tid; e < C * V; e += NT) {
+            const int r = e / V, j = e % V;
+            float acc = 0.f;
+            for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * CP + s], sv[s * V + j], acc);
+            u[e] = acc;
+        }
     }
 }
 
@@ -396,10 +467,6 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
 // 16-byte runs of a row of A and of a row of B^T; it holds D[4 lg + e][li].
 // Wave wv owns rows 16 wv .. 16 wv + 15 of the strip (of the state, or of its
 // gradient) in that layout.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 lds4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
-
 template <typename T>
 __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
     constexpr int K = 128, V = 128, C = 64, NCOL = 16, NT = 512, NG = V / NCOL;
