@@ -18,7 +18,9 @@
 // and every chunk quantity passes its gradient on to q, k, v, beta and the
 // within-chunk cumulative decay G (dg is the reverse cumulative sum of dG).
 //
-// Four launches, all fp32 arithmetic on the vector ALU:
+// Four launches (a fifth sums dq, dk over grouped key heads), all fp32
+// arithmetic; at K = V = 128, C = 64 the products run as fp32 matrix-core
+// tiles, elsewhere (and for the small shape) on the vector ALU:
 //   1. prep   (chunk, head):    T, attn, Dec (.) K K^T, w, u
 //   2. states (chain, head, column group), chunks in order: the state at
 //      every chunk start (stored transposed, V x K) and delta
@@ -166,7 +168,6 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
             }
         }
     } else {
-    float *Ak = a.Ak + ch * C * C, *attn = a.attn + ch * C * C;
         for (int e = tid; e < C * C; e += NT) {
             const int r = e / C, s = e % C;
             float kk = 0.f, qk = 0.f, dec = 0.f;
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
                 u[r * V + col] = au[tr][e];
             }
     } else {
-    for (int e = tid; e < C * K; e += NT) {
+        for (int e = tid; e < C * K; e += NT) {
             const int r = e / K, i = e % K;
             float acc = 0.f;
             for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * CP + s], sbg[s] * sk[s * KP + i], acc);
@@ -822,7 +823,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
         }
         __syncthreads();
     } else {
-    // Products with register tiles: a thread owns TR rows x TW consecutive
+        // Products with register tiles: a thread owns TR rows x TW consecutive
         // columns of the output, so each operand it loads feeds several FMAs.
         // C x C outputs: tiles of CR rows x CW columns.
         constexpr int CW = C >= 64 ? 4 : 1;
@@ -956,7 +957,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
                 add_row<16>(sdb, r, part);
             }
     } else {
-    // dv = diag(beta) T^T ddelta;  dbeta += (T^T ddelta) . v
+        // dv = diag(beta) T^T ddelta;  dbeta += (T^T ddelta) . v
         for (int o = tid; o < C * V; o += NT) {
             const int r = o / V, j = o % V;
             float dvb = 0.f;
@@ -1070,8 +1071,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
                 add_row<16>(sdb, r, pk);
             }
         }
-    } else
-    {
+    } else {
         // dq and dk: C x K outputs, tiles of QR rows x QW consecutive columns
         constexpr int QW = K >= 128 ? 4 : 2;
         constexpr int QG = K / QW;                   // column groups of a row
