@@ -157,3 +157,22 @@ def test_backward_grouped_key_heads(dtype, H, Hk, packed):
     say(f"  errors {errs}")
     for n in NAMES:
         assert errs[n] <= TOL[dtype], (n, errs[n])
+
+
+@pytest.mark.parametrize("wl,heads", [(1, (0, 9)), (2, (21,))])
+def test_backward_bench_workloads_sampled_heads(wl, heads):
+    """The backward lines of the benchmark as it times them (4k tokens x 16 heads;
+    64k tokens x 32 heads), every head on the GPU, sampled heads through the
+    oracle (heads are independent chains)."""
+    from workloads import workload
+    x = workload(wl)
+    do, dhT = make_cotangents(47, x)
+    say(f"backward workload {wl}: {x.k.shape}, oracle on heads {heads}")
+    got = gpu_grads(x, do, dhT)
+    hs = list(heads)
+    ref = oracle.backward(x.q[:, :, hs], x.k[:, :, hs], x.v[:, :, hs], x.g[:, :, hs], x.beta[:, :, hs],
+                          x.h0[:, hs], do[:, :, hs], dhT[:, hs])
+    for n, g_, r in zip(NAMES, got, ref):
+        e = rel_err(g_[:, hs] if n == "dh0" else g_[:, :, hs], r)
+        say(f"  {n}: {e:.3e}")
+        assert e <= TOL[x.dtype], (n, e)
