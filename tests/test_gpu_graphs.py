@@ -86,3 +86,33 @@ def test_decode_steps_in_a_graph():
         steps(ref_state, ref_out)
         torch.cuda.synchronize()
         assert torch.equal(state, ref_state) and torch.equal(out, ref_out)
+
+
+def test_backward_in_a_graph():
+    """gdn_backward (four kernels, grouped key heads: five) captured once; every
+    replay reproduces the eager dq, dk, dv, dh0 bit for bit.  dg and dbeta are
+    summed per chunk with LDS float atomics, whose order varies from run to run
+    (eager runs included), so they agree to rounding."""
+    from workloads import make_cotangents
+    for Hk in (4, 2):
+        x = workload(1, H=4, S=700, decay="slow")
+        x.q = np.ascontiguousarray(x.q[:, :, :Hk])
+        x.k = np.ascontiguousarray(x.k[:, :, :Hk])
+        do, dhT = make_cotangents(5, x)
+        d = device_inputs(x)
+        dO, dH = to_dev(do, torch.bfloat16), to_dev(dhT)
+        run = lambda: gdn.backward(d["q"], d["k"], d["v"], d["g"], d["beta"], dO, h0=d["h0"], dhT=dH)
+        ref = run()
+        torch.cuda.synchronize()
+        g, out = capture(run)
+        for _ in range(3):
+            g.replay()
+            torch.cuda.synchronize()
+            for n, (a, b) in enumerate(zip(out, ref)):
+                if n in (3, 4):                # dg, dbeta
+                    err = ((a - b).abs().max() / b.abs().max()).item()
+                    assert err <= 1e-6, (n, err)
+                else:
+                    assert torch.equal(a, b), n
+            run()                              # eager work between replays
+            torch.cuda.synchronize()

@@ -193,7 +193,8 @@ def make_cotangents(seed, x, dhT_std=1.0):
     N = x.B if x.cu_seqlens is None else len(x.cu_seqlens) - 1
     dhT = None
     if dhT_std > 0:
-        dhT = rng.standard_normal((N, x.H, x.K, x.V), dtype=np.float32) * np.float32(dhT_std)
+        H = x.v.shape[2]                       # value (state) heads
+        dhT = rng.standard_normal((N, H, x.K, x.V), dtype=np.float32) * np.float32(dhT_std)
     return do, dhT
 
 
