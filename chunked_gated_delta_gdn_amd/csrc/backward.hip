@@ -92,14 +92,17 @@ __device__ __forceinline__ void load_cumdecay(float *sG, float *sEg, float *sEk,
     __syncthreads();
 }
 
-// Adds x, summed over the N consecutive lanes that share `row`, to dst[row]
-// (N a power of two; every lane of the wave must call it).
+// Adds x, summed over the N consecutive lanes that share `row`, to slot[row],
+// where slot is the calling wave's own array: the first of those lanes writes
+// it, so a (wave, row) pair must have one writing lane per phase.  Partial
+// sums are combined later in a fixed order, so the result does not depend on
+// timing (N a power of two; every lane of the wave must call it).
 template <int N>
-__device__ __forceinline__ void add_row(float *dst, int row, float x) {
+__device__ __forceinline__ void put_row(float *slot, int row, float x) {
     constexpr int W = N < 64 ? N : 64;
 #pragma unroll
     for (int off = W / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    if ((threadIdx.x & (W - 1)) == 0) atomicAdd(&dst[row], x);
+    if ((threadIdx.x & (W - 1)) == 0) slot[row] += x;
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -704,7 +707,8 @@ template <typename T, int K, int V, int C, int NT>
 __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     constexpr int VP = V + 1, CP = C + 1;
     static_assert((C * C) % NT == 0 && (C * K) % NT == 0 && (C * V) % NT == 0 &&
-                  (K * C) % NT == 0, "uniform trip counts (add_row needs whole waves)");
+                  (K * C) % NT == 0 && 2 * C <= NT, "uniform trip counts (put_row needs whole waves)");
+    constexpr int NW = NT / 64;
     static_assert(C * CP <= C * VP, "Z fits where delta was");
     __shared__ float bDZ[C * VP];               // delta (read by dattn), then Z = dT T^T
     __shared__ float bdD[C * VP];               // ddelta
@@ -713,7 +717,12 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     __shared__ float bY[C * CP];                // dT^T, then dA
     __shared__ float bW[K * CP];                // dw^T
     float *const bD = bDZ, *const bZ = bDZ;
-    __shared__ float sG[C], sEg[C], sEk[C], sb[C], sdG[C], sdb[C];
+    __shared__ float sG[C], sEg[C], sEk[C], sb[C];
+    // dG and dbeta of the chunk's rows: per-wave partial sums (sPw, sBw), the
+    // extra terms of the last row (sLast), and the row and column sums of the
+    // C x C terms (sRowA, sColA, sRowB)
+    __shared__ float sPw[NW * C], sBw[NW * C], sLast[NW], sRowA[C], sColA[C], sRowB[C];
+    const int wave = threadIdx.x >> 6;
     const int tid = threadIdx.x, H = a.H;
     const int h = blockIdx.x % H;
     const int64_t chunk = blockIdx.x / H;
@@ -747,9 +756,12 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
         for (int e = tid; e < C * C; e += NT) bT[(e / C) * CP + e % C] = Tm[e];
         if (tid < C) {
             sb[tid] = tid < L ? a.beta[(tc + tid) * H + h] : 0.f;
-            sdG[tid] = 0.f;
-            sdb[tid] = 0.f;
         }
+        for (int e = tid; e < NW * C; e += NT) {
+            sPw[e] = 0.f;
+            sBw[e] = 0.f;
+        }
+        if (tid < NW) sLast[tid] = 0.f;
     }
     load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);   // (synchronises)
 
@@ -954,7 +966,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
                     Elem<T>::store(a.dv, (tc + r) * rowV + h * V + j, sb[r] * acc[tr][e]);
                     part = acc[tr][e] * vx(r, j);
                 }
-                add_row<16>(sdb, r, part);
+                put_row<16>(sBw + wave * C, r, part);
             }
     } else {
         // dv = diag(beta) T^T ddelta;  dbeta += (T^T ddelta) . v
@@ -967,19 +979,30 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
                 Elem<T>::store(a.dv, (tc + r) * rowV + h * V + j, sb[r] * dvb);
                 part = dvb * vx(r, j);
             }
-            add_row<V>(sdb, r, part);
+            put_row<V>(sBw + wave * C, r, part);
         }
     }
-    // attn and A through the decay: dG_r += e, dG_s -= e;  dbeta from A
-    for (int o = tid; o < C * C; o += NT) {
-        const int r = o / C, s = o % C;
-        float ea = 0.f, eA = 0.f;
-        if (s <= r) ea = bX[r * CP + s] * attn[o];
-        if (s < r) eA = bY[r * CP + s] * Ak[o];
-        const float e = ea + sb[r] * eA;
-        if (e != 0.f) atomicAdd(&sdG[s], -e);
-        add_row<C>(sdG, r, e);
-        add_row<C>(sdb, r, eA);
+    // attn and A through the decay: with e = dattn attn + beta_r dA Ak (the
+    // raw gradient matrices), dG_r += e(r, s) and dG_s -= e(r, s); dbeta_r += dA Ak.
+    // One thread sums each row and each column, in order.
+    if (tid < C) {
+        const int r = tid;
+        float re = 0.f, rb = 0.f;
+        for (int s2 = 0; s2 <= r; ++s2) {
+            const float eA = s2 < r ? bY[r * CP + s2] * Ak[r * C + s2] : 0.f;
+            re += bX[r * CP + s2] * attn[r * C + s2] + sb[r] * eA;
+            rb += eA;
+        }
+        sRowA[r] = re;
+        sRowB[r] = rb;
+    } else if (tid < 2 * C) {
+        const int s2 = tid - C;
+        float ce = 0.f;
+        for (int r = s2; r < C; ++r) {
+            const float eA = s2 < r ? bY[r * CP + s2] * Ak[r * C + s2] : 0.f;
+            ce += bX[r * CP + s2] * attn[r * C + s2] + sb[r] * eA;
+        }
+        sColA[s2] = ce;
     }
     __syncthreads();
     // fold the decay in once: bX <- dattn (.) D,  bY <- dA (.) beta_r D  (= dKK)
@@ -1051,6 +1074,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
             }
         }
         // lane holds rows 16 tr + 4 lg + e of column i
+        float pdl = 0.f;   // this lane's part of the last row's k_tilde term
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr) {
 #pragma unroll
@@ -1066,11 +1090,12 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
                     pd = er * dkt[tr][e] * kri;
                     pk = eG * dkb[tr][e] * kri;
                 }
-                add_row<16>(sdG, r, pg);
-                add_row<16>(sdG, C - 1, pd);
-                add_row<16>(sdb, r, pk);
+                put_row<16>(sPw + wave * C, r, pg);
+                put_row<16>(sBw + wave * C, r, pk);
+                pdl += pd;
             }
         }
+        put_row<64>(sLast, wave, pdl);
     } else {
         // dq and dk: C x K outputs, tiles of QR rows x QW consecutive columns
         constexpr int QW = K >= 128 ? 4 : 2;
@@ -1123,6 +1148,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
                 }
             }
         }
+        float pdl = 0.f;   // this lane's part of the last row's k_tilde term
 #pragma unroll
         for (int m = 0; m < QR; ++m) {
             const int r = r0 + m;
@@ -1140,26 +1166,35 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
                     pk += eG * dkb[m][n] * kri;
                 }
             }
-            add_row<QG>(sdG, r, pg);
-            add_row<QG>(sdG, C - 1, pd);
-            add_row<QG>(sdb, r, pk);
+            put_row<QG>(sPw + wave * C, r, pg);
+            put_row<QG>(sBw + wave * C, r, pk);
+            pdl += pd;
         }
+        put_row<64>(sLast, wave, pdl);
     }
     // gamma: dG_last += gamma <h, dh>
     {
         float x = 0.f;
 #pragma unroll 4
         for (int e = tid; e < K * V; e += NT) x = fmaf(hsT[e], dhsT[e], x);
-        add_row<64>(sdG, C - 1, sEg[C - 1] * x);
+        put_row<64>(sLast, wave, sEg[C - 1] * x);
     }
     __syncthreads();
     if (tid == 0) {
+        float last = 0.f;
+        for (int w = 0; w < NW; ++w) last += sLast[w];
         float acc = 0.f;
         for (int r = C - 1; r >= 0; --r) {
-            acc += sdG[r];
+            float dG = sRowA[r] - sColA[r], db = sRowB[r];
+            for (int w = 0; w < NW; ++w) {
+                dG += sPw[w * C + r];
+                db += sBw[w * C + r];
+            }
+            if (r == C - 1) dG += last;
+            acc += dG;
             if (r < L) {
                 a.dg[(tc + r) * H + h] = acc;
-                a.dbeta[(tc + r) * H + h] = sdb[r];
+                a.dbeta[(tc + r) * H + h] = db;
             }
         }
     }

@@ -176,3 +176,15 @@ def test_backward_bench_workloads_sampled_heads(wl, heads):
         e = rel_err(g_[:, hs] if n == "dh0" else g_[:, :, hs], r)
         say(f"  {n}: {e:.3e}")
         assert e <= TOL[x.dtype], (n, e)
+
+
+def test_backward_is_deterministic():
+    """Two calls on the same inputs give the same bits: every reduction (dg and
+    dbeta included) runs in a fixed order, none through floating-point atomics."""
+    x = make_inputs(48, 1, 1000, 4, 128, 128, 64, "bf16", h0_std=0.02, decay="slow", name="bwd-det")
+    do, dhT = make_cotangents(49, x)
+    say("backward: determinism")
+    a = gpu_grads(x, do, dhT)
+    b = gpu_grads(x, do, dhT)
+    for n, u, v in zip(NAMES, a, b):
+        np.testing.assert_array_equal(u, v, err_msg=n)

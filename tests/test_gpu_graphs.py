@@ -90,9 +90,7 @@ def test_decode_steps_in_a_graph():
 
 def test_backward_in_a_graph():
     """gdn_backward (four kernels, grouped key heads: five) captured once; every
-    replay reproduces the eager dq, dk, dv, dh0 bit for bit.  dg and dbeta are
-    summed per chunk with LDS float atomics, whose order varies from run to run
-    (eager runs included), so they agree to rounding."""
+    replay reproduces the eager gradients bit for bit."""
     from workloads import make_cotangents
     for Hk in (4, 2):
         x = workload(1, H=4, S=700, decay="slow")
@@ -109,10 +107,6 @@ def test_backward_in_a_graph():
             g.replay()
             torch.cuda.synchronize()
             for n, (a, b) in enumerate(zip(out, ref)):
-                if n in (3, 4):                # dg, dbeta
-                    err = ((a - b).abs().max() / b.abs().max()).item()
-                    assert err <= 1e-6, (n, err)
-                else:
-                    assert torch.equal(a, b), n
+                assert torch.equal(a, b), n
             run()                              # eager work between replays
             torch.cuda.synchronize()
