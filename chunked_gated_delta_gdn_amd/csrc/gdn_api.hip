@@ -648,13 +648,16 @@ static size_t backward_ws_per_chunk(const gdn_problem *p) {
                             (size_t)2 * p->K * p->V);
 }
 
+// The backward pass runs every sequence as one chain.  Segments and pieces
+// only schedule the forward (its result does not depend on them), so a problem
+// that carries them is validated as given and then run without them.
 static gdn_status backward_problem(const gdn_problem *p, Resolved &r) {
     GDN_TRY(resolve(p, r));
-    if (p->n_seqs == 0 && p->n_segments != 1)
-        return fail(GDN_EUNSUPPORTED, "the backward pass runs whole sequences (n_segments must be 1)");
-    if (p->max_piece_chunks != 0)
-        return fail(GDN_EUNSUPPORTED, "the backward pass runs whole sequences (max_piece_chunks must be 0)");
-    return GDN_OK;
+    gdn_problem whole = *p;
+    whole.n_segments = 1;
+    whole.seg_starts = nullptr;
+    whole.max_piece_chunks = 0;
+    return resolve(&whole, r);
 }
 
 static bool grouped(const gdn_problem *p) { return p->H_qk != 0 && p->H_qk != p->H; }

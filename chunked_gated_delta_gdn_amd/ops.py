@@ -592,9 +592,9 @@ def backward(q, k, v, g, beta, do, h0=None, dhT=None, chunk_size=64, cu_seqlens=
 
 class _ChunkGatedDeltaRule(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, h0, chunk_size, cu_seqlens):
+    def forward(ctx, q, k, v, g, beta, h0, chunk_size, cu_seqlens, n_segments):
         o, hT = forward(q, k, v, g, beta, h0=h0, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
-                        max_piece_chunks=0 if cu_seqlens is not None else None)
+                        n_segments=n_segments)
         ctx.save_for_backward(q, k, v, g, beta, h0)
         ctx.chunk_size, ctx.cu_seqlens = chunk_size, cu_seqlens
         return o, hT
@@ -606,11 +606,12 @@ class _ChunkGatedDeltaRule(torch.autograd.Function):
             q, k, v, g, beta, do.contiguous(), h0=h0,
             dhT=None if dhT is None else dhT.contiguous(), chunk_size=ctx.chunk_size,
             cu_seqlens=ctx.cu_seqlens, want_dh0=h0 is not None and ctx.needs_input_grad[5])
-        return dq, dk, dv, dg, dbeta, dh0, None, None
+        return dq, dk, dv, dg, dbeta, dh0, None, None, None
 
 
-def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None):
+def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segments=1):
     """Differentiable forward: (o, final state), with ``backward`` as its
-    gradient (torch.autograd).  Shapes as ``forward`` (q, k may have fewer heads
-    than v: grouped key heads)."""
-    return _ChunkGatedDeltaRule.apply(q, k, v, g, beta, h0, chunk_size, cu_seqlens)
+    gradient (torch.autograd).  Shapes and the forward's schedule (segments;
+    packed batches cut into pieces) as ``forward``; q, k may have fewer heads
+    than v (grouped key heads)."""
+    return _ChunkGatedDeltaRule.apply(q, k, v, g, beta, h0, chunk_size, cu_seqlens, n_segments)

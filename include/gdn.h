@@ -277,8 +277,9 @@ gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t V, int32_t dtype, float eps, 
 
 /*
  * gdn_backward -- gradients of a loss l(o, hT) through the forward of the
- * problem (batch or packed, grouped key heads included; n_segments == 1 and
- * max_piece_chunks == 0: a sequence runs as one chain), given
+ * problem (batch or packed, grouped key heads included; segments and
+ * pieces, which only schedule the forward, are validated and then ignored:
+ * every sequence runs as one chain), given
  * dout = dl/do [same layout as o, `dtype`] and dhT = dl/dhT
  * ([N,H,K,V] fp32, nullable = zero).  The MaxText PR "Add context
  * parallelism to the Gated Delta Net" tests a backward pass against the

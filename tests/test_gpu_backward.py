@@ -188,3 +188,35 @@ def test_backward_is_deterministic():
     b = gpu_grads(x, do, dhT)
     for n, u, v in zip(NAMES, a, b):
         np.testing.assert_array_equal(u, v, err_msg=n)
+
+
+@pytest.mark.parametrize("mode", ["segments", "packed_pieces"])
+def test_autograd_wrapper_with_forward_schedules(mode):
+    """The differentiable forward with segments or a packed batch cut into pieces:
+    the schedule changes the forward's launches, not its result, and the backward
+    (whole sequences) gives the oracle's gradients."""
+    if mode == "segments":
+        x = make_inputs(50, 1, 700, 2, 128, 128, 64, "bf16", h0_std=0.02, decay="slow", name="bwd-seg")
+        kw = dict(n_segments=3)
+    else:
+        x = make_packed_inputs(51, 3, 900, 2, 128, 128, 64, "bf16", h0_std=0.02, median=300,
+                               pad_to_chunk=False, name="bwd-pieces")
+        x.meta = {}
+        kw = dict(cu_seqlens=[int(c) for c in x.cu_seqlens])
+    do, dhT = make_cotangents(52, x)
+    say(f"backward: autograd with {mode}")
+    bf = torch.bfloat16
+    q, k, v = (to_dev(a, bf).requires_grad_() for a in (x.q, x.k, x.v))
+    g, beta, h0 = (to_dev(a).requires_grad_() for a in (x.g, x.beta, x.h0))
+    o, hT = gdn.chunk_gated_delta_rule(q, k, v, g, beta, h0, chunk_size=64, **kw)
+    loss = (o.float() * to_dev(do)).sum() + (hT * to_dev(dhT)).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    ref = oracle_grads(x, do, dhT)
+    for n, t, r in zip(NAMES, (q, k, v, g, beta, h0), ref):
+        gr = t.grad.float().cpu().numpy()
+        if x.cu_seqlens is not None and n != "dh0":
+            gr = gr[0]
+        e = rel_err(gr, r)
+        say(f"  {n}: {e:.3e}")
+        assert e <= TOL["bf16"], (n, e)

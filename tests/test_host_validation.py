@@ -256,7 +256,9 @@ def test_backward_validation():
     p = prob()                                    # B1 S256 H2 K32 V32 C16 fp32
     ws = b.gdn_backward_workspace_bytes(p)
     assert ws == 16 * 2 * 4 * (3 * 16 * 16 + 16 * 32 + 3 * 16 * 32 + 2 * 32 * 32)
-    assert b.gdn_backward_workspace_bytes(prob(n_segments=2)) == 0
+    # segments and pieces only schedule the forward: the backward runs whole sequences
+    assert b.gdn_backward_workspace_bytes(prob(n_segments=2)) == ws
+    assert b.gdn_backward_workspace_bytes(prob(n_segments=2, seg_starts=[0, 100])) == 0   # invalid as given
     # grouped key heads add fp32 dq, dk rows of every value head
     wg = b.gdn_backward_workspace_bytes(prob(H=4, H_qk=2))
     assert wg == 2 * ws + 2 * 256 * 4 * 32 * 4
@@ -270,9 +272,8 @@ def test_backward_validation():
         a.update(over)
         return lib.gdn_backward(ref(pp), *[a[n] for n in names], over.get("ws_bytes", ws), None)
 
-    assert call(prob(n_segments=2)) == b.GDN_EUNSUPPORTED
     assert call(prob(H=4, H_qk=2), ws_bytes=wg - 1) == b.GDN_EINVAL
-    assert call(prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=2)) == b.GDN_EUNSUPPORTED
+    assert call(prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=-1)) == b.GDN_EINVAL
     assert call(p, ws_bytes=ws - 1) == b.GDN_EINVAL
     assert call(p, q=None) == b.GDN_EINVAL
     assert call(p, dout=None) == b.GDN_EINVAL
