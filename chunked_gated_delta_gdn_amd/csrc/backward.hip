@@ -256,8 +256,9 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- 2. states
-// A chunk's operands in registers, loaded one chunk ahead of their use.
-template <int C, int NT>
+// First token tc and real length L of chunk c of the chain [t0, t1).  The
+// scans load a chunk's operands into registers one chunk ahead of their use.
+template <int C>
 __device__ __forceinline__ void chunk_rows(int64_t t0, int64_t t1, int64_t c, int &L, int64_t &tc) {
     tc = t0 + c * C;
     L = (int)((t1 - tc) < C ? (t1 - tc) : C);
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
     auto fetch = [&](int64_t c) {
         int L;
         int64_t tc;
-        chunk_rows<C, NT>(sp.t0, sp.t1, c, L, tc);
+        chunk_rows<C>(sp.t0, sp.t1, c, L, tc);
         const float *w = a.w + ((sp.chunk0 + c) * H + h) * C * K;
 #pragma unroll
         for (int m = 0; m < LPT; ++m) {
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
     auto fetch = [&](int64_t c) {
         int L;
         int64_t tc;
-        chunk_rows<C, NT>(sp.t0, sp.t1, c, L, tc);
+        chunk_rows<C>(sp.t0, sp.t1, c, L, tc);
         const int64_t ch = (sp.chunk0 + c) * H + h;
         const float *w = a.w + ch * C * K, *attn = a.attn + ch * C * C;
 #pragma unroll
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
     auto fetch = [&](int64_t c) {
         int L;
         int64_t tc;
-        chunk_rows<C, NT>(sp.t0, sp.t1, c, L, tc);
+        chunk_rows<C>(sp.t0, sp.t1, c, L, tc);
         const int64_t ch = (sp.chunk0 + c) * H + h;
         if (wv < 4) {
             const float *w = a.w + ch * C * K + (16 * wv + li) * K;
@@ -600,7 +601,7 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
     auto fetch = [&](int64_t c) {
         int L;
         int64_t tc;
-        chunk_rows<C, NT>(sp.t0, sp.t1, c, L, tc);
+        chunk_rows<C>(sp.t0, sp.t1, c, L, tc);
         const int64_t ch = (sp.chunk0 + c) * H + h;
         const float *w = a.w + ch * C * K, *attn = a.attn + ch * C * C;
 #pragma unroll
