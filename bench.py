@@ -112,6 +112,46 @@ def measured_traffic(kernel):
     return float(row.group(1))
 
 
+def measured_peaks(torch, dev):
+    """Peaks measured on this GPU, quoted beside the datasheet ones: a dense bf16
+    matrix-core loop (libgdn_probe.so: register operands, no memory traffic) and
+    a 1 GiB device copy (read once, written once), each timed with HIP events
+    over 5 launches after a warm-up."""
+    import ctypes
+    from chunked_gated_delta_gdn_amd import _build
+    lib = ctypes.CDLL(_build.PROBE_LIB)
+    lib.gdn_probe_mfma_bf16.restype = ctypes.c_int32
+    lib.gdn_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    n_blocks = 4 * torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 4096
+    out = torch.empty(n_blocks * 256, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def timed(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    def probe():
+        if lib.gdn_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), n_blocks, iters, stream) != 0:
+            raise RuntimeError("gdn_probe_mfma_bf16 failed")
+    t_m = timed(probe)
+    flops = n_blocks * 4 * 4 * iters * 16 * 16 * 32 * 2
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t_c = timed(lambda: torch.neg(src, out=dst))
+    del src, dst, out
+    return {"bf16_mfma_tflops": flops / t_m / 1e12, "hbm_copy_gbs": 2 * COPY_BYTES / t_c / 1e9,
+            "how": f"bf16 MFMA loop ({n_blocks} workgroups x 4 waves x 4 chains x {iters} "
+                   "v_mfma_f32_16x16x32_bf16); 1 GiB device copy (read + write)"}
+
+
 def copy_calibration(torch):
     """A plain device copy of COPY_BYTES, read once and written once per launch
     (elementwise negation, so it is an ordinary shader kernel that the counters see)."""
@@ -285,6 +325,11 @@ def main():
         "scan_backend": "mfma" if backend == 1 else "valu",
     }
     del seg_step
+    peaks = measured_peaks(torch, dev)
+    result["measured_peaks"] = peaks
+    if roof["bound"] == "mfma":
+        roof["frac_of_measured_peak"] = roof["achieved"] / peaks["bf16_mfma_tflops"]
+    roof["hbm_frac_of_measured_copy"] = nbytes / t_dom / 1e9 / peaks["hbm_copy_gbs"]
 
     # ---------------------------------------------------------------- secondary lines
     extra = {}

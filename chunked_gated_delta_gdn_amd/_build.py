@@ -10,6 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
+PROBE_LIB = os.path.join(PKG, "libgdn_probe.so")   # the benchmark's matrix-core rate probe
 SOURCES = ["gdn_api.hip", "scan_generic.hip", "scan_mfma.hip", "prepare_mfma.hip", "decode.hip",
            "compose.hip", "layers.hip", "backward.hip"]
 
@@ -44,6 +45,10 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    probe = _compile("peak_probe.hip", verbose)
+    tmp = PROBE_LIB + ".tmp"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, probe], check=True)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

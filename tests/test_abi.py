@@ -62,3 +62,18 @@ def test_problem_struct_layout_matches_c(tmp_path):
                                           check=True).stdout.split()]
     assert got[0] == ctypes.sizeof(b.GdnProblem)
     assert got[1:] == [getattr(b.GdnProblem, f).offset for f in fields]
+
+
+def test_probe_library_exports_its_declared_symbol():
+    """The benchmark's matrix-core rate probe (include/gdn_probe.h, libgdn_probe.so)."""
+    import re
+    from chunked_gated_delta_gdn_amd import _build
+    text = open(os.path.join(ROOT, "include", "gdn_probe.h")).read()
+    declared = set(re.findall(r"\b(gdn_probe_\w+)\s*\(", text))
+    assert declared == {"gdn_probe_mfma_bf16"}
+    if not os.path.exists(_build.PROBE_LIB):
+        pytest.skip("libgdn_probe.so not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", _build.PROBE_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    for name in declared:
+        assert re.search(rf"\b{name}\b", out), name
