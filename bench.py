@@ -120,8 +120,9 @@ def measured_peaks(torch, dev):
     import ctypes
     from chunked_gated_delta_gdn_amd import _build
     lib = ctypes.CDLL(_build.PROBE_LIB)
-    lib.gdn_probe_mfma_bf16.restype = ctypes.c_int32
-    lib.gdn_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    for fn in (lib.gdn_probe_mfma_bf16, lib.gdn_probe_mfma_f32):
+        fn.restype = ctypes.c_int32
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     n_blocks = 4 * torch.cuda.get_device_properties(dev).multi_processor_count
     iters = 4096
     out = torch.empty(n_blocks * 256, dtype=torch.float32, device=dev)
@@ -138,18 +139,21 @@ def measured_peaks(torch, dev):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n * 1e-3
 
-    def probe():
-        if lib.gdn_probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), n_blocks, iters, stream) != 0:
-            raise RuntimeError("gdn_probe_mfma_bf16 failed")
-    t_m = timed(probe)
+    def probe(fn):
+        if fn(ctypes.c_void_p(out.data_ptr()), n_blocks, iters, stream) != 0:
+            raise RuntimeError("matrix-core probe failed")
+    t_m = timed(lambda: probe(lib.gdn_probe_mfma_bf16))
+    t_f = timed(lambda: probe(lib.gdn_probe_mfma_f32))
     flops = n_blocks * 4 * 4 * iters * 16 * 16 * 32 * 2
+    flops_f = n_blocks * 4 * 4 * iters * 16 * 16 * 4 * 2
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     t_c = timed(lambda: torch.neg(src, out=dst))
     del src, dst, out
-    return {"bf16_mfma_tflops": flops / t_m / 1e12, "hbm_copy_gbs": 2 * COPY_BYTES / t_c / 1e9,
-            "how": f"bf16 MFMA loop ({n_blocks} workgroups x 4 waves x 4 chains x {iters} "
-                   "v_mfma_f32_16x16x32_bf16); 1 GiB device copy (read + write)"}
+    return {"bf16_mfma_tflops": flops / t_m / 1e12, "f32_mfma_tflops": flops_f / t_f / 1e12,
+            "hbm_copy_gbs": 2 * COPY_BYTES / t_c / 1e9,
+            "how": f"MFMA loops ({n_blocks} workgroups x 4 waves x 4 chains x {iters} "
+                   "v_mfma_f32_16x16x32_bf16, or v_mfma_f32_16x16x4_f32); 1 GiB device copy (read + write)"}
 
 
 def copy_calibration(torch):
@@ -516,7 +520,8 @@ def main():
             extra[name] = {
                 "tokens_per_s": Sb / (ms_b * 1e-3), "ms": ms_b,
                 "roofline": {"bound": "mfma", "achieved": fl / t_b / 1e12, "peak": PEAK_F32_VALU_TFLOPS,
-                             "unit": "TFLOP/s", "frac": fl / t_b / 1e12 / PEAK_F32_VALU_TFLOPS},
+                             "unit": "TFLOP/s", "frac": fl / t_b / 1e12 / PEAK_F32_VALU_TFLOPS,
+                             "frac_of_measured_peak": fl / t_b / 1e12 / peaks["f32_mfma_tflops"]},
             }
             del bq, bk, bv, bg, bb, bh, bdo, bdh
             torch.cuda.empty_cache()

@@ -1,6 +1,6 @@
 /*
  * gdn_probe.h -- measurement helper of the benchmark, not part of the gated
- * delta rule's API: the dense bf16 matrix-core rate of the GPU it runs on, so
+ * delta rule's API: the dense bf16 and fp32 matrix-core rates of the GPU it runs on, so
  * that the benchmark can state fractions of a measured peak next to the
  * datasheet one.  Built as libgdn_probe.so, beside libgdn.so.
  */
@@ -22,6 +22,10 @@ extern "C" {
  * bad arguments, 2 if the launch failed.
  */
 int32_t gdn_probe_mfma_bf16(float *out, int32_t n_blocks, int32_t iters, void *stream);
+
+/* The same with v_mfma_f32_16x16x4_f32 (16*16*4*2 FLOP each): the fp32
+ * matrix-core rate the backward pass's products run at. */
+int32_t gdn_probe_mfma_f32(float *out, int32_t n_blocks, int32_t iters, void *stream);
 
 #ifdef __cplusplus
 }

@@ -70,7 +70,7 @@ def test_probe_library_exports_its_declared_symbol():
     from chunked_gated_delta_gdn_amd import _build
     text = open(os.path.join(ROOT, "include", "gdn_probe.h")).read()
     declared = set(re.findall(r"\b(gdn_probe_\w+)\s*\(", text))
-    assert declared == {"gdn_probe_mfma_bf16"}
+    assert declared == {"gdn_probe_mfma_bf16", "gdn_probe_mfma_f32"}
     if not os.path.exists(_build.PROBE_LIB):
         pytest.skip("libgdn_probe.so not built")
     out = subprocess.run(["nm", "-D", "--defined-only", _build.PROBE_LIB], capture_output=True,
