@@ -441,3 +441,61 @@ def test_silu_and_gated_rmsnorm_closed_forms():
     ref = o * np.sqrt(V) / np.linalg.norm(o, axis=-1, keepdims=True) * w
     np.testing.assert_allclose(oracle.gated_rmsnorm(o, w, eps=0.0), ref, rtol=1e-13)
     np.testing.assert_allclose(oracle.gated_rmsnorm(o, w, z, eps=0.0), ref * z * expit(z), rtol=1e-13)
+
+
+@pytest.mark.parametrize("L", [1, 5, 16])
+def test_chunk_transition_is_one_chunks_affine_map(L):
+    """(M_c, U_c) of one chunk from the chunk form (gamma I - k_tilde^T w,
+    k_tilde^T u) equals the pair the recurrence defines over the same tokens:
+    M by running it from the identity with v = 0, U from the zero state."""
+    rng = np.random.default_rng(40 + L)
+    K, V = 5, 3
+    k = rng.standard_normal((L, K)); k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((L, V))
+    g = -np.log1p(np.exp(rng.standard_normal(L) - 2.0))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(L)))
+    Mc, Uc = oracle.chunk_transition(k, v, g, beta)
+    M, U = oracle.transition_pair(k[None, :, None], v[None, :, None], g[None, :, None], beta[None, :, None])
+    np.testing.assert_allclose(Mc, M[0, 0], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(Uc, U[0, 0], rtol=1e-12, atol=1e-14)
+    # and a state pushed through it equals the recurrence's end state
+    h0 = rng.standard_normal((K, V))
+    _, hT = oracle.forward(np.zeros((1, L, 1, K)), k[None, :, None], v[None, :, None], g[None, :, None],
+                           beta[None, :, None], h0=h0[None, None])
+    np.testing.assert_allclose(Mc @ h0 + Uc, hT[0, 0], rtol=1e-12, atol=1e-14)
+
+
+def test_causal_conv_packed_equals_per_sequence():
+    """The packed conv is the per-sequence conv laid end to end: every
+    sequence, including empty ones and ones shorter than the W - 1 state
+    positions, starts from its own state row and leaves its own final state
+    (bit-exact, the same fp64 operations in the same order)."""
+    rng = np.random.default_rng(7)
+    D, W = 6, 4
+    lens = [5, 0, 1, 2, 9, 0, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    x = rng.standard_normal((int(cu[-1]), D))
+    w = rng.standard_normal((D, W))
+    st = rng.standard_normal((len(lens), D, W - 1))
+    for act in ("silu", "none"):
+        y, s = oracle.causal_conv1d_packed(x, w, cu, st, activation=act)
+        for n in range(len(lens)):
+            a, b = int(cu[n]), int(cu[n + 1])
+            yn, sn = oracle.causal_conv1d(x[a:b], w, st[n], activation=act)
+            assert np.array_equal(y[a:b], yn) and np.array_equal(s[n], sn)
+        # an empty sequence hands its state through unchanged; a one-token
+        # sequence shifts it by one position
+        assert np.array_equal(s[1], st[1]) and np.array_equal(s[5], st[5])
+        assert np.array_equal(s[2][:, :-1], st[2][:, 1:]) and np.array_equal(s[2][:, -1], x[cu[2]])
+        # the first output of a sequence reads its own state, not the tokens
+        # of the sequence before it (taps (1, 0, 0, 0) pick the oldest position)
+        shift = np.zeros((D, W)); shift[:, 0] = 1
+        ys, _ = oracle.causal_conv1d_packed(x, shift, cu, st, activation="none")
+        assert np.array_equal(ys[cu[4]], st[4][:, 0])
+    # no state: zeros before every sequence start
+    y0, s0 = oracle.causal_conv1d_packed(x, w, cu, None, activation="none")
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        yn, sn = oracle.causal_conv1d(x[a:b], w, None, activation="none")
+        assert np.array_equal(y0[a:b], yn) and np.array_equal(s0[n], sn)
+    assert np.array_equal(s0[1], np.zeros((D, W - 1)))
