@@ -3,7 +3,8 @@
 Argument marshalling only: every function here forwards plain integers and
 device addresses to the entry point of the same name and turns a non-zero
 status into an exception (``ValueError`` for invalid, unsupported or
-out-of-order arguments, ``RuntimeError`` for launch failures).  Nothing is
+out-of-order arguments and short workspaces, ``RuntimeError`` for launch
+failures).  Nothing is
 computed on the host and there is no fallback: if the library is missing the
 first call raises.
 """
@@ -13,7 +14,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libgdn.so")
 
-GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EORDER, GDN_ELAUNCH = range(5)
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EORDER, GDN_ELAUNCH, GDN_EWORKSPACE = range(6)
 GDN_F32, GDN_BF16 = 0, 1
 GDN_SCAN_EMIT, GDN_SCAN_CARRY, GDN_SCAN_HEAD_EMIT_CARRY, GDN_SCAN_TAIL_EMIT = 0, 1, 2, 3
 GDN_MAX_SEQS, GDN_MAX_SEGMENTS = 256, 64
@@ -85,8 +86,8 @@ def library():
             "gdn_num_pieces": (_i32, [P]),
             "gdn_wy_workspace_bytes": (ctypes.c_size_t, [P]),
             "gdn_segment_workspace_bytes": (ctypes.c_size_t, [P]),
-            "gdn_chunk_prepare": (_i32, [P, _vp, _vp, _vp, _vp, _vp, _vp]),
-            "gdn_scan": (_i32, [P, _i32] + [_vp] * 12),
+            "gdn_chunk_prepare": (_i32, [P, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+            "gdn_scan": (_i32, [P, _i32] + [_vp] * 6 + [ctypes.c_size_t] + [_vp] * 6),
             "gdn_segment_compose": (_i32, [_i32] * 5 + [_vp] * 6),
             "gdn_piece_compose": (_i32, [P, _i32] + [_vp] * 6),
             "gdn_decode_step": (_i32, [_i32] * 6 + [_vp] * 8),
@@ -139,13 +140,13 @@ def gdn_segment_workspace_bytes(problem):
     return int(library().gdn_segment_workspace_bytes(ctypes.byref(problem)))
 
 
-def gdn_chunk_prepare(problem, k, v, g, beta, wy, stream=0):
-    _check(library().gdn_chunk_prepare(ctypes.byref(problem), k, v, g, beta, wy, stream),
+def gdn_chunk_prepare(problem, k, v, g, beta, wy, wy_bytes, stream=0):
+    _check(library().gdn_chunk_prepare(ctypes.byref(problem), k, v, g, beta, wy, wy_bytes, stream),
            "gdn_chunk_prepare")
 
 
-def gdn_scan(problem, mode, q, k, v, g, beta, wy, h_in, o, h_out, M_out, U_out, stream=0):
-    _check(library().gdn_scan(ctypes.byref(problem), mode, q, k, v, g, beta, wy, h_in, o, h_out,
+def gdn_scan(problem, mode, q, k, v, g, beta, wy, wy_bytes, h_in, o, h_out, M_out, U_out, stream=0):
+    _check(library().gdn_scan(ctypes.byref(problem), mode, q, k, v, g, beta, wy, wy_bytes, h_in, o, h_out,
                               M_out, U_out, stream), "gdn_scan")
 
 

@@ -207,6 +207,17 @@ gdn_status resolve(const gdn_problem *p, Resolved &out) {
     const int64_t wgs = (int64_t)out.P * p->H * (p->K + p->V);
     if (wgs > 0x7fffffffLL || out.n_chunks * p->H > 0x7fffffffLL)
         return fail(GDN_EUNSUPPORTED, "problem too large for one launch");
+    // The kernels address the rows of one chunk through a buffer resource at the
+    // chunk's first row with 32-bit byte offsets (and 2^31 - 1 records), so C rows
+    // of q, k (H_qk heads) and of v, o (H heads) must span less than 2 GiB.
+    {
+        const int64_t es = p->dtype == GDN_F32 ? 4 : 2;
+        const int64_t Hk = p->H_qk > 0 ? p->H_qk : p->H;
+        const int64_t span = (int64_t)C * std::max(Hk * p->K, (int64_t)p->H * p->V) * es;
+        if (span >= 0x80000000LL || (int64_t)C * p->H * 4 >= 0x80000000LL)
+            return fail(GDN_EUNSUPPORTED, "%d token rows of the inputs span %lld bytes, at or above the "
+                                          "2 GiB a chunk may span", C, (long long)span);
+    }
     return GDN_OK;
 }
 
@@ -283,6 +294,16 @@ size_t gdn_wy_workspace_bytes(const gdn_problem *p) {
     return (size_t)r.n_chunks * p->H * p->C * (p->K + p->V) * elem_size(p->dtype);
 }
 
+// A WY workspace given to gdn_chunk_prepare or gdn_scan must hold the whole
+// problem's factors.
+static gdn_status check_wy(const gdn_problem *p, const Resolved &r, const void *wy, size_t wy_bytes) {
+    if (!wy) return GDN_OK;
+    const size_t need = (size_t)r.n_chunks * p->H * p->C * (p->K + p->V) * elem_size(p->dtype);
+    if (wy_bytes < need)
+        return fail(GDN_EWORKSPACE, "WY workspace of %zu bytes, the problem needs %zu", wy_bytes, need);
+    return GDN_OK;
+}
+
 size_t gdn_segment_workspace_bytes(const gdn_problem *p) {
     Resolved r;
     if (resolve(p, r) != GDN_OK) return 0;
@@ -290,7 +311,7 @@ size_t gdn_segment_workspace_bytes(const gdn_problem *p) {
 }
 
 gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
-                             const float *g, const float *beta, void *wy, void *stream) {
+                             const float *g, const float *beta, void *wy, size_t wy_bytes, void *stream) {
     g_err[0] = 0;
     Resolved r;
     GDN_TRY(resolve(p, r));
@@ -300,6 +321,7 @@ gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
     GDN_TRY(check_ptr(g, "g", any));
     GDN_TRY(check_ptr(beta, "beta", any));
     GDN_TRY(check_ptr(wy, "wy", r.n_chunks > 0));
+    GDN_TRY(check_wy(p, r, wy, wy_bytes));
     if (r.n_chunks == 0) return GDN_OK;
     PrepArgs a;
     a.k = k;
@@ -320,7 +342,8 @@ gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
 // GDN_SCAN_HEAD_EMIT_CARRY: segment 0 (first piece) of every sequence emitted, the
 // others carried, in one launch on the matrix-core path.
 static gdn_status scan_head(const gdn_problem *p, Resolved &r, const void *q, const void *k, const void *v,
-                            const float *g, const float *beta, const void *wy, const float *h_in, void *o,
+                            const float *g, const float *beta, const void *wy, size_t wy_bytes,
+                            const float *h_in, void *o,
                             float *h_out, float *M_out, float *U_out, void *stream) {
     if (!r.ct.packed && r.R < 2)
         return fail(GDN_EINVAL, "GDN_SCAN_HEAD_EMIT_CARRY needs n_segments >= 2 in batch mode (got %d)", r.R);
@@ -333,6 +356,7 @@ static gdn_status scan_head(const gdn_problem *p, Resolved &r, const void *q, co
     GDN_TRY(check_ptr(g, "g", any));
     GDN_TRY(check_ptr(beta, "beta", any));
     GDN_TRY(check_ptr(wy, "wy", false));
+    GDN_TRY(check_wy(p, r, wy, wy_bytes));
     GDN_TRY(check_ptr(o, "o", any));
     GDN_TRY(check_ptr(h_in, "h_in", false));
     GDN_TRY(check_ptr(h_out, "h_out", false));
@@ -370,7 +394,7 @@ static gdn_status scan_head(const gdn_problem *p, Resolved &r, const void *q, co
 }
 
 gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const void *k,
-                    const void *v, const float *g, const float *beta, const void *wy,
+                    const void *v, const float *g, const float *beta, const void *wy, size_t wy_bytes,
                     const float *h_in, void *o, float *h_out, float *M_out, float *U_out,
                     void *stream) {
     g_err[0] = 0;
@@ -379,8 +403,8 @@ gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const voi
     if (mode != GDN_SCAN_EMIT && mode != GDN_SCAN_CARRY && mode != GDN_SCAN_HEAD_EMIT_CARRY &&
         mode != GDN_SCAN_TAIL_EMIT)
         return fail(GDN_EINVAL, "unknown scan mode %d", mode);
-    if (mode == GDN_SCAN_HEAD_EMIT_CARRY) return scan_head(p, r, q, k, v, g, beta, wy, h_in, o, h_out, M_out, U_out,
-                                                           stream);
+    if (mode == GDN_SCAN_HEAD_EMIT_CARRY)
+        return scan_head(p, r, q, k, v, g, beta, wy, wy_bytes, h_in, o, h_out, M_out, U_out, stream);
     if (mode == GDN_SCAN_TAIL_EMIT && !r.ct.packed)
         return fail(GDN_EINVAL, "GDN_SCAN_TAIL_EMIT needs a packed problem (batch callers slice the tensors)");
     const bool carry = mode == GDN_SCAN_CARRY;
@@ -392,6 +416,7 @@ gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const voi
     GDN_TRY(check_ptr(g, "g", any));
     GDN_TRY(check_ptr(beta, "beta", any));
     GDN_TRY(check_ptr(wy, "wy", false));
+    GDN_TRY(check_wy(p, r, wy, wy_bytes));
     if (carry) {
         GDN_TRY(check_ptr(M_out, "M_out", true));
         GDN_TRY(check_ptr(U_out, "U_out", true));
@@ -700,7 +725,7 @@ gdn_status gdn_backward(const gdn_problem *p, const void *q, const void *k, cons
     const size_t need = backward_ws_bytes(p, r);
     GDN_TRY(check_ptr(workspace, "workspace", need > 0));
     if (workspace_bytes < need)
-        return fail(GDN_EINVAL, "backward workspace %zu bytes < %zu needed", workspace_bytes, need);
+        return fail(GDN_EWORKSPACE, "backward workspace %zu bytes < %zu needed", workspace_bytes, need);
     const size_t es = elem_size(p->dtype);
     const int Hk = p->H_qk > 0 ? p->H_qk : p->H;
     const size_t nqk = (size_t)r.T * Hk * p->K * es, nv = (size_t)r.T * p->H * p->V * es;
@@ -777,6 +802,7 @@ const char *gdn_status_string(int32_t status) {
         case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED: shape or dtype not supported";
         case GDN_EORDER: return "GDN_EORDER: segments or sequences not contiguous and in order";
         case GDN_ELAUNCH: return "GDN_ELAUNCH: kernel launch failed";
+        case GDN_EWORKSPACE: return "GDN_EWORKSPACE: workspace smaller than the problem needs";
         default: return "unknown gdn_status";
     }
 }

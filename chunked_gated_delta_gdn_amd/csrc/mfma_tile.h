@@ -233,19 +233,31 @@ __device__ __forceinline__ void gram_to_ab(KT kt, const float *G2, const float *
 // Inverses of diagonal 16 x 16 blocks of T' = (I + A0 diag(beta))^{-1}, for
 // the NBLK blocks listed in blk (compile-time constants), from the raw Gram
 // blocks of gram_to_ab.  With N = (A0 diag(beta))_aa, strictly lower
-// triangular, T'_aa = (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8)
-// (N^16 = 0).  P accumulates in B layout, P <- P + N^(2^k) P; the powers are
-// formed in both layouts (N^2 = N N in B layout, (N^2)^T = N^T N^T is the A
-// layout).  Each stage runs over all listed blocks before the next, so their
-// dependent chains interleave.  Out: P[j] (bf16 B layout of T'_aa, which as an
-// A operand is T'_aa^T) and Qf[j] (fp32 A layout of T'_aa, by an identity
-// product).
+// triangular, the inverse is built by recursive doubling of the block size:
+// T_1 = I - N restricted to the 2 x 2 diagonal blocks (exact), then for
+// l = 2, 4, 8, with B_l the part of N that joins two l x l diagonal blocks into
+// one 2l x 2l block,
+//   T_{2l} = T_l - T_l B_l T_l,
+// which is the block formula [[A, 0], [B, D]]^{-1} = [[A^-1, 0],
+// [-D^-1 B A^-1, D^-1]] applied to every 2l block at once.  Every product
+// involves entries of the inverse itself, so nothing grows beyond it; the
+// expansion (I - N)(I + N^2)(I + N^4)(I + N^8) does the same in exact
+// arithmetic, but its powers of N reach binomial sizes (6435 for a key
+// repeated over 16 tokens with beta = 1, g = 0), and rounding them to bf16
+// loses the result.  T is kept in fp32 in both operand layouts (B layout TB:
+// lane (j, g) holds T[4g+e][j]; A layout TA: lane (i, g) holds T[i][4g+e]):
+//   W = B_l T (A = B_l, B = T);  T <- T - T W (A = T, B = W);
+//   T^T <- T^T - W^T T^T (A = W^T, whose A layout is W's B layout; B = T^T,
+//   whose B layout is T's A layout).
+// Each level runs over all listed blocks before the next, so their dependent
+// chains interleave.  Out: P[j] (bf16 B layout of T'_aa, which as an A
+// operand is T'_aa^T) and Qf[j] (fp32 A layout of T'_aa).
 template <int NBLK>
 __device__ __forceinline__ void diag_inverse(const int (&blk)[NBLK], const uint2 (*ab)[64], const float *G2,
                                              const float *Bv, int lane, bf16x4 (&P)[NBLK], f32x4 (&Qf)[NBLK]) {
     const int li = lane & 15, lg = lane >> 4;
-    bf16x4 NB[NBLK], NA[NBLK];
-    f32x4 p[NBLK];   // I - N, from N before rounding
+    f32x4 TB[NBLK], TA[NBLK];
+    bf16x4 BL[3][NBLK];   // A layout of B_l, l = 2, 4, 8
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) {
         const int aa = blk[j];
@@ -255,46 +267,45 @@ __device__ __forceinline__ void diag_inverse(const int (&blk)[NBLK], const uint2
         // raw k_{16a+4g+e} . k_{16a+j} (symmetric): B layout entry (r = 16a+4g+e,
         // s = 16a+j) if s < r, A layout entry (r' = 16a+j, s' = 16a+4g+e) if s' < r'
         const bf16x4 kk4 = __builtin_bit_cast(bf16x4, ab[6 + aa][lane]);
-        f32x4 vb, va;
+        f32x4 vb, va, bl[3];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int x = 4 * lg + e;
-            const float ex = ex2(-fabsf(Gr4[e] - Gc));
+            // exp(G_r - G_s) of the one layout entry that is kept (r > s), with
+            // its sign, so that increasing decays (g > 0) stay exact
+            const float ex = ex2(li < x ? Gr4[e] - Gc : Gc - Gr4[e]);
             const float kv = (float)kk4[e];
             vb[e] = (li < x) ? Bc * ex * kv : 0.f;
             va[e] = (x < li) ? Br4[e] * ex * kv : 0.f;
+            const float d = (x == li) ? 1.f : 0.f;
+            const bool same2 = (li >> 1) == (x >> 1);
+            TB[j][e] = d - (same2 ? vb[e] : 0.f);
+            TA[j][e] = d - (same2 ? va[e] : 0.f);
+#pragma unroll
+            for (int lv = 0; lv < 3; ++lv)
+                bl[lv][e] = ((li >> (lv + 2)) == (x >> (lv + 2)) && (li >> (lv + 1)) != (x >> (lv + 1))) ? va[e]
+                                                                                                         : 0.f;
         }
-        NB[j] = to4(vb);
-        NA[j] = to4(va);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[j][e] = ((4 * lg + e == li) ? 1.f : 0.f) - vb[e];
-    }
-    bf16x4 i16;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) i16[e] = (bf16)((4 * lg + e == li) ? 1.f : 0.f);
-    bf16x4 n2b[NBLK], n2a[NBLK], n4b[NBLK], n4a[NBLK], n8a[NBLK];
-#pragma unroll
-    for (int j = 0; j < NBLK; ++j) {
-        n2b[j] = to4(mma16(NA[j], NB[j], zero4()));
-        n2a[j] = to4(mma16(NB[j], NA[j], zero4()));
+        for (int lv = 0; lv < 3; ++lv) BL[lv][j] = to4(bl[lv]);
     }
 #pragma unroll
-    for (int j = 0; j < NBLK; ++j) {
-        n4b[j] = to4(mma16(n2a[j], n2b[j], zero4()));
-        n4a[j] = to4(mma16(n2b[j], n2a[j], zero4()));
-        p[j] = mma16(n2a[j], to4(p[j]), p[j]);
+    for (int lv = 0; lv < 3; ++lv) {
+        f32x4 W[NBLK];
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j) W[j] = mma16(BL[lv][j], to4(TB[j]), zero4());
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j) {
+            const bf16x4 wn = to4(-W[j]);
+            const bf16x4 ta = to4(TA[j]);
+            TB[j] = mma16(ta, wn, TB[j]);
+            TA[j] = mma16(wn, ta, TA[j]);
+        }
     }
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) {
-        n8a[j] = to4(mma16(n4b[j], n4a[j], zero4()));
-        p[j] = mma16(n4a[j], to4(p[j]), p[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < NBLK; ++j) p[j] = mma16(n8a[j], to4(p[j]), p[j]);
-#pragma unroll
-    for (int j = 0; j < NBLK; ++j) {
-        P[j] = to4(p[j]);
-        Qf[j] = mma16(P[j], i16, zero4());
+        P[j] = to4(TB[j]);
+        Qf[j] = TA[j];
     }
 }
 

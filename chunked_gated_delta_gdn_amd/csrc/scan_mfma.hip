@@ -74,7 +74,6 @@ template <> struct Lds<false> {
     float B[2][C];          // beta (zero past the chunk end)
     float gam[2][C];        // exp(G_r); gam[63] = exp(G_C)
     float kdec[2][C];       // exp(G_C - G_r) beta_r (folded into the kT tile)
-    float Gb[2][C];         // G2 - log2(beta): exp2(G2_r - Gb_s) = exp(G_r - G_s) beta_s
 };
 // WY factors read from a workspace: w rows replace the k rows as the
 // consumers' operand, there is no Gram or T'; k is read only by producers, so
@@ -444,10 +443,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], woff(16 * c + li, 4 * kk + lg));
-                const float bl = lane < L ? bv_ : 0.f;
-                sm.B[b2][lane] = bl;
-                // log2(0) = -inf: padded columns of attn vanish
-                sm.Gb[b2][lane] = g2 - __builtin_amdgcn_logf(bl);
+                sm.B[b2][lane] = lane < L ? bv_ : 0.f;
                 gram_to_ab([&](int c, int kk) { return kt[c][kk]; }, sm.G2[b2], sm.B[b2], sm.ab[b2], lane);
             }
         };
@@ -480,12 +476,6 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
             store_rows(sm.qR[b2], qraw, lane);
 
             const float *G2 = sm.G2[b2];
-            // column exponents: with G2 - log2(beta) the tile is attn diag(beta),
-            // which is what multiplies D when recomputing; plain attn for the WY
-            // factors (beta is inside u and w)
-            const float *Gcol;
-            if constexpr (WY) Gcol = G2;
-            else Gcol = sm.Gb[b2];
             (void)L;
             // Gram block (b, a) of K Q^T: lane (j, g) element e holds
             // k_{16b+4g+e} . q_{16a+j} = raw attn[r = 16a + j][s = 16b + 4g + e]
@@ -515,12 +505,17 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                     const float Gr = G2[r];
 #pragma unroll
                     for (int bb = 0; bb <= aa; ++bb, ++i) {
-                        const f32x4 Gs = *reinterpret_cast<const f32x4 *>(&Gcol[16 * bb + 4 * lg]);
+                        const f32x4 Gs = *reinterpret_cast<const f32x4 *>(&G2[16 * bb + 4 * lg]);
+                        // attn diag(beta) when recomputing (the factor that multiplies D;
+                        // beta = 0 zeroes padded columns), plain attn for the WY factors
+                        // (beta is inside u and w)
+                        f32x4 sc = acc[i];
+                        if constexpr (!WY) sc *= *reinterpret_cast<const f32x4 *>(&sm.B[b2][16 * bb + 4 * lg]);
                         f32x4 v;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int s_ = 16 * bb + 4 * lg + e;
-                            v[e] = (s_ <= r) ? ex2(Gr - Gs[e]) * acc[i][e] : 0.f;
+                            v[e] = (s_ <= r) ? ex2(Gr - Gs[e]) * sc[e] : 0.f;
                         }
                         at[aa][bb] = to4(v);
                     }

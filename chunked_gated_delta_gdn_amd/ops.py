@@ -34,6 +34,10 @@ def _addr(t):
     return None if t is None else t.data_ptr()
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -102,7 +106,7 @@ def chunk_prepare(k, v, g, beta, chunk_size=64, cu_seqlens=None):
     _b.gdn_validate(p)
     nbytes = _b.gdn_wy_workspace_bytes(p)
     wy = torch.empty(nbytes // k.element_size(), dtype=k.dtype, device=k.device)
-    _b.gdn_chunk_prepare(p, _addr(k), _addr(v), _addr(g), _addr(beta), _addr(wy),
+    _b.gdn_chunk_prepare(p, _addr(k), _addr(v), _addr(g), _addr(beta), _addr(wy), _nbytes(wy),
                          _stream(k.device))
     return wy
 
@@ -140,7 +144,7 @@ def scan_emit(q, k, v, g, beta, h_in=None, wy=None, chunk_size=64, cu_seqlens=No
     _need(o, "o", (B, S, H, V), k.dtype, dev)
     h_out = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
     _b.gdn_scan(p, _b.GDN_SCAN_EMIT, _addr(q), _addr(k), _addr(v), _addr(g), _addr(beta),
-                _addr(wy), _addr(h_in), _addr(o), _addr(h_out), None, None, _stream(dev))
+                _addr(wy), _nbytes(wy), _addr(h_in), _addr(o), _addr(h_out), None, None, _stream(dev))
     return o, h_out
 
 
@@ -174,7 +178,7 @@ def scan_head_carry(q, k, v, g, beta, h_in=None, wy=None, chunk_size=64, n_segme
     M = torch.empty(lead + (H, K, K), dtype=torch.float32, device=dev)
     U = torch.empty(lead + (H, K, V), dtype=torch.float32, device=dev)
     _b.gdn_scan(p, _b.GDN_SCAN_HEAD_EMIT_CARRY, _addr(q), _addr(k), _addr(v), _addr(g), _addr(beta),
-                _addr(wy), _addr(h_in), _addr(o), _addr(h1), _addr(M), _addr(U), _stream(dev))
+                _addr(wy), _nbytes(wy), _addr(h_in), _addr(o), _addr(h1), _addr(M), _addr(U), _stream(dev))
     return o, h1, M, U
 
 
@@ -193,7 +197,7 @@ def scan_carry(k, v, g, beta, wy=None, chunk_size=64, n_segments=1, seg_starts=N
     M = torch.empty(lead + (H, K, K), dtype=torch.float32, device=dev)
     U = torch.empty(lead + (H, K, V), dtype=torch.float32, device=dev)
     _b.gdn_scan(p, _b.GDN_SCAN_CARRY, None, _addr(k), _addr(v), _addr(g), _addr(beta),
-                _addr(wy), None, None, None, _addr(M), _addr(U), _stream(dev))
+                _addr(wy), _nbytes(wy), None, None, None, _addr(M), _addr(U), _stream(dev))
     return M, U
 
 
@@ -235,7 +239,7 @@ def scan_tail_emit(q, k, v, g, beta, h_in, cu_seqlens, max_piece_chunks, wy=None
         h_out = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
     _need(h_out, "h_out", (N, H, K, V), torch.float32, dev)
     _b.gdn_scan(p, _b.GDN_SCAN_TAIL_EMIT, _addr(q), _addr(k), _addr(v), _addr(g), _addr(beta),
-                _addr(wy), _addr(h_in), _addr(o), _addr(h_out), None, None, _stream(dev))
+                _addr(wy), _nbytes(wy), _addr(h_in), _addr(o), _addr(h_out), None, None, _stream(dev))
     return o, h_out
 
 
@@ -345,7 +349,7 @@ def forward_packed(q, k, v, g, beta, cu_seqlens, h0=None, chunk_size=64, max_pie
     if wy is not None:
         _need(wy, "wy", (_b.gdn_wy_workspace_bytes(p) // k.element_size(),), k.dtype, dev)
     st = _stream(dev)
-    args = (_addr(q), _addr(k), _addr(v), _addr(g), _addr(beta), _addr(wy))
+    args = (_addr(q), _addr(k), _addr(v), _addr(g), _addr(beta), _addr(wy), _nbytes(wy))
     o = torch.empty((B, S, H, V), dtype=k.dtype, device=dev)
     if P == N:
         hT = torch.empty((N, H, K, V), dtype=torch.float32, device=dev) if output_final_state else None
@@ -592,9 +596,9 @@ def backward(q, k, v, g, beta, do, h0=None, dhT=None, chunk_size=64, cu_seqlens=
 
 class _ChunkGatedDeltaRule(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, h0, chunk_size, cu_seqlens, n_segments):
+    def forward(ctx, q, k, v, g, beta, h0, chunk_size, cu_seqlens, n_segments, max_piece_chunks):
         o, hT = forward(q, k, v, g, beta, h0=h0, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
-                        n_segments=n_segments)
+                        n_segments=n_segments, max_piece_chunks=max_piece_chunks)
         ctx.save_for_backward(q, k, v, g, beta, h0)
         ctx.chunk_size, ctx.cu_seqlens = chunk_size, cu_seqlens
         return o, hT
@@ -606,12 +610,15 @@ class _ChunkGatedDeltaRule(torch.autograd.Function):
             q, k, v, g, beta, do.contiguous(), h0=h0,
             dhT=None if dhT is None else dhT.contiguous(), chunk_size=ctx.chunk_size,
             cu_seqlens=ctx.cu_seqlens, want_dh0=h0 is not None and ctx.needs_input_grad[5])
-        return dq, dk, dv, dg, dbeta, dh0, None, None, None
+        return dq, dk, dv, dg, dbeta, dh0, None, None, None, None
 
 
-def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segments=1):
+def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segments=1,
+                           max_piece_chunks=None):
     """Differentiable forward: (o, final state), with ``backward`` as its
     gradient (torch.autograd).  Shapes and the forward's schedule (segments;
-    packed batches cut into pieces) as ``forward``; q, k may have fewer heads
-    than v (grouped key heads)."""
-    return _ChunkGatedDeltaRule.apply(q, k, v, g, beta, h0, chunk_size, cu_seqlens, n_segments)
+    packed batches cut into pieces of at most max_piece_chunks chunks, None =
+    planned) as ``forward``; q, k may have fewer heads than v (grouped key
+    heads)."""
+    return _ChunkGatedDeltaRule.apply(q, k, v, g, beta, h0, chunk_size, cu_seqlens, n_segments,
+                                      max_piece_chunks)

@@ -33,6 +33,13 @@
  *     GDN_ELAUNCH.  No C++ exception crosses the ABI.
  *   - Supported (K, V, C): (32, 32, 16) and (128, 128, 64).  Anything else is
  *     GDN_EUNSUPPORTED; there is no fallback.
+ *   - The kernels address one chunk of C token rows with 32-bit offsets, so a
+ *     problem whose C rows of q, k (H_qk heads) or of v, o (H heads) span
+ *     2 GiB or more is GDN_EUNSUPPORTED (H of 131072 or more at K = V = 128,
+ *     C = 64 in bf16).
+ *   - The decay g may have either sign and beta any value on every path; the
+ *     method's own ranges are g <= 0 (alpha = exp(g) in (0, 1]) and
+ *     0 <= beta <= 1.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -49,7 +56,8 @@ typedef enum gdn_status {
     GDN_EINVAL = 1,        /* null pointer, bad size, misaligned buffer          */
     GDN_EUNSUPPORTED = 2,  /* shape / dtype combination not built                */
     GDN_EORDER = 3,        /* segments or sequence offsets not contiguous+ordered */
-    GDN_ELAUNCH = 4        /* HIP reported an error at launch                    */
+    GDN_ELAUNCH = 4,       /* HIP reported an error at launch                    */
+    GDN_EWORKSPACE = 5     /* a workspace buffer is smaller than the problem needs */
 } gdn_status;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
@@ -144,10 +152,13 @@ size_t gdn_segment_workspace_bytes(const gdn_problem *p);
  *   w = T diag(beta exp(G)) K_c,  u = T diag(beta) V_c.
  * k, v, g, beta as in the problem; wy receives gdn_wy_workspace_bytes(p)
  * bytes (w blocks [n_chunks,H,C,K] followed by u blocks [n_chunks,H,C,V]).
+ * wy_bytes is the size of the buffer at wy: GDN_EWORKSPACE (nothing written)
+ * when it is smaller than gdn_wy_workspace_bytes(p).
  * Rows past the end of a ragged chunk are zero.  Segments are ignored.
  */
 gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
-                             const float *g, const float *beta, void *wy, void *stream);
+                             const float *g, const float *beta, void *wy, size_t wy_bytes,
+                             void *stream);
 
 /*
  * gdn_scan -- the inter-chunk affine scan (MaxText PR, "Why" equations;
@@ -155,6 +166,8 @@ gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
  *
  * wy: NULL recomputes the WY factors inside the scan; otherwise a workspace
  *   filled by gdn_chunk_prepare for the same problem and inputs is reused.
+ *   wy_bytes is the size of the buffer at wy (ignored when wy is NULL):
+ *   GDN_EWORKSPACE when it is smaller than gdn_wy_workspace_bytes(p).
  *
  * GDN_SCAN_EMIT: for every segment r of every sequence n, starts from
  *   h_in[r,n] (h_in [R,N,H,K,V] fp32; NULL = zero state for every segment),
@@ -195,7 +208,7 @@ gdn_status gdn_chunk_prepare(const gdn_problem *p, const void *k, const void *v,
  */
 gdn_status gdn_scan(const gdn_problem *p, int32_t mode,
                     const void *q, const void *k, const void *v,
-                    const float *g, const float *beta, const void *wy,
+                    const float *g, const float *beta, const void *wy, size_t wy_bytes,
                     const float *h_in, void *o, float *h_out,
                     float *M_out, float *U_out, void *stream);
 

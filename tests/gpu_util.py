@@ -1,6 +1,7 @@
 """Helpers shared by the GPU parity tests: move seeded inputs to the device,
 run the HIP path through the C ABI, run the oracle on the same values, and
-measure the normwise error max|x - ref| / max|ref|."""
+measure the normwise error max|x - ref| / max|ref|, over a whole tensor and
+over its worst (sequence, head) slice."""
 import sys
 
 import numpy as np
@@ -64,3 +65,47 @@ def rel_err(x, ref):
     den = np.max(np.abs(ref))
     num = np.max(np.abs(x - ref))
     return float(num / den) if den > 0 else float(num)
+
+
+def slice_err(x, ref, axes):
+    """Worst normwise error over the slices that fix the given axes (e.g. the
+    (b, h) slices of o [B,S,H,V] for axes (0, 2)): a fault confined to one
+    head or one sequence is not diluted by the magnitude of the others."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rest = [a for a in range(ref.ndim) if a not in axes]
+    xs = np.transpose(x, list(axes) + rest).reshape(-1, int(np.prod([ref.shape[a] for a in rest])))
+    rs = np.transpose(ref, list(axes) + rest).reshape(xs.shape)
+    num = np.max(np.abs(xs - rs), axis=1)
+    den = np.max(np.abs(rs), axis=1)
+    return float(np.max(np.where(den > 0, num / np.where(den > 0, den, 1.0), num)))
+
+
+def o_axes(o):
+    """Slice axes of an output tensor: (b, h) of [B,S,H,V], h of packed [T,H,V]."""
+    return (0, 2) if np.ndim(o) == 4 else (1,)
+
+
+def check_forward(x, o, hT, o_ref, h_ref, tol=None, what=""):
+    """Outputs and final states against the oracle: the normwise error of each
+    tensor and of its worst (sequence, head) slice, both within tol."""
+    tol = TOL[x.dtype] if tol is None else tol
+    eo, eh = rel_err(o, o_ref), rel_err(hT, h_ref)
+    so, sh = slice_err(o, o_ref, o_axes(o_ref)), slice_err(hT, h_ref, (0, 1))
+    cu = getattr(x, "cu_seqlens", None)
+    if cu is not None and np.ndim(o_ref) == 3 and len(o_ref) == int(cu[-1]):
+        # packed [T,H,V]: every (sequence, head) slice on its own
+        for n in range(len(cu) - 1):
+            a, b = int(cu[n]), int(cu[n + 1])
+            if b > a:
+                so = max(so, slice_err(np.asarray(o)[a:b], o_ref[a:b], (1,)))
+    say(f"  {x.name} {what}: err(o)={eo:.3e} (worst head {so:.3e}) err(hT)={eh:.3e} "
+        f"(worst head {sh:.3e}) tol={tol:g}")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
+    assert eo <= tol, f"output error {eo} > {tol}"
+    assert eh <= tol, f"final state error {eh} > {tol}"
+    assert so <= tol, f"worst (sequence, head) output error {so} > {tol}"
+    assert sh <= tol, f"worst (sequence, head) final state error {sh} > {tol}"
+    return max(eo, eh, so, sh)

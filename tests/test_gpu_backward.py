@@ -19,6 +19,7 @@ import torch
 
 import oracle
 import chunked_gated_delta_gdn_amd as gdn
+from chunked_gated_delta_gdn_amd import binding as b
 from workloads import make_inputs, make_packed_inputs, make_cotangents
 from gpu_util import TOL, DEV, say, to_dev, tdt, rel_err
 
@@ -202,7 +203,11 @@ def test_autograd_wrapper_with_forward_schedules(mode):
         x = make_packed_inputs(51, 3, 900, 2, 128, 128, 64, "bf16", h0_std=0.02, median=300,
                                pad_to_chunk=False, name="bwd-pieces")
         x.meta = {}
-        kw = dict(cu_seqlens=[int(c) for c in x.cu_seqlens])
+        kw = dict(cu_seqlens=[int(c) for c in x.cu_seqlens], max_piece_chunks=2)
+        # the forward really is cut into pieces (sequences of 4, 4 and 7 chunks)
+        p = gdn.problem_for(to_dev(x.k, torch.bfloat16), to_dev(x.v, torch.bfloat16), 64, kw["cu_seqlens"],
+                            max_piece_chunks=2)
+        assert b.gdn_num_pieces(p) > len(x.cu_seqlens) - 1
     do, dhT = make_cotangents(52, x)
     say(f"backward: autograd with {mode}")
     bf = torch.bfloat16

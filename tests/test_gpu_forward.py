@@ -9,18 +9,12 @@ import oracle
 import chunked_gated_delta_gdn_amd as gdn
 from workloads import make_inputs, make_packed_inputs, workload
 from gpu_util import (TOL, DEV, say, device_inputs, oracle_forward, rel_err, run_forward, tdt,
-                      to_dev)
+                      to_dev, check_forward, slice_err)
 
 pytestmark = pytest.mark.gpu
 
 
-def check(x, o, hT, o_ref, h_ref, tol=None, what=""):
-    tol = TOL[x.dtype] if tol is None else tol
-    eo, eh = rel_err(o, o_ref), rel_err(hT, h_ref)
-    say(f"  {x.name} {what}: err(o)={eo:.3e} err(hT)={eh:.3e} tol={tol:g}")
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
-    assert eo <= tol, f"output error {eo} > {tol}"
-    assert eh <= tol, f"final state error {eh} > {tol}"
+check = check_forward
 
 
 # ---- tiny fp32 workload (B1 H2 S256 K=V=32 C16) -------------------------------------------
@@ -47,11 +41,16 @@ def test_tiny_f32_slow_decay_segments(decay):
 
 def test_tiny_f32_segment_matches_monolithic_closely():
     """fp32 segment pass vs monolithic pass: the MaxText PR reports f32 parity of
-    ~1e-7 (output) and ~1e-7 (final state) at cp=4 ('Measured results')."""
+    9.9e-8 (output) and 1.4e-7 (final state) at cp=4 ('Measured results').  The
+    bound here is 1e-6, a few times that level (a different summation order
+    over 64 fp32 products per entry); the achieved figures are printed."""
     x = workload(0, decay="slow")
     o1, h1 = run_forward(x, n_segments=1)
-    o4, h4 = run_forward(x, n_segments=4)
-    assert rel_err(o4, o1) < 1e-5 and rel_err(h4, h1) < 1e-5
+    for R in (2, 4):
+        oR, hR = run_forward(x, n_segments=R)
+        eo, eh = rel_err(oR, o1), rel_err(hR, h1)
+        say(f"  fp32 segments R={R} vs monolithic: err(o)={eo:.2e} err(hT)={eh:.2e}")
+        assert eo < 1e-6 and eh < 1e-6
 
 
 # ---- bf16 at head dim 128 -------------------------------------------------------------------
@@ -216,7 +215,7 @@ def test_state_in_place_continuation():
         part = torch.empty_like(vs)
         p = gdn.problem_for(ks, vs, 64)
         b.gdn_scan(p, b.GDN_SCAN_EMIT, qs.data_ptr(), ks.data_ptr(), vs.data_ptr(),
-                   gs.data_ptr(), bs.data_ptr(), None, state.data_ptr(), part.data_ptr(),
+                   gs.data_ptr(), bs.data_ptr(), None, 0, state.data_ptr(), part.data_ptr(),
                    state.data_ptr(), None, None, stream)
         o[:, a:e] = part
     torch.cuda.synchronize()
@@ -461,3 +460,90 @@ def test_no_decay_4k():
     o_ref, h_ref = oracle_forward(x)
     o, hT = run_forward(x, n_segments=4)
     check(x, o, hT, o_ref, h_ref, what="g=0 R=4")
+
+
+# ---- the overwrite table at full size, and gates outside the usual ranges --------------------
+
+def _overwrite_inputs(S=512, H=2, seed=21):
+    """One-hot keys and queries, beta = 1, g = 0 (the textbook overwrite
+    table: writing key e_i replaces row i of the state by v), at K = V = 128,
+    C = 64, bf16.  Head h's first chunk writes one key 64 times; the next two
+    chunks write runs of 1 to 24 tokens over four keys; the rest random keys.
+    Repeated keys make A0 diag(beta) an all-ones block, the hardest case for
+    the triangular inverse (its powers reach binomial sizes)."""
+    rng = np.random.default_rng(seed)
+    K = V = 128
+    idx = np.zeros((S, H), dtype=np.int64)
+    for h in range(H):
+        seq = [int(rng.integers(K))] * 64
+        while len(seq) < 192:
+            seq += [int(rng.integers(4))] * int(rng.integers(1, 25))
+        seq = seq[:192] + [int(i) for i in rng.integers(K, size=S - 192)]
+        idx[:, h] = seq
+    qidx = rng.integers(K, size=(S, H))
+    qidx[::3] = idx[::3]                      # often read the row just written
+    t_, h_ = np.arange(S)[:, None], np.arange(H)[None, :]
+    k = np.zeros((1, S, H, K), np.float32)
+    k[0, t_, h_, idx] = 1.0
+    q = np.zeros((1, S, H, K), np.float32)
+    q[0, t_, h_, qidx] = 1.0
+    from workloads import GdnInputs, round_bf16
+    v = round_bf16(rng.standard_normal((1, S, H, V)).astype(np.float32))
+    h0 = (rng.standard_normal((1, H, K, V)) * 0.5).astype(np.float32)
+    x = GdnInputs(q, k, v, np.zeros((1, S, H), np.float32), np.ones((1, S, H), np.float32), h0, "bf16", 64,
+                  real_tokens=S, name="overwrite-128")
+    # the table itself: row idx[t] := v[t], o[t] = row qidx[t] after the write
+    st = h0[0].astype(np.float64).copy()
+    o = np.zeros((S, H, V))
+    for t in range(S):
+        for h in range(H):
+            st[h, idx[t, h]] = v[0, t, h]
+            o[t, h] = st[h, qidx[t, h]]
+    return x, o[None], st[None]
+
+
+@pytest.mark.parametrize("R,reuse_wy", [(1, False), (2, False), (1, True), (4, True)])
+def test_overwrite_table_full_size_bf16(R, reuse_wy):
+    """Repeated unit keys with beta = 1, g = 0 inside chunks at K = V = 128: the
+    GPU result equals the overwrite table (and the oracle), on the recomputing
+    scan and on the prepared WY factors, with and without segments."""
+    x, o_tab, h_tab = _overwrite_inputs()
+    o_ref, h_ref = oracle_forward(x)
+    assert rel_err(o_ref, o_tab) < 1e-12 and rel_err(h_ref, h_tab) < 1e-12   # the oracle is the table
+    o, hT = run_forward(x, n_segments=R, reuse_wy=reuse_wy)
+    check(x, o, hT, o_tab, h_tab, what=f"overwrite R={R} wy={reuse_wy}")
+
+
+def _signed_gates(x, seed=31):
+    """Gates outside the method's usual ranges: a run of increasing decay
+    (g > 0) inside a chunk, scattered positive g, and scattered negative beta."""
+    rng = np.random.default_rng(seed)
+    S = x.g.shape[1]
+    x.g = x.g.copy()
+    x.beta = x.beta.copy()
+    x.g[:, 70:90] = 0.03                      # G rises within chunk 1
+    x.g[:, 200::11] = 0.02
+    neg = rng.random(x.beta.shape) < 0.15
+    x.beta[neg] = -0.3 * x.beta[neg]
+    x.name += "-signed-gates"
+    assert S > 200
+    return x
+
+
+@pytest.mark.parametrize("R,reuse_wy", [(1, False), (3, False), (1, True)])
+def test_signed_gates_bf16(R, reuse_wy):
+    """g > 0 and beta < 0 on the matrix-core path give the oracle's result, like
+    the vector path (the kernels use the signed exponent of each kept entry and
+    multiply beta in, instead of taking its logarithm)."""
+    x = _signed_gates(workload(1, H=4, S=1024, decay="slow"))
+    o_ref, h_ref = oracle_forward(x)
+    o, hT = run_forward(x, n_segments=R, reuse_wy=reuse_wy)
+    check(x, o, hT, o_ref, h_ref, what=f"R={R} wy={reuse_wy}")
+
+
+def test_signed_gates_f32():
+    x = _signed_gates(workload(0, S=256, decay="slow"))
+    o_ref, h_ref = oracle_forward(x)
+    for R, wy in [(1, False), (2, True)]:
+        o, hT = run_forward(x, n_segments=R, reuse_wy=wy)
+        check(x, o, hT, o_ref, h_ref, what=f"R={R} wy={wy}")

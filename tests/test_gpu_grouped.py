@@ -13,7 +13,7 @@ import torch
 import oracle
 import chunked_gated_delta_gdn_amd as gdn
 from workloads import make_inputs, make_decode_inputs
-from gpu_util import TOL, DEV, say, oracle_forward, rel_err, run_forward, to_dev
+from gpu_util import TOL, DEV, say, oracle_forward, rel_err, run_forward, to_dev, check_forward
 
 pytestmark = pytest.mark.gpu
 
@@ -36,11 +36,7 @@ def expanded(x):
 
 
 def check(x, o, hT, o_ref, h_ref, what):
-    tol = TOL[x.dtype]
-    eo, eh = rel_err(o, o_ref), rel_err(hT, h_ref)
-    say(f"  {x.name} {what}: err(o)={eo:.3e} err(hT)={eh:.3e} tol={tol:g}")
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
-    assert eo <= tol and eh <= tol
+    check_forward(x, o, hT, o_ref, h_ref, what=what)
 
 
 @pytest.mark.parametrize("Hk", [1, 2])

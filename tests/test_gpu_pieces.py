@@ -10,7 +10,7 @@ import torch
 
 import chunked_gated_delta_gdn_amd as gdn
 from workloads import make_inputs, workload
-from gpu_util import TOL, DEV, say, device_inputs, oracle_forward, rel_err, run_forward
+from gpu_util import TOL, DEV, say, device_inputs, oracle_forward, rel_err, run_forward, check_forward
 
 pytestmark = pytest.mark.gpu
 
@@ -24,11 +24,7 @@ def packed(seed, cu, H, K, C, dtype, decay="slow", h0_std=0.1):
 
 
 def check(x, o, hT, o_ref, h_ref, what):
-    tol = TOL[x.dtype]
-    eo, eh = rel_err(o, o_ref), rel_err(hT, h_ref)
-    say(f"  {x.name} {what}: err(o)={eo:.3e} err(hT)={eh:.3e} tol={tol:g}")
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
-    assert eo <= tol and eh <= tol
+    check_forward(x, o, hT, o_ref, h_ref, what=what)
 
 
 # chunks per sequence at C = 16: 3, 0, 8, 1, 28 (ragged tails, an empty and a one-token sequence)

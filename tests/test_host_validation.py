@@ -66,6 +66,46 @@ def test_packed_mode_rules():
     assert status(prob(S=many[-1], cu_seqlens=many)) == b.GDN_EUNSUPPORTED
 
 
+def test_wy_workspace_must_hold_the_problem():
+    """A WY workspace smaller than gdn_wy_workspace_bytes is GDN_EWORKSPACE for
+    gdn_chunk_prepare and for every scan mode, before anything is launched
+    (the pointers here are never dereferenced); wy = NULL ignores wy_bytes."""
+    import ctypes
+    lib = b.library()
+    for p in (prob(S=250, B=3), prob(K=128, V=128, C=64, dtype=b.GDN_BF16, S=1000, H=4, n_segments=3),
+              prob(S=100, cu_seqlens=[0, 17, 17, 100], dtype=b.GDN_BF16, max_piece_chunks=2)):
+        need = b.gdn_wy_workspace_bytes(p)
+        assert need > 0
+        assert lib.gdn_chunk_prepare(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
+            b.GDN_EWORKSPACE
+        assert lib.gdn_chunk_prepare(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == b.GDN_EWORKSPACE
+        modes = [b.GDN_SCAN_EMIT, b.GDN_SCAN_CARRY]
+        modes += [b.GDN_SCAN_HEAD_EMIT_CARRY] if p.n_seqs or p.n_segments > 1 else []
+        modes += [b.GDN_SCAN_TAIL_EMIT] if p.n_seqs else []
+        for mode in modes:
+            full = dict(M=FAKE, U=FAKE, h_out=FAKE + (1 << 30))
+            assert _scan_status(p, mode, wy=FAKE, wy_bytes=need - 16, **full) == b.GDN_EWORKSPACE, mode
+            assert _scan_status(p, mode, wy=FAKE, wy_bytes=0, **full) == b.GDN_EWORKSPACE, mode
+            # no workspace: wy_bytes is not looked at (the call then fails later,
+            # at the launch, because this machine has no GPU -- but not on size)
+            assert _scan_status(p, mode, wy=None, wy_bytes=0, **full) != b.GDN_EWORKSPACE, mode
+    assert "GDN_EWORKSPACE" in lib.gdn_status_string(b.GDN_EWORKSPACE).decode()
+
+
+def test_chunk_rows_must_span_less_than_2gib():
+    """The kernels reach the C rows of a chunk through 32-bit byte offsets from
+    the chunk's first row: problems whose C rows of q, k or of v, o span 2 GiB
+    or more are GDN_EUNSUPPORTED instead of silently reading zeros."""
+    big = dict(K=128, V=128, C=64, dtype=b.GDN_BF16, S=64)
+    assert status(prob(H=131071, **big)) == b.GDN_OK              # 64 * 131071 * 256 B < 2 GiB
+    assert status(prob(H=131072, **big)) == b.GDN_EUNSUPPORTED    # = 2 GiB
+    assert status(prob(H=131072, H_qk=1, **big)) == b.GDN_EUNSUPPORTED   # v, o rows alone
+    assert status(prob(H=65536, **dict(big, dtype=b.GDN_F32))) == b.GDN_EUNSUPPORTED
+    assert status(prob(H=65535, **dict(big, dtype=b.GDN_F32))) == b.GDN_OK
+    # and the scan refuses it before any launch
+    assert _scan_status(prob(H=131072, **big)) == b.GDN_EUNSUPPORTED
+
+
 def test_workspace_sizes():
     p = prob(S=250, B=3)                      # 16 chunks per sequence, ragged tail
     assert b.gdn_wy_workspace_bytes(p) == 3 * 16 * 2 * 16 * (32 + 32) * 4
@@ -94,10 +134,11 @@ def _scan_status(p, mode=b.GDN_SCAN_EMIT, **ptrs):
     args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, wy=None, h_in=None, o=FAKE,
                 h_out=None, M=None, U=None)
     args.update(ptrs)
+    wy_bytes = args.pop("wy_bytes", b.gdn_wy_workspace_bytes(p))
     lib = b.library()
     import ctypes
     return lib.gdn_scan(ctypes.byref(p), mode, args["q"], args["k"], args["v"], args["g"],
-                        args["beta"], args["wy"], args["h_in"], args["o"], args["h_out"],
+                        args["beta"], args["wy"], wy_bytes, args["h_in"], args["o"], args["h_out"],
                         args["M"], args["U"], None)
 
 
@@ -272,9 +313,9 @@ def test_backward_validation():
         a.update(over)
         return lib.gdn_backward(ref(pp), *[a[n] for n in names], over.get("ws_bytes", ws), None)
 
-    assert call(prob(H=4, H_qk=2), ws_bytes=wg - 1) == b.GDN_EINVAL
+    assert call(prob(H=4, H_qk=2), ws_bytes=wg - 1) == b.GDN_EWORKSPACE
     assert call(prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=-1)) == b.GDN_EINVAL
-    assert call(p, ws_bytes=ws - 1) == b.GDN_EINVAL
+    assert call(p, ws_bytes=ws - 1) == b.GDN_EWORKSPACE
     assert call(p, q=None) == b.GDN_EINVAL
     assert call(p, dout=None) == b.GDN_EINVAL
     assert call(p, dg=buf[1] + 4) == b.GDN_EINVAL          # misaligned
