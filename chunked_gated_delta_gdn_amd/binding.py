@@ -93,6 +93,8 @@ def library():
             "gdn_decode_step": (_i32, [_i32] * 6 + [_vp] * 8),
             "gdn_scan_backend": (_i32, [P]),
             "gdn_backward_workspace_bytes": (ctypes.c_size_t, [P]),
+            "gdn_forward_workspace_bytes": (ctypes.c_size_t, [P]),
+            "gdn_forward": (_i32, [P] + [_vp] * 9 + [ctypes.c_size_t, _vp]),
             "gdn_backward": (_i32, [P] + [_vp] * 15 + [ctypes.c_size_t, _vp]),
             "gdn_causal_conv1d": (_i32, [_i32] * 6 + [ctypes.POINTER(_i32), _i32] + [_vp] * 6),
             "gdn_gated_rmsnorm": (_i32, [ctypes.c_int64, _i32, _i32, ctypes.c_float] + [_vp] * 5),
@@ -148,6 +150,15 @@ def gdn_chunk_prepare(problem, k, v, g, beta, wy, wy_bytes, stream=0):
 def gdn_scan(problem, mode, q, k, v, g, beta, wy, wy_bytes, h_in, o, h_out, M_out, U_out, stream=0):
     _check(library().gdn_scan(ctypes.byref(problem), mode, q, k, v, g, beta, wy, wy_bytes, h_in, o, h_out,
                               M_out, U_out, stream), "gdn_scan")
+
+
+def gdn_forward_workspace_bytes(problem):
+    return int(library().gdn_forward_workspace_bytes(ctypes.byref(problem)))
+
+
+def gdn_forward(problem, q, k, v, g, beta, h0, o, h_out, workspace, workspace_bytes, stream=0):
+    _check(library().gdn_forward(ctypes.byref(problem), q, k, v, g, beta, h0, o, h_out, workspace,
+                                 workspace_bytes, stream), "gdn_forward")
 
 
 def gdn_segment_compose(R, N, H, K, V, M, U, h0, h_in, h_final, stream=0):

@@ -457,6 +457,205 @@ gdn_status gdn_scan(const gdn_problem *p, int32_t mode, const void *q, const voi
                     "gdn_scan");
 }
 
+// ---- gdn_forward: the whole forward in one call ----------------------------------------
+
+// Byte offsets of gdn_forward's workspace (fp32 state rows; every region a
+// multiple of H*K*V*4 bytes, so 16-byte aligned when the base is):
+//   batch, R >= 2:  h1 [N,H,K,V] | M [R-2,N,H,K,K] | U [R-2,N,H,K,V] | h_all [R-1,N,H,K,V]
+//   packed, P > N:  hs [N,H,K,V] | M [P,H,K,K]     | U [P,H,K,V]     | h_in [P,H,K,V]
+// Problems whose sequences are one chain each need none (total = 0).
+struct FwdLayout {
+    size_t h1 = 0, M = 0, U = 0, hin = 0, total = 0;
+};
+
+static FwdLayout forward_layout(const gdn_problem *p, const Resolved &r) {
+    FwdLayout L;
+    const size_t sk = (size_t)p->H * p->K * p->K * sizeof(float);
+    const size_t sv = (size_t)p->H * p->K * p->V * sizeof(float);
+    size_t nm, nh;   // state rows of M and U; of h_all / h_in
+    if (!r.ct.packed) {
+        if (r.R < 2) return L;
+        nm = (size_t)(r.R - 2) * r.N;
+        nh = (size_t)(r.R - 1) * r.N;
+    } else {
+        if (r.P == r.N) return L;
+        nm = nh = (size_t)r.P;
+    }
+    L.M = (size_t)r.N * sv;
+    L.U = L.M + nm * sk;
+    L.hin = L.U + nm * sv;
+    L.total = L.hin + nh * sv;
+    return L;
+}
+
+// The schedule of gdn_forward (the segment pass of the MaxText PR, section
+// "Implementation", without its redundant work), on the stream, with the
+// workspace at ws (FwdLayout).  Arguments are already validated.
+static gdn_status forward_run(const gdn_problem *p, Resolved &r, const void *q, const void *k, const void *v,
+                              const float *g, const float *beta, const float *h0, void *o, float *h_out,
+                              char *ws, hipStream_t s, const char *who) {
+    ScanArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.wy_w = a.wy_u = nullptr;
+    a.H = p->H;
+    a.Hk = p->H_qk > 0 ? p->H_qk : p->H;
+    const int K = p->K, V = p->V, C = p->C, dt = p->dtype;
+    const FwdLayout L = forward_layout(p, r);
+    (void)hipGetLastError();
+    if (L.total == 0) {
+        // one chain per sequence: the emitting scan alone
+        a.h_in = h0;
+        a.o = o;
+        a.h_out = h_out;
+        if (r.ct.packed) {
+            int ne, nc;
+            packed_items(r, GDN_SCAN_EMIT, ne, nc);
+            a.n_chains = r.ct.n_items;
+        } else {
+            a.n_chains = r.N * r.R;
+        }
+        a.ct = r.ct;
+        if (a.n_chains == 0) return GDN_OK;
+        return launched(launch_scan(K, V, C, dt, false, a, s), who);
+    }
+    float *h1 = reinterpret_cast<float *>(ws + L.h1);
+    float *M = reinterpret_cast<float *>(ws + L.M);
+    float *U = reinterpret_cast<float *>(ws + L.U);
+    float *hin = reinterpret_cast<float *>(ws + L.hin);
+    if (!r.ct.packed) {
+        const int R = r.R, N = r.N;
+        // 1. segment 0 emitted from h0, its final state (the state entering
+        //    segment 1) to h1; segments 1 .. R-2 carried into M, U.  The chain
+        //    table stops at the start of segment R-1.
+        ScanArgs hd = a;
+        hd.ct = r.ct;
+        hd.ct.n_seg = R - 1;
+        if (R == 2) {
+            hd.h_in = h0;
+            hd.o = o;
+            hd.h_out = h1;
+            hd.n_chains = N;
+            GDN_TRY(launched(launch_scan(K, V, C, dt, false, hd, s), who));
+        } else {
+            hd.M_out = M;
+            hd.U_out = U;
+            hd.n_chains = N * (R - 2);
+            GDN_TRY(launched(launch_scan_head(K, V, C, dt, hd, h0, o, h1, s), who));
+            // 2. the states entering segments 1 .. R-1: h_all[0] = h1,
+            //    h_all[r] = M_r h_all[r-1] + U_r
+            ComposeArgs c;
+            memset(&c, 0, sizeof(c));
+            c.M = M;
+            c.U = U;
+            c.h0 = h1;
+            c.h_in = hin;
+            c.h_final = hin + (size_t)(R - 2) * N * p->H * K * V;
+            c.R = R - 2;
+            c.N = N;
+            c.H = p->H;
+            GDN_TRY(launched(launch_compose(K, V, c, s), who));
+        }
+        // 3. segments 1 .. R-1 emitted from those states; the last writes h_out
+        ScanArgs e = a;
+        e.ct = r.ct;
+        e.ct.n_seg = R - 1;
+        for (int i = 0; i < R; ++i) e.ct.seg_start[i] = r.ct.seg_start[i + 1];
+        e.h_in = R == 2 ? h1 : hin;
+        e.o = o;
+        e.h_out = h_out;
+        e.n_chains = N * (R - 1);
+        return launched(launch_scan(K, V, C, dt, false, e, s), who);
+    }
+    // packed, some sequence cut into pieces: first pieces emitted and middle
+    // pieces carried; the pieces' incoming states per sequence; the other
+    // pieces emitted.  hs holds the state after each first piece (the final
+    // state of a one-piece sequence), then every final state.
+    float *hs = h_out ? h_out : h1;
+    int ne, nc;
+    packed_items(r, GDN_SCAN_HEAD_EMIT_CARRY, ne, nc);
+    ScanArgs hd = a;
+    hd.ct = r.ct;
+    hd.h_in = h0;
+    hd.o = o;
+    hd.h_out = hs;
+    hd.M_out = M;
+    hd.U_out = U;
+    hd.n_chains = r.ct.n_items;
+    GDN_TRY(launched(launch_scan_head(K, V, C, dt, hd, h0, o, hs, s), who));
+    ComposeArgs c;
+    memset(&c, 0, sizeof(c));
+    c.M = M;
+    c.U = U;
+    c.h0 = hs;
+    c.h_in = hin;
+    c.h_final = nullptr;
+    c.R = 0;
+    c.N = r.N;
+    c.H = p->H;
+    c.packed = 1;
+    c.first = 1;
+    for (int n = 0; n <= r.N; ++n) c.seq_first[n] = r.seq_first[n];
+    GDN_TRY(launched(launch_compose(K, V, c, s), who));
+    packed_items(r, GDN_SCAN_TAIL_EMIT, ne, nc);
+    ScanArgs t = a;
+    t.ct = r.ct;
+    t.h_in = hin;
+    t.o = o;
+    t.h_out = hs;
+    t.n_chains = r.ct.n_items;
+    if (t.n_chains == 0) return GDN_OK;
+    return launched(launch_scan(K, V, C, dt, false, t, s), who);
+}
+
+// Checks shared by the forward entry points (everything but the workspace).
+static gdn_status forward_check(const gdn_problem *p, Resolved &r, const void *q, const void *k, const void *v,
+                                const float *g, const float *beta, const float *h0, void *o, float *h_out) {
+    GDN_TRY(resolve(p, r));
+    const bool any = r.T > 0;
+    GDN_TRY(check_ptr(q, "q", any));
+    GDN_TRY(check_ptr(k, "k", any));
+    GDN_TRY(check_ptr(v, "v", any));
+    GDN_TRY(check_ptr(g, "g", any));
+    GDN_TRY(check_ptr(beta, "beta", any));
+    GDN_TRY(check_ptr(h0, "h0", false));
+    GDN_TRY(check_ptr(o, "o", any));
+    GDN_TRY(check_ptr(h_out, "h_out", false));
+    return GDN_OK;
+}
+
+size_t gdn_forward_workspace_bytes(const gdn_problem *p) {
+    Resolved r;
+    if (resolve(p, r) != GDN_OK) return 0;
+    return forward_layout(p, r).total;
+}
+
+gdn_status gdn_forward(const gdn_problem *p, const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *h0, void *o, float *h_out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    g_err[0] = 0;
+    Resolved r;
+    GDN_TRY(forward_check(p, r, q, k, v, g, beta, h0, o, h_out));
+    const FwdLayout L = forward_layout(p, r);
+    GDN_TRY(check_ptr(workspace, "workspace", L.total > 0));
+    if (L.total > 0 && workspace_bytes < L.total)
+        return fail(GDN_EWORKSPACE, "forward workspace %zu bytes < %zu needed", workspace_bytes, L.total);
+    if (L.total > 0) {
+        const size_t es = elem_size(p->dtype);
+        const size_t nst = (size_t)r.N * p->H * p->K * p->V * sizeof(float);
+        const size_t no = (size_t)r.T * p->H * p->V * es;
+        if (overlaps(workspace, L.total, o, no) || overlaps(workspace, L.total, h_out, nst) ||
+            overlaps(workspace, L.total, h0, nst))
+            return fail(GDN_EINVAL, "the workspace overlaps o, h0 or h_out");
+    }
+    return forward_run(p, r, q, k, v, g, beta, h0, o, h_out, static_cast<char *>(workspace), (hipStream_t)stream,
+                       "gdn_forward");
+}
+
 gdn_status gdn_segment_compose(int32_t R, int32_t N, int32_t H, int32_t K, int32_t V,
                                const float *M, const float *U, const float *h0, float *h_in,
                                float *h_final, void *stream) {

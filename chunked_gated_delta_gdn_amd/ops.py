@@ -501,6 +501,42 @@ def forward_segmented(q, k, v, g, beta, h0=None, chunk_size=64, n_segments=2, se
     return o, hT
 
 
+def forward_fused(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segments=1, seg_starts=None,
+                  max_piece_chunks=None, output_final_state=True, out=None, h_out=None, workspace=None):
+    """The whole forward in one library call (``gdn_forward``): one emitting
+    scan per sequence, the segment pass (batch, n_segments > 1) or the piece
+    schedule (packed; max_piece_chunks None = ``plan_pieces``).  Returns (o,
+    final state or None).  ``workspace`` (uint8, at least
+    gdn_forward_workspace_bytes) is allocated when not given."""
+    B, S, H, K, V = _check_inputs(q, k, v, g, beta)
+    dev = k.device
+    N = _n_seqs(k, cu_seqlens)
+    if cu_seqlens is not None:
+        cu = [int(x) for x in cu_seqlens]
+        if max_piece_chunks is None:
+            chunks = tuple(-(-(cu[n + 1] - cu[n]) // chunk_size) for n in range(N))
+            max_piece_chunks = plan_pieces(chunks, H, _n_cu(dev))
+    else:
+        cu = None
+        max_piece_chunks = 0
+    p = problem_for(k, v, chunk_size, cu, n_segments, seg_starts, max_piece_chunks)
+    _b.gdn_validate(p)
+    if h0 is not None:
+        _need(h0, "h0", (N, H, K, V), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, S, H, V), dtype=k.dtype, device=dev)
+    _need(o, "o", (B, S, H, V), k.dtype, dev)
+    if h_out is None and output_final_state:
+        h_out = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    if h_out is not None:
+        _need(h_out, "h_out", (N, H, K, V), torch.float32, dev)
+    need = _b.gdn_forward_workspace_bytes(p)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _b.gdn_forward(p, _addr(q), _addr(k), _addr(v), _addr(g), _addr(beta), _addr(h0), _addr(o), _addr(h_out),
+                   _addr(workspace), _nbytes(workspace), _stream(dev))
+    return o, h_out
+
+
 def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segments=1,
             seg_starts=None, reuse_wy=False, output_final_state=True, schedule="auto",
             max_piece_chunks=None):
@@ -508,14 +544,16 @@ def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segment
 
     n_segments > 1 runs the three-phase segment pass; reuse_wy prepares the WY
     factors once (``gdn_chunk_prepare``) and hands them to both scans instead of
-    recomputing them inside each scan.  schedule="auto" uses forward_segmented
-    for one sequence with recomputed WY factors, "plain" always runs the full
-    carrying pass over every segment.
+    recomputing them inside each scan.  schedule="auto" with recomputed WY
+    factors is one ``gdn_forward`` call (``forward_fused``: the segment pass
+    without its redundant work); "plain" always runs the full carrying pass
+    over every segment.
 
     Packed batches (cu_seqlens) take max_piece_chunks instead of segments:
     None or "auto" lets schedule="auto" choose the cut (``plan_pieces``; no cut
     when the WY factors are reused or the schedule is "plain"), 0 keeps every
-    sequence whole; "auto" runs ``forward_packed``, "plain" the carrying pass
+    sequence whole; "auto" runs ``gdn_forward`` (``forward_packed`` with reused
+    WY factors), "plain" the carrying pass
     over every piece, ``gdn_piece_compose`` from the initial states, and the
     emitting pass over every piece.  A batch [B,S,H,*] given max_piece_chunks
     ("auto" or a number) runs as the packed batch of its B sequences."""
@@ -539,6 +577,9 @@ def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segment
         wy = chunk_prepare(k, v, g, beta, chunk_size, cu_seqlens) if reuse_wy else None
         if schedule == "auto":
             m = max_piece_chunks if max_piece_chunks is not None else (0 if reuse_wy else None)
+            if wy is None:
+                return forward_fused(q, k, v, g, beta, h0=h0, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
+                                     max_piece_chunks=m, output_final_state=output_final_state)
             return forward_packed(q, k, v, g, beta, cu_seqlens, h0=h0, chunk_size=chunk_size,
                                   max_piece_chunks=m, wy=wy, output_final_state=output_final_state)
         m = max_piece_chunks or 0
@@ -549,11 +590,9 @@ def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segment
         h_in, _ = piece_compose(k, v, M, U, cu_seqlens, m, chunk_size, first=0, h_seed=h0)
         return scan_emit(q, k, v, g, beta, h_in=h_in, wy=wy, chunk_size=chunk_size, cu_seqlens=cu_seqlens,
                          output_final_state=output_final_state, max_piece_chunks=m)
-    if (schedule == "auto" and n_segments > 1 and cu_seqlens is None and not reuse_wy
-            and k.shape[0] == 1):
-        return forward_segmented(q, k, v, g, beta, h0=h0, chunk_size=chunk_size,
-                                 n_segments=n_segments, seg_starts=seg_starts,
-                                 output_final_state=output_final_state)
+    if schedule == "auto" and not reuse_wy:
+        return forward_fused(q, k, v, g, beta, h0=h0, chunk_size=chunk_size, n_segments=n_segments,
+                             seg_starts=seg_starts, output_final_state=output_final_state)
     wy = chunk_prepare(k, v, g, beta, chunk_size, cu_seqlens) if reuse_wy else None
     if n_segments == 1:
         return scan_emit(q, k, v, g, beta, h_in=h0, wy=wy, chunk_size=chunk_size,

@@ -213,6 +213,34 @@ gdn_status gdn_scan(const gdn_problem *p, int32_t mode,
                     float *M_out, float *U_out, void *stream);
 
 /*
+ * gdn_forward -- the whole chunked forward of a problem in one call: outputs
+ * o and final states h_out from inputs q, k, v, g, beta and initial states h0
+ * (nullable = zero), with the WY factors recomputed inside the scans.
+ *   - One chain per sequence (batch with n_segments == 1, or packed with no
+ *     sequence cut into pieces): the emitting scan alone (gdn_scan
+ *     GDN_SCAN_EMIT).
+ *   - Segments (batch, R >= 2): the three-phase pass of the MaxText PR,
+ *     section "Implementation", without its redundant work: segment 0 emitted
+ *     from h0 beside the carrying pass of segments 1 .. R-2, the exclusive
+ *     prefix scan of their (M_r, U_r) seeded with segment 0's final state, and
+ *     the emitting pass of segments 1 .. R-1 (GDN_SCAN_HEAD_EMIT_CARRY,
+ *     gdn_segment_compose, GDN_SCAN_EMIT).
+ *   - Packed pieces (max_piece_chunks): GDN_SCAN_HEAD_EMIT_CARRY,
+ *     gdn_piece_compose(first = 1), GDN_SCAN_TAIL_EMIT.
+ * Layouts as gdn_scan; h0, h_out [N,H,K,V] fp32, h_out nullable and allowed to
+ * alias h0 (in-place continuation).  workspace: caller-owned device memory of
+ * gdn_forward_workspace_bytes(p) bytes, 16-byte aligned, not overlapping o,
+ * h0 or h_out (contents undefined on return; NULL allowed when that size is
+ * 0); GDN_EWORKSPACE when workspace_bytes is smaller.  The workspace holds the
+ * (M, U) pairs and the incoming states of the segments or pieces, whose size
+ * does not depend on S.  Errors as gdn_scan; nothing is written on failure.
+ */
+size_t gdn_forward_workspace_bytes(const gdn_problem *p);
+gdn_status gdn_forward(const gdn_problem *p, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, const float *h0, void *o, float *h_out,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * gdn_segment_compose -- exclusive prefix scan over segment pairs (MaxText
  * PR, "Implementation" phase 2):
  *   h_in[0] = h0 (NULL = zero), h_in[r+1] = M[r] h_in[r] + U[r],

@@ -547,3 +547,52 @@ def test_signed_gates_f32():
     for R, wy in [(1, False), (2, True)]:
         o, hT = run_forward(x, n_segments=R, reuse_wy=wy)
         check(x, o, hT, o_ref, h_ref, what=f"R={R} wy={wy}")
+
+
+# ---- gdn_forward: the whole forward in one call -----------------------------------------------
+
+@pytest.mark.parametrize("R", [2, 3, 4])
+def test_forward_fused_equals_the_chained_entry_points(R):
+    """gdn_forward runs the same kernels in the same order as the chained calls
+    (GDN_SCAN_HEAD_EMIT_CARRY, gdn_segment_compose, GDN_SCAN_EMIT), so the
+    results are bit-identical; and within tolerance of the oracle."""
+    x = workload(1, H=4, S=2048 + 40, decay="slow")
+    d = device_inputs(x)
+    a = gdn.forward_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], n_segments=R)
+    c = gdn.forward_segmented(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], n_segments=R)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+    o_ref, h_ref = oracle_forward(x)
+    check(x, a[0].float().cpu().numpy(), a[1].cpu().numpy(), o_ref, h_ref, what=f"gdn_forward R={R}")
+
+
+@pytest.mark.parametrize("dtype,K,C", [("bf16", 128, 64), ("f32", 32, 16)])
+def test_forward_fused_batch_of_two_with_segments(dtype, K, C):
+    """Segments of a batch of two sequences in one call (the Python chain only
+    takes one sequence), ragged length, in place (h_out aliasing h0)."""
+    x = make_inputs(23, 2, 13 * C + 5, 2, K, K, C, dtype, 0.05, "slow", name=f"fused-b2-{dtype}")
+    o_ref, h_ref = oracle_forward(x)
+    d = device_inputs(x)
+    state = d["h0"].clone()
+    o, hT = gdn.forward_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=state, chunk_size=C, n_segments=4,
+                              h_out=state)
+    torch.cuda.synchronize()
+    assert hT.data_ptr() == state.data_ptr()
+    check(x, o.float().cpu().numpy(), state.cpu().numpy(), o_ref, h_ref, what="B=2 R=4 in place")
+
+
+def test_forward_fused_packed_pieces_equals_chained():
+    """Packed batch cut into pieces: gdn_forward equals forward_packed's three
+    launches bit for bit, with and without final states."""
+    x = make_packed_inputs(24, 5, 3000, 2, 128, 128, 64, "bf16", h0_std=0.02, decay="slow", median=400,
+                           pad_to_chunk=False, name="fused-packed")
+    cu = [int(c) for c in x.cu_seqlens]
+    d = device_inputs(x)
+    a = gdn.forward_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], cu_seqlens=cu, max_piece_chunks=3)
+    c = gdn.forward_packed(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, h0=d["h0"], max_piece_chunks=3)
+    a2 = gdn.forward_fused(d["q"], d["k"], d["v"], d["g"], d["beta"], h0=d["h0"], cu_seqlens=cu, max_piece_chunks=3,
+                           output_final_state=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1]) and torch.equal(a2[0], a[0]) and a2[1] is None
+    o_ref, h_ref = oracle_forward(x)
+    check(x, a[0][0].float().cpu().numpy(), a[1].cpu().numpy(), o_ref, h_ref, what="gdn_forward pieces")

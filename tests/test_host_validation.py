@@ -323,3 +323,43 @@ def test_backward_validation():
     assert call(p, dk=buf[14]) == b.GDN_EINVAL             # dk overlaps the workspace
     assert call(p, dv=buf[8]) == b.GDN_EINVAL              # dv overlaps dq
     assert call(prob(K=64, V=64, C=16)) == b.GDN_EUNSUPPORTED
+
+
+def test_forward_workspace_and_checks():
+    """gdn_forward: workspace sized by gdn_forward_workspace_bytes (none for one
+    chain per sequence), GDN_EWORKSPACE when short, no overlap of the workspace
+    with o, h0 or h_out, and the usual pointer checks -- all before a launch."""
+    import ctypes
+    lib = b.library()
+    sv = 2 * 32 * 32 * 4                       # H K V fp32
+    assert b.gdn_forward_workspace_bytes(prob()) == 0
+    # batch R = 4, B = 3: h1 [3] | M [2,3] | U [2,3] | h_all [3,3] state rows (K = V)
+    assert b.gdn_forward_workspace_bytes(prob(B=3, n_segments=4)) == (3 + 6 + 6 + 9) * sv
+    assert b.gdn_forward_workspace_bytes(prob(B=3, n_segments=2)) == (3 + 0 + 0 + 3) * sv
+    # packed: 3 chunks + 8 chunks at m = 2 -> 2 + 4 pieces; hs [2] | M, U, h_in [6]
+    pk = prob(S=176, cu_seqlens=[0, 48, 176], max_piece_chunks=2)
+    assert b.gdn_num_pieces(pk) == 6
+    assert b.gdn_forward_workspace_bytes(pk) == (2 + 3 * 6) * sv
+    assert b.gdn_forward_workspace_bytes(prob(S=176, cu_seqlens=[0, 48, 176])) == 0
+    step = 1 << 24
+    buf = [FAKE + i * step for i in range(12)]
+
+    def call(pp, ws_bytes=None, **over):
+        names = ["q", "k", "v", "g", "beta", "h0", "o", "h_out", "ws"]
+        a = dict(zip(names, buf))
+        a.update(over)
+        n = b.gdn_forward_workspace_bytes(pp) if ws_bytes is None else ws_bytes
+        return lib.gdn_forward(ctypes.byref(pp), *[a[x] for x in names], n, None)
+
+    p4 = prob(n_segments=4)
+    need = b.gdn_forward_workspace_bytes(p4)
+    assert call(p4, ws_bytes=need - 1) == b.GDN_EWORKSPACE
+    assert call(pk, ws_bytes=0) == b.GDN_EWORKSPACE
+    assert call(p4, ws=None) == b.GDN_EINVAL
+    assert call(p4, ws=buf[6]) == b.GDN_EINVAL           # overlaps o
+    assert call(p4, ws=buf[5] + 4096) == b.GDN_EINVAL     # overlaps h0 (8 KiB)
+    assert call(p4, ws=buf[7] - 4096) == b.GDN_EINVAL     # overlaps h_out
+    assert call(p4, q=None) == b.GDN_EINVAL
+    assert call(p4, o=buf[6] + 8) == b.GDN_EINVAL         # misaligned
+    assert call(prob(K=64, V=64, C=32, n_segments=4)) == b.GDN_EUNSUPPORTED
+    assert call(prob(n_segments=4, seg_starts=[0, 32, 16, 64])) == b.GDN_EORDER
