@@ -95,6 +95,7 @@ def library():
             "gdn_backward_workspace_bytes": (ctypes.c_size_t, [P]),
             "gdn_forward_workspace_bytes": (ctypes.c_size_t, [P]),
             "gdn_forward": (_i32, [P] + [_vp] * 9 + [ctypes.c_size_t, _vp]),
+            "gdn_forward_noalloc": (_i32, [P] + [_vp] * 9),
             "gdn_backward": (_i32, [P] + [_vp] * 15 + [ctypes.c_size_t, _vp]),
             "gdn_causal_conv1d": (_i32, [_i32] * 6 + [ctypes.POINTER(_i32), _i32] + [_vp] * 6),
             "gdn_gated_rmsnorm": (_i32, [ctypes.c_int64, _i32, _i32, ctypes.c_float] + [_vp] * 5),
@@ -159,6 +160,14 @@ def gdn_forward_workspace_bytes(problem):
 def gdn_forward(problem, q, k, v, g, beta, h0, o, h_out, workspace, workspace_bytes, stream=0):
     _check(library().gdn_forward(ctypes.byref(problem), q, k, v, g, beta, h0, o, h_out, workspace,
                                  workspace_bytes, stream), "gdn_forward")
+
+
+def gdn_forward_noalloc(problem, q, k, v, g, beta, h0, o, h_out, stream=0):
+    _check(library().gdn_forward_noalloc(ctypes.byref(problem), q, k, v, g, beta, h0, o, h_out, stream),
+           "gdn_forward_noalloc")
+
+
+GDN_FORWARD_SCRATCH_BYTES = 64 << 20
 
 
 def gdn_segment_compose(R, N, H, K, V, M, U, h0, h_in, h_final, stream=0):

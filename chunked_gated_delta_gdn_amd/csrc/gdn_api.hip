@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "gdn_internal.h"
 
@@ -654,6 +655,68 @@ gdn_status gdn_forward(const gdn_problem *p, const void *q, const void *k, const
     }
     return forward_run(p, r, q, k, v, g, beta, h0, o, h_out, static_cast<char *>(workspace), (hipStream_t)stream,
                        "gdn_forward");
+}
+
+// ---- gdn_forward_noalloc: gdn_forward with a scratch array instead of a workspace -------
+//
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops): gdn_forward's workspace lives in this
+// file-scope device array, one copy on every GPU the library runs on, held
+// until the process ends.  In host code `scratch` names a host-side stand-in;
+// the device address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address reaches the kernels.
+// Every call on a GPU uses that GPU's array, so calls that overlap on one GPU
+// (other streams, other threads) race.  Nothing in it needs to start at zero:
+// every byte a call reads there is written earlier in the same call.
+static __device__ __align__(256) unsigned char scratch[GDN_FORWARD_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The scratch array's device address on the device of `stream` (the current
+// device for the null stream).
+gdn_status scratch_address(hipStream_t stream, char **out) {
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(GDN_ELAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    dev = cur;
+    if (stream) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return fail(GDN_ELAUNCH, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GDN_EUNSUPPORTED, "device %d: the scratch table holds %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(GDN_ELAUNCH, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !ptr)
+            return fail(GDN_ELAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = static_cast<char *>(g_scratch_ptr[dev]);
+    return GDN_OK;
+}
+}  // namespace
+
+gdn_status gdn_forward_noalloc(const gdn_problem *p, const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *h0, void *o, float *h_out, void *stream) {
+    g_err[0] = 0;
+    Resolved r;
+    GDN_TRY(forward_check(p, r, q, k, v, g, beta, h0, o, h_out));
+    const size_t need = forward_layout(p, r).total;
+    if (need > GDN_FORWARD_SCRATCH_BYTES)
+        return fail(GDN_EWORKSPACE, "the problem needs %zu bytes of scratch, more than the %zu bytes of "
+                                    "gdn_forward_noalloc (use gdn_forward with a workspace)",
+                    need, (size_t)GDN_FORWARD_SCRATCH_BYTES);
+    char *ws = nullptr;
+    if (need > 0) GDN_TRY(scratch_address((hipStream_t)stream, &ws));
+    return forward_run(p, r, q, k, v, g, beta, h0, o, h_out, ws, (hipStream_t)stream, "gdn_forward_noalloc");
 }
 
 gdn_status gdn_segment_compose(int32_t R, int32_t N, int32_t H, int32_t K, int32_t V,

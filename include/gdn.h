@@ -241,6 +241,24 @@ gdn_status gdn_forward(const gdn_problem *p, const void *q, const void *k, const
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_forward_noalloc -- gdn_forward without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * file-scope device array of GDN_FORWARD_SCRATCH_BYTES (64 MiB) inside the
+ * library, one per GPU it runs on (on the device of `stream`), held until the
+ * process ends; the call allocates nothing.  A problem whose
+ * gdn_forward_workspace_bytes exceeds it is GDN_EWORKSPACE (the 64k-token,
+ * 32-head, K = V = 128 forward in 4 segments needs 16 MiB; R segments of N
+ * sequences need about (3R - 4) * N * H * K * V * 4 bytes).  Every call on a
+ * GPU uses the same array, so calls that overlap on one GPU (other streams or
+ * threads) race: serialise them.  Otherwise as gdn_forward.
+ */
+#define GDN_FORWARD_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_forward_noalloc(const gdn_problem *p, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const float *h0, void *o, float *h_out,
+                               void *stream);
+
+/*
  * gdn_segment_compose -- exclusive prefix scan over segment pairs (MaxText
  * PR, "Implementation" phase 2):
  *   h_in[0] = h0 (NULL = zero), h_in[r+1] = M[r] h_in[r] + U[r],

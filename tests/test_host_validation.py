@@ -363,3 +363,22 @@ def test_forward_workspace_and_checks():
     assert call(p4, o=buf[6] + 8) == b.GDN_EINVAL         # misaligned
     assert call(prob(K=64, V=64, C=32, n_segments=4)) == b.GDN_EUNSUPPORTED
     assert call(prob(n_segments=4, seg_starts=[0, 32, 16, 64])) == b.GDN_EORDER
+
+
+def test_forward_noalloc_rejects_problems_beyond_its_scratch():
+    """gdn_forward_noalloc holds a fixed scratch array: a problem whose
+    workspace exceeds it is GDN_EWORKSPACE before anything is launched (the
+    pointers here are never dereferenced)."""
+    import ctypes
+    lib = b.library()
+    big = prob(K=128, V=128, C=64, dtype=b.GDN_BF16, S=64 * 64, H=64, n_segments=64)
+    assert b.gdn_forward_workspace_bytes(big) > b.GDN_FORWARD_SCRATCH_BYTES
+    assert lib.gdn_forward_noalloc(ctypes.byref(big), *([FAKE + (i << 28) for i in range(8)]), None) == \
+        b.GDN_EWORKSPACE
+    assert "64" in lib.gdn_last_error().decode() or "scratch" in lib.gdn_last_error().decode()
+    # the 64k-token, 32-head forward in 4 segments fits (16 MiB)
+    head = prob(K=128, V=128, C=64, dtype=b.GDN_BF16, S=65536, H=32, n_segments=4)
+    assert b.gdn_forward_workspace_bytes(head) == 16 << 20
+    assert lib.gdn_forward_noalloc(ctypes.byref(big), *([FAKE] * 5), None, FAKE, None, None) == b.GDN_EWORKSPACE
+    assert lib.gdn_forward_noalloc(ctypes.byref(head), None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None) == \
+        b.GDN_EINVAL
