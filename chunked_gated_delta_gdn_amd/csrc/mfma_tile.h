@@ -63,17 +63,21 @@ __device__ __forceinline__ void lds_barrier() {
 
 // LDS tiles.  A row of a "wide" tile holds 128 bf16 (16 chunks of 16 B), a row
 // of a "narrow" tile 64 bf16 (8 chunks).  Within a 32-element block, chunk g
-// holds the k-slots 8g .. 8g+7, i.e. logical elements 4g .. 4g+3 and
-// 16+4g .. 16+4g+3.
+// holds the k-slots 8g .. 8g+7 that lane group g feeds to a 16x16x32 MFMA.
+// Wide tiles written by store_rows hold them in natural order (k-slot 8g + e
+// is element 8g + e of the block); the other tiles, whose reduction runs over
+// the tokens of a chunk, hold logical elements 4g .. 4g+3 and 16+4g .. 16+4g+3
+// there, so that two accumulator tiles (rows 0-15 and 16-31) are directly the
+// operand reducing over those 32 rows (pack_pair).
 // The 16-byte chunks are swizzled against LDS bank conflicts (gfx950: 64
 // banks of 4 B; a 16-byte read is served 16 lanes per pass, an 8-byte store
 // 16 lanes per pass over 32 banks; measured with the bank-conflict counter):
-//  * wide: chunk q of row r lives at chunk q ^ (r & 7) ^ (q >> 3 & 1).  The
-//    8-byte stores of store_rows (the even, then the odd chunks of one row)
-//    fall on distinct banks; a 16-byte read of one chunk by 16 consecutive
-//    rows takes two passes.  (q ^ (r & 15) ^ (q >> 3 & 1) makes those reads
-//    single-pass too, but its lane-dependent addresses cost the consumers
-//    registers they do not have.)
+//  * wide: chunk q of row r lives at chunk q ^ (r & 7) ^ (q >> 3 & 1).  A
+//    16-byte store of a whole row by 16 lanes, and 8-byte stores of the even,
+//    then the odd chunks of one row, fall on distinct banks; a 16-byte read of
+//    one chunk by 16 consecutive rows takes two passes.  (q ^ (r & 15) ^
+//    (q >> 3 & 1) makes those reads single-pass too, but its lane-dependent
+//    addresses cost the consumers registers they do not have.)
 //  * narrow: chunk q of row r lives at chunk q ^ (r & 7); two consecutive
 //    rows span the 64 banks.
 __device__ __forceinline__ int woff(int r, int q) { return r * 256 + ((q ^ (r & 7) ^ ((q >> 3) & 1)) << 4); }
@@ -130,19 +134,15 @@ __device__ __forceinline__ void load_rows(uint4 (&t)[16], const bf16 *base, uint
 #pragma unroll
     for (int m = 0; m < 16; ++m) t[m] = bload16(r, min(own + (uint32_t)(4 * m) * row_bytes, lim) + col, 0);
 }
-// Store rows loaded by load_rows into a wide tile: the 16 B of elements
-// 8s .. 8s+7 split into two 8 B halves that land on k-slots 16(s&1) + 4(s/2&1)
-// and +8 of their 32-element block, i.e. chunks 4(s/4) + 2(s&1) and the next
-// one, at byte 8 (s/2 & 1) within the chunk.
+// Store rows loaded by load_rows into a wide tile in natural order: the 16 B
+// of elements 8s .. 8s+7 are chunk s of the row, one 16-byte store per row
+// and lane.
 __device__ __forceinline__ void store_rows(bf16 *tile, const uint4 (&t)[16], int lane) {
     const int s = lane & 15;
-    const int q0 = 4 * (s >> 2) + 2 * (s & 1), within = 8 * ((s >> 1) & 1);
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
         const int r = 4 * m + (lane >> 4);
-        char *b = reinterpret_cast<char *>(tile);
-        *reinterpret_cast<uint2 *>(b + woff(r, q0) + within) = make_uint2(t[m].x, t[m].y);
-        *reinterpret_cast<uint2 *>(b + woff(r, q0 + 1) + within) = make_uint2(t[m].z, t[m].w);
+        *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(tile) + woff(r, s)) = t[m];
     }
 }
 
@@ -252,12 +252,65 @@ __device__ __forceinline__ void gram_to_ab(KT kt, const float *G2, const float *
 // Each level runs over all listed blocks before the next, so their dependent
 // chains interleave.  Out: P[j] (bf16 B layout of T'_aa, which as an A
 // operand is T'_aa^T) and Qf[j] (fp32 A layout of T'_aa).
+// Per-lane 0/1 multipliers of diag_inverse (they depend on the lane only, so a
+// caller that inverts many blocks forms them once).  For lane (i, g) and
+// element e, x = 4g + e:
+//   tb[e]   = 1 where B layout entry (x, i) lies in a 2 x 2 diagonal block below
+//             the diagonal (x = i + 1, i even),
+//   two[e]  = 1 where A layout entry (i, x) does (i = x + 1, x even),
+//   lvl[l][e] = 1 where A layout entry (i, x), x < i, joins two 2^(l+1) blocks
+//             into one 2^(l+2) block (the highest bit in which i and x differ
+//             is bit l + 1),
+//   eye[e]  = 1 on the diagonal (x = i).
+struct InvMasks {
+    f32x4 tb, two, eye, lvl[3];
+};
+__device__ __forceinline__ InvMasks inv_masks(int lane) {
+    const int li = lane & 15, lg = lane >> 4;
+    InvMasks m;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int x = 4 * lg + e;
+        m.tb[e] = (x == li + 1 && !(li & 1)) ? 1.f : 0.f;
+        m.two[e] = (li == x + 1 && !(x & 1)) ? 1.f : 0.f;
+        m.eye[e] = x == li ? 1.f : 0.f;
+#pragma unroll
+        for (int l = 0; l < 3; ++l)
+            m.lvl[l][e] = (x < li && (li >> (l + 2)) == (x >> (l + 2)) && (li >> (l + 1)) != (x >> (l + 1))) ? 1.f
+                                                                                                               : 0.f;
+    }
+    return m;
+}
+
+// Inverses of diagonal 16 x 16 blocks of T' = (I + A0 diag(beta))^{-1}, for
+// the NBLK blocks listed in blk (compile-time constants), from the raw Gram
+// blocks of gram_to_ab.  With N = (A0 diag(beta))_aa, strictly lower
+// triangular, the inverse is built by recursive doubling of the block size:
+// T_1 = I - N restricted to the 2 x 2 diagonal blocks (exact), then for
+// l = 2, 4, 8, with B_l the part of N that joins two l x l diagonal blocks into
+// one 2l x 2l block,
+//   T_{2l} = T_l - T_l B_l T_l,
+// which is the block formula [[A, 0], [B, D]]^{-1} = [[A^-1, 0],
+// [-D^-1 B A^-1, D^-1]] applied to every 2l block at once.  Every product
+// involves entries of the inverse itself, so nothing grows beyond it; the
+// expansion (I - N)(I + N^2)(I + N^4)(I + N^8) does the same in exact
+// arithmetic, but its powers of N reach binomial sizes (6435 for a key
+// repeated over 16 tokens with beta = 1, g = 0), and rounding them to bf16
+// loses the result.  T is kept in fp32 in both operand layouts (B layout TB:
+// lane (j, g) holds T[4g+e][j]; A layout TA: lane (i, g) holds T[i][4g+e]):
+//   W' = -B_l T (A = -B_l, B = T);  T <- T + T W' (A = T, B = W');
+//   T^T <- T^T + W'^T T^T (A = W'^T, whose A layout is W''s B layout; B = T^T,
+//   whose B layout is T's A layout).
+// Each level runs over all listed blocks before the next, so their dependent
+// chains interleave.  Out: P[j] (bf16 B layout of T'_aa, which as an A
+// operand is T'_aa^T) and Qf[j] (fp32 A layout of T'_aa).
 template <int NBLK>
 __device__ __forceinline__ void diag_inverse(const int (&blk)[NBLK], const uint2 (*ab)[64], const float *G2,
-                                             const float *Bv, int lane, bf16x4 (&P)[NBLK], f32x4 (&Qf)[NBLK]) {
+                                             const float *Bv, int lane, const InvMasks &m, bf16x4 (&P)[NBLK],
+                                             f32x4 (&Qf)[NBLK]) {
     const int li = lane & 15, lg = lane >> 4;
     f32x4 TB[NBLK], TA[NBLK];
-    bf16x4 BL[3][NBLK];   // A layout of B_l, l = 2, 4, 8
+    bf16x4 BL[3][NBLK];   // A layout of -B_l, l = 2, 4, 8
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) {
         const int aa = blk[j];
@@ -267,39 +320,34 @@ __device__ __forceinline__ void diag_inverse(const int (&blk)[NBLK], const uint2
         // raw k_{16a+4g+e} . k_{16a+j} (symmetric): B layout entry (r = 16a+4g+e,
         // s = 16a+j) if s < r, A layout entry (r' = 16a+j, s' = 16a+4g+e) if s' < r'
         const bf16x4 kk4 = __builtin_bit_cast(bf16x4, ab[6 + aa][lane]);
-        f32x4 vb, va, bl[3];
+        f32x4 bl[3];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int x = 4 * lg + e;
             // exp(G_r - G_s) of the one layout entry that is kept (r > s), with
             // its sign, so that increasing decays (g > 0) stay exact
-            const float ex = ex2(li < x ? Gr4[e] - Gc : Gc - Gr4[e]);
-            const float kv = (float)kk4[e];
-            vb[e] = (li < x) ? Bc * ex * kv : 0.f;
-            va[e] = (x < li) ? Br4[e] * ex * kv : 0.f;
-            const float d = (x == li) ? 1.f : 0.f;
-            const bool same2 = (li >> 1) == (x >> 1);
-            TB[j][e] = d - (same2 ? vb[e] : 0.f);
-            TA[j][e] = d - (same2 ? va[e] : 0.f);
+            const float kx = ex2(li < x ? Gr4[e] - Gc : Gc - Gr4[e]) * (float)kk4[e];
+            // A layout entry N[i][x] (x < i, beta of column x); zero elsewhere
+            const float va = x < li ? Br4[e] * kx : 0.f;
+            TB[j][e] = __builtin_fmaf(-m.tb[e] * Bc, kx, m.eye[e]);
+            TA[j][e] = __builtin_fmaf(-m.two[e], va, m.eye[e]);
 #pragma unroll
-            for (int lv = 0; lv < 3; ++lv)
-                bl[lv][e] = ((li >> (lv + 2)) == (x >> (lv + 2)) && (li >> (lv + 1)) != (x >> (lv + 1))) ? va[e]
-                                                                                                         : 0.f;
+            for (int l = 0; l < 3; ++l) bl[l][e] = -m.lvl[l][e] * va;
         }
 #pragma unroll
-        for (int lv = 0; lv < 3; ++lv) BL[lv][j] = to4(bl[lv]);
+        for (int l = 0; l < 3; ++l) BL[l][j] = to4(bl[l]);
     }
 #pragma unroll
-    for (int lv = 0; lv < 3; ++lv) {
+    for (int l = 0; l < 3; ++l) {
         f32x4 W[NBLK];
 #pragma unroll
-        for (int j = 0; j < NBLK; ++j) W[j] = mma16(BL[lv][j], to4(TB[j]), zero4());
+        for (int j = 0; j < NBLK; ++j) W[j] = mma16(BL[l][j], to4(TB[j]), zero4());
 #pragma unroll
         for (int j = 0; j < NBLK; ++j) {
-            const bf16x4 wn = to4(-W[j]);
+            const bf16x4 w = to4(W[j]);
             const bf16x4 ta = to4(TA[j]);
-            TB[j] = mma16(ta, wn, TB[j]);
-            TA[j] = mma16(wn, ta, TA[j]);
+            TB[j] = mma16(ta, w, TB[j]);
+            TA[j] = mma16(w, ta, TA[j]);
         }
     }
 #pragma unroll
@@ -393,13 +441,13 @@ __device__ __forceinline__ void offdiag_store(const uint2 (*ab)[64], const float
 
 // T' = (I + A0 diag(beta))^{-1} from the tiles of gram_to_ab, by one wave:
 // the four diagonal inverses interleaved, then the off-diagonal blocks (see
-// offdiag_store for tb and tg).
+// offdiag_store for tb and tg); m from inv_masks(lane).
 __device__ __forceinline__ void invert_tprime(const uint2 (*ab)[64], const float *G2, const float *Bv,
-                                              bf16 *tb, bf16 *tg, int lane) {
+                                              bf16 *tb, bf16 *tg, int lane, const InvMasks &m) {
     const int all[4] = {0, 1, 2, 3};
     bf16x4 P[4];
     f32x4 Qf[4];
-    diag_inverse(all, ab, G2, Bv, lane, P, Qf);
+    diag_inverse(all, ab, G2, Bv, lane, m, P, Qf);
     offdiag_store(ab, G2, P, Qf, tb, tg, lane);
 }
 

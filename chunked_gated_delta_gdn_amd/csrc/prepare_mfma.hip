@@ -136,7 +136,7 @@ __global__ __launch_bounds__(NTP) void prepare_mfma_kernel(PrepArgs a) {
         auto one = [&](const int (&b)[1]) {
             bf16x4 P[1];
             f32x4 Qf[1];
-            diag_inverse(b, sm.ab, sm.G2, sm.B, lane, P, Qf);
+            diag_inverse(b, sm.ab, sm.G2, sm.B, lane, inv_masks(lane), P, Qf);
             sm.dg.P[b[0]][lane] = __builtin_bit_cast(uint2, P[0]);
             sm.dg.Qf[b[0]][lane] = Qf[0];
         };

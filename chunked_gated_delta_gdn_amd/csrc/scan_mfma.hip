@@ -43,10 +43,17 @@
 //      wave 7: the per-row decay factors, and K^T diag(exp(G_C - G) beta) by
 //              identity MFMAs (the operand of the state update).
 //  * Every LDS operand tile stores the eight k-slots a lane group feeds to a
-//    16x16x32 MFMA in one 16-byte run, with the slot order chosen so that two
+//    16x16x32 MFMA in one 16-byte run.  Where the reduction runs over the
+//    tokens of a chunk (T', attn, K^T), the slot order is chosen so that two
 //    accumulator tiles (rows 0-15, 16-31) are directly the B operand of the
-//    next product: the sequential path never goes through LDS.  16-byte chunks
-//    are XOR-swizzled by row (woff, noff) against LDS bank conflicts.
+//    next product: the sequential path never goes through LDS.  The q, k (and
+//    w) row tiles keep their elements in natural order, stored as whole rows;
+//    the state rows are permuted to match instead: accumulator row
+//    32b + 16h + 4g + e of X holds state row 32b + 8g + 4h + e (srow),
+//    so that pack_pair of accumulator tiles 2b, 2b + 1 meets k-slots
+//    8g .. 8g+7 of block b in their natural order.  The permutation only shows
+//    where states enter and leave (h_in, h_out, M, U).  16-byte chunks are
+//    XOR-swizzled by row (woff, noff) against LDS bank conflicts.
 //  * Barriers wait for LDS traffic only, so register prefetches stay in flight
 //    across them.
 #include "dev_common.h"
@@ -74,6 +81,8 @@ template <> struct Lds<false> {
     float B[2][C];          // beta (zero past the chunk end)
     float gam[2][C];        // exp(G_r); gam[63] = exp(G_C)
     float kdec[2][C];       // exp(G_C - G_r) beta_r (folded into the kT tile)
+    float Gb[2][C];         // G2 - log2|beta|: exp2(G2_r - Gb_s) = exp(G_r - G_s) |beta_s|
+    int negb[2];            // 1 if some beta of the chunk is negative
 };
 // WY factors read from a workspace: w rows replace the k rows as the
 // consumers' operand, there is no Gram or T'; k is read only by producers, so
@@ -112,6 +121,11 @@ __device__ __forceinline__ ScanUnit scan_unit(const UnitRef &r, int h) {
 
 // Workgroup id -> (unit, column half): the two halves of a unit are 8 ids apart,
 // so that round-robin dispatch puts them on one XCD.
+// State row held by element e of accumulator tile t in lane group g (see the
+// layout notes above): accumulator row 16t + 4g + e is state row
+// 8g + srow(t, e), srow(t, e) = 32(t / 2) + 4(t % 2) + e (a constant).
+__host__ __device__ constexpr int srow(int t, int e) { return 32 * (t >> 1) + 4 * (t & 1) + e; }
+
 __device__ __forceinline__ int unit_of_block(int bid) { return ((bid >> 4) << 3) | (bid & 7); }
 __device__ __forceinline__ int half_of_block(int bid) { return (bid >> 3) & 1; }
 
@@ -155,15 +169,17 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
             for (int t = 0; t < 8; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    X[0][t][e] = hin ? hin[(slot * K + 16 * t + 4 * lg + e) * V + col_w + li] : 0.f;
+                    X[0][t][e] = hin ? hin[(slot * K + 8 * lg + srow(t, e)) * V + col_w + li] : 0.f;
         } else {
+            // M starts as the identity: state row 8g + srow(t, e) == column col_w + 16n + j
+            const int diag = 8 * lg - col_w - li;
 #pragma unroll
             for (int n = 0; n < NCT; ++n)
 #pragma unroll
                 for (int t = 0; t < 8; ++t)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        X[n][t][e] = (is_M && 16 * t + 4 * lg + e == col_w + 16 * n + li) ? 1.f : 0.f;
+                        X[n][t][e] = (is_M && diag == 16 * n - srow(t, e)) ? 1.f : 0.f;
         }
         // value rows of this wave's columns, A layout of a 16x16x16 operand:
         // lane (i, g) holds v[16 c + i][col 4g .. 4g+3]
@@ -258,28 +274,36 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                 if (EMIT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            // -- O = Q X (emitting), reading T' and the decays meanwhile
+            // -- O^T = X^T Q^T (emitting), reading T' and the decays meanwhile.  The
+            // output is formed transposed: the operands are the same registers
+            // with their roles swapped (the B layout of X is the A layout of
+            // X^T, the A layout of Q the B layout of Q^T), and tile c of O^T
+            // leaves lane (j, g) holding row 16c + j, columns 4g .. 4g+3 of O --
+            // eight contiguous bytes of an output row.
             const float *gam = sm.gam[b2];
             f32x4 O[4];
             bf16x8 ta[6];    // T' tiles (c, kk), kk <= c / 2
-            f32x4 gv[4];
+            f32x4 gv[4];     // gamma at rows 16c + 4g + e (B layout rows)
+            float gr[4];     // gamma at row 16c + j (the rows of O^T's columns)
 #pragma unroll
             for (int c = 0; c < 4; ++c) O[c] = zero4();
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                if (EMIT) O[i & 3] = mma32(qa[i], hb[0][i >> 2], O[i & 3]);
+                if (EMIT) O[i & 3] = mma32(hb[0][i >> 2], qa[i], O[i & 3]);
                 if (i < 6) {
                     const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
                     if constexpr (!WY) ta[i] = ldv(sm.tb[b2], noff(16 * c + li, 4 * kk + lg));
                 } else if (i < 10) {
                     gv[i - 6] = *reinterpret_cast<const f32x4 *>(&gam[16 * (i - 6) + 4 * lg]);
+                } else if (EMIT && i < 14) {
+                    gr[i - 10] = gam[16 * (i - 10) + li];
                 }
             }
             if (EMIT) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (i < 10 && (!WY || i >= 6)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (i < 14 && (!WY || i >= 6)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -339,16 +363,15 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
 #pragma unroll
                 for (int n = 0; n < NCT; ++n) dk[n][kk] = pack_pair(D[n][2 * kk], D[n][2 * kk + 1]);
             if (EMIT) {
-                // attn delta = (attn diag(beta)) D when recomputing (the attn tile carries
-                // beta on its columns), attn D when the WY factors are given
+                // (attn delta)^T = D^T (attn diag(beta))^T when recomputing (the attn
+                // tile carries beta on its columns), D^T attn^T when the WY factors
+                // are given; gamma_r scales column r of O^T
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) O[c][e] *= gv[c][e];
+                for (int c = 0; c < 4; ++c) O[c] *= gr[c];
 #pragma unroll
                 for (int i = 0; i < 6; ++i) {
                     const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
-                    O[c] = mma32(at6[i], dk[0][kk], O[c]);
+                    O[c] = mma32(dk[0][kk], at6[i], O[c]);
                 }
             }
             // -- X = gamma_C X + K^T diag(exp(G_C - G)) delta = gamma_C X + (K^T diag(kdec)) D
@@ -363,14 +386,11 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                     for (int n = 0; n < NCT; ++n) X[n][t] = mma32(kt16[2 * t + kk], dk[n][kk], X[n][t]);
             }
             if (EMIT) {
-                // O tile c in B layout (lane (j, g): rows 4g..4g+3, column j) ->
-                // transposed by an identity product: lane (j, g) then holds row j,
-                // columns 4g..4g+3, i.e. 8 contiguous bytes of the output row.
+                // tile c of O^T: lane (j, g) holds row 16c + j, columns 4g .. 4g+3
                 const __amdgpu_buffer_rsrc_t orr = rsrc(static_cast<bf16 *>(a.o) + tok(j, 0) * rowV);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const f32x4 ot = mma16(to4(O[c]), i16, zero4());
-                    const uint2 v = __builtin_bit_cast(uint2, to4(ot));
+                    const uint2 v = __builtin_bit_cast(uint2, to4(O[c]));
                     const int r = 16 * c + li;
                     if (L == C || r < L) bstore8(orr, (uint32_t)r * (uint32_t)(rowV * 2) + out_off, v);
                 }
@@ -387,7 +407,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                 for (int t = 0; t < 8; ++t)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        a.h_out[(so * K + 16 * t + 4 * lg + e) * V + col_w + li] = X[0][t][e];
+                        a.h_out[(so * K + 8 * lg + srow(t, e)) * V + col_w + li] = X[0][t][e];
             }
         } else {
             float *dst = is_M ? a.M_out : a.U_out;
@@ -398,7 +418,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                 for (int t = 0; t < 8; ++t)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        dst[(slot * K + 16 * t + 4 * lg + e) * ld + col_w + 16 * n + li] = X[n][t][e];
+                        dst[(slot * K + 8 * lg + srow(t, e)) * ld + col_w + 16 * n + li] = X[n][t][e];
         }
         return;
     }
@@ -443,7 +463,12 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], woff(16 * c + li, 4 * kk + lg));
-                sm.B[b2][lane] = lane < L ? bv_ : 0.f;
+                const float bl = lane < L ? bv_ : 0.f;
+                sm.B[b2][lane] = bl;
+                // log2(0) = -inf: padded columns of attn vanish
+                sm.Gb[b2][lane] = g2 - __builtin_amdgcn_logf(fabsf(bl));
+                const bool neg = __builtin_amdgcn_ballot_w64(bl < 0.f) != 0;
+                if (lane == 0) sm.negb[b2] = neg;
                 gram_to_ab([&](int c, int kk) { return kt[c][kk]; }, sm.G2[b2], sm.B[b2], sm.ab[b2], lane);
             }
         };
@@ -496,8 +521,13 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
 #pragma unroll
                     for (int bb = 0; bb <= aa; ++bb, ++i) acc[i] = mma32(kb[bb], qa[aa], acc[i]);
             }
+            // attn diag(beta) when recomputing (the factor that multiplies D), from
+            // the column exponents G2 - log2|beta| (beta = 0 zeroes padded
+            // columns), with beta multiplied in instead when some beta of the
+            // chunk is negative; plain attn for the WY factors (beta is inside
+            // u and w)
             bf16x4 at[4][4];
-            {
+            auto form = [&](const float *Gcol, bool times_beta) {
                 int i = 0;
 #pragma unroll
                 for (int aa = 0; aa < 4; ++aa) {
@@ -505,12 +535,10 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                     const float Gr = G2[r];
 #pragma unroll
                     for (int bb = 0; bb <= aa; ++bb, ++i) {
-                        const f32x4 Gs = *reinterpret_cast<const f32x4 *>(&G2[16 * bb + 4 * lg]);
-                        // attn diag(beta) when recomputing (the factor that multiplies D;
-                        // beta = 0 zeroes padded columns), plain attn for the WY factors
-                        // (beta is inside u and w)
+                        const f32x4 Gs = *reinterpret_cast<const f32x4 *>(&Gcol[16 * bb + 4 * lg]);
                         f32x4 sc = acc[i];
-                        if constexpr (!WY) sc *= *reinterpret_cast<const f32x4 *>(&sm.B[b2][16 * bb + 4 * lg]);
+                        if constexpr (!WY)
+                            if (times_beta) sc *= *reinterpret_cast<const f32x4 *>(&sm.B[b2][16 * bb + 4 * lg]);
                         f32x4 v;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -520,6 +548,12 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                         at[aa][bb] = to4(v);
                     }
                 }
+            };
+            if constexpr (WY) {
+                form(G2, false);
+            } else {
+                if (__builtin_amdgcn_readfirstlane(sm.negb[b2])) form(G2, true);
+                else form(sm.Gb[b2], false);
             }
             bf16x4 z4;
             z4[0] = z4[1] = z4[2] = z4[3] = (bf16)0.f;
@@ -567,6 +601,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
         }
         return;
     }
+    const InvMasks im = inv_masks(lane);   // (wave 4's inverse)
     // identity selectors (B operands) picking columns 0-15 / 16-31 of a 32-wide block
     bf16x8 id0, id1;
 #pragma unroll
@@ -614,7 +649,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                 }
             } else {
                 // ---- role 0: T' = (I + A0 diag(beta))^{-1} from the loader's Gram tiles
-                if constexpr (!WY) invert_tprime(sm.ab[b2], G2, sm.B[b2], sm.tb[b2], nullptr, lane);
+                if constexpr (!WY) invert_tprime(sm.ab[b2], G2, sm.B[b2], sm.tb[b2], nullptr, lane, im);
             }
         }
         lds_barrier();
