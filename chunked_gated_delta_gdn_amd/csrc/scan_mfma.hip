@@ -27,13 +27,18 @@
 //    meet in that XCD's L2.
 //  * Waves 0-3 (consumers) own 16 (emit) or 32 (carry) state columns each,
 //    kept in fp32 MFMA accumulators for the whole chain, and run the chunk
-//    step for chunk j.  Waves 4-7 (producers) work ahead, so the
+//    step for chunk j, reading the operand fragments of a k-block (or of two
+//    row tiles) while the products of the previous one run.  Each consumer
+//    shares its SIMD with one producer: a lone wave per SIMD cannot hide the
+//    LDS and MFMA latencies of the chunk step (two 32-column consumers, each
+//    alone on a SIMD, took 7.6k cycles per chunk against 4.5k for four
+//    16-column ones).  Waves 4-7 (producers) work ahead, so the
 //    latency-bound preparation overlaps the scan; one barrier per chunk:
 //      wave 4: the inverse T = (I + A)^{-1} for chunk j+1, all on MFMA:
-//              diagonal 16 x 16 blocks by the product
-//              (I - N)(I + N^2)(I + N^4)(I + N^8), off-diagonal blocks by block
-//              recursion on T^T so that T comes out row-major, ready as the A
-//              operand of T diag(beta);
+//              diagonal 16 x 16 blocks by recursive doubling of the block
+//              size (diag_inverse), off-diagonal blocks by block recursion on
+//              T^T so that T comes out row-major, ready as the A operand of
+//              T diag(beta);
 //      wave 5: loads k, g, beta of chunk j+2 (issued one chunk earlier still,
 //              so two chunks are in flight), stores k, the cumulative decay,
 //              and, from the k rows still in its registers, the Gram k k^T
@@ -131,8 +136,9 @@ __device__ __forceinline__ int half_of_block(int bid) { return (bid >> 3) & 1; }
 
 template <bool EMIT, bool WY, bool PACKED>
 __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const ScanUnit &u, int cg) {
-    constexpr int CPW = EMIT ? 16 : 32;   // state columns per consumer wave
-    constexpr int NCT = CPW / 16;
+    constexpr int CPW = EMIT ? 16 : 32;     // state columns per consumer wave
+    constexpr int NCT = CPW / 16;           // 16-column tiles per consumer wave
+    constexpr int NCONS = 4;                // consumer waves
     auto kslot = [](int64_t j) { return WY ? (int)(j & 1) : (int)(j % 3); };
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -158,7 +164,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
     };
     auto tok = [&](int64_t j, int r) -> int64_t { return sp.t0 + j * C + r; };
 
-    if (wv < 4) {
+    if (wv < NCONS) {
         // =========================== consumers ===========================
         const bool is_M = !EMIT && cg == 0;
         const int col_w = (EMIT ? 64 * cg : 0) + CPW * wv;   // first state column
@@ -166,10 +172,12 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
         if (EMIT) {
             const float *hin = a.h_in;
 #pragma unroll
-            for (int t = 0; t < 8; ++t)
+            for (int n = 0; n < NCT; ++n)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    X[0][t][e] = hin ? hin[(slot * K + 8 * lg + srow(t, e)) * V + col_w + li] : 0.f;
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        X[n][t][e] = hin ? hin[(slot * K + 8 * lg + srow(t, e)) * V + col_w + 16 * n + li] : 0.f;
         } else {
             // M starts as the identity: state row 8g + srow(t, e) == column col_w + 16n + j
             const int diag = 8 * lg - col_w - li;
@@ -205,10 +213,6 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                 return;
             }
             const int L = chunk_len(j);
-            // (the base includes the wave's columns, so the descriptor is not
-            // wave-uniform to the compiler; moving col_w into the lane offset
-            // removes about 50 instructions per chunk but measured 4% slower:
-            // the consumers then crowd the producers sharing their SIMDs)
             const __amdgpu_buffer_rsrc_t vr = rsrc(gv + tok(j, 0) * rowV + h * V + col_w);
             const uint32_t lim = (uint32_t)(L - 1) * row_bytes_v;
 #pragma unroll
@@ -232,81 +236,64 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
             const bf16 *kR;
             if constexpr (WY) kR = sm.wR[b2];
             else kR = sm.kR[kslot(j)];
-            // LDS operands are read in batches ahead of the products that use
-            // them (the scheduler would otherwise place each read just before its
-            // product and pay the LDS latency once per product).  Group
-            // barriers interleave the reads of the next phase with the current
-            // phase's products.
-            // -- k tiles of the chunk
-            bf16x8 ka[16];   // [kk][c]
-#pragma unroll
-            for (int i = 0; i < 16; ++i) ka[i] = ldv(kR, woff(16 * (i & 3) + li, 4 * (i >> 2) + lg));
-            __builtin_amdgcn_sched_barrier(0);
-            // value tiles of this chunk in B layout, then prefetch the next chunk's
-            f32x4 Vt[NCT][4];
-#pragma unroll
-            for (int n = 0; n < NCT; ++n)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    Vt[n][c] = mma16(__builtin_bit_cast(bf16x4, vA[n][c]), i16, zero4());
-            if (j + 1 < n_chunks) load_v(j + 1);
+            // X as the operand reducing over the state rows
             bf16x8 hb[NCT][4];
 #pragma unroll
             for (int n = 0; n < NCT; ++n)
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) hb[n][kk] = pack_pair(X[n][2 * kk], X[n][2 * kk + 1]);
-            // -- Y = K X, reading the q tiles meanwhile
+            // -- Y = K X, k-block by k-block, the next block's fragments read
+            // during the current block's products (each fragment feeds NCT
+            // products, so one block ahead covers the LDS latency)
             f32x4 Y[NCT][4];
 #pragma unroll
             for (int n = 0; n < NCT; ++n)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) Y[n][c] = zero4();
-            bf16x8 qa[16];
+            {
+                bf16x8 ka[2][4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+                for (int c = 0; c < 4; ++c) ka[0][c] = ldv(kR, woff(16 * c + li, lg));
 #pragma unroll
-                for (int n = 0; n < NCT; ++n) Y[n][i & 3] = mma32(ka[i], hb[n][i >> 2], Y[n][i & 3]);
-                if (EMIT) qa[i] = ldv(sm.qR[b2], woff(16 * (i & 3) + li, 4 * (i >> 2) + lg));
+                for (int kk = 0; kk < 4; ++kk) {
+                    if (kk < 3)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) ka[(kk + 1) & 1][c] = ldv(kR, woff(16 * c + li, 4 * (kk + 1) + lg));
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int n = 0; n < NCT; ++n) Y[n][c] = mma32(ka[kk & 1][c], hb[n][kk], Y[n][c]);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+                for (int i = 0; i < 12; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, NCT, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * NCT, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, NCT, 0);
-                if (EMIT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // -- O^T = X^T Q^T (emitting), reading T' and the decays meanwhile.  The
-            // output is formed transposed: the operands are the same registers
-            // with their roles swapped (the B layout of X is the A layout of
-            // X^T, the A layout of Q the B layout of Q^T), and tile c of O^T
-            // leaves lane (j, g) holding row 16c + j, columns 4g .. 4g+3 of O --
-            // eight contiguous bytes of an output row.
+            // value tiles of this chunk in B layout, then the next chunk's loads;
+            // T' and the decays read meanwhile
             const float *gam = sm.gam[b2];
-            f32x4 O[4];
+            f32x4 Vt[NCT][4];
             bf16x8 ta[6];    // T' tiles (c, kk), kk <= c / 2
             f32x4 gv[4];     // gamma at rows 16c + 4g + e (B layout rows)
             float gr[4];     // gamma at row 16c + j (the rows of O^T's columns)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) O[c] = zero4();
+            for (int n = 0; n < NCT; ++n)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (EMIT) O[i & 3] = mma32(hb[0][i >> 2], qa[i], O[i & 3]);
-                if (i < 6) {
-                    const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
-                    if constexpr (!WY) ta[i] = ldv(sm.tb[b2], noff(16 * c + li, 4 * kk + lg));
-                } else if (i < 10) {
-                    gv[i - 6] = *reinterpret_cast<const f32x4 *>(&gam[16 * (i - 6) + 4 * lg]);
-                } else if (EMIT && i < 14) {
-                    gr[i - 10] = gam[16 * (i - 10) + li];
-                }
-            }
-            if (EMIT) {
+                for (int c = 0; c < 4; ++c) Vt[n][c] = mma16(__builtin_bit_cast(bf16x4, vA[n][c]), i16, zero4());
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (i < 14 && (!WY || i >= 6)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
+            for (int c = 0; c < 4; ++c) {
+                gv[c] = *reinterpret_cast<const f32x4 *>(&gam[16 * c + 4 * lg]);
+                if (EMIT) gr[c] = gam[16 * c + li];
             }
-            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 6; ++i) {
+                const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
+                if constexpr (!WY) ta[i] = ldv(sm.tb[b2], noff(16 * c + li, 4 * kk + lg));
+            }
             f32x4 D[NCT][4];
             if constexpr (WY) {
                 // -- delta = u - w X (the row factors are inside u and w)
@@ -314,6 +301,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                 for (int n = 0; n < NCT; ++n)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) D[n][c] = Vt[n][c] - Y[n][c];
+                if (j + 1 < n_chunks) load_v(j + 1);
             } else {
                 // -- R = V - gamma (K X), packed as the operand reducing over the chunk
                 bf16x8 R[NCT][2];
@@ -329,6 +317,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                         }
                         R[n][kk] = pack_pair(lo, hi);
                     }
+                if (j + 1 < n_chunks) load_v(j + 1);
                 // -- D = T' R (delta = diag(beta) D)
 #pragma unroll
                 for (int n = 0; n < NCT; ++n)
@@ -341,19 +330,6 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                     for (int n = 0; n < NCT; ++n) D[n][c] = mma32(ta[i], R[n][kk], D[n][c]);
                 }
             }
-            // reading the attn tiles and k^T meanwhile
-            bf16x8 at6[6], kt16[16];
-#pragma unroll
-            for (int i = 0; i < 6; ++i) {
-                const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
-                if (EMIT) at6[i] = ldv(sm.attn[b2], noff(16 * c + li, 4 * kk + lg));
-                // k^T tiles m = 2t + kk for t = i
-                kt16[2 * i] = ldv(sm.kT[b2], noff(16 * i + li, lg));
-                kt16[2 * i + 1] = ldv(sm.kT[b2], noff(16 * i + li, 4 + lg));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 12; i < 16; ++i) kt16[i] = ldv(sm.kT[b2], noff(16 * (i >> 1) + li, 4 * (i & 1) + lg));
             // D as the operand reducing over the chunk, for both products that
             // follow: the kT tile carries the row factors of the state update and
             // the attn tile those of the output
@@ -362,38 +338,88 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int n = 0; n < NCT; ++n) dk[n][kk] = pack_pair(D[n][2 * kk], D[n][2 * kk + 1]);
-            if (EMIT) {
-                // (attn delta)^T = D^T (attn diag(beta))^T when recomputing (the attn
-                // tile carries beta on its columns), D^T attn^T when the WY factors
-                // are given; gamma_r scales column r of O^T
+            // -- X = gamma_C X + K^T diag(exp(G_C - G)) delta = gamma_C X + (K^T diag(kdec)) D,
+            // the k^T fragments of two row tiles read ahead of their products
+            const float gc = gam[63];
+            {
+                bf16x8 kt[2][4];   // [t & 1][2 (t / 2 parity) + kk] fragments of row tiles
 #pragma unroll
-                for (int c = 0; c < 4; ++c) O[c] *= gr[c];
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) kt[0][2 * t + kk] = ldv(sm.kT[b2], noff(16 * t + li, 4 * kk + lg));
+#pragma unroll
+                for (int tp = 0; tp < 4; ++tp) {   // row tiles 2tp, 2tp + 1
+                    if (tp < 3)
+#pragma unroll
+                        for (int t = 0; t < 2; ++t)
+#pragma unroll
+                            for (int kk = 0; kk < 2; ++kk)
+                                kt[(tp + 1) & 1][2 * t + kk] =
+                                    ldv(sm.kT[b2], noff(16 * (2 * tp + 2 + t) + li, 4 * kk + lg));
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int n = 0; n < NCT; ++n) {
+                            X[n][2 * tp + t] *= gc;
+#pragma unroll
+                            for (int kk = 0; kk < 2; ++kk)
+                                X[n][2 * tp + t] = mma32(kt[tp & 1][2 * t + kk], dk[n][kk], X[n][2 * tp + t]);
+                        }
+                }
+            }
+            if (EMIT) {
+                // -- O^T = X^T Q^T + D^T (attn diag(beta))^T, formed transposed: the
+                // operands are the registers of X (B layout of X = A layout of X^T)
+                // and the q row fragments (A layout of Q = B layout of Q^T), and
+                // tile c of O^T leaves lane (j, g) holding row 16c + j, columns
+                // 4g .. 4g+3 of O -- eight contiguous bytes of an output row.
+                // (attn diag(beta) when recomputing: the attn tile carries beta on
+                // its columns; attn alone when the WY factors are given.)
+                f32x4 O[NCT][4];
+#pragma unroll
+                for (int n = 0; n < NCT; ++n)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) O[n][c] = zero4();
+                bf16x8 qa[2][4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) qa[0][c] = ldv(sm.qR[b2], woff(16 * c + li, lg));
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    if (kk < 3)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            qa[(kk + 1) & 1][c] = ldv(sm.qR[b2], woff(16 * c + li, 4 * (kk + 1) + lg));
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int n = 0; n < NCT; ++n) O[n][c] = mma32(hb[n][kk], qa[kk & 1][c], O[n][c]);
+                }
+                bf16x8 at6[6];
 #pragma unroll
                 for (int i = 0; i < 6; ++i) {
                     const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
-                    O[c] = mma32(dk[0][kk], at6[i], O[c]);
+                    at6[i] = ldv(sm.attn[b2], noff(16 * c + li, 4 * kk + lg));
                 }
-            }
-            // -- X = gamma_C X + K^T diag(exp(G_C - G)) delta = gamma_C X + (K^T diag(kdec)) D
-            const float gc = gam[63];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+                for (int n = 0; n < NCT; ++n)
 #pragma unroll
-                for (int n = 0; n < NCT; ++n) X[n][t] *= gc;
+                    for (int c = 0; c < 4; ++c) O[n][c] *= gr[c];
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
+                for (int i = 0; i < 6; ++i) {
+                    const int c = i < 1 ? 0 : i < 2 ? 1 : i < 4 ? 2 : 3, kk = (i == 3 || i == 5) ? 1 : 0;
 #pragma unroll
-                    for (int n = 0; n < NCT; ++n) X[n][t] = mma32(kt16[2 * t + kk], dk[n][kk], X[n][t]);
-            }
-            if (EMIT) {
-                // tile c of O^T: lane (j, g) holds row 16c + j, columns 4g .. 4g+3
+                    for (int n = 0; n < NCT; ++n) O[n][c] = mma32(dk[n][kk], at6[i], O[n][c]);
+                }
                 const __amdgpu_buffer_rsrc_t orr = rsrc(static_cast<bf16 *>(a.o) + tok(j, 0) * rowV);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint2 v = __builtin_bit_cast(uint2, to4(O[c]));
-                    const int r = 16 * c + li;
-                    if (L == C || r < L) bstore8(orr, (uint32_t)r * (uint32_t)(rowV * 2) + out_off, v);
-                }
+                for (int n = 0; n < NCT; ++n)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint2 v = __builtin_bit_cast(uint2, to4(O[n][c]));
+                        const int r = 16 * c + li;
+                        if (L == C || r < L)
+                            bstore8(orr, (uint32_t)r * (uint32_t)(rowV * 2) + out_off + 32u * n, v);
+                    }
             }
             lds_barrier();
         }
@@ -404,10 +430,12 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                 // kept live through the loop)
                 const int64_t so = PACKED ? u.out_slot : (int64_t)sp.seq * H + h;
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
+                for (int n = 0; n < NCT; ++n)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        a.h_out[(so * K + 8 * lg + srow(t, e)) * V + col_w + li] = X[0][t][e];
+                    for (int t = 0; t < 8; ++t)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            a.h_out[(so * K + 8 * lg + srow(t, e)) * V + col_w + 16 * n + li] = X[n][t][e];
             }
         } else {
             float *dst = is_M ? a.M_out : a.U_out;
@@ -431,9 +459,8 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
     // their loop unrolled by two so each register set has a fixed home, and
     // always issue a load (of the last chunk when past the end).
     const int role = wv - 4;
-    if (n_chunks == 0) {
-        lds_barrier();
-        lds_barrier();
+    if (n_chunks == 0 || role < 0) {
+        for (int64_t it = -2; it < n_chunks; ++it) lds_barrier();
         return;
     }
     auto clampj = [&](int64_t j) { return j < n_chunks ? j : n_chunks - 1; };
