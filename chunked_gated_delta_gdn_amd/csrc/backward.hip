@@ -495,9 +495,14 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
     for (int e = 0; e < 4; ++e)
         hacc[e] = a.h0 ? a.h0[((int64_t)n * H + h) * KV + (int64_t)(row0 + e) * V + j0 + li] : 0.f;
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
-    // next chunk: w rows (A operands of delta, waves 0-3), u seeds, raw k, g
+    // next chunk: w rows (A operands of delta, waves 0-3), u seeds, raw k, g.
+    // Rows past the chunk end are loaded from its last row (every address
+    // valid) and zeroed where they are used, a chunk later: a load whose value
+    // is masked or converted at once would make the wave wait for it here.
     f32x4 pw[8];
-    float pu[4], pk[KPT], pg = 0.f;
+    float pu[4], pg = 0.f;
+    typename Elem<T>::raw_t pk[KPT];
+    int pL = 0;
     auto fetch = [&](int64_t c) {
         int L;
         int64_t tc;
@@ -514,9 +519,10 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
             const int e = tid + NT * m, r = e / K, i = e % K;
-            pk[m] = r < L ? Elem<T>::load(a.k, (tc + r) * rowK + hk * K + i) : 0.f;
+            pk[m] = Elem<T>::load_raw(a.k, (tc + min(r, L - 1)) * rowK + hk * K + i);
         }
-        pg = tid < C && tid < L ? a.g[(tc + tid) * H + h] : 0.f;
+        pg = a.g[(tc + min(tid, L - 1)) * H + h];
+        pL = L;
     };
     if (nch > 0) fetch(0);
     for (int64_t c = 0; c < nch; ++c) {
@@ -526,9 +532,9 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
             const int e = tid + NT * m;
-            kT[(e % K) * LDC + e / K] = pk[m];
+            kT[(e % K) * LDC + e / K] = e / K < pL ? Elem<T>::from_raw(pk[m]) : 0.f;
         }
-        if (tid < 64) chunk_decay<C>(pg, sG, sEg, sEk);
+        if (tid < 64) chunk_decay<C>(tid < C && tid < pL ? pg : 0.f, sG, sEg, sEk);
         __syncthreads();
         f32x4 wc[8];
         float uc[4];
@@ -597,7 +603,11 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
     for (int e = 0; e < 4; ++e)
         dacc[e] = a.dhT ? a.dhT[((int64_t)n * H + h) * KV + (int64_t)(row0 + e) * V + j0 + li] : 0.f;
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
-    float pk[KPT], pq[KPT], pw[KPT], pa[APT], pd[DPT], pg = 0.f;
+    // the previous chunk's operands, fetched a chunk ahead (rows past the chunk
+    // end loaded from its last row and zeroed where used, as in the states scan)
+    typename Elem<T>::raw_t pk[KPT], pq[KPT], pd[DPT];
+    float pw[KPT], pa[APT], pg = 0.f;
+    int pL = 0;
     auto fetch = [&](int64_t c) {
         int L;
         int64_t tc;
@@ -607,20 +617,20 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
             const int e = tid + NT * m, r = e / K, i = e % K;
-            const bool ok = r < L;
-            const int64_t x = (tc + r) * rowK + hk * K + i;
-            pk[m] = ok ? Elem<T>::load(a.k, x) : 0.f;
-            pq[m] = ok ? Elem<T>::load(a.q, x) : 0.f;
+            const int64_t x = (tc + min(r, L - 1)) * rowK + hk * K + i;
+            pk[m] = Elem<T>::load_raw(a.k, x);
+            pq[m] = Elem<T>::load_raw(a.q, x);
             pw[m] = w[e];
         }
 #pragma unroll
         for (int m = 0; m < APT; ++m) pa[m] = attn[tid + NT * m];
 #pragma unroll
         for (int m = 0; m < DPT; ++m) {
-            const int e = tid + NT * m, t = e / NCOL, jj = e % NCOL;
-            pd[m] = t < L ? Elem<T>::load(a.dout, (tc + t) * rowV + h * V + j0 + jj) : 0.f;
+            const int e = tid + NT * m, t = min(e / NCOL, L - 1), jj = e % NCOL;
+            pd[m] = Elem<T>::load_raw(a.dout, (tc + t) * rowV + h * V + j0 + jj);
         }
-        pg = tid < C && tid < L ? a.g[(tc + tid) * H + h] : 0.f;
+        pg = a.g[(tc + min(tid, L - 1)) * H + h];
+        pL = L;
     };
     if (nch > 0) fetch(nch - 1);
     for (int64_t c = nch - 1; c >= 0; --c) {
@@ -630,8 +640,9 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
             const int e = tid + NT * m, r = e / K, i = e % K;
-            sk[r * LDK + i] = pk[m];
-            qT[i * LDC + r] = pq[m];
+            const bool ok = r < pL;
+            sk[r * LDK + i] = ok ? Elem<T>::from_raw(pk[m]) : 0.f;
+            qT[i * LDC + r] = ok ? Elem<T>::from_raw(pq[m]) : 0.f;
             wT[i * LDC + r] = pw[m];
         }
 #pragma unroll
@@ -642,9 +653,9 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < DPT; ++m) {
             const int e = tid + NT * m;
-            doT[(e % NCOL) * LDC + e / NCOL] = pd[m];
+            doT[(e % NCOL) * LDC + e / NCOL] = e < C * NCOL && e / NCOL < pL ? Elem<T>::from_raw(pd[m]) : 0.f;
         }
-        if (tid < 64) chunk_decay<C>(pg, sG, sEg, sEk);
+        if (tid < 64) chunk_decay<C>(tid < C && tid < pL ? pg : 0.f, sG, sEg, sEk);
         __syncthreads();
         if (c > 0) fetch(c - 1);
         if (wv < 4) {

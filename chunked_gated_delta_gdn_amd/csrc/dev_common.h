@@ -25,19 +25,31 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 template <typename T> struct Elem;
 
+// load_raw / from_raw split a load from its conversion, so that a value
+// fetched ahead of its use does not make the loading wave wait for it.
 template <> struct Elem<float> {
+    typedef float raw_t;
     static __device__ __forceinline__ float load(const void *p, int64_t i) {
         return static_cast<const float *>(p)[i];
     }
+    static __device__ __forceinline__ raw_t load_raw(const void *p, int64_t i) {
+        return static_cast<const float *>(p)[i];
+    }
+    static __device__ __forceinline__ float from_raw(raw_t x) { return x; }
     static __device__ __forceinline__ void store(void *p, int64_t i, float x) {
         static_cast<float *>(p)[i] = x;
     }
 };
 
 template <> struct Elem<bf16_t> {
+    typedef uint16_t raw_t;
     static __device__ __forceinline__ float load(const void *p, int64_t i) {
         return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
     }
+    static __device__ __forceinline__ raw_t load_raw(const void *p, int64_t i) {
+        return static_cast<const uint16_t *>(p)[i];
+    }
+    static __device__ __forceinline__ float from_raw(raw_t x) { return bf16_to_f32(x); }
     static __device__ __forceinline__ void store(void *p, int64_t i, float x) {
         static_cast<uint16_t *>(p)[i] = f32_to_bf16(x);
     }
