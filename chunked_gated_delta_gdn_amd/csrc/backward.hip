@@ -1212,6 +1212,412 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     }
 }
 
+// ------------------------------------------------------ 4b. grads, K = V = 128, C = 64
+// The same gradients as bwd_grads_kernel (bf16 inputs), arranged so that every operand of a
+// matrix-core loop comes from LDS: the chunk's rows of do, k, v and q are
+// staged once (coalesced 16-byte loads) into regions whose earlier contents
+// are dead, and h, dh are fetched into registers before the staging so their
+// latency overlaps it.  Row and column sums and the final reverse cumulative
+// sum run over many threads (each combination in a fixed order, so two calls
+// give the same bits).  Products are 16 x 16 fp32 matrix-core tiles as in the
+// state scans: lane (li, lg) gives A[li][k] and B[k][li] with
+// k = 4 (4 q + lg) + e, and holds D[4 lg + e][li].
+template <typename T>
+__global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
+    static_assert(sizeof(typename Elem<T>::raw_t) == 2, "k, v, q rows are staged as bf16");
+    constexpr int K = 128, V = 128, C = 64, NT = 512, NW = 8;
+    constexpr int VP = V + 4;   // fp32 rows of C x V tiles (16-byte aligned; 16 rows hit distinct banks)
+    constexpr int CP = C + 1;   // fp32 rows of C x C tiles and of dw^T [K][CP]
+    constexpr int RS = K + 4;   // bf16 rows of the staged k, v rows [C][RS]
+    constexpr int TS = C + 4;   // bf16 rows of the staged k^T, q^T [K][TS] (8-byte aligned)
+    constexpr int R1F = 2 * K * TS / 2 > C * VP ? 2 * K * TS / 2 : C * VP;
+    typedef uint16_t u16;
+    // LDS regions, reused as their contents die:
+    //   R1: delta [C][VP] -> k, v rows (bf16 [C][RS] each) -> Z [C][CP] -> k^T, q^T (bf16 [K][TS] each)
+    //   R2: do [C][VP] (fp32) -> dw^T [K][CP]
+    __shared__ __attribute__((aligned(16))) float R1[R1F];
+    __shared__ __attribute__((aligned(16))) float bdD[C * VP];   // ddelta
+    __shared__ __attribute__((aligned(16))) float R2[C * VP];
+    __shared__ float bT[C * CP];   // T
+    __shared__ float bX[C * CP];   // dattn
+    __shared__ float bY[C * CP];   // dT^T, then dA
+    static_assert(2 * C * RS * 2 <= R1F * 4 && 2 * K * TS * 2 <= R1F * 4 && K * CP <= C * VP &&
+                      C * CP <= R1F && (RS * 2) % 8 == 0 && (TS * 2) % 8 == 0,
+                  "staged tiles fit their regions; bf16 rows keep 8-byte alignment");
+    float *const bD = R1, *const bZ = R1, *const bdo = R2, *const bW = R2;
+    u16 *const rk = reinterpret_cast<u16 *>(R1), *const rv = rk + C * RS;   // k, v rows
+    u16 *const tk = reinterpret_cast<u16 *>(R1), *const tq = tk + K * TS;   // k^T, q^T
+    __shared__ float sG[C], sEg[C], sEk[C], sb[C];
+    __shared__ float sPw[NW * C], sBw[NW * C], sLast[NW], sRowA[C], sColA[C], sRowB[C];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+    const int H = a.H;
+    const int h = blockIdx.x % H;
+    const int64_t chunk = blockIdx.x / H;
+    const ChunkLoc cl = locate_chunk(a.ct, chunk, C);
+    const int L = cl.L;
+    const int64_t tc = cl.tc;
+    const int64_t rowK = (int64_t)a.Hk * K, rowV = (int64_t)H * V;
+    const int hk = h / (H / a.Hk);
+    const int64_t ch = chunk * H + h;
+    const int64_t KV = (int64_t)K * V;
+    const float *hsT = a.hs + ch * KV, *dhsT = a.dhs + ch * KV;   // [V][K]
+    const float *attn = a.attn + ch * C * C, *Ak = a.Ak + ch * C * C;
+    const int i = 16 * wv + li;   // this lane's column of the K-wide outputs (dq, dk, dw^T rows)
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    auto put_qk = [&](void *out, float *acc, int r, int ii, float x) {
+        if (acc) acc[((tc + r) * H + h) * K + ii] = x;
+        else Elem<T>::store(out, (tc + r) * rowK + hk * K + ii, x);
+    };
+    // 8 consecutive elements of row r (clamped into the chunk) of a [T, H, D] tensor
+    auto row8 = [&](const void *base, int64_t row_elems, int64_t col0, int r) {
+        const int64_t e = (tc + min(r, L - 1)) * row_elems + col0;
+        return *reinterpret_cast<const uint4 *>(static_cast<const u16 *>(base) + e);
+    };
+    auto f32of = [](uint32_t w, int half) { return __uint_as_float(half ? (w & 0xffff0000u) : (w << 16)); };
+    // four bf16 (8 bytes) -> four floats
+    auto ld4b = [&](const u16 *p) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(p);
+        return f32x4{f32of(w.x, 0), f32of(w.x, 1), f32of(w.y, 0), f32of(w.y, 1)};
+    };
+
+    // ---- h and dh of this lane's column i, fetched first (dq, dk^~ and dw use them)
+    float hv[8][4], dhv[8][4];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * (4 * q + lg) + e;
+            hv[q][e] = hsT[(int64_t)j * K + i];
+            dhv[q][e] = dhsT[(int64_t)j * K + i];
+        }
+    // ---- staging: delta, ddelta, T (fp32 workspace), do (rows past L zero), beta, decay
+    {
+        const float *d = a.d + ch * C * V, *dd = a.dd + ch * C * V, *Tm = a.T + ch * C * C;
+#pragma unroll
+        for (int m = 0; m < (C * V / 4) / NT; ++m) {
+            const int e4 = tid + NT * m, r = (4 * e4) / V, j = (4 * e4) % V;
+            *reinterpret_cast<f32x4 *>(&bD[r * VP + j]) = *reinterpret_cast<const f32x4 *>(d + 4 * e4);
+            *reinterpret_cast<f32x4 *>(&bdD[r * VP + j]) = *reinterpret_cast<const f32x4 *>(dd + 4 * e4);
+        }
+#pragma unroll
+        for (int m = 0; m < (C * C / 4) / NT; ++m) {
+            const int e4 = tid + NT * m, r = (4 * e4) / C, c0 = (4 * e4) % C;
+            const f32x4 t = *reinterpret_cast<const f32x4 *>(Tm + 4 * e4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bT[r * CP + c0 + e] = t[e];
+        }
+#pragma unroll
+        for (int m = 0; m < (C * V / 8) / NT; ++m) {
+            const int e8 = tid + NT * m, r = (8 * e8) / V, j = (8 * e8) % V;
+            float x[8];
+            const uint4 w = row8(a.dout, rowV, h * V + j, r);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = f32of(ww[e >> 1], e & 1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bdo[r * VP + j + e] = r < L ? x[e] : 0.f;
+        }
+        if (tid < C) sb[tid] = tid < L ? a.beta[(tc + tid) * H + h] : 0.f;
+        for (int e = tid; e < NW * C; e += NT) {
+            sPw[e] = 0.f;
+            sBw[e] = 0.f;
+        }
+        if (tid < NW) sLast[tid] = 0.f;
+    }
+    load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);   // (synchronises)
+
+    // ---- dattn = causal(do delta^T): 4 x 4 tiles of C x C, wave wv owns two
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tile = 2 * wv + u, tr = tile >> 2, tcol = tile & 3;
+        const int r = 16 * tr + li, sc = 16 * tcol + li;   // A row, B column
+        f32x4 acc = z4;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int j0q = 4 * (4 * q + lg);
+            const f32x4 ao = lds4(&bdo[r * VP + j0q]), bo = lds4(&bD[sc * VP + j0q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ao[e], bo[e], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int rr = 16 * tr + 4 * lg + e;
+            bX[rr * CP + sc] = sc <= rr ? acc[e] : 0.f;
+        }
+    }
+    // ---- over V: dqg = do h^T, dkt = delta dh^T (the k_tilde gradient), and
+    // dw^T = -(h ddelta^T) for this wave's row tile of dw^T (column i of h)
+    f32x4 dqg[4], dkt[4], dwa[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dqg[t] = dkt[t] = dwa[t] = z4;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int j0q = 4 * (4 * q + lg);
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr) {
+            const int r = 16 * tr + li;
+            const f32x4 ao = lds4(&bdo[r * VP + j0q]), dl = lds4(&bD[r * VP + j0q]), dd = lds4(&bdD[r * VP + j0q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dqg[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao[e], hv[q][e], dqg[tr], 0, 0, 0);
+                dkt[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(dl[e], dhv[q][e], dkt[tr], 0, 0, 0);
+                dwa[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(hv[q][e], dd[e], dwa[tr], 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();
+    // ---- dw^T into R2 (do is dead); k, v rows into R1 (delta is dead)
+#pragma unroll
+    for (int tcol = 0; tcol < 4; ++tcol)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bW[(16 * wv + 4 * lg + e) * CP + 16 * tcol + li] = -dwa[tcol][e];
+#pragma unroll
+    for (int m = 0; m < (C * K / 8) / NT; ++m) {
+        const int e8 = tid + NT * m, r = (8 * e8) / K, j = (8 * e8) % K;
+        uint4 wk = row8(a.k, rowK, hk * K + j, r), wvv = row8(a.v, rowV, h * V + j, r);
+        if (r >= L) wk = wvv = make_uint4(0, 0, 0, 0);
+        // 8-byte stores: a row of RS bf16 is 8-byte but not 16-byte aligned
+        uint2 *pk = reinterpret_cast<uint2 *>(&rk[r * RS + j]), *pv = reinterpret_cast<uint2 *>(&rv[r * RS + j]);
+        pk[0] = make_uint2(wk.x, wk.y);
+        pk[1] = make_uint2(wk.z, wk.w);
+        pv[0] = make_uint2(wvv.x, wvv.y);
+        pv[1] = make_uint2(wvv.z, wvv.w);
+    }
+    __syncthreads();
+    // ---- dT^T[s][r] = beta_s ((V ddelta^T)[s][r] + exp(G_s) (K dw^T)[s][r]): two tiles per wave
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tile = 2 * wv + u, ts = tile >> 2, tcol = tile & 3;
+        const int sr = 16 * ts + li, rc = 16 * tcol + li;   // A row, B column
+        f32x4 av = z4, ak = z4;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int j0q = 4 * (4 * q + lg);
+            const f32x4 v4 = ld4b(&rv[sr * RS + j0q]), k4 = ld4b(&rk[sr * RS + j0q]);
+            const f32x4 db = lds4(&bdD[rc * VP + j0q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                av = __builtin_amdgcn_mfma_f32_16x16x4f32(v4[e], db[e], av, 0, 0, 0);
+                ak = __builtin_amdgcn_mfma_f32_16x16x4f32(k4[e], bW[(j0q + e) * CP + rc], ak, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ss = 16 * ts + 4 * lg + e;
+            bY[ss * CP + rc] = sb[ss] * (av[e] + sEg[ss] * ak[e]);
+        }
+    }
+    __syncthreads();
+    // ---- Z = dT T^T  (bZ over the dead k, v rows)
+    for (int o = tid; o < C * C; o += NT) {
+        const int r = o / C, s2 = o % C;
+        float acc = 0.f;
+        for (int pp = 0; pp < C; ++pp) acc = fmaf(bY[pp * CP + r], bT[s2 * CP + pp], acc);
+        bZ[r * CP + s2] = acc;
+    }
+    __syncthreads();
+    // ---- dA = -strict_lower(T^T Z)   (T[p][r] = 0 for p < r)
+    for (int o = tid; o < C * C; o += NT) {
+        const int r = o / C, s2 = o % C;
+        float acc = 0.f;
+        if (s2 < r)
+            for (int pp = r; pp < C; ++pp) acc = fmaf(-bT[pp * CP + r], bZ[pp * CP + s2], acc);
+        bY[r * CP + s2] = acc;
+    }
+    __syncthreads();
+    // ---- k^T, q^T into R1 (Z is dead); dv and dbeta's T^T ddelta . v term;
+    // the row and column sums of the C x C terms
+#pragma unroll
+    for (int m = 0; m < (C * K / 8) / NT; ++m) {
+        const int e8 = tid + NT * m, r = (8 * e8) / K, j = (8 * e8) % K;
+        u16 kk8[8], qq8[8];
+        const uint4 wk = row8(a.k, rowK, hk * K + j, r), wq = row8(a.q, rowK, hk * K + j, r);
+        const uint32_t ak4[4] = {wk.x, wk.y, wk.z, wk.w}, aq4[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kk8[e] = (u16)(ak4[e >> 1] >> (16 * (e & 1)));
+            qq8[e] = (u16)(aq4[e >> 1] >> (16 * (e & 1)));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            tk[(j + e) * TS + r] = r < L ? kk8[e] : (u16)0;
+            tq[(j + e) * TS + r] = r < L ? qq8[e] : (u16)0;
+        }
+    }
+    {
+        // dv = diag(beta) T^T ddelta, dbeta += (T^T ddelta) . v: 4 x 8 tiles of C x V,
+        // wave wv owns column tile wv
+        const int j = 16 * wv + li;   // B column
+        f32x4 acc[4] = {z4, z4, z4, z4};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int p0 = 4 * (4 * q + lg);
+            float bb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bb[e] = bdD[(p0 + e) * VP + j];
+#pragma unroll
+            for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(bT[(p0 + e) * CP + 16 * tr + li], bb[e], acc[tr], 0, 0, 0);
+        }
+        float vv[4][4];
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                vv[tr][e] = Elem<T>::load(a.v, (tc + min(16 * tr + 4 * lg + e, L - 1)) * rowV + h * V + j);
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tr + 4 * lg + e;
+                float part = 0.f;
+                if (r < L) {
+                    Elem<T>::store(a.dv, (tc + r) * rowV + h * V + j, sb[r] * acc[tr][e]);
+                    part = acc[tr][e] * vv[tr][e];
+                }
+                put_row<16>(sBw + wv * C, r, part);
+            }
+    }
+    {
+        // e(r, s) = dattn attn + beta_r dA Ak (the raw gradient matrices):
+        // dG_r += e(r, s), dG_s -= e(r, s), dbeta_r += dA Ak.  Thread t sums
+        // eight columns of row t / 8 and eight rows of column t / 8; the eight
+        // partial sums of a row (column) are combined in a fixed order.
+        const int rr = tid >> 3, seg = tid & 7;
+        float re = 0.f, rb = 0.f, ce = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int s2 = 8 * seg + m;   // columns of row rr
+            if (s2 <= rr) {
+                const float eA = s2 < rr ? bY[rr * CP + s2] * Ak[rr * C + s2] : 0.f;
+                re += bX[rr * CP + s2] * attn[rr * C + s2] + sb[rr] * eA;
+                rb += eA;
+            }
+            const int r2 = 8 * seg + m;   // rows of column rr
+            if (r2 >= rr) {
+                const float eA = rr < r2 ? bY[r2 * CP + rr] * Ak[r2 * C + rr] : 0.f;
+                ce += bX[r2 * CP + rr] * attn[r2 * C + rr] + sb[r2] * eA;
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) {
+            re += __shfl_xor(re, off);
+            rb += __shfl_xor(rb, off);
+            ce += __shfl_xor(ce, off);
+        }
+        if (seg == 0) {
+            sRowA[rr] = re;
+            sRowB[rr] = rb;
+            sColA[rr] = ce;
+        }
+    }
+    __syncthreads();
+    // ---- fold the decay in once: bX <- dattn (.) D,  bY <- dA (.) beta_r D  (= dKK)
+    for (int o = tid; o < C * C; o += NT) {
+        const int r = o / C, s2 = o % C;
+        if (s2 <= r) {
+            const float dec = expf(sG[r] - sG[s2]);
+            bX[r * CP + s2] *= dec;
+            bY[r * CP + s2] *= sb[r] * dec;
+        }
+    }
+    __syncthreads();
+    // ---- over the chunk's tokens p (zero past L in every B operand):
+    //   qa = (dattn D) k,  dkr = (dattn D)^T q + (dKK + dKK^T) k,  dkb = T^T dw
+    f32x4 qa[4], dkr[4], dkb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) qa[t] = dkr[t] = dkb[t] = z4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int p0 = 4 * (4 * q + lg);
+        const f32x4 kb = ld4b(&tk[i * TS + p0]), qb = ld4b(&tq[i * TS + p0]);
+        float wb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wb[e] = bW[i * CP + p0 + e];
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr) {
+            const int r = 16 * tr + li;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pp = p0 + e;
+                const float xa = bX[r * CP + pp], xat = bX[pp * CP + r];
+                const float xy = bY[r * CP + pp] + bY[pp * CP + r], xt = bT[pp * CP + r];
+                qa[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa, kb[e], qa[tr], 0, 0, 0);
+                dkr[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(xat, qb[e], dkr[tr], 0, 0, 0);
+                dkr[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(xy, kb[e], dkr[tr], 0, 0, 0);
+                dkb[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(xt, wb[e], dkb[tr], 0, 0, 0);
+            }
+        }
+    }
+    // ---- dq, dk; this lane's parts of dG, dbeta and of the last row's k_tilde term
+    float pdl = 0.f;
+#pragma unroll
+    for (int tr = 0; tr < 4; ++tr) {
+        const f32x4 kr4 = ld4b(&tk[i * TS + 16 * tr + 4 * lg]), qr4 = ld4b(&tq[i * TS + 16 * tr + 4 * lg]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * tr + 4 * lg + e;
+            float pg = 0.f, pd = 0.f, pk = 0.f;
+            if (r < L) {
+                const float eG = sEg[r], er = sEk[r], br = sb[r];
+                const float kri = kr4[e], qri = qr4[e];
+                put_qk(a.dq, a.dq_acc, r, i, eG * dqg[tr][e] + qa[tr][e]);
+                put_qk(a.dk, a.dk_acc, r, i, dkr[tr][e] + er * dkt[tr][e] + br * eG * dkb[tr][e]);
+                pg = eG * dqg[tr][e] * qri - er * dkt[tr][e] * kri + br * eG * dkb[tr][e] * kri;
+                pd = er * dkt[tr][e] * kri;
+                pk = eG * dkb[tr][e] * kri;
+            }
+            put_row<16>(sPw + wv * C, r, pg);
+            put_row<16>(sBw + wv * C, r, pk);
+            pdl += pd;
+        }
+    }
+    put_row<64>(sLast, wv, pdl);
+    // gamma: dG_last += gamma <h, dh>
+    {
+        float x = 0.f;
+#pragma unroll
+        for (int m = 0; m < (K * V / 4) / NT; ++m) {
+            const f32x4 hh = *reinterpret_cast<const f32x4 *>(hsT + 4 * (tid + NT * m));
+            const f32x4 dh = *reinterpret_cast<const f32x4 *>(dhsT + 4 * (tid + NT * m));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x = fmaf(hh[e], dh[e], x);
+        }
+        put_row<64>(sLast, wv, sEg[C - 1] * x);
+    }
+    __syncthreads();
+    // ---- dg = reverse cumulative sum of dG over the chunk; dbeta (wave 0, lane = row)
+    if (wv == 0) {
+        const int r = lane;
+        float dG = sRowA[r] - sColA[r], db = sRowB[r];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            dG += sPw[w * C + r];
+            db += sBw[w * C + r];
+        }
+        if (r == C - 1) {
+            float last = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) last += sLast[w];
+            dG += last;
+        }
+        // inclusive scan from the last row down: x_r = sum_{r' >= r} dG_r'
+        float x = dG;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_down(x, off);
+            if (r + off < 64) x += y;
+        }
+        if (r < L) {
+            a.dg[(tc + r) * H + h] = x;
+            a.dbeta[(tc + r) * H + h] = db;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- 5. grouped key heads
 // A key head serves G = H / Hk value heads, so its dq, dk are the sums of
 // theirs: out[t][hk][i] = sum_g acc[t][hk G + g][i].
@@ -1254,7 +1660,10 @@ hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (chunk_grid > 0) {
-        hipLaunchKernelGGL((bwd_grads_kernel<T, K, V, C, NT>), dim3(chunk_grid), dim3(NT), 0, s, a);
+        if constexpr (K == 128 && V == 128 && C == 64 && NT == 512 && sizeof(typename Elem<T>::raw_t) == 2)
+            hipLaunchKernelGGL((bwd_grads_mfma_kernel<T>), dim3(chunk_grid), dim3(NT), 0, s, a);
+        else
+            hipLaunchKernelGGL((bwd_grads_kernel<T, K, V, C, NT>), dim3(chunk_grid), dim3(NT), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || !a.dq_acc) return e;
         const int64_t n = a.tokens * a.Hk * K;
