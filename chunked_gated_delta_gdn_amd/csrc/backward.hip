@@ -31,6 +31,7 @@
 // reverse), so a workgroup of 2. and 3. owns NCOL of them.
 #include "dev_common.h"
 #include "gdn_internal.h"
+#include "mfma_tile.h"
 
 namespace gdn {
 namespace {
@@ -252,6 +253,180 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
             for (int s = 0; s <= r; ++s) acc = fmaf(sT[r * CP + s], sv[s * V + j], acc);
             u[e] = acc;
         }
+    }
+}
+
+// ------------------------------------------------ 1b. prep, K = V = 128, C = 64, bf16
+// The same per-chunk quantities as bwd_prep_kernel, for bf16 inputs.  k, q and
+// v are kept in LDS as the bf16 values they are, so the Grams K K^T and Q K^T
+// run on the bf16 matrix cores with fp32 accumulation: every product of two
+// bf16 values is exact in fp32, so only the order of the fp32 sums differs
+// from an fp32 evaluation.  T = (I + A)^{-1} is formed blockwise over 16 x 16
+// blocks: the four diagonal blocks by forward substitution (one lane per
+// column), then T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj one block diagonal at
+// a time, on the fp32 matrix cores -- three dependent levels instead of 64
+// dependent rows.  The LDS footprint (about 70 KB) lets two chunks share a CU.
+template <typename T>
+__global__ __launch_bounds__(512) void bwd_prep_mfma_kernel(BwdArgs a) {
+    static_assert(sizeof(typename Elem<T>::raw_t) == 2, "k, q, v are kept as bf16");
+    constexpr int K = 128, V = 128, C = 64, NT = 512;
+    constexpr int RS = K + 8;   // bf16 rows [C][RS], 16-byte aligned
+    constexpr int CP = C + 1;   // fp32 rows of C x C tiles
+    typedef uint16_t u16;
+    __shared__ __attribute__((aligned(16))) u16 sk[C * RS];
+    __shared__ __attribute__((aligned(16))) u16 sv[C * RS];
+    __shared__ __attribute__((aligned(16))) float RQ[C * RS / 2];   // q rows (bf16), then T [C][CP]
+    __shared__ float sA[C * CP];
+    __shared__ float sG[C], sEg[C], sEk[C], sb[C], sbg[C];
+    static_assert(C * CP <= C * RS / 2 && (RS * 2) % 16 == 0, "T fits where q was");
+    u16 *const sq = reinterpret_cast<u16 *>(RQ);
+    float *const sT = RQ;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
+    const int H = a.H;
+    const int h = blockIdx.x % H;
+    const int64_t chunk = blockIdx.x / H;
+    const ChunkLoc cl = locate_chunk(a.ct, chunk, C);
+    const int L = cl.L;
+    const int64_t tc = cl.tc;
+    const int64_t rowK = (int64_t)a.Hk * K, rowV = (int64_t)H * V;
+    const int hk = h / (H / a.Hk);
+    const int64_t ch = chunk * H + h;
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+    auto bf = [](u16 x) { return __uint_as_float((uint32_t)x << 16); };
+
+    // rows of k, q, v (rows past L zero), 16 bytes per load
+#pragma unroll
+    for (int m = 0; m < (C * K / 8) / NT; ++m) {
+        const int e8 = tid + NT * m, r = (8 * e8) / K, j = (8 * e8) % K;
+        const int64_t rr = tc + min(r, L - 1);
+        uint4 wk = *reinterpret_cast<const uint4 *>(static_cast<const u16 *>(a.k) + rr * rowK + hk * K + j);
+        uint4 wq = *reinterpret_cast<const uint4 *>(static_cast<const u16 *>(a.q) + rr * rowK + hk * K + j);
+        uint4 wvv = *reinterpret_cast<const uint4 *>(static_cast<const u16 *>(a.v) + rr * rowV + h * V + j);
+        if (r >= L) wk = wq = wvv = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(&sk[r * RS + j]) = wk;
+        *reinterpret_cast<uint4 *>(&sq[r * RS + j]) = wq;
+        *reinterpret_cast<uint4 *>(&sv[r * RS + j]) = wvv;
+    }
+    if (tid < C) sb[tid] = tid < L ? a.beta[(tc + tid) * H + h] : 0.f;
+    load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);   // (synchronises)
+    if (tid < C) sbg[tid] = sb[tid] * sEg[tid];
+
+    // ---- Grams: wave wv owns tiles 2 wv, 2 wv + 1 of the 4 x 4; a 16 x 16 x 32
+    // bf16 product takes 8 consecutive k of a row from each lane
+    float *Ak = a.Ak + ch * C * C, *attn = a.attn + ch * C * C;
+#pragma unroll
+    for (int u2 = 0; u2 < 2; ++u2) {
+        const int tile = 2 * wv + u2, tr = tile >> 2, tcol = tile & 3;
+        f32x4 kk = z4, qk = z4;
+        if (tcol <= tr) {
+            const int r = 16 * tr + li, sc = 16 * tcol + li;
+#pragma unroll
+            for (int kb = 0; kb < K / 32; ++kb) {
+                const int o = 32 * kb + 8 * lg;
+                const mfma::bf16x8 b = mfma::as8(*reinterpret_cast<const uint4 *>(&sk[sc * RS + o]));
+                kk = mfma::mma32(mfma::as8(*reinterpret_cast<const uint4 *>(&sk[r * RS + o])), b, kk);
+                qk = mfma::mma32(mfma::as8(*reinterpret_cast<const uint4 *>(&sq[r * RS + o])), b, qk);
+            }
+        }
+        const int sc = 16 * tcol + li;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int rr = 16 * tr + 4 * lg + e;
+            const float dec = sc <= rr ? expf(sG[rr] - sG[sc]) : 0.f;
+            const float ak = sc < rr ? dec * kk[e] : 0.f;
+            sA[rr * CP + sc] = sb[rr] * ak;   // A itself
+            Ak[rr * C + sc] = ak;
+            attn[rr * C + sc] = dec * qk[e];
+        }
+    }
+    __syncthreads();   // sq is dead from here: sT takes its place
+
+    // ---- diagonal blocks: lane 16 b + c of wave 0 forms column c of T_bb;
+    // the other waves clear the blocks above the diagonal
+    if (wv == 0) {
+        const int b = lane >> 4, c = lane & 15;
+        const float *Ab = sA + 16 * b * CP + 16 * b;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float x = r == c ? 1.f : 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < r; ++s2) x = fmaf(-Ab[r * CP + s2], t[s2], x);
+            t[r] = x;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(16 * b + r) * CP + 16 * b + c] = t[r];
+    } else {
+        for (int e = tid - 64; e < 6 * 256; e += NT - 64) {
+            const int blk = e >> 8, w = e & 255;   // blocks (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+            const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+            const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+            sT[(16 * bi + (w >> 4)) * CP + 16 * bj + (w & 15)] = 0.f;
+        }
+    }
+    __syncthreads();
+    // ---- below the diagonal, one block diagonal per level:
+    // T_ij = -T_ii (sum_{m=j}^{i-1} A_im T_mj)
+    auto off_block = [&](int i, int j) {
+        f32x4 P = z4;
+        for (int m = j; m < i; ++m)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                P = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * i + li) * CP + 16 * m + 4 * kk + lg],
+                                                         sT[(16 * m + 4 * kk + lg) * CP + 16 * j + li], P, 0, 0, 0);
+        // P is held as P[4 lg + e][li]: step e of the second product sums
+        // over k = 4 lg + e
+        f32x4 R = z4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            R = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[(16 * i + li) * CP + 16 * i + 4 * lg + e], P[e], R, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sT[(16 * i + 4 * lg + e) * CP + 16 * j + li] = -R[e];
+    };
+#pragma unroll
+    for (int lvl = 1; lvl < 4; ++lvl) {
+        if (wv < 4 - lvl) off_block(wv + lvl, wv);
+        __syncthreads();
+    }
+
+    // ---- T out; w = T diag(beta exp(G)) K and u = T diag(beta) V: wave wv owns
+    // column tile wv of both and the four row tiles (T's zero blocks skipped)
+    float *To = a.T + ch * C * C, *w = a.w + ch * C * K, *u = a.u + ch * C * V;
+#pragma unroll
+    for (int m = 0; m < (C * C) / NT; ++m) {
+        const int e = tid + NT * m;
+        To[e] = sT[(e / C) * CP + e % C];
+    }
+    {
+        const int col = 16 * wv + li;
+        f32x4 aw[4] = {z4, z4, z4, z4}, au[4] = {z4, z4, z4, z4};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int s0 = 4 * (4 * q + lg);
+            float bw[4], bu[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bw[e] = sbg[s0 + e] * bf(sk[(s0 + e) * RS + col]);
+                bu[e] = sb[s0 + e] * bf(sv[(s0 + e) * RS + col]);
+            }
+#pragma unroll
+            for (int tr = q; tr < 4; ++tr)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ta = sT[(16 * tr + li) * CP + s0 + e];
+                    aw[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta, bw[e], aw[tr], 0, 0, 0);
+                    au[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(ta, bu[e], au[tr], 0, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tr + 4 * lg + e;
+                w[r * K + col] = aw[tr][e];
+                u[r * V + col] = au[tr][e];
+            }
     }
 }
 
@@ -1639,7 +1814,10 @@ hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
     const unsigned chunk_grid = (unsigned)(a.n_chunks * a.H);
     const unsigned chain_grid = (unsigned)((int64_t)n_chains * a.H * (V / NCOL));
     if (chunk_grid > 0) {
-        hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C, NT>), dim3(chunk_grid), dim3(NT), 0, s, a);
+        if constexpr (K == 128 && V == 128 && C == 64 && NT == 512 && sizeof(typename Elem<T>::raw_t) == 2)
+            hipLaunchKernelGGL((bwd_prep_mfma_kernel<T>), dim3(chunk_grid), dim3(NT), 0, s, a);
+        else
+            hipLaunchKernelGGL((bwd_prep_kernel<T, K, V, C, NT>), dim3(chunk_grid), dim3(NT), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
