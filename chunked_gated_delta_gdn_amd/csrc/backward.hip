@@ -439,25 +439,48 @@ __device__ __forceinline__ void chunk_rows(int64_t t0, int64_t t1, int64_t c, in
     L = (int)((t1 - tc) < C ? (t1 - tc) : C);
 }
 
+// The state a chain's forward scan starts from (h0 of its sequence, or the
+// composed state of the chain before it), and the gradient its reverse scan
+// starts from (dhT, or the composed gradient of the chain after it); NULL =
+// zero.  [K, V] row-major.
+__device__ __forceinline__ const float *chain_h_start(const BwdArgs &a, const ChainPos &cp, int h, int64_t KV) {
+    if (!cp.first) return a.h_in + (cp.slot * a.H + h) * KV;
+    return a.h0 ? a.h0 + ((int64_t)cp.seq * a.H + h) * KV : nullptr;
+}
+__device__ __forceinline__ const float *chain_dh_end(const BwdArgs &a, const ChainPos &cp, int h, int64_t KV) {
+    if (!cp.last) return a.dh_in + (cp.slot * a.H + h) * KV;
+    return a.dhT ? a.dhT + ((int64_t)cp.seq * a.H + h) * KV : nullptr;
+}
+
 template <typename T, int K, int V, int C, int NCOL, int NT>
 __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
     constexpr int KP = K + 1, NP = NCOL + 1, NG = V / NCOL, EPT = K * NCOL / NT, LPT = C * K / NT;
     static_assert(V % NCOL == 0 && (K * NCOL) % NT == 0 && (C * K) % NT == 0, "column groups");
+    static_assert(K % NCOL == 0, "strips of M");
+    constexpr int NGK = K / NCOL;
     __shared__ float sw[C * KP], sk[C * KP], sh[K * NP], sd[C * NP];
     __shared__ float sG[C], sEg[C], sEk[C];
     const int tid = threadIdx.x, H = a.H;
-    const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
-    const int j0 = cg * NCOL;
+    // carry launches add NGK strips of M (identity start, u taken as 0)
+    const int ng = a.carry ? NGK + NG : NG;
+    const int cg = blockIdx.x % ng, h = (blockIdx.x / ng) % H, n = blockIdx.x / (ng * H);
+    const ChainPos cp = chain_pos(a.ct, n, a.N);
+    const bool is_M = a.carry && cg < NGK;
+    // carries: M of every chain of a split sequence (the forward compose uses
+    // all but the last, the reverse one all but the first), U of all but the last
+    if (a.carry && (cp.first && cp.last || (!is_M && cp.last))) return;
+    const int j0 = (is_M ? cg : cg - (a.carry ? NGK : 0)) * NCOL;
     const ChainSpan sp = chain_span(a.ct, n, C);
     const int64_t rowK = (int64_t)a.Hk * K;
     const int hk = h / (H / a.Hk);
     const int64_t KV = (int64_t)K * V;
 
     float hr[EPT];
+    const float *hst = a.carry ? nullptr : chain_h_start(a, cp, h, KV);
 #pragma unroll
     for (int m = 0; m < EPT; ++m) {
         const int e = tid + NT * m, i = e % K, jj = e / K;
-        hr[m] = a.h0 ? a.h0[((int64_t)n * H + h) * KV + (int64_t)i * V + j0 + jj] : 0.f;
+        hr[m] = is_M ? (i == j0 + jj ? 1.f : 0.f) : hst ? hst[(int64_t)i * V + j0 + jj] : 0.f;
     }
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
     // w, raw k and g of the next chunk, fetched while the current one computes
@@ -482,7 +505,7 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < EPT; ++m) {
             const int e = tid + NT * m, i = e % K, jj = e / K;
-            hs[(int64_t)(j0 + jj) * K + i] = hr[m];
+            if (!a.carry) hs[(int64_t)(j0 + jj) * K + i] = hr[m];
             sh[i * NP + jj] = hr[m];
         }
 #pragma unroll
@@ -500,11 +523,11 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
         // delta = u - w h (own columns); k_tilde^T delta = k^T (exp(G_C - G) delta)
         for (int o = tid; o < C * NCOL; o += NT) {
             const int r = o / NCOL, jj = o % NCOL;
-            float acc = u[r * V + j0 + jj];
+            float acc = is_M ? 0.f : u[r * V + j0 + jj];
 #pragma unroll 8
             for (int i = 0; i < K; ++i) acc = fmaf(-sw[r * KP + i], sh[i * NP + jj], acc);
             sd[r * NP + jj] = sEk[r] * acc;
-            d[r * V + j0 + jj] = acc;
+            if (!a.carry) d[r * V + j0 + jj] = acc;
         }
         __syncthreads();
 #pragma unroll
@@ -516,6 +539,19 @@ __global__ __launch_bounds__(NT) void bwd_states_kernel(BwdArgs a) {
             hr[m] = acc;
         }
         __syncthreads();
+    }
+    if (a.carry) {
+        const int64_t row = cp.slot * H + h;
+#pragma unroll
+        for (int m = 0; m < EPT; ++m) {
+            const int e = tid + NT * m, i = e % K, jj = e / K;
+            if (is_M) {
+                a.M[row * K * K + (int64_t)i * K + j0 + jj] = hr[m];
+                a.Mt[row * K * K + (int64_t)(j0 + jj) * K + i] = hr[m];
+            } else {
+                a.U[row * KV + (int64_t)i * V + j0 + jj] = hr[m];
+            }
+        }
     }
 }
 
@@ -532,16 +568,19 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
     const int tid = threadIdx.x, H = a.H;
     const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
     const int j0 = cg * NCOL;
+    const ChainPos cp = chain_pos(a.ct, n, a.N);
+    if (a.carry && cp.first) return;   // (carry: zero gradient at the chain's end)
     const ChainSpan sp = chain_span(a.ct, n, C);
     const int64_t rowK = (int64_t)a.Hk * K, rowV = (int64_t)H * V;
     const int hk = h / (H / a.Hk);
     const int64_t KV = (int64_t)K * V;
 
     float dh[EPT];
+    const float *dst = a.carry ? nullptr : chain_dh_end(a, cp, h, KV);
 #pragma unroll
     for (int m = 0; m < EPT; ++m) {
         const int e = tid + NT * m, i = e % K, jj = e / K;
-        dh[m] = a.dhT ? a.dhT[((int64_t)n * H + h) * KV + (int64_t)i * V + j0 + jj] : 0.f;
+        dh[m] = dst ? dst[(int64_t)i * V + j0 + jj] : 0.f;
     }
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
     // the next chunk's (in reverse order) w, raw k and q, attn, do columns and g
@@ -577,7 +616,7 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < EPT; ++m) {
             const int e = tid + NT * m, i = e % K, jj = e / K;
-            dhs[(int64_t)(j0 + jj) * K + i] = dh[m];
+            if (!a.carry) dhs[(int64_t)(j0 + jj) * K + i] = dh[m];
             sdh[i * NP + jj] = dh[m];
         }
 #pragma unroll
@@ -613,7 +652,7 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
             acc = fmaf(sEk[r], acck, acc);
             sdd[r * NP + jj] = acc;
             sdoG[r * NP + jj] = sEg[r] * sdo[r * NP + jj];
-            dd[r * V + j0 + jj] = acc;
+            if (!a.carry) dd[r * V + j0 + jj] = acc;
         }
         __syncthreads();
 #pragma unroll
@@ -629,11 +668,13 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
         }
         __syncthreads();
     }
-    if (a.dh0) {
+    float *out = a.carry ? a.E + (cp.slot * H + h) * KV
+                         : (a.dh0 && cp.first ? a.dh0 + ((int64_t)cp.seq * H + h) * KV : nullptr);
+    if (out) {
 #pragma unroll
         for (int m = 0; m < EPT; ++m) {
             const int e = tid + NT * m, i = e % K, jj = e / K;
-            a.dh0[((int64_t)n * H + h) * KV + (int64_t)i * V + j0 + jj] = dh[m];
+            out[(int64_t)i * V + j0 + jj] = dh[m];
         }
     }
 }
@@ -649,7 +690,7 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
 // gradient) in that layout.
 template <typename T>
 __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
-    constexpr int K = 128, V = 128, C = 64, NCOL = 16, NT = 512, NG = V / NCOL;
+    constexpr int K = 128, V = 128, C = 64, NCOL = 16, NT = 512, NG = V / NCOL, NGK = K / NCOL;
     constexpr int LDK = K + 4, LDC = C + 4, KPT = C * K / NT;
     __shared__ __attribute__((aligned(16))) float hT[NCOL * LDK];   // state strip [column][row]
     __shared__ __attribute__((aligned(16))) float kT[K * LDC];      // raw k [i][r]
@@ -657,8 +698,15 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
     __shared__ float sG[C], sEg[C], sEk[C];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
     const int H = a.H;
-    const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
-    const int j0 = cg * NCOL;
+    // carry launches add NGK strips of M (identity start, u taken as 0)
+    const int ng = a.carry ? NGK + NG : NG;
+    const int cg = blockIdx.x % ng, h = (blockIdx.x / ng) % H, n = blockIdx.x / (ng * H);
+    const ChainPos cp = chain_pos(a.ct, n, a.N);
+    const bool is_M = a.carry && cg < NGK;
+    // carries: M of every chain of a split sequence (the forward compose uses
+    // all but the last, the reverse one all but the first), U of all but the last
+    if (a.carry && (cp.first && cp.last || (!is_M && cp.last))) return;
+    const int j0 = (is_M ? cg : cg - (a.carry ? NGK : 0)) * NCOL;
     const ChainSpan sp = chain_span(a.ct, n, C);
     const int64_t rowK = (int64_t)a.Hk * K;
     const int hk = h / (H / a.Hk);
@@ -666,9 +714,10 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
     const int row0 = 16 * wv + 4 * lg;   // this lane's rows of the strip: row0 .. row0 + 3
 
     f32x4 hacc;
+    const float *hst = a.carry ? nullptr : chain_h_start(a, cp, h, KV);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        hacc[e] = a.h0 ? a.h0[((int64_t)n * H + h) * KV + (int64_t)(row0 + e) * V + j0 + li] : 0.f;
+        hacc[e] = is_M ? (row0 + e == j0 + li ? 1.f : 0.f) : hst ? hst[(int64_t)(row0 + e) * V + j0 + li] : 0.f;
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
     // next chunk: w rows (A operands of delta, waves 0-3), u seeds, raw k, g.
     // Rows past the chunk end are loaded from its last row (every address
@@ -689,7 +738,7 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
             for (int q = 0; q < 8; ++q) pw[q] = *reinterpret_cast<const f32x4 *>(w + 4 * (4 * q + lg));
             const float *u = a.u + ch * C * V;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pu[e] = u[(row0 + e) * V + j0 + li];
+            for (int e = 0; e < 4; ++e) pu[e] = is_M ? 0.f : u[(row0 + e) * V + j0 + li];
         }
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
@@ -702,7 +751,7 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
     if (nch > 0) fetch(0);
     for (int64_t c = 0; c < nch; ++c) {
         const int64_t ch = (sp.chunk0 + c) * H + h;
-        *reinterpret_cast<f32x4 *>(a.hs + ch * KV + (int64_t)(j0 + li) * K + row0) = hacc;
+        if (!a.carry) *reinterpret_cast<f32x4 *>(a.hs + ch * KV + (int64_t)(j0 + li) * K + row0) = hacc;
         *reinterpret_cast<f32x4 *>(&hT[li * LDK + row0]) = hacc;
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
@@ -731,7 +780,7 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
             f32x4 sc;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                d[(row0 + e) * V + j0 + li] = acc[e];
+                if (!a.carry) d[(row0 + e) * V + j0 + li] = acc[e];
                 sc[e] = sEk[row0 + e] * acc[e];
             }
             *reinterpret_cast<f32x4 *>(&dT[li * LDC + row0]) = sc;
@@ -747,6 +796,17 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
             for (int e = 0; e < 4; ++e) hacc = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[e], db[e], hacc, 0, 0, 0);
         }
         __syncthreads();
+    }
+    if (a.carry) {
+        const int64_t row = cp.slot * H + h;
+        if (is_M) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.M[row * K * K + (int64_t)(row0 + e) * K + j0 + li] = hacc[e];
+            *reinterpret_cast<f32x4 *>(a.Mt + row * K * K + (int64_t)(j0 + li) * K + row0) = hacc;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.U[row * KV + (int64_t)(row0 + e) * V + j0 + li] = hacc[e];
+        }
     }
 }
 
@@ -767,6 +827,8 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
     const int H = a.H;
     const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
     const int j0 = cg * NCOL;
+    const ChainPos cp = chain_pos(a.ct, n, a.N);
+    if (a.carry && cp.first) return;   // (carry: zero gradient at the chain's end)
     const ChainSpan sp = chain_span(a.ct, n, C);
     const int64_t rowK = (int64_t)a.Hk * K, rowV = (int64_t)H * V;
     const int hk = h / (H / a.Hk);
@@ -774,9 +836,9 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
     const int row0 = 16 * wv + 4 * lg;
 
     f32x4 dacc;
+    const float *dst = a.carry ? nullptr : chain_dh_end(a, cp, h, KV);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        dacc[e] = a.dhT ? a.dhT[((int64_t)n * H + h) * KV + (int64_t)(row0 + e) * V + j0 + li] : 0.f;
+    for (int e = 0; e < 4; ++e) dacc[e] = dst ? dst[(int64_t)(row0 + e) * V + j0 + li] : 0.f;
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
     // the previous chunk's operands, fetched a chunk ahead (rows past the chunk
     // end loaded from its last row and zeroed where used, as in the states scan)
@@ -810,7 +872,7 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
     if (nch > 0) fetch(nch - 1);
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int64_t ch = (sp.chunk0 + c) * H + h;
-        *reinterpret_cast<f32x4 *>(a.dhs + ch * KV + (int64_t)(j0 + li) * K + row0) = dacc;
+        if (!a.carry) *reinterpret_cast<f32x4 *>(a.dhs + ch * KV + (int64_t)(j0 + li) * K + row0) = dacc;
         *reinterpret_cast<f32x4 *>(&dhT[li * LDK + row0]) = dacc;
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
@@ -855,7 +917,7 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 v4[e] = fmaf(sEk[row0 + e], acc2[e], acc1[e]);
-                dd[(row0 + e) * V + j0 + li] = v4[e];
+                if (!a.carry) dd[(row0 + e) * V + j0 + li] = v4[e];
             }
             *reinterpret_cast<f32x4 *>(&ddT[li * LDC + row0]) = v4;
         } else {
@@ -882,10 +944,11 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
         }
         __syncthreads();
     }
-    if (a.dh0) {
+    float *out = a.carry ? a.E + (cp.slot * H + h) * KV
+                         : (a.dh0 && cp.first ? a.dh0 + ((int64_t)cp.seq * H + h) * KV : nullptr);
+    if (out) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            a.dh0[((int64_t)n * H + h) * KV + (int64_t)(row0 + e) * V + j0 + li] = dacc[e];
+        for (int e = 0; e < 4; ++e) out[(int64_t)(row0 + e) * V + j0 + li] = dacc[e];
     }
 }
 
@@ -1810,7 +1873,45 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float *acc, vo
 }
 
 template <typename T, int K, int V, int C, int NCOL, int NT>
-hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
+hipError_t launch_scans(const BwdArgs &a, int n_chains, const ComposeArgs *fwd, const ComposeArgs *rev,
+                        hipStream_t s) {
+    const unsigned grid = (unsigned)((int64_t)n_chains * a.H * (V / NCOL));
+    const unsigned carry_grid = (unsigned)((int64_t)n_chains * a.H * ((K + V) / NCOL));
+    constexpr bool mf = K == 128 && V == 128 && C == 64 && NCOL == 16 && NT == 512;
+    auto states = [&](const BwdArgs &x, unsigned g) {
+        if constexpr (mf)
+            hipLaunchKernelGGL((bwd_states_mfma_kernel<T>), dim3(g), dim3(NT), 0, s, x);
+        else
+            hipLaunchKernelGGL((bwd_states_kernel<T, K, V, C, NCOL, NT>), dim3(g), dim3(NT), 0, s, x);
+        return hipGetLastError();
+    };
+    auto dstates = [&](const BwdArgs &x, unsigned g) {
+        if constexpr (mf)
+            hipLaunchKernelGGL((bwd_dstates_mfma_kernel<T>), dim3(g), dim3(NT), 0, s, x);
+        else
+            hipLaunchKernelGGL((bwd_dstates_kernel<T, K, V, C, NCOL, NT>), dim3(g), dim3(NT), 0, s, x);
+        return hipGetLastError();
+    };
+    hipError_t e;
+    if (fwd) {
+        // chains that split sequences: each chain's maps (M, U) and reverse
+        // offsets E, the boundary states composed from them, then the emitting scans
+        BwdArgs c = a;
+        c.carry = 1;
+        if ((e = states(c, carry_grid)) != hipSuccess) return e;
+        if ((e = dstates(c, grid)) != hipSuccess) return e;
+        if ((e = launch_compose(K, V, *fwd, s)) != hipSuccess) return e;
+        if ((e = launch_compose(K, V, *rev, s)) != hipSuccess) return e;
+    }
+    BwdArgs x = a;
+    x.carry = 0;
+    if ((e = states(x, grid)) != hipSuccess) return e;
+    return dstates(x, grid);
+}
+
+template <typename T, int K, int V, int C, int NCOL, int NT>
+hipError_t launch_all(const BwdArgs &a, int n_chains, const ComposeArgs *fwd, const ComposeArgs *rev,
+                      hipStream_t s) {
     const unsigned chunk_grid = (unsigned)(a.n_chunks * a.H);
     const unsigned chain_grid = (unsigned)((int64_t)n_chains * a.H * (V / NCOL));
     if (chunk_grid > 0) {
@@ -1822,19 +1923,7 @@ hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     if (chain_grid > 0) {
-        if constexpr (K == 128 && V == 128 && C == 64 && NCOL == 16 && NT == 512) {
-            hipLaunchKernelGGL((bwd_states_mfma_kernel<T>), dim3(chain_grid), dim3(NT), 0, s, a);
-        } else {
-            hipLaunchKernelGGL((bwd_states_kernel<T, K, V, C, NCOL, NT>), dim3(chain_grid), dim3(NT), 0, s, a);
-        }
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if constexpr (K == 128 && V == 128 && C == 64 && NCOL == 16 && NT == 512) {
-            hipLaunchKernelGGL((bwd_dstates_mfma_kernel<T>), dim3(chain_grid), dim3(NT), 0, s, a);
-        } else {
-            hipLaunchKernelGGL((bwd_dstates_kernel<T, K, V, C, NCOL, NT>), dim3(chain_grid), dim3(NT), 0, s, a);
-        }
-        e = hipGetLastError();
+        const hipError_t e = launch_scans<T, K, V, C, NCOL, NT>(a, n_chains, fwd, rev, s);
         if (e != hipSuccess) return e;
     }
     if (chunk_grid > 0) {
@@ -1856,15 +1945,15 @@ hipError_t launch_all(const BwdArgs &a, int n_chains, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_backward(int K, int V, int C, int dtype, const BwdArgs &a, int n_chains,
-                           hipStream_t s) {
-    // The two state scans run one workgroup per (chain, head, 16-column strip)
-    // for the whole sequence, on the fp32 matrix cores at K = V = 128.
+                           const ComposeArgs *fwd, const ComposeArgs *rev, hipStream_t s) {
+    // The two state scans run one workgroup per (chain, head, 16-column strip),
+    // on the fp32 matrix cores at K = V = 128.
     if (K == 128 && V == 128 && C == 64)
-        return dtype == GDN_F32 ? launch_all<float, 128, 128, 64, 16, 512>(a, n_chains, s)
-                                : launch_all<bf16_t, 128, 128, 64, 16, 512>(a, n_chains, s);
+        return dtype == GDN_F32 ? launch_all<float, 128, 128, 64, 16, 512>(a, n_chains, fwd, rev, s)
+                                : launch_all<bf16_t, 128, 128, 64, 16, 512>(a, n_chains, fwd, rev, s);
     if (K == 32 && V == 32 && C == 16)
-        return dtype == GDN_F32 ? launch_all<float, 32, 32, 16, 8, 256>(a, n_chains, s)
-                                : launch_all<bf16_t, 32, 32, 16, 8, 256>(a, n_chains, s);
+        return dtype == GDN_F32 ? launch_all<float, 32, 32, 16, 8, 256>(a, n_chains, fwd, rev, s)
+                                : launch_all<bf16_t, 32, 32, 16, 8, 256>(a, n_chains, fwd, rev, s);
     return hipErrorInvalidValue;
 }
 

@@ -4,7 +4,14 @@
 // h_final = M[R-1] h_in[R-1] + U[R-1].
 // Batch mode walks the R segments of a (sequence, head) with state rows
 // [R, N, H]; packed mode walks the pieces of one sequence (rows [P, H]) from
-// its piece `first` on.
+// its piece `first` on.  With `reverse` the steps run last to first (the
+// backward pass composes its reverse scan so, with M holding the transposed
+// maps): h_in of the last step is h0, and each earlier one is M h + U of the
+// step after it.
+//
+// The NS strips of one (sequence, head) all read the same M rows, so they are
+// placed on one XCD (workgroups go to the 8 XCDs in turn by index, and each
+// XCD has its own L2): M is then fetched from HBM about once per pair.
 //
 // The columns of the state are independent under h <- M h + U, so one
 // workgroup owns a 16-column strip of one (sequence, head) state and walks
@@ -37,6 +44,20 @@ __device__ __forceinline__ Steps compose_steps(const ComposeArgs &a, int64_t nh)
 __device__ __forceinline__ int64_t compose_row(const ComposeArgs &a, int r, int64_t nh) {
     return a.packed ? (int64_t)r * a.H + nh % a.H : (int64_t)r * a.N * a.H + nh;
 }
+// step i (0 .. r1 - r0 - 1) of the walk
+__device__ __forceinline__ int compose_step(const ComposeArgs &a, const Steps &st, int i) {
+    return a.reverse ? st.r1 - 1 - i : st.r0 + i;
+}
+// (sequence, head) pair and strip of this workgroup: the strips of a pair
+// share an XCD (see above); pairs past N * H (grid padding) get nh = -1
+constexpr int kXcds = 8;
+template <int NS>
+__device__ __forceinline__ void compose_unit(const ComposeArgs &a, int64_t &nh, int &strip) {
+    const int64_t b = blockIdx.x, idx = b / kXcds;
+    strip = (int)(idx % NS);
+    nh = (idx / NS) * kXcds + b % kXcds;
+    if (nh >= (int64_t)a.N * a.H) nh = -1;
+}
 
 template <int K, int V>
 __global__ __launch_bounds__(kThreads) void compose_kernel(ComposeArgs a) {
@@ -49,8 +70,10 @@ __global__ __launch_bounds__(kThreads) void compose_kernel(ComposeArgs a) {
     __shared__ float sh[K * kStrip];
 
     const int tid = threadIdx.x;
-    const int strip = blockIdx.x % NS;
-    const int64_t nh = blockIdx.x / NS;        // (n, h) flattened
+    int64_t nh;   // (n, h) flattened
+    int strip;
+    compose_unit<NS>(a, nh, strip);
+    if (nh < 0) return;
     const Steps st = compose_steps(a, nh);
     const int j = tid % kStrip, rg = tid / kStrip;
     const int c0 = strip * kStrip;
@@ -61,13 +84,14 @@ __global__ __launch_bounds__(kThreads) void compose_kernel(ComposeArgs a) {
     }
     __syncthreads();
 
-    for (int r = st.r0; r < st.r1; ++r) {
+    for (int i0 = 0; i0 < st.r1 - st.r0; ++i0) {
+        const int r = compose_step(a, st, i0);
         const int64_t slot = compose_row(a, r, nh);
         for (int e = tid; e < K * kStrip; e += kThreads) {
             const int i = e / kStrip, jj = e % kStrip;
             a.h_in[(slot * K + i) * V + c0 + jj] = sh[e];
         }
-        if (r == st.r1 - 1 && !a.h_final) break;
+        if (i0 == st.r1 - st.r0 - 1 && !a.h_final) break;
         const float *Mr = a.M + slot * K * K;
         for (int e = tid; e < K * K; e += kThreads) sM[(e / K) * KP + e % K] = Mr[e];
         __syncthreads();
@@ -107,8 +131,10 @@ __global__ __launch_bounds__(kThreads) void compose_mfma_kernel(ComposeArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int strip = blockIdx.x % NS;
-    const int64_t nh = blockIdx.x / NS;
+    int64_t nh;
+    int strip;
+    compose_unit<NS>(a, nh, strip);
+    if (nh < 0) return;
     const Steps st = compose_steps(a, nh);
     const int c0 = strip * kStrip;
 
@@ -118,13 +144,14 @@ __global__ __launch_bounds__(kThreads) void compose_mfma_kernel(ComposeArgs a) {
     }
     __syncthreads();
     int cur = 0;
-    for (int r = st.r0; r < st.r1; ++r) {
+    for (int i0 = 0; i0 < st.r1 - st.r0; ++i0) {
+        const int r = compose_step(a, st, i0);
         const int64_t slot = compose_row(a, r, nh);
         for (int e = tid; e < K * kStrip; e += kThreads) {
             const int i = e / kStrip, jj = e % kStrip;
             a.h_in[(slot * K + i) * V + c0 + jj] = hT[cur][jj * LD + i];
         }
-        if (r == st.r1 - 1 && !a.h_final) break;
+        if (i0 == st.r1 - st.r0 - 1 && !a.h_final) break;
         const float *Mr = a.M + slot * K * K;
         f32x4 ma[2][8];
 #pragma unroll
@@ -162,25 +189,24 @@ __global__ __launch_bounds__(kThreads) void compose_mfma_kernel(ComposeArgs a) {
     }
 }
 
-template <int K, int V>
-hipError_t launch_t(const ComposeArgs &a, hipStream_t s) {
-    const int64_t n = (int64_t)a.N * a.H * (V / kStrip);
-    if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL((compose_kernel<K, V>), dim3((unsigned)n), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+// workgroups: N * H pairs rounded up to whole XCD groups, times the strips
+int64_t compose_grid(const ComposeArgs &a, int V) {
+    const int64_t pairs = (int64_t)a.N * a.H;
+    return (pairs + kXcds - 1) / kXcds * kXcds * (V / kStrip);
 }
 
 }  // namespace
 
 hipError_t launch_compose(int K, int V, const ComposeArgs &a, hipStream_t s) {
-    if (K == 32 && V == 32) return launch_t<32, 32>(a, s);
-    if (K == 128 && V == 128) {
-        const int64_t n = (int64_t)a.N * a.H * (V / kStrip);
-        if (n == 0) return hipSuccess;
+    const int64_t n = compose_grid(a, V);
+    if (n == 0) return hipSuccess;
+    if (K == 32 && V == 32)
+        hipLaunchKernelGGL((compose_kernel<32, 32>), dim3((unsigned)n), dim3(kThreads), 0, s, a);
+    else if (K == 128 && V == 128)
         hipLaunchKernelGGL(compose_mfma_kernel, dim3((unsigned)n), dim3(kThreads), 0, s, a);
-        return hipGetLastError();
-    }
-    return hipErrorInvalidValue;
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 }  // namespace gdn

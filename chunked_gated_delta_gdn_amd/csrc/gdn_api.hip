@@ -935,24 +935,24 @@ static size_t backward_ws_per_chunk(const gdn_problem *p) {
                             (size_t)2 * p->K * p->V);
 }
 
-// The backward pass runs every sequence as one chain.  Segments and pieces
-// only schedule the forward (its result does not depend on them), so a problem
-// that carries them is validated as given and then run without them.
-static gdn_status backward_problem(const gdn_problem *p, Resolved &r) {
-    GDN_TRY(resolve(p, r));
-    gdn_problem whole = *p;
-    whole.n_segments = 1;
-    whole.seg_starts = nullptr;
-    whole.max_piece_chunks = 0;
-    return resolve(&whole, r);
-}
+// The backward pass runs the chains of the forward's schedule: a sequence cut
+// into segments (batch) or pieces (packed) scans each part in parallel, from
+// boundary states composed of the parts' carries.
+static gdn_status backward_problem(const gdn_problem *p, Resolved &r) { return resolve(p, r); }
 
 static bool grouped(const gdn_problem *p) { return p->H_qk != 0 && p->H_qk != p->H; }
 
-// per-chunk-head workspace, then (grouped key heads) dq, dk of every value head
+// chains that split sequences need carries and boundary states
+static bool split_chains(const Resolved &r) { return r.P > r.N; }
+
+// per-chunk-head workspace; then (grouped key heads) dq, dk of every value
+// head; then (split chains), per chain and head, M and Mt [K,K] and U, E,
+// h_in, dh_in [K,V] (fp32)
 static size_t backward_ws_bytes(const gdn_problem *p, const Resolved &r) {
     size_t n = (size_t)r.n_chunks * p->H * backward_ws_per_chunk(p);
     if (grouped(p)) n += 2 * (size_t)r.T * p->H * p->K * sizeof(float);
+    if (split_chains(r))
+        n += (size_t)r.P * p->H * sizeof(float) * ((size_t)2 * p->K * p->K + (size_t)4 * p->K * p->V);
     return n;
 }
 
@@ -1037,17 +1037,53 @@ gdn_status gdn_backward(const gdn_problem *p, const void *q, const void *k, cons
     a.hs = a.dd + CH * p->C * p->V;
     a.dhs = a.hs + CH * p->K * p->V;
     a.dq_acc = a.dk_acc = nullptr;
+    float *tail = a.dhs + CH * p->K * p->V;
     if (grouped(p)) {
-        a.dq_acc = a.dhs + CH * p->K * p->V;
+        a.dq_acc = tail;
         a.dk_acc = a.dq_acc + (size_t)r.T * p->H * p->K;
+        tail = a.dk_acc + (size_t)r.T * p->H * p->K;
     }
+    a.h_in = a.dh_in = nullptr;
+    a.M = a.Mt = a.U = a.E = nullptr;
+    ComposeArgs fwd, rev;
+    const bool split = split_chains(r);
+    if (split) {
+        const size_t KK = (size_t)r.P * p->H * p->K * p->K, KV = (size_t)r.P * p->H * p->K * p->V;
+        a.M = tail;
+        a.Mt = a.M + KK;
+        a.U = a.Mt + KK;
+        a.E = a.U + KV;
+        float *hin = a.E + KV, *dhin = hin + KV;
+        a.h_in = hin;
+        a.dh_in = dhin;
+        memset(&fwd, 0, sizeof(fwd));
+        fwd.R = r.R;
+        fwd.N = r.N;
+        fwd.H = p->H;
+        fwd.packed = r.ct.packed;
+        fwd.first = 0;
+        for (int n = 0; n <= r.N && r.ct.packed; ++n) fwd.seq_first[n] = r.seq_first[n];
+        rev = fwd;
+        fwd.M = a.M;        // h_in[next] = M h_in + U, from h0
+        fwd.U = a.U;
+        fwd.h0 = h0;
+        fwd.h_in = hin;
+        rev.M = a.Mt;       // dh_in[previous] = Mt dh_in + E, from dhT
+        rev.U = a.E;
+        rev.h0 = dhT;
+        rev.h_in = dhin;
+        rev.reverse = 1;
+    }
+    a.carry = 0;
+    a.N = r.N;
     a.H = p->H;
     a.Hk = Hk;
     a.tokens = r.T;
     a.n_chunks = r.n_chunks;
     a.ct = r.ct;
     (void)hipGetLastError();
-    return launched(launch_backward(p->K, p->V, p->C, p->dtype, a, r.P, (hipStream_t)stream),
+    return launched(launch_backward(p->K, p->V, p->C, p->dtype, a, r.P, split ? &fwd : nullptr,
+                                    split ? &rev : nullptr, (hipStream_t)stream),
                     "gdn_backward");
 }
 

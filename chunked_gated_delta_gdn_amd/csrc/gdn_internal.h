@@ -145,6 +145,9 @@ struct ComposeArgs {
     // packed mode: sequence n's pieces are seq_first[n] .. seq_first[n+1]-1;
     // the scan starts at piece `first` of each; state rows are [P, H]
     int32_t packed, first;
+    // 1: walk the steps last to first (the reverse scan of the backward pass,
+    // with M holding the transposed maps)
+    int32_t reverse;
     int16_t seq_first[GDN_MAX_SEQS + 1];
 };
 
@@ -183,10 +186,45 @@ struct BwdArgs {
     float *dg, *dbeta, *dh0;
     float *T, *attn, *Ak, *w, *u, *hs, *dhs, *d, *dd;
     float *dq_acc, *dk_acc;   // grouped key heads: per value head dq, dk [T, H, K]; else NULL
+    // Chains that split a sequence (segments, pieces), state rows [slots, H]
+    // (slot as in ComposeArgs): a chain that does not start its sequence
+    // starts from h_in, one that does not end it from dh_in (NULL when every
+    // chain is a whole sequence).  Carry launches write, per chain of a split
+    // sequence, the affine map of the forward scan (M [K,K] and its transpose
+    // Mt for every chain; U [K,V] for all but the last) and the reverse
+    // scan's offset E [K,V] for all but the first (the gradient at the
+    // chain's start given a zero gradient at its end).
+    const float *h_in, *dh_in;
+    float *M, *Mt, *U, *E;
+    int32_t carry;
+    int32_t N;                // sequences
     int32_t H, Hk;            // value heads; heads of q and k (value head h reads key head h / (H / Hk))
     int64_t n_chunks, tokens; // chunks over all sequences; tokens
     ChainTable ct;
 };
+
+// Where chain `chain` sits in its sequence.
+struct ChainPos {
+    int64_t slot;   // state row / H of the chain's boundary states and carries
+    int32_t seq;
+    bool first, last;
+};
+__host__ __device__ inline ChainPos chain_pos(const ChainTable &ct, int chain, int N) {
+    ChainPos c;
+    if (ct.packed) {
+        c.seq = ct.piece_seq[chain];
+        c.slot = chain;
+        c.first = chain == 0 || ct.piece_seq[chain - 1] != ct.piece_seq[chain];
+        c.last = ct.piece_last[chain] != 0;
+    } else {
+        const int seg = chain % ct.n_seg;
+        c.seq = chain / ct.n_seg;
+        c.slot = (int64_t)seg * N + c.seq;
+        c.first = seg == 0;
+        c.last = seg == ct.n_seg - 1;
+    }
+    return c;
+}
 static_assert(sizeof(BwdArgs) + 64 <= 4096, "backward kernel arguments too large");
 
 // Launchers (return the hipError_t of the launch).
@@ -202,9 +240,11 @@ hipError_t launch_decode(int K, int V, int dtype, const DecodeArgs &a, hipStream
 hipError_t launch_compose(int K, int V, const ComposeArgs &a, hipStream_t s);
 hipError_t launch_causal_conv(int dtype, const ConvArgs &a, hipStream_t s);
 hipError_t launch_gated_rmsnorm(int dtype, const NormArgs &a, hipStream_t s);
-// the four backward launches; n_chains = sequences
+// the backward launches; n_chains = chains (sequences, or their segments or
+// pieces); when chains split sequences, fwd and rev describe the compose
+// launches between the carry and emit scans (else both NULL)
 hipError_t launch_backward(int K, int V, int C, int dtype, const BwdArgs &a, int n_chains,
-                           hipStream_t s);
+                           const ComposeArgs *fwd, const ComposeArgs *rev, hipStream_t s);
 
 bool shape_supported(int K, int V, int C);
 

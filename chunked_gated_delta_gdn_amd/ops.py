@@ -605,13 +605,16 @@ def forward(q, k, v, g, beta, h0=None, chunk_size=64, cu_seqlens=None, n_segment
                      output_final_state=output_final_state)
 
 
-def backward(q, k, v, g, beta, do, h0=None, dhT=None, chunk_size=64, cu_seqlens=None, want_dh0=True):
+def backward(q, k, v, g, beta, do, h0=None, dhT=None, chunk_size=64, cu_seqlens=None, want_dh0=True,
+             n_segments=1, seg_starts=None, max_piece_chunks=0):
     """Gradients through the forward pass (``gdn_backward``).
 
     q, k [B,S,H_qk,K]; v, do [B,S,H,V] (fp32 or bf16); g, beta [B,S,H] fp32;
     h0, dhT [N,H,K,V] fp32 or None (zero).  Packed batches pass B == 1 and
-    cu_seqlens.  Returns (dq, dk, dv, dg, dbeta, dh0 or None), each in the
-    layout and dtype of its input (dh0 fp32)."""
+    cu_seqlens.  n_segments / seg_starts (batch) and max_piece_chunks
+    (packed) cut each sequence into parts whose state scans run in parallel,
+    as in ``forward``.  Returns (dq, dk, dv, dg, dbeta, dh0 or None), each in
+    the layout and dtype of its input (dh0 fp32)."""
     B, S, H, K, V = _check_inputs(q, k, v, g, beta)
     dev = k.device
     N = _n_seqs(k, cu_seqlens)
@@ -620,7 +623,8 @@ def backward(q, k, v, g, beta, do, h0=None, dhT=None, chunk_size=64, cu_seqlens=
         _need(h0, "h0", (N, H, K, V), torch.float32, dev)
     if dhT is not None:
         _need(dhT, "dhT", (N, H, K, V), torch.float32, dev)
-    p = problem_for(k, v, chunk_size, cu_seqlens)
+    p = problem_for(k, v, chunk_size, cu_seqlens, n_segments=n_segments, seg_starts=seg_starts,
+                    max_piece_chunks=max_piece_chunks or 0)
     _b.gdn_validate(p)
     nbytes = _b.gdn_backward_workspace_bytes(p)
     ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=dev)
@@ -640,6 +644,10 @@ class _ChunkGatedDeltaRule(torch.autograd.Function):
                         n_segments=n_segments, max_piece_chunks=max_piece_chunks)
         ctx.save_for_backward(q, k, v, g, beta, h0)
         ctx.chunk_size, ctx.cu_seqlens = chunk_size, cu_seqlens
+        # the backward's state scans take the same cut (an automatic piece plan
+        # is the forward's choice, so the backward keeps whole sequences)
+        ctx.n_segments = n_segments if cu_seqlens is None else 1
+        ctx.max_piece_chunks = max_piece_chunks if isinstance(max_piece_chunks, int) else 0
         return o, hT
 
     @staticmethod
@@ -648,7 +656,8 @@ class _ChunkGatedDeltaRule(torch.autograd.Function):
         dq, dk, dv, dg, dbeta, dh0 = backward(
             q, k, v, g, beta, do.contiguous(), h0=h0,
             dhT=None if dhT is None else dhT.contiguous(), chunk_size=ctx.chunk_size,
-            cu_seqlens=ctx.cu_seqlens, want_dh0=h0 is not None and ctx.needs_input_grad[5])
+            cu_seqlens=ctx.cu_seqlens, want_dh0=h0 is not None and ctx.needs_input_grad[5],
+            n_segments=ctx.n_segments, max_piece_chunks=ctx.max_piece_chunks)
         return dq, dk, dv, dg, dbeta, dh0, None, None, None, None
 
 

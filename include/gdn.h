@@ -336,11 +336,14 @@ gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t V, int32_t dtype, float eps, 
 
 /*
  * gdn_backward -- gradients of a loss l(o, hT) through the forward of the
- * problem (batch or packed, grouped key heads included; segments and
- * pieces, which only schedule the forward, are validated and then ignored:
- * every sequence runs as one chain), given
+ * problem (batch or packed, grouped key heads included), given
  * dout = dl/do [same layout as o, `dtype`] and dhT = dl/dhT
- * ([N,H,K,V] fp32, nullable = zero).  The MaxText PR "Add context
+ * ([N,H,K,V] fp32, nullable = zero).  Segments (batch) and pieces (packed)
+ * schedule the two state scans as they do the forward's: every part of a
+ * sequence is scanned at once, from boundary states composed of the parts'
+ * affine carries (the state scan's M, U; the reverse scan's M^T and offset),
+ * so a sequence of few heads still fills the GPU.  The result is that of one
+ * chain per sequence up to fp32 rounding.  The MaxText PR "Add context
  * parallelism to the Gated Delta Net" tests a backward pass against the
  * single-device recurrence (section "Tests") without printing one; this is
  * the chain rule through the chunk equations of its section "Why".
@@ -351,7 +354,11 @@ gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t V, int32_t dtype, float eps, 
  * not h0 is given).  h0 nullable (zero state).  Every output is fully
  * written for the real tokens; none may overlap an input.  workspace: caller
  * owned device memory of gdn_backward_workspace_bytes(p) bytes, 16-byte
- * aligned (contents undefined on return).  Arithmetic is fp32 throughout.
+ * aligned (contents undefined on return; it grows by P*H*(2*K*K + 4*K*V)*4
+ * bytes when the P chains split the sequences).  Arithmetic is fp32
+ * throughout, except that for bf16 inputs at K = V = 128 the Grams K K^T and
+ * Q K^T multiply the bf16 values on the bf16 matrix cores (exact products,
+ * fp32 sums).
  * Errors as gdn_scan; nothing is written on failure.
  */
 size_t gdn_backward_workspace_bytes(const gdn_problem *p);

@@ -9,7 +9,10 @@ for bf16 inputs (the kernels compute in fp32; bf16 enters through the inputs
 and the rounding of dq, dk, dv).  Cases span several chunks, ragged tails,
 both built shapes, packed streams with an empty sequence, absent h0 / dhT
 the autograd wrapper and grouped key heads (whose dq, dk are the sums over
-the value heads that read them: the chain rule through repeating a key head).
+the value heads that read them: the chain rule through repeating a key head),
+and sequences cut into segments or pieces whose state scans run in parallel
+from composed boundary states (checked against the oracle and against the
+one-chain backward).
 """
 import copy
 
@@ -36,20 +39,20 @@ def oracle_grads(x, do, dhT, h0=True):
     return oracle.backward(x.q, x.k, x.v, x.g, x.beta, h0a, do, dhT)
 
 
-def gpu_grads(x, do, dhT, h0=True):
+def gpu_grads(x, do, dhT, h0=True, **kw):
     dt = tdt(x.dtype)
     cu = None if x.cu_seqlens is None else [int(c) for c in x.cu_seqlens]
     out = gdn.backward(to_dev(x.q, dt), to_dev(x.k, dt), to_dev(x.v, dt), to_dev(x.g),
                        to_dev(x.beta), to_dev(do, dt),
                        h0=to_dev(x.h0) if (h0 and x.h0 is not None) else None,
-                       dhT=None if dhT is None else to_dev(dhT), chunk_size=x.C, cu_seqlens=cu)
+                       dhT=None if dhT is None else to_dev(dhT), chunk_size=x.C, cu_seqlens=cu, **kw)
     torch.cuda.synchronize()
     return [t.float().cpu().numpy() for t in out]
 
 
-def check(x, do, dhT, h0=True, tag=""):
-    say(f"backward {tag}: {x.name} dtype={x.dtype} shape={x.k.shape} C={x.C}")
-    got = gpu_grads(x, do, dhT, h0)
+def check(x, do, dhT, h0=True, tag="", **kw):
+    say(f"backward {tag}: {x.name} dtype={x.dtype} shape={x.k.shape} C={x.C} {kw}")
+    got = gpu_grads(x, do, dhT, h0, **kw)
     ref = oracle_grads(x, do, dhT, h0)
     if x.cu_seqlens is not None:
         got = [g_[0] if i < 5 else g_ for i, g_ in enumerate(got)]
@@ -160,16 +163,16 @@ def test_backward_grouped_key_heads(dtype, H, Hk, packed):
         assert errs[n] <= TOL[dtype], (n, errs[n])
 
 
-@pytest.mark.parametrize("wl,heads", [(1, (0, 9)), (2, (21,))])
-def test_backward_bench_workloads_sampled_heads(wl, heads):
+@pytest.mark.parametrize("wl,heads,R", [(1, (0, 9), 1), (2, (21,), 1), (2, (5,), 4)])
+def test_backward_bench_workloads_sampled_heads(wl, heads, R):
     """The backward lines of the benchmark as it times them (4k tokens x 16 heads;
-    64k tokens x 32 heads), every head on the GPU, sampled heads through the
-    oracle (heads are independent chains)."""
+    64k tokens x 32 heads; the latter also cut into 4 segments), every head on
+    the GPU, sampled heads through the oracle (heads are independent chains)."""
     from workloads import workload
     x = workload(wl)
     do, dhT = make_cotangents(47, x)
-    say(f"backward workload {wl}: {x.k.shape}, oracle on heads {heads}")
-    got = gpu_grads(x, do, dhT)
+    say(f"backward workload {wl}: {x.k.shape}, R={R}, oracle on heads {heads}")
+    got = gpu_grads(x, do, dhT, n_segments=R)
     hs = list(heads)
     ref = oracle.backward(x.q[:, :, hs], x.k[:, :, hs], x.v[:, :, hs], x.g[:, :, hs], x.beta[:, :, hs],
                           x.h0[:, hs], do[:, :, hs], dhT[:, hs])
@@ -185,17 +188,74 @@ def test_backward_is_deterministic():
     x = make_inputs(48, 1, 1000, 4, 128, 128, 64, "bf16", h0_std=0.02, decay="slow", name="bwd-det")
     do, dhT = make_cotangents(49, x)
     say("backward: determinism")
-    a = gpu_grads(x, do, dhT)
-    b = gpu_grads(x, do, dhT)
-    for n, u, v in zip(NAMES, a, b):
-        np.testing.assert_array_equal(u, v, err_msg=n)
+    for kw in ({}, {"n_segments": 3}):
+        a = gpu_grads(x, do, dhT, **kw)
+        b = gpu_grads(x, do, dhT, **kw)
+        for n, u, v in zip(NAMES, a, b):
+            np.testing.assert_array_equal(u, v, err_msg=f"{n} {kw}")
+
+
+def _vs_one_chain(x, got, whole):
+    """Cut chains against the one-chain backward: fp32 outputs agree to 1e-5
+    normwise (only the rounding of the composed maps differs); outputs stored in
+    bf16 (dq, dk, dv of bf16 inputs) to two units in the last place."""
+    worst = 0.0
+    for i, (n, u, w) in enumerate(zip(NAMES, got, whole)):
+        e = rel_err(u, w)
+        tol = 8e-3 if (x.dtype == "bf16" and i < 3) else 1e-5
+        say(f"  {n} vs one chain: {e:.3e} (bound {tol:g})")
+        assert e <= tol, (n, e)
+        worst = max(worst, e)
+    return worst
+
+
+@pytest.mark.parametrize("dtype,B,R,seg_starts", [("f32", 2, 2, None), ("f32", 1, 4, None),
+                                                  ("bf16", 1, 4, [0, 64, 320, 448]), ("bf16", 2, 2, None)])
+def test_backward_segments(dtype, B, R, seg_starts):
+    """Segments cut each sequence's two state scans into parts scanned at once:
+    the state scan's carries (M, U) compose the parts' start states, the reverse
+    scan's (M^T, E) their end gradients.  Slow decay keeps the state and its
+    gradient alive across every boundary, so a wrong carry or compose shows."""
+    x = make_inputs(53, B, 600, 2, 128, 128, 64, dtype, h0_std=0.3, decay="slow", name=f"bwd-seg{R}")
+    do, dhT = make_cotangents(54, x)
+    got, _ = check(x, do, dhT, tag=f"R={R}", n_segments=R, seg_starts=seg_starts)
+    _vs_one_chain(x, got, gpu_grads(x, do, dhT))
+
+
+def test_backward_segments_small_shape():
+    x = make_inputs(55, 2, 150, 3, 32, 32, 16, "f32", h0_std=0.3, decay="slow", name="bwd-seg-small")
+    do, dhT = make_cotangents(56, x)
+    got, _ = check(x, do, dhT, tag="R=3", n_segments=3)
+    _vs_one_chain(x, got, gpu_grads(x, do, dhT))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_pieces(dtype):
+    """A packed batch cut into pieces of at most 2 chunks (an empty sequence
+    and a one-piece sequence among them): oracle parity and agreement with the
+    one-chain backward."""
+    x = make_packed_inputs(57, 4, 900, 2, 128, 128, 64, dtype, h0_std=0.3, median=250, decay="slow",
+                           pad_to_chunk=False, name="bwd-pieces")
+    cu = [int(c) for c in x.cu_seqlens]
+    x.cu_seqlens = np.array(cu[:2] + [cu[1]] + cu[2:], dtype=np.int32)
+    x.h0 = np.concatenate([x.h0[:1], np.full_like(x.h0[:1], 0.3), x.h0[1:]])
+    x.meta = {}
+    do, dhT = make_cotangents(58, x)
+    p = gdn.problem_for(to_dev(x.k, tdt(dtype)), to_dev(x.v, tdt(dtype)), 64,
+                        [int(c) for c in x.cu_seqlens], max_piece_chunks=2)
+    assert b.gdn_num_pieces(p) > len(x.cu_seqlens) + 1
+    got, _ = check(x, do, dhT, tag="pieces", max_piece_chunks=2)
+    np.testing.assert_array_equal(got[5][1], dhT[1])
+    whole = gpu_grads(x, do, dhT)
+    whole = [g_[0] if i < 5 else g_ for i, g_ in enumerate(whole)]
+    _vs_one_chain(x, got, whole)
 
 
 @pytest.mark.parametrize("mode", ["segments", "packed_pieces"])
 def test_autograd_wrapper_with_forward_schedules(mode):
     """The differentiable forward with segments or a packed batch cut into pieces:
-    the schedule changes the forward's launches, not its result, and the backward
-    (whole sequences) gives the oracle's gradients."""
+    the schedule changes the launches (the backward's state scans take the same
+    cut), not the result: the oracle's gradients."""
     if mode == "segments":
         x = make_inputs(50, 1, 700, 2, 128, 128, 64, "bf16", h0_std=0.02, decay="slow", name="bwd-seg")
         kw = dict(n_segments=3)

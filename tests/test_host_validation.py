@@ -289,17 +289,24 @@ def test_conv_and_norm_validation():
 
 
 def test_backward_validation():
-    """gdn_backward: whole sequences, every buffer distinct, the workspace sized
-    by gdn_backward_workspace_bytes."""
+    """gdn_backward: every buffer distinct, the workspace sized by
+    gdn_backward_workspace_bytes (growing by the carries and boundary states
+    of chains that split sequences)."""
     import ctypes
     lib = b.library()
     ref = ctypes.byref
     p = prob()                                    # B1 S256 H2 K32 V32 C16 fp32
     ws = b.gdn_backward_workspace_bytes(p)
     assert ws == 16 * 2 * 4 * (3 * 16 * 16 + 16 * 32 + 3 * 16 * 32 + 2 * 32 * 32)
-    # segments and pieces only schedule the forward: the backward runs whole sequences
-    assert b.gdn_backward_workspace_bytes(prob(n_segments=2)) == ws
+    # segments and pieces: per chain and head M, Mt [K,K] and U, E, h_in, dh_in [K,V]
+    per_chain = 2 * 4 * (2 * 32 * 32 + 4 * 32 * 32)
+    assert b.gdn_backward_workspace_bytes(prob(n_segments=2)) == ws + 2 * per_chain
+    assert b.gdn_backward_workspace_bytes(prob(B=3, n_segments=4)) == 3 * ws + 12 * per_chain
     assert b.gdn_backward_workspace_bytes(prob(n_segments=2, seg_starts=[0, 100])) == 0   # invalid as given
+    # packed: 3 chunks + 8 chunks at m = 2 -> 2 + 4 pieces
+    pk = prob(S=176, cu_seqlens=[0, 48, 176], max_piece_chunks=2)
+    pk0 = prob(S=176, cu_seqlens=[0, 48, 176])
+    assert b.gdn_backward_workspace_bytes(pk) == b.gdn_backward_workspace_bytes(pk0) + 6 * per_chain
     # grouped key heads add fp32 dq, dk rows of every value head
     wg = b.gdn_backward_workspace_bytes(prob(H=4, H_qk=2))
     assert wg == 2 * ws + 2 * 256 * 4 * 32 * 4
@@ -316,6 +323,7 @@ def test_backward_validation():
     assert call(prob(H=4, H_qk=2), ws_bytes=wg - 1) == b.GDN_EWORKSPACE
     assert call(prob(S=100, cu_seqlens=[0, 30, 100], max_piece_chunks=-1)) == b.GDN_EINVAL
     assert call(p, ws_bytes=ws - 1) == b.GDN_EWORKSPACE
+    assert call(prob(n_segments=2), ws_bytes=ws + 2 * per_chain - 1) == b.GDN_EWORKSPACE
     assert call(p, q=None) == b.GDN_EINVAL
     assert call(p, dout=None) == b.GDN_EINVAL
     assert call(p, dg=buf[1] + 4) == b.GDN_EINVAL          # misaligned
