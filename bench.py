@@ -194,22 +194,56 @@ class StreamTimer:
         return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.marks.items()}
 
 
-def time_steps(torch, step, steps, warmup, only=None):
+def time_steps(torch, step, steps, warmup, only=None, per_step=None):
     """Mean ms per step over `steps` steps after `warmup`, and the mean HIP-event
     time of each named kernel (only those in `only`, if given: every event pair
-    recorded inside the timed steps costs the step a little)."""
+    recorded inside the timed steps costs the step a little).  With a list
+    `per_step`, an event between consecutive steps gives each step's own time
+    (appended to it)."""
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
     timer = StreamTimer(torch, only)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st = torch.cuda.current_stream()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    start.record(torch.cuda.current_stream())
-    for _ in range(steps):
+    marks[0].record(st)
+    for i in range(steps):
         step(timer)
-    end.record(torch.cuda.current_stream())
+        marks[i + 1].record(st)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps, timer.avg_ms()
+    if per_step is not None:
+        per_step.extend(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    return marks[0].elapsed_time(marks[steps]) / steps, timer.avg_ms()
+
+
+def time_cold_steps(torch, step, steps, flush_bytes=1 << 30):
+    """Per-step ms with the GPU's caches (L2 and the 256 MB MALL) flushed before
+    each step by writing a buffer larger than them; only the step is timed."""
+    dev = torch.cuda.current_device()
+    junk = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    out = []
+    step(None)
+    for _ in range(steps):
+        junk.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step(None)
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    del junk
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def time_with_breakdown(torch, step, steps, warmup):
@@ -268,7 +302,8 @@ def main():
     # the timed steps carry HIP events around the dominant kernel only (the roofline
     # kernel); a short second pass times every launch of the step for the breakdown
     dom_name = "scan_emit"
-    ms, kern_dom = time_steps(torch, seg_step, args.steps, args.warmup, only={dom_name})
+    step_ms = []
+    ms, kern_dom = time_steps(torch, seg_step, args.steps, args.warmup, only={dom_name}, per_step=step_ms)
     _, kern = time_steps(torch, seg_step, min(args.steps, 10), 1)
     kern[dom_name] = kern_dom[dom_name]
     tokens = B * S
@@ -315,6 +350,7 @@ def main():
     result = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_median": float(np.median(step_ms)), "ms_per_step_min": float(np.min(step_ms)),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; q,k L2-normalised, beta sigmoid, g -softplus)",
         "config": {"workload": f"B{B} H{H} S{S} K{K} V{V} C{C}, {R} contiguous segments "
@@ -426,6 +462,14 @@ def main():
                 extra[name + tag] = {"tokens_per_s": y.real_tokens / (ms2 * 1e-3), "ms": ms2, "max_piece_chunks": mm,
                                      "step_roofline": step_roofline(y.real_tokens, y.q.shape[2], ms2),
                                      "pieces": gdn.num_pieces(yk, yv, 64, cu, mm), "kernels_ms": k2}
+                if wl == 1 and tag == "":
+                    # the 4k-token inputs (48 MiB of bf16 q, k, v) fit the 256 MB MALL:
+                    # the same step with every cache flushed first
+                    cold = time_cold_steps(torch, fwd, steps2)
+                    extra[name + "_cold_caches"] = {
+                        "tokens_per_s": y.real_tokens / (float(np.median(cold)) * 1e-3),
+                        "ms_median": float(np.median(cold)), "ms_min": float(np.min(cold)),
+                        "how": "1 GiB buffer written before each step; each step timed alone"}
             del yq, yk, yv, yg, yb, yh
 
         # the steps beside the core at the 64k workload's size: the depthwise causal conv
@@ -551,12 +595,21 @@ def main():
             dt = time.perf_counter() - t0
             if dt >= 0.9 * args.cpu_seconds:
                 break
+        # one core: one head of the same tokens (about a sixteenth of the work above)
+        n1 = ns
+        t1 = time.perf_counter()
+        oracle.forward(x.q[:, :n1, :1], x.k[:, :n1, :1], x.v[:, :n1, :1], x.g[:, :n1, :1],
+                       x.beta[:, :n1, :1], h0=x.h0[:, :1], nthreads=1)
+        d1 = time.perf_counter() - t1
         result["cpu_baseline"] = {
             "value": reps * ns * nh / H / dt, "unit": "tokens/s", "cores": min(threads, nh),
             "kind": "oracle",
             "sample": f"first {ns} tokens x {nh} of {H} heads of the 64k-token workload, "
                       f"{reps} pass(es), fp64 token recurrence, {dt:.1f} s; tokens/s counts "
                       f"whole {H}-head tokens",
+            "cpu_model": cpu_model(),
+            "single_core": {"value": n1 / H / d1, "unit": "tokens/s",
+                            "sample": f"first {n1} tokens x 1 head, 1 thread, {d1:.1f} s"},
         }
     print(json.dumps(result), flush=True)
 

@@ -52,5 +52,31 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host code only: device code is never built with a sanitizer.
+SANITIZE_HOST = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(out_dir: str) -> str:
+    """libgdn.so with AddressSanitizer and UndefinedBehaviorSanitizer on its host
+    code (argument checks, layouts, launch set-up), for the CPU tests; load it
+    with GDN_LIBRARY and clang's ASan runtime preloaded."""
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, *SANITIZE_HOST, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    lib = os.path.join(out_dir, "libgdn_sanitized.so")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                    "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", lib, *objs], check=True)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose="-q" not in sys.argv))

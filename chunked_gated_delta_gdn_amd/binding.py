@@ -12,7 +12,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libgdn.so")
+# GDN_LIBRARY names another build of the same library (the sanitized host build of the CPU tests)
+LIB_PATH = os.environ.get("GDN_LIBRARY") or os.path.join(PKG, "libgdn.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EORDER, GDN_ELAUNCH, GDN_EWORKSPACE = range(6)
 GDN_F32, GDN_BF16 = 0, 1
