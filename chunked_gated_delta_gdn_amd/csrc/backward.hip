@@ -23,9 +23,10 @@
 // tiles, elsewhere (and for the small shape) on the vector ALU:
 //   1. prep   (chunk, head):    T, attn, Dec (.) K K^T, w, u
 //   2. states (chain, head, column group), chunks in order: the state at
-//      every chunk start (stored transposed, V x K) and delta
+//      every chunk start and delta
 //   3. dstates (chain, head, column group), chunks in reverse: dl/dh at every
-//      chunk end (transposed) and ddelta; dh0 at the end
+//      chunk end and ddelta; dh0 at the end
+//   (the stored states are K x V at K = V = 128, transposed V x K elsewhere)
 //   4. grads  (chunk, head):    dq, dk, dv, dg, dbeta of the chunk's tokens
 // The state columns are independent under both scans (the forward's and its
 // reverse), so a workgroup of 2. and 3. owns NCOL of them.
@@ -751,7 +752,9 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
     if (nch > 0) fetch(0);
     for (int64_t c = 0; c < nch; ++c) {
         const int64_t ch = (sp.chunk0 + c) * H + h;
-        if (!a.carry) *reinterpret_cast<f32x4 *>(a.hs + ch * KV + (int64_t)(j0 + li) * K + row0) = hacc;
+        if (!a.carry)   // [K][V], the layout the grads kernels read
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.hs[ch * KV + (int64_t)(row0 + e) * V + j0 + li] = hacc[e];
         *reinterpret_cast<f32x4 *>(&hT[li * LDK + row0]) = hacc;
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
@@ -872,7 +875,9 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
     if (nch > 0) fetch(nch - 1);
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int64_t ch = (sp.chunk0 + c) * H + h;
-        if (!a.carry) *reinterpret_cast<f32x4 *>(a.dhs + ch * KV + (int64_t)(j0 + li) * K + row0) = dacc;
+        if (!a.carry)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.dhs[ch * KV + (int64_t)(row0 + e) * V + j0 + li] = dacc[e];
         *reinterpret_cast<f32x4 *>(&dhT[li * LDK + row0]) = dacc;
 #pragma unroll
         for (int m = 0; m < KPT; ++m) {
@@ -983,7 +988,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
     const int hk = h / (H / a.Hk);
     const int64_t ch = chunk * H + h;
     const int64_t KV = (int64_t)K * V;
-    const float *hsT = a.hs + ch * KV, *dhsT = a.dhs + ch * KV;   // [V][K]
+    // states: [K][V] at K = V = 128 (the matrix-core scans), else [V][K]
+    const float *hsT = a.hs + ch * KV, *dhsT = a.dhs + ch * KV;
     const float *attn = a.attn + ch * C * C, *Ak = a.Ak + ch * C * C;
     const float *dws = a.d + ch * C * V;
     auto qx = [&](int r, int i) { return Elem<T>::load(a.q, (tc + r) * rowK + hk * K + i); };
@@ -1047,7 +1053,7 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
                 const int j0q = 4 * (4 * q + lg);
                 float ha[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ha[e] = hsT[(int64_t)(j0q + e) * K + i];
+                for (int e = 0; e < 4; ++e) ha[e] = hsT[(int64_t)i * V + j0q + e];   // [K][V] at K = V = 128
 #pragma unroll
                 for (int tcol = 0; tcol < 4; ++tcol) {
                     const int rc = 16 * tcol + li;   // B column
@@ -1282,8 +1288,8 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
             float hb[4], dhb[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                hb[e] = hsT[(int64_t)(j0q + e) * K + i];
-                dhb[e] = dhsT[(int64_t)(j0q + e) * K + i];
+                hb[e] = hsT[(int64_t)i * V + j0q + e];
+                dhb[e] = dhsT[(int64_t)i * V + j0q + e];
             }
 #pragma unroll
             for (int tr = 0; tr < 4; ++tr) {
@@ -1451,40 +1457,41 @@ __global__ __launch_bounds__(NT) void bwd_grads_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------ 4b. grads, K = V = 128, C = 64
-// The same gradients as bwd_grads_kernel (bf16 inputs), arranged so that every operand of a
-// matrix-core loop comes from LDS: the chunk's rows of do, k, v and q are
-// staged once (coalesced 16-byte loads) into regions whose earlier contents
-// are dead, and h, dh are fetched into registers before the staging so their
-// latency overlaps it.  Row and column sums and the final reverse cumulative
-// sum run over many threads (each combination in a fixed order, so two calls
-// give the same bits).  Products are 16 x 16 fp32 matrix-core tiles as in the
-// state scans: lane (li, lg) gives A[li][k] and B[k][li] with
-// k = 4 (4 q + lg) + e, and holds D[4 lg + e][li].
+// The same gradients as bwd_grads_kernel (bf16 inputs), arranged so that every
+// matrix-core operand comes from LDS or registers: the chunk's rows of do, k,
+// v and q are staged once (16-byte loads) into regions whose earlier contents
+// are dead, and h, dh (stored K x V) are fetched into registers first, so
+// their latency overlaps the staging; gamma <h, dh> is summed from those
+// registers.  Row and column sums and the final reverse cumulative sum run
+// over many threads, each combination in a fixed order (two calls give the
+// same bits).  Products are 16 x 16 fp32 matrix-core tiles as in the state
+// scans: lane (li, lg) gives A[li][k] and B[k][li] with k = 4 (4 q + lg) + e,
+// and holds D[4 lg + e][li].
 template <typename T>
 __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
     static_assert(sizeof(typename Elem<T>::raw_t) == 2, "k, v, q rows are staged as bf16");
     constexpr int K = 128, V = 128, C = 64, NT = 512, NW = 8;
     constexpr int VP = V + 4;   // fp32 rows of C x V tiles (16-byte aligned; 16 rows hit distinct banks)
     constexpr int CP = C + 1;   // fp32 rows of C x C tiles and of dw^T [K][CP]
-    constexpr int RS = K + 4;   // bf16 rows of the staged k, v rows [C][RS]
-    constexpr int TS = C + 4;   // bf16 rows of the staged k^T, q^T [K][TS] (8-byte aligned)
-    constexpr int R1F = 2 * K * TS / 2 > C * VP ? 2 * K * TS / 2 : C * VP;
+    constexpr int RS = K + 4;   // bf16 rows of the staged k, v, q rows [C][RS] (8-byte aligned)
     typedef uint16_t u16;
     // LDS regions, reused as their contents die:
-    //   R1: delta [C][VP] -> k, v rows (bf16 [C][RS] each) -> Z [C][CP] -> k^T, q^T (bf16 [K][TS] each)
-    //   R2: do [C][VP] (fp32) -> dw^T [K][CP]
-    __shared__ __attribute__((aligned(16))) float R1[R1F];
-    __shared__ __attribute__((aligned(16))) float bdD[C * VP];   // ddelta
+    //   R1:  delta [C][VP] -> k rows | v rows (bf16 [C][RS] each) -> k rows | Z [C][CP]
+    //   bdD: ddelta [C][VP] -> q rows (bf16 [C][RS])
+    //   R2:  do [C][VP] (fp32) -> dw^T [K][CP]
+    __shared__ __attribute__((aligned(16))) float R1[C * VP];
+    __shared__ __attribute__((aligned(16))) float bdD[C * VP];
     __shared__ __attribute__((aligned(16))) float R2[C * VP];
     __shared__ float bT[C * CP];   // T
     __shared__ float bX[C * CP];   // dattn
     __shared__ float bY[C * CP];   // dT^T, then dA
-    static_assert(2 * C * RS * 2 <= R1F * 4 && 2 * K * TS * 2 <= R1F * 4 && K * CP <= C * VP &&
-                      C * CP <= R1F && (RS * 2) % 8 == 0 && (TS * 2) % 8 == 0,
+    static_assert(2 * C * RS * 2 <= C * VP * 4 && C * CP * 4 <= C * RS * 2 && K * CP <= C * VP &&
+                      (RS * 2) % 8 == 0,
                   "staged tiles fit their regions; bf16 rows keep 8-byte alignment");
-    float *const bD = R1, *const bZ = R1, *const bdo = R2, *const bW = R2;
-    u16 *const rk = reinterpret_cast<u16 *>(R1), *const rv = rk + C * RS;   // k, v rows
-    u16 *const tk = reinterpret_cast<u16 *>(R1), *const tq = tk + K * TS;   // k^T, q^T
+    float *const bD = R1, *const bdo = R2, *const bW = R2;
+    u16 *const rk = reinterpret_cast<u16 *>(R1), *const rv = rk + C * RS;
+    u16 *const rq = reinterpret_cast<u16 *>(bdD);
+    float *const bZ = reinterpret_cast<float *>(rv);
     __shared__ float sG[C], sEg[C], sEk[C], sb[C];
     __shared__ float sPw[NW * C], sBw[NW * C], sLast[NW], sRowA[C], sColA[C], sRowB[C];
 
@@ -1499,7 +1506,7 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
     const int hk = h / (H / a.Hk);
     const int64_t ch = chunk * H + h;
     const int64_t KV = (int64_t)K * V;
-    const float *hsT = a.hs + ch * KV, *dhsT = a.dhs + ch * KV;   // [V][K]
+    const float *hs = a.hs + ch * KV, *dhs = a.dhs + ch * KV;   // [K][V]
     const float *attn = a.attn + ch * C * C, *Ak = a.Ak + ch * C * C;
     const int i = 16 * wv + li;   // this lane's column of the K-wide outputs (dq, dk, dw^T rows)
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
@@ -1507,28 +1514,22 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
         if (acc) acc[((tc + r) * H + h) * K + ii] = x;
         else Elem<T>::store(out, (tc + r) * rowK + hk * K + ii, x);
     };
-    // 8 consecutive elements of row r (clamped into the chunk) of a [T, H, D] tensor
+    // 8 consecutive bf16 of row r (clamped into the chunk) of a [T, H, D] tensor
     auto row8 = [&](const void *base, int64_t row_elems, int64_t col0, int r) {
         const int64_t e = (tc + min(r, L - 1)) * row_elems + col0;
         return *reinterpret_cast<const uint4 *>(static_cast<const u16 *>(base) + e);
     };
     auto f32of = [](uint32_t w, int half) { return __uint_as_float(half ? (w & 0xffff0000u) : (w << 16)); };
-    // four bf16 (8 bytes) -> four floats
-    auto ld4b = [&](const u16 *p) {
-        const uint2 w = *reinterpret_cast<const uint2 *>(p);
-        return f32x4{f32of(w.x, 0), f32of(w.x, 1), f32of(w.y, 0), f32of(w.y, 1)};
-    };
+    auto bf = [](u16 x) { return __uint_as_float((uint32_t)x << 16); };
 
-    // ---- h and dh of this lane's column i, fetched first (dq, dk^~ and dw use them)
-    float hv[8][4], dhv[8][4];
+    // ---- h and dh of this lane's row i, columns 16 q + 4 lg .. + 3 (the B
+    // operands of dqg, dkt and the A operand of dw^T), fetched first
+    f32x4 hv[8], dhv[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = 4 * (4 * q + lg) + e;
-            hv[q][e] = hsT[(int64_t)j * K + i];
-            dhv[q][e] = dhsT[(int64_t)j * K + i];
-        }
+    for (int q = 0; q < 8; ++q) {
+        hv[q] = *reinterpret_cast<const f32x4 *>(hs + (int64_t)i * V + 16 * q + 4 * lg);
+        dhv[q] = *reinterpret_cast<const f32x4 *>(dhs + (int64_t)i * V + 16 * q + 4 * lg);
+    }
     // ---- staging: delta, ddelta, T (fp32 workspace), do (rows past L zero), beta, decay
     {
         const float *d = a.d + ch * C * V, *dd = a.dd + ch * C * V, *Tm = a.T + ch * C * C;
@@ -1548,13 +1549,10 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
 #pragma unroll
         for (int m = 0; m < (C * V / 8) / NT; ++m) {
             const int e8 = tid + NT * m, r = (8 * e8) / V, j = (8 * e8) % V;
-            float x[8];
             const uint4 w = row8(a.dout, rowV, h * V + j, r);
             const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = f32of(ww[e >> 1], e & 1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bdo[r * VP + j + e] = r < L ? x[e] : 0.f;
+            for (int e = 0; e < 8; ++e) bdo[r * VP + j + e] = r < L ? f32of(ww[e >> 1], e & 1) : 0.f;
         }
         if (tid < C) sb[tid] = tid < L ? a.beta[(tc + tid) * H + h] : 0.f;
         for (int e = tid; e < NW * C; e += NT) {
@@ -1585,13 +1583,16 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
         }
     }
     // ---- over V: dqg = do h^T, dkt = delta dh^T (the k_tilde gradient), and
-    // dw^T = -(h ddelta^T) for this wave's row tile of dw^T (column i of h)
+    // dw^T = -(h ddelta^T) for this wave's row tile of dw^T (row i of h)
     f32x4 dqg[4], dkt[4], dwa[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) dqg[t] = dkt[t] = dwa[t] = z4;
+    float gam = 0.f;   // this lane's part of <h, dh> (the lanes cover every element once)
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int j0q = 4 * (4 * q + lg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gam = fmaf(hv[q][e], dhv[q][e], gam);
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr) {
             const int r = 16 * tr + li;
@@ -1603,6 +1604,15 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
                 dwa[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(hv[q][e], dd[e], dwa[tr], 0, 0, 0);
             }
         }
+    }
+    // gamma: dG_last += gamma <h, dh>
+    put_row<64>(sLast, wv, sEg[C - 1] * gam);
+    // q rows, fetched now for the q row tile staged after dT
+    uint4 pq[(C * K / 8) / NT];
+#pragma unroll
+    for (int m = 0; m < (C * K / 8) / NT; ++m) {
+        const int e8 = tid + NT * m, r = (8 * e8) / K, j = (8 * e8) % K;
+        pq[m] = row8(a.q, rowK, hk * K + j, r);
     }
     __syncthreads();
     // ---- dw^T into R2 (do is dead); k, v rows into R1 (delta is dead)
@@ -1632,7 +1642,10 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int j0q = 4 * (4 * q + lg);
-            const f32x4 v4 = ld4b(&rv[sr * RS + j0q]), k4 = ld4b(&rk[sr * RS + j0q]);
+            const uint2 v2 = *reinterpret_cast<const uint2 *>(&rv[sr * RS + j0q]);
+            const uint2 k2 = *reinterpret_cast<const uint2 *>(&rk[sr * RS + j0q]);
+            const float v4[4] = {f32of(v2.x, 0), f32of(v2.x, 1), f32of(v2.y, 0), f32of(v2.y, 1)};
+            const float k4[4] = {f32of(k2.x, 0), f32of(k2.x, 1), f32of(k2.y, 0), f32of(k2.y, 1)};
             const f32x4 db = lds4(&bdD[rc * VP + j0q]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -1646,46 +1659,9 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
             bY[ss * CP + rc] = sb[ss] * (av[e] + sEg[ss] * ak[e]);
         }
     }
-    __syncthreads();
-    // ---- Z = dT T^T  (bZ over the dead k, v rows)
-    for (int o = tid; o < C * C; o += NT) {
-        const int r = o / C, s2 = o % C;
-        float acc = 0.f;
-        for (int pp = 0; pp < C; ++pp) acc = fmaf(bY[pp * CP + r], bT[s2 * CP + pp], acc);
-        bZ[r * CP + s2] = acc;
-    }
-    __syncthreads();
-    // ---- dA = -strict_lower(T^T Z)   (T[p][r] = 0 for p < r)
-    for (int o = tid; o < C * C; o += NT) {
-        const int r = o / C, s2 = o % C;
-        float acc = 0.f;
-        if (s2 < r)
-            for (int pp = r; pp < C; ++pp) acc = fmaf(-bT[pp * CP + r], bZ[pp * CP + s2], acc);
-        bY[r * CP + s2] = acc;
-    }
-    __syncthreads();
-    // ---- k^T, q^T into R1 (Z is dead); dv and dbeta's T^T ddelta . v term;
-    // the row and column sums of the C x C terms
-#pragma unroll
-    for (int m = 0; m < (C * K / 8) / NT; ++m) {
-        const int e8 = tid + NT * m, r = (8 * e8) / K, j = (8 * e8) % K;
-        u16 kk8[8], qq8[8];
-        const uint4 wk = row8(a.k, rowK, hk * K + j, r), wq = row8(a.q, rowK, hk * K + j, r);
-        const uint32_t ak4[4] = {wk.x, wk.y, wk.z, wk.w}, aq4[4] = {wq.x, wq.y, wq.z, wq.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            kk8[e] = (u16)(ak4[e >> 1] >> (16 * (e & 1)));
-            qq8[e] = (u16)(aq4[e >> 1] >> (16 * (e & 1)));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            tk[(j + e) * TS + r] = r < L ? kk8[e] : (u16)0;
-            tq[(j + e) * TS + r] = r < L ? qq8[e] : (u16)0;
-        }
-    }
     {
         // dv = diag(beta) T^T ddelta, dbeta += (T^T ddelta) . v: 4 x 8 tiles of C x V,
-        // wave wv owns column tile wv
+        // wave wv owns column tile wv (v read from its staged rows)
         const int j = 16 * wv + li;   // B column
         f32x4 acc[4] = {z4, z4, z4, z4};
 #pragma unroll
@@ -1700,12 +1676,6 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
                 for (int e = 0; e < 4; ++e)
                     acc[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(bT[(p0 + e) * CP + 16 * tr + li], bb[e], acc[tr], 0, 0, 0);
         }
-        float vv[4][4];
-#pragma unroll
-        for (int tr = 0; tr < 4; ++tr)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                vv[tr][e] = Elem<T>::load(a.v, (tc + min(16 * tr + 4 * lg + e, L - 1)) * rowV + h * V + j);
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr)
 #pragma unroll
@@ -1714,30 +1684,90 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
                 float part = 0.f;
                 if (r < L) {
                     Elem<T>::store(a.dv, (tc + r) * rowV + h * V + j, sb[r] * acc[tr][e]);
-                    part = acc[tr][e] * vv[tr][e];
+                    part = acc[tr][e] * bf(rv[r * RS + j]);
                 }
                 put_row<16>(sBw + wv * C, r, part);
             }
     }
+    __syncthreads();
+    // ---- Z = dT T^T (over the dead v rows), two of the 4 x 4 tiles per wave:
+    // A[r][p] = dT[r][p] = bY[p][r], B[p][s] = T[s][p]; q rows into bdD (ddelta is dead)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tile = 2 * wv + u, tr = tile >> 2, tcol = tile & 3;
+        f32x4 acc = z4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int pp = 4 * (4 * q + lg) + e;
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bY[pp * CP + 16 * tr + li], bT[(16 * tcol + li) * CP + pp],
+                                                           acc, 0, 0, 0);
+            }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bZ[(16 * tr + 4 * lg + e) * CP + 16 * tcol + li] = acc[e];
+    }
+#pragma unroll
+    for (int m = 0; m < (C * K / 8) / NT; ++m) {
+        const int e8 = tid + NT * m, r = (8 * e8) / K, j = (8 * e8) % K;
+        const uint4 w = r < L ? pq[m] : make_uint4(0, 0, 0, 0);
+        uint2 *p2 = reinterpret_cast<uint2 *>(&rq[r * RS + j]);
+        p2[0] = make_uint2(w.x, w.y);
+        p2[1] = make_uint2(w.z, w.w);
+    }
+    // attn and Ak for the row and column sums, fetched before dA
+    const int rr = tid >> 3, seg = tid & 7;
+    float at_r[8], ak_r[8], at_c[8], ak_c[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int c8 = 8 * seg + m;
+        at_r[m] = attn[rr * C + c8];
+        ak_r[m] = Ak[rr * C + c8];
+        at_c[m] = attn[c8 * C + rr];
+        ak_c[m] = Ak[c8 * C + rr];
+    }
+    __syncthreads();
+    // ---- dA = -strict_lower(T^T Z), two tiles per wave (those above the
+    // diagonal are zero): A[r][p] = T[p][r] (zero for p < r), B[p][s] = Z[p][s]
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int tile = 2 * wv + u, tr = tile >> 2, tcol = tile & 3;
+        f32x4 acc = z4;
+        if (tcol <= tr) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int pp = 4 * (4 * q + lg) + e;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bT[pp * CP + 16 * tr + li], bZ[pp * CP + 16 * tcol + li],
+                                                               acc, 0, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 16 * tr + 4 * lg + e, s2 = 16 * tcol + li;
+            bY[r * CP + s2] = s2 < r ? -acc[e] : 0.f;
+        }
+    }
+    __syncthreads();
     {
         // e(r, s) = dattn attn + beta_r dA Ak (the raw gradient matrices):
         // dG_r += e(r, s), dG_s -= e(r, s), dbeta_r += dA Ak.  Thread t sums
         // eight columns of row t / 8 and eight rows of column t / 8; the eight
         // partial sums of a row (column) are combined in a fixed order.
-        const int rr = tid >> 3, seg = tid & 7;
         float re = 0.f, rb = 0.f, ce = 0.f;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int s2 = 8 * seg + m;   // columns of row rr
             if (s2 <= rr) {
-                const float eA = s2 < rr ? bY[rr * CP + s2] * Ak[rr * C + s2] : 0.f;
-                re += bX[rr * CP + s2] * attn[rr * C + s2] + sb[rr] * eA;
+                const float eA = s2 < rr ? bY[rr * CP + s2] * ak_r[m] : 0.f;
+                re += bX[rr * CP + s2] * at_r[m] + sb[rr] * eA;
                 rb += eA;
             }
             const int r2 = 8 * seg + m;   // rows of column rr
             if (r2 >= rr) {
-                const float eA = rr < r2 ? bY[r2 * CP + rr] * Ak[r2 * C + rr] : 0.f;
-                ce += bX[r2 * CP + rr] * attn[r2 * C + rr] + sb[r2] * eA;
+                const float eA = rr < r2 ? bY[r2 * CP + rr] * ak_c[m] : 0.f;
+                ce += bX[r2 * CP + rr] * at_c[m] + sb[r2] * eA;
             }
         }
 #pragma unroll
@@ -1765,16 +1795,20 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
     __syncthreads();
     // ---- over the chunk's tokens p (zero past L in every B operand):
     //   qa = (dattn D) k,  dkr = (dattn D)^T q + (dKK + dKK^T) k,  dkb = T^T dw
+    // (k and q read down column i of their staged rows)
     f32x4 qa[4], dkr[4], dkb[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) qa[t] = dkr[t] = dkb[t] = z4;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int p0 = 4 * (4 * q + lg);
-        const f32x4 kb = ld4b(&tk[i * TS + p0]), qb = ld4b(&tq[i * TS + p0]);
-        float wb[4];
+        float kb[4], qb[4], wb[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) wb[e] = bW[i * CP + p0 + e];
+        for (int e = 0; e < 4; ++e) {
+            kb[e] = bf(rk[(p0 + e) * RS + i]);
+            qb[e] = bf(rq[(p0 + e) * RS + i]);
+            wb[e] = bW[i * CP + p0 + e];
+        }
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr) {
             const int r = 16 * tr + li;
@@ -1794,14 +1828,13 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
     float pdl = 0.f;
 #pragma unroll
     for (int tr = 0; tr < 4; ++tr) {
-        const f32x4 kr4 = ld4b(&tk[i * TS + 16 * tr + 4 * lg]), qr4 = ld4b(&tq[i * TS + 16 * tr + 4 * lg]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * tr + 4 * lg + e;
             float pg = 0.f, pd = 0.f, pk = 0.f;
             if (r < L) {
                 const float eG = sEg[r], er = sEk[r], br = sb[r];
-                const float kri = kr4[e], qri = qr4[e];
+                const float kri = bf(rk[r * RS + i]), qri = bf(rq[r * RS + i]);
                 put_qk(a.dq, a.dq_acc, r, i, eG * dqg[tr][e] + qa[tr][e]);
                 put_qk(a.dk, a.dk_acc, r, i, dkr[tr][e] + er * dkt[tr][e] + br * eG * dkb[tr][e]);
                 pg = eG * dqg[tr][e] * qri - er * dkt[tr][e] * kri + br * eG * dkb[tr][e] * kri;
@@ -1814,18 +1847,6 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
         }
     }
     put_row<64>(sLast, wv, pdl);
-    // gamma: dG_last += gamma <h, dh>
-    {
-        float x = 0.f;
-#pragma unroll
-        for (int m = 0; m < (K * V / 4) / NT; ++m) {
-            const f32x4 hh = *reinterpret_cast<const f32x4 *>(hsT + 4 * (tid + NT * m));
-            const f32x4 dh = *reinterpret_cast<const f32x4 *>(dhsT + 4 * (tid + NT * m));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x = fmaf(hh[e], dh[e], x);
-        }
-        put_row<64>(sLast, wv, sEg[C - 1] * x);
-    }
     __syncthreads();
     // ---- dg = reverse cumulative sum of dG over the chunk; dbeta (wave 0, lane = row)
     if (wv == 0) {

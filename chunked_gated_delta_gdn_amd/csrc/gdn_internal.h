@@ -178,7 +178,8 @@ struct NormArgs {
 // Backward pass.  Gradients in the layouts of their inputs; the fp32
 // workspace holds, per (chunk, head): T = (I + A)^{-1}, attn and the decayed
 // Gram Dec (.) K K^T (C x C each), w (C x K), u, delta, ddelta (C x V), and
-// the state and its gradient at the chunk's start and end (V x K, transposed).
+// the state and its gradient at the chunk's start and end (K x V at K = V =
+// 128, else transposed V x K).
 struct BwdArgs {
     const void *q, *k, *v, *dout;
     const float *g, *beta, *h0, *dhT;

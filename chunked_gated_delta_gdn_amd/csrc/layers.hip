@@ -205,8 +205,16 @@ __device__ __forceinline__ void raw_unpack(const float4 (&r)[2], float (&v)[8]) 
 
 // The same convolution, 8 channels per thread (D % 8 == 0), over a block of
 // TB tokens whose loads are all issued before the first is used, so each
-// thread keeps TB 16-byte reads in flight.
-template <typename T> constexpr int conv8_tokens() { return sizeof(T) == 2 ? 16 : 8; }
+// thread keeps TB 16-byte reads in flight.  TB = 8 keeps a thread within 128
+// registers (4 waves per SIMD); the W-1 tokens before a block are read again
+// by it, from L2 when the block before it ran on the same XCD, so token
+// blocks are dealt to the 8 XCDs in contiguous runs (workgroups go to the
+// XCDs in turn by index): XCD j takes blocks j * per .. (j + 1) * per - 1.
+// (Measured on the 65,536-token x 8,192-channel bf16 case: about 5% faster than
+// 16-token blocks dealt round-robin; 512- or 1,024-thread blocks were slower.)
+template <typename T> constexpr int conv8_tokens() { return 8; }
+constexpr int kXcds = 8;
+__host__ __device__ inline int64_t conv8_rounded(int64_t n_blocks) { return (n_blocks + kXcds - 1) / kXcds * kXcds; }
 
 template <typename T, int MT>   // MT: at least W (4 or 8), the size of the tap and window arrays
 __global__ __launch_bounds__(kConvThreads) void causal_conv8_kernel(ConvArgs a) {
@@ -221,7 +229,18 @@ __global__ __launch_bounds__(kConvThreads) void causal_conv8_kernel(ConvArgs a) 
     auto state_at = [&](int n, int k, int j) -> float {   // state of channel c + k, position j (oldest first)
         return a.state_in ? Elem<T>::load(a.state_in, ((int64_t)n * D + c + k) * P + j) : 0.f;
     };
-    const int bx = blockIdx.x;
+    // token block of this workgroup (see above); index nbr is the extra block
+    // for sequences without tokens, the rest of the padding exits
+    const int64_t nbr = conv8_rounded(a.n_blocks), per = nbr / kXcds;
+    int bx;
+    if ((int64_t)blockIdx.x >= nbr) {
+        if ((int64_t)blockIdx.x != nbr) return;
+        bx = (int)a.n_blocks;
+    } else {
+        const int64_t l = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+        if (l >= a.n_blocks) return;
+        bx = (int)l;
+    }
     if (bx >= a.n_blocks) {
         // the extra block column: sequences with no tokens keep their state
         if (!a.state_out) return;
@@ -386,7 +405,7 @@ hipError_t launch_causal_conv(int dtype, const ConvArgs &a, hipStream_t s) {
             b.n_blocks = (int64_t)a.N * ((a.S + TB - 1) / TB);
         }
         const int64_t groups = a.D / 8;
-        const dim3 grid((unsigned)(b.n_blocks + 1), (unsigned)((groups + kConvThreads - 1) / kConvThreads)),
+        const dim3 grid((unsigned)(conv8_rounded(b.n_blocks) + 1), (unsigned)((groups + kConvThreads - 1) / kConvThreads)),
             block(kConvThreads);
         if (a.W <= 4) {
             if (dtype == GDN_F32) hipLaunchKernelGGL((causal_conv8_kernel<float, 4>), grid, block, 0, s, b);
