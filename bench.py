@@ -85,8 +85,9 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_scan_mfma_seq64k_4seg.md")
+# the sources of the scan kernels whose counters the traffic summary holds
 KERNEL_SOURCES = [os.path.join(ROOT, "chunked_gated_delta_gdn_amd", "csrc", f)
-                  for f in ("scan_mfma.hip", "mfma_tile.h", "dev_common.h", "gdn_internal.h")]
+                  for f in ("scan_mfma.hip", "mfma_tile.h", "dev_common.h")]
 COPY_BYTES = 1 << 30
 
 
