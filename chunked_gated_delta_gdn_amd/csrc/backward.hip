@@ -726,8 +726,13 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
     // is masked or converted at once would make the wave wait for it here.
     f32x4 pw[8];
     float pu[4], pg = 0.f;
-    typename Elem<T>::raw_t pk[KPT];
+    // k: 8 consecutive elements of row 16 rb + li at column 32 cb + 8 lg per
+    // load, (rb, cb) = (s & 3, s >> 2) for s = 2 wv + m (16 loads of 64 lanes
+    // cover the 64 x 128 tile)
+    Raw8<T> pk[KPT / 8];
     int pL = 0;
+    auto krow = [&](int m) { return 16 * ((2 * wv + m) & 3) + li; };
+    auto kcol = [&](int m) { return 32 * ((2 * wv + m) >> 2) + 8 * lg; };
     auto fetch = [&](int64_t c) {
         int L;
         int64_t tc;
@@ -742,10 +747,7 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
             for (int e = 0; e < 4; ++e) pu[e] = is_M ? 0.f : u[(row0 + e) * V + j0 + li];
         }
 #pragma unroll
-        for (int m = 0; m < KPT; ++m) {
-            const int e = tid + NT * m, r = e / K, i = e % K;
-            pk[m] = Elem<T>::load_raw(a.k, (tc + min(r, L - 1)) * rowK + hk * K + i);
-        }
+        for (int m = 0; m < KPT / 8; ++m) pk[m].load(a.k, (tc + min(krow(m), L - 1)) * rowK + hk * K + kcol(m));
         pg = a.g[(tc + min(tid, L - 1)) * H + h];
         pL = L;
     };
@@ -757,9 +759,10 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
             for (int e = 0; e < 4; ++e) a.hs[ch * KV + (int64_t)(row0 + e) * V + j0 + li] = hacc[e];
         *reinterpret_cast<f32x4 *>(&hT[li * LDK + row0]) = hacc;
 #pragma unroll
-        for (int m = 0; m < KPT; ++m) {
-            const int e = tid + NT * m;
-            kT[(e % K) * LDC + e / K] = e / K < pL ? Elem<T>::from_raw(pk[m]) : 0.f;
+        for (int m = 0; m < KPT / 8; ++m) {
+            const int r = krow(m), i0 = kcol(m);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kT[(i0 + j) * LDC + r] = r < pL ? pk[m].at(j) : 0.f;
         }
         if (tid < 64) chunk_decay<C>(tid < C && tid < pL ? pg : 0.f, sG, sEg, sEk);
         __syncthreads();
@@ -845,9 +848,20 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
     const int64_t nch = (sp.t1 - sp.t0 + C - 1) / C;
     // the previous chunk's operands, fetched a chunk ahead (rows past the chunk
     // end loaded from its last row and zeroed where used, as in the states scan)
-    typename Elem<T>::raw_t pk[KPT], pq[KPT], pd[DPT];
-    float pw[KPT], pa[APT], pg = 0.f;
+    // k, q: 8 consecutive elements of row 16 rb + li at column 32 cb + 8 lg per
+    // load, (rb, cb) = (s & 3, s >> 2) for s = 2 wv + m; w (fp32 [C][K]): 4 of row
+    // 16 rb + li at column 16 cb + 4 lg, (rb, cb) = (s & 3, s >> 2) for s = 4 wv + m;
+    // attn ([C][C]): 4 of row 16 tb + li at column 16 sb + 4 lg for s = 2 wv + m
+    Raw8<T> pk[KPT / 8], pq[KPT / 8];
+    typename Elem<T>::raw_t pd[DPT];
+    f32x4 pw[KPT / 4], pa[APT / 4];
+    float pg = 0.f;
     int pL = 0;
+    auto krow = [&](int m) { return 16 * ((2 * wv + m) & 3) + li; };
+    auto kcol = [&](int m) { return 32 * ((2 * wv + m) >> 2) + 8 * lg; };
+    auto wrow = [&](int m) { return 16 * ((4 * wv + m) & 3) + li; };
+    auto wcol = [&](int m) { return 16 * ((4 * wv + m) >> 2) + 4 * lg; };
+    auto acol = [&](int m) { return 16 * ((2 * wv + m) >> 2) + 4 * lg; };   // (attn rows: krow)
     auto fetch = [&](int64_t c) {
         int L;
         int64_t tc;
@@ -855,15 +869,15 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
         const int64_t ch = (sp.chunk0 + c) * H + h;
         const float *w = a.w + ch * C * K, *attn = a.attn + ch * C * C;
 #pragma unroll
-        for (int m = 0; m < KPT; ++m) {
-            const int e = tid + NT * m, r = e / K, i = e % K;
-            const int64_t x = (tc + min(r, L - 1)) * rowK + hk * K + i;
-            pk[m] = Elem<T>::load_raw(a.k, x);
-            pq[m] = Elem<T>::load_raw(a.q, x);
-            pw[m] = w[e];
+        for (int m = 0; m < KPT / 8; ++m) {
+            const int64_t x = (tc + min(krow(m), L - 1)) * rowK + hk * K + kcol(m);
+            pk[m].load(a.k, x);
+            pq[m].load(a.q, x);
         }
 #pragma unroll
-        for (int m = 0; m < APT; ++m) pa[m] = attn[tid + NT * m];
+        for (int m = 0; m < KPT / 4; ++m) pw[m] = *reinterpret_cast<const f32x4 *>(w + wrow(m) * K + wcol(m));
+#pragma unroll
+        for (int m = 0; m < APT / 4; ++m) pa[m] = *reinterpret_cast<const f32x4 *>(attn + krow(m) * C + acol(m));
 #pragma unroll
         for (int m = 0; m < DPT; ++m) {
             const int e = tid + NT * m, t = min(e / NCOL, L - 1), jj = e % NCOL;
@@ -880,17 +894,31 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
             for (int e = 0; e < 4; ++e) a.dhs[ch * KV + (int64_t)(row0 + e) * V + j0 + li] = dacc[e];
         *reinterpret_cast<f32x4 *>(&dhT[li * LDK + row0]) = dacc;
 #pragma unroll
-        for (int m = 0; m < KPT; ++m) {
-            const int e = tid + NT * m, r = e / K, i = e % K;
+        for (int m = 0; m < KPT / 8; ++m) {
+            const int r = krow(m), i0 = kcol(m);
             const bool ok = r < pL;
-            sk[r * LDK + i] = ok ? Elem<T>::from_raw(pk[m]) : 0.f;
-            qT[i * LDC + r] = ok ? Elem<T>::from_raw(pq[m]) : 0.f;
-            wT[i * LDC + r] = pw[m];
+            f32x4 k0, k1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                k0[j] = ok ? pk[m].at(j) : 0.f;
+                k1[j] = ok ? pk[m].at(4 + j) : 0.f;
+            }
+            *reinterpret_cast<f32x4 *>(&sk[r * LDK + i0]) = k0;
+            *reinterpret_cast<f32x4 *>(&sk[r * LDK + i0 + 4]) = k1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qT[(i0 + j) * LDC + r] = ok ? pq[m].at(j) : 0.f;
         }
 #pragma unroll
-        for (int m = 0; m < APT; ++m) {
-            const int e = tid + NT * m;
-            aT[(e % C) * LDC + e / C] = pa[m];
+        for (int m = 0; m < KPT / 4; ++m) {
+            const int r = wrow(m), i0 = wcol(m);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wT[(i0 + j) * LDC + r] = pw[m][j];
+        }
+#pragma unroll
+        for (int m = 0; m < APT / 4; ++m) {
+            const int t = krow(m), s0 = acol(m);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) aT[(s0 + j) * LDC + t] = pa[m][j];
         }
 #pragma unroll
         for (int m = 0; m < DPT; ++m) {

@@ -55,4 +55,30 @@ template <> struct Elem<bf16_t> {
     }
 };
 
+// Eight consecutive elements fetched as one (bf16: 16 B) or two (fp32: 2 x 16 B)
+// loads and converted where used; `at` takes a constant index after unrolling.
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+    uint4 v;
+    __device__ __forceinline__ void load(const void *p, int64_t i) {
+        v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + i);
+    }
+    __device__ __forceinline__ float at(int j) const {
+        const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+        return __uint_as_float((j & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const void *p, int64_t i) {
+        a = *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+        b = *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i + 4);
+    }
+    __device__ __forceinline__ float at(int j) const {
+        const float4 &x = j < 4 ? a : b;
+        const int k = j & 3;
+        return k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w;
+    }
+};
+
 }  // namespace gdn
