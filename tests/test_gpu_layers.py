@@ -141,3 +141,38 @@ def test_gated_rmsnorm_in_place_and_zero_rows():
     assert y.data_ptr() == t.data_ptr()
     assert rel_err(y.cpu().numpy(), oracle.gated_rmsnorm(o, w, eps=1e-6)) <= TOL["f32"]
     assert not np.any(y[1, 2].cpu().numpy())
+
+
+def test_conv_and_norm_bench_size_sampled():
+    """The conv and the norm at the sizes the benchmark times them (65,536 tokens;
+    conv over 8,192 channels, 4 taps, SiLU, with a state; norm over 32 heads of
+    128 values with a gate, bf16), in that launch configuration: every output on the
+    GPU, sampled channels (conv: 64 channels from each 2,048-channel workgroup
+    column) and rows (norm: 4,096 rows) through the oracle."""
+    Tn, D, W, H, V = 65536, 8192, 4, 32, 128
+    rng = np.random.default_rng(61)
+    x = round_bf16(rng.standard_normal((1, Tn, D), dtype=np.float32))
+    w = vals(rng, (D, W), "bf16", 0.5)
+    st = vals(rng, (1, D, W - 1), "bf16")
+    say(f"conv at bench size: T={Tn} D={D} W={W}")
+    y, s2 = gdn.causal_conv1d(to_dev(x, torch.bfloat16), to_dev(w, torch.bfloat16), to_dev(st, torch.bfloat16))
+    torch.cuda.synchronize()
+    ch = np.concatenate([np.arange(64) + 2048 * c for c in range(4)]) + 7
+    ch = ch[ch < D]
+    y_ref, s_ref = oracle.causal_conv1d(x[0][:, ch], w[ch], st[0][ch])
+    ey = rel_err(y[0][:, ch].float().cpu().numpy(), y_ref)
+    say(f"  conv sampled channels: err(y)={ey:.2e}")
+    assert ey <= TOL["bf16"]
+    np.testing.assert_array_equal(s2[0][ch].float().cpu().numpy(), s_ref)
+    del x, y, s2
+    o = round_bf16(rng.standard_normal((Tn, H, V), dtype=np.float32) * 3.0)
+    z = round_bf16(rng.standard_normal((Tn, H, V), dtype=np.float32))
+    wn = rng.standard_normal(V).astype(np.float32)
+    say(f"norm at bench size: rows={Tn * H} V={V}")
+    yn = gdn.gated_rmsnorm(to_dev(o, torch.bfloat16), to_dev(wn), to_dev(z, torch.bfloat16))
+    torch.cuda.synchronize()
+    rows = rng.choice(Tn, size=128, replace=False)
+    yr = oracle.gated_rmsnorm(o[rows].reshape(-1, V), wn, z[rows].reshape(-1, V))
+    e = rel_err(yn[torch.as_tensor(rows, device=yn.device)].float().cpu().numpy().reshape(-1, V), yr)
+    say(f"  norm sampled rows: err={e:.2e}")
+    assert e <= TOL["bf16"]
