@@ -1549,6 +1549,45 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
     };
     auto f32of = [](uint32_t w, int half) { return __uint_as_float(half ? (w & 0xffff0000u) : (w << 16)); };
     auto bf = [](u16 x) { return __uint_as_float((uint32_t)x << 16); };
+    // x[4 tr + e] is this lane's term of row 16 tr + 4 lg + e; the sum over the
+    // 16 lanes li of its lane group comes back in lane li for row index li
+    // (a transposing butterfly: 15 exchanges instead of 16 x 4)
+    auto rows16 = [&](float (&x)[16]) {
+        float y8[8], y4[4], y2[2];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const bool hi = li & 8;
+            const float send = hi ? x[t] : x[8 + t];
+            y8[t] = (hi ? x[8 + t] : x[t]) + __shfl_xor(send, 8);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bool hi = li & 4;
+            const float send = hi ? y8[t] : y8[4 + t];
+            y4[t] = (hi ? y8[4 + t] : y8[t]) + __shfl_xor(send, 4);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const bool hi = li & 2;
+            const float send = hi ? y4[t] : y4[2 + t];
+            y2[t] = (hi ? y4[2 + t] : y4[t]) + __shfl_xor(send, 2);
+        }
+        const bool hi = li & 1;
+        const float send = hi ? y2[0] : y2[1];
+        return (hi ? y2[1] : y2[0]) + __shfl_xor(send, 1);
+    };
+    const int rrow = 16 * (li >> 2) + 4 * lg + (li & 3);   // the row whose sum lane li receives
+    // a C x 128 bf16 tile of this chunk's rows, staged in LDS (row stride 128)
+    // and written as whole rows, 16 bytes per lane
+    auto write_rows = [&](const u16 *tile, void *out, int64_t row_elems, int64_t col0) {
+#pragma unroll
+        for (int m = 0; m < (C * 128 / 8) / NT; ++m) {
+            const int e8 = tid + NT * m, r = e8 >> 4, c8 = 8 * (e8 & 15);
+            if (r < L)
+                *reinterpret_cast<uint4 *>(static_cast<u16 *>(out) + (tc + r) * row_elems + col0 + c8) =
+                    *reinterpret_cast<const uint4 *>(&tile[r * 128 + c8]);
+        }
+    };
 
     // ---- h and dh of this lane's row i, columns 16 q + 4 lg .. + 3 (the B
     // operands of dqg, dkt and the A operand of dw^T), fetched first
@@ -1687,6 +1726,7 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
             bY[ss * CP + rc] = sb[ss] * (av[e] + sEg[ss] * ak[e]);
         }
     }
+    f32x4 dvk[4];   // dv rows 16 tr + 4 lg + e of column 16 wv + li, stored once a tile is free
     {
         // dv = diag(beta) T^T ddelta, dbeta += (T^T ddelta) . v: 4 x 8 tiles of C x V,
         // wave wv owns column tile wv (v read from its staged rows)
@@ -1704,18 +1744,16 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
                 for (int e = 0; e < 4; ++e)
                     acc[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(bT[(p0 + e) * CP + 16 * tr + li], bb[e], acc[tr], 0, 0, 0);
         }
+        float part[16];
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * tr + 4 * lg + e;
-                float part = 0.f;
-                if (r < L) {
-                    Elem<T>::store(a.dv, (tc + r) * rowV + h * V + j, sb[r] * acc[tr][e]);
-                    part = acc[tr][e] * bf(rv[r * RS + j]);
-                }
-                put_row<16>(sBw + wv * C, r, part);
+                part[4 * tr + e] = r < L ? acc[tr][e] * bf(rv[r * RS + j]) : 0.f;
+                dvk[tr][e] = sb[r] * acc[tr][e];
             }
+        sBw[wv * C + rrow] = rows16(part);   // (the first write of this slot)
     }
     __syncthreads();
     // ---- Z = dT T^T (over the dead v rows), two of the 4 x 4 tiles per wave:
@@ -1778,6 +1816,11 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
+    // dv into the dead Z tile (the v rows' region), written out after the next barrier
+#pragma unroll
+    for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv[(16 * tr + 4 * lg + e) * 128 + 16 * wv + li] = f32_to_bf16(dvk[tr][e]);
     {
         // e(r, s) = dattn attn + beta_r dA Ak (the raw gradient matrices):
         // dG_r += e(r, s), dG_s -= e(r, s), dbeta_r += dA Ak.  Thread t sums
@@ -1811,6 +1854,7 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
+    write_rows(rv, a.dv, rowV, (int64_t)h * V);
     // ---- fold the decay in once: bX <- dattn (.) D,  bY <- dA (.) beta_r D  (= dKK)
     for (int o = tid; o < C * C; o += NT) {
         const int r = o / C, s2 = o % C;
@@ -1853,29 +1897,57 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
         }
     }
     // ---- dq, dk; this lane's parts of dG, dbeta and of the last row's k_tilde term
-    float pdl = 0.f;
+    float pdl = 0.f, pgs[16], pks[16];
+    float dqv[4][4], dkv[4][4];
 #pragma unroll
     for (int tr = 0; tr < 4; ++tr) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = 16 * tr + 4 * lg + e;
-            float pg = 0.f, pd = 0.f, pk = 0.f;
-            if (r < L) {
-                const float eG = sEg[r], er = sEk[r], br = sb[r];
-                const float kri = bf(rk[r * RS + i]), qri = bf(rq[r * RS + i]);
-                put_qk(a.dq, a.dq_acc, r, i, eG * dqg[tr][e] + qa[tr][e]);
-                put_qk(a.dk, a.dk_acc, r, i, dkr[tr][e] + er * dkt[tr][e] + br * eG * dkb[tr][e]);
-                pg = eG * dqg[tr][e] * qri - er * dkt[tr][e] * kri + br * eG * dkb[tr][e] * kri;
-                pd = er * dkt[tr][e] * kri;
-                pk = eG * dkb[tr][e] * kri;
-            }
-            put_row<16>(sPw + wv * C, r, pg);
-            put_row<16>(sBw + wv * C, r, pk);
-            pdl += pd;
+            const float eG = sEg[r], er = sEk[r], br = sb[r];
+            const float kri = bf(rk[r * RS + i]), qri = bf(rq[r * RS + i]);
+            dqv[tr][e] = eG * dqg[tr][e] + qa[tr][e];
+            dkv[tr][e] = dkr[tr][e] + er * dkt[tr][e] + br * eG * dkb[tr][e];
+            const bool ok = r < L;
+            pgs[4 * tr + e] = ok ? eG * dqg[tr][e] * qri - er * dkt[tr][e] * kri + br * eG * dkb[tr][e] * kri : 0.f;
+            pks[4 * tr + e] = ok ? eG * dkb[tr][e] * kri : 0.f;
+            pdl += ok ? er * dkt[tr][e] * kri : 0.f;
         }
     }
+    sPw[wv * C + rrow] = rows16(pgs);
+    sBw[wv * C + rrow] += rows16(pks);   // (this lane wrote the slot's dv term)
     put_row<64>(sLast, wv, pdl);
+    if (a.dq_acc) {
+        // grouped key heads: fp32 rows of every value head, summed by a later kernel
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tr + 4 * lg + e;
+                if (r < L) {
+                    put_qk(a.dq, a.dq_acc, r, i, dqv[tr][e]);
+                    put_qk(a.dk, a.dk_acc, r, i, dkv[tr][e]);
+                }
+            }
+    }
+    __syncthreads();   // (dw^T is dead: R2 takes the dq and dk rows)
+    if (!a.dq_acc) {
+        u16 *tq2 = reinterpret_cast<u16 *>(R2), *tk2 = tq2 + C * 128;
+#pragma unroll
+        for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * tr + 4 * lg + e;
+                tq2[r * 128 + i] = f32_to_bf16(dqv[tr][e]);
+                tk2[r * 128 + i] = f32_to_bf16(dkv[tr][e]);
+            }
+    }
     __syncthreads();
+    if (!a.dq_acc) {
+        const u16 *tq2 = reinterpret_cast<const u16 *>(R2), *tk2 = tq2 + C * 128;
+        write_rows(tq2, a.dq, rowK, (int64_t)hk * K);
+        write_rows(tk2, a.dk, rowK, (int64_t)hk * K);
+    }
     // ---- dg = reverse cumulative sum of dG over the chunk; dbeta (wave 0, lane = row)
     if (wv == 0) {
         const int r = lane;
