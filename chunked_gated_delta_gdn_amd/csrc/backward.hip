@@ -1502,21 +1502,27 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
     constexpr int VP = V + 4;   // fp32 rows of C x V tiles (16-byte aligned; 16 rows hit distinct banks)
     constexpr int CP = C + 1;   // fp32 rows of C x C tiles and of dw^T [K][CP]
     constexpr int RS = K + 4;   // bf16 rows of the staged k, v, q rows [C][RS] (8-byte aligned)
+    constexpr int PS = V + 8;   // bf16 rows of the delta, ddelta planes and of do [C][PS] (16-byte aligned)
+    constexpr int PF = C * PS;  // floats of two [C][PS] bf16 planes
     typedef uint16_t u16;
     // LDS regions, reused as their contents die:
-    //   R1:  delta [C][VP] -> k rows | v rows (bf16 [C][RS] each) -> k rows | Z [C][CP]
-    //   bdD: ddelta [C][VP] -> q rows (bf16 [C][RS])
-    //   R2:  do [C][VP] (fp32) -> dw^T [K][CP]
-    __shared__ __attribute__((aligned(16))) float R1[C * VP];
-    __shared__ __attribute__((aligned(16))) float bdD[C * VP];
+    //   R1:  delta as bf16 hi, lo planes -> k rows | v rows (bf16 [C][RS] each) -> k rows | Z [C][CP]
+    //   bdD: ddelta as bf16 hi, lo planes -> q rows (bf16 [C][RS])
+    //   R2:  do (bf16 [C][PS]) -> dw^T [K][CP]
+    __shared__ __attribute__((aligned(16))) float R1[PF];
+    __shared__ __attribute__((aligned(16))) float bdD[PF];
     __shared__ __attribute__((aligned(16))) float R2[C * VP];
     __shared__ float bT[C * CP];   // T
     __shared__ float bX[C * CP];   // dattn
     __shared__ float bY[C * CP];   // dT^T, then dA
-    static_assert(2 * C * RS * 2 <= C * VP * 4 && C * CP * 4 <= C * RS * 2 && K * CP <= C * VP &&
-                      (RS * 2) % 8 == 0,
-                  "staged tiles fit their regions; bf16 rows keep 8-byte alignment");
-    float *const bD = R1, *const bdo = R2, *const bW = R2;
+    static_assert(2 * C * RS * 2 <= PF * 4 && C * CP * 4 <= C * RS * 2 && K * CP <= C * VP &&
+                      C * PS * 2 <= C * VP * 4 && 2 * C * 128 * 2 <= C * VP * 4 && (RS * 2) % 8 == 0 &&
+                      (PS * 2) % 16 == 0,
+                  "staged tiles fit their regions; bf16 rows keep their alignment");
+    float *const bW = R2;
+    u16 *const dhi = reinterpret_cast<u16 *>(R1), *const dlo = dhi + C * PS;    // delta = hi + lo
+    u16 *const ddhi = reinterpret_cast<u16 *>(bdD), *const ddlo = ddhi + C * PS;  // ddelta
+    u16 *const bdo = reinterpret_cast<u16 *>(R2);                                // do
     u16 *const rk = reinterpret_cast<u16 *>(R1), *const rv = rk + C * RS;
     u16 *const rq = reinterpret_cast<u16 *>(bdD);
     float *const bZ = reinterpret_cast<float *>(rv);
@@ -1589,22 +1595,63 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
         }
     };
 
-    // ---- h and dh of this lane's row i, columns 16 q + 4 lg .. + 3 (the B
-    // operands of dqg, dkt and the A operand of dw^T), fetched first
-    f32x4 hv[8], dhv[8];
+    // An fp32 operand x enters a bf16 matrix-core product as the pair hi = bf16(x),
+    // lo = bf16(x - hi), |x - hi - lo| <= 2^-18 |x|: products of two such operands
+    // take hi.hi + hi.lo + lo.hi, those with an exact bf16 input (do) hi + lo;
+    // every product of bf16 values is exact in fp32 and the sums run in fp32.
+    auto split2 = [](float x0, float x1, uint32_t &hi, uint32_t &lo) {
+        hi = mfma::cvt2(x0, x1);
+        lo = mfma::cvt2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
+    };
+    // ---- h and dh of this lane's row i, columns 32 kb + 8 lg .. + 7 (the B
+    // operands of dqg, dk~ and the A operand of dw^T), fetched first, split
+    // into hi, lo pairs; gamma <h, dh> summed from them (the lanes cover
+    // every element once)
+    mfma::bf16x8 hhi[4], hlo[4], dhhi[4], dhlo[4];
+    float gam = 0.f;
+    {
+        f32x4 hv[8], dhv[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        hv[q] = *reinterpret_cast<const f32x4 *>(hs + (int64_t)i * V + 16 * q + 4 * lg);
-        dhv[q] = *reinterpret_cast<const f32x4 *>(dhs + (int64_t)i * V + 16 * q + 4 * lg);
+        for (int m = 0; m < 8; ++m) {
+            const int64_t o = (int64_t)i * V + 32 * (m >> 1) + 8 * lg + 4 * (m & 1);
+            hv[m] = *reinterpret_cast<const f32x4 *>(hs + o);
+            dhv[m] = *reinterpret_cast<const f32x4 *>(dhs + o);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            uint32_t a0[4], a1[4], b0[4], b1[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x4 &x = hv[2 * kb + (t >> 1)], &y = dhv[2 * kb + (t >> 1)];
+                const int e = 2 * (t & 1);
+                gam = fmaf(x[e], y[e], fmaf(x[e + 1], y[e + 1], gam));
+                split2(x[e], x[e + 1], a0[t], a1[t]);
+                split2(y[e], y[e + 1], b0[t], b1[t]);
+            }
+            hhi[kb] = mfma::as8(make_uint4(a0[0], a0[1], a0[2], a0[3]));
+            hlo[kb] = mfma::as8(make_uint4(a1[0], a1[1], a1[2], a1[3]));
+            dhhi[kb] = mfma::as8(make_uint4(b0[0], b0[1], b0[2], b0[3]));
+            dhlo[kb] = mfma::as8(make_uint4(b1[0], b1[1], b1[2], b1[3]));
+        }
     }
-    // ---- staging: delta, ddelta, T (fp32 workspace), do (rows past L zero), beta, decay
+    // ---- staging: delta and ddelta (fp32 workspace) as hi, lo planes, T, do
+    // (rows past L zero), beta, decay
     {
         const float *d = a.d + ch * C * V, *dd = a.dd + ch * C * V, *Tm = a.T + ch * C * C;
 #pragma unroll
         for (int m = 0; m < (C * V / 4) / NT; ++m) {
             const int e4 = tid + NT * m, r = (4 * e4) / V, j = (4 * e4) % V;
-            *reinterpret_cast<f32x4 *>(&bD[r * VP + j]) = *reinterpret_cast<const f32x4 *>(d + 4 * e4);
-            *reinterpret_cast<f32x4 *>(&bdD[r * VP + j]) = *reinterpret_cast<const f32x4 *>(dd + 4 * e4);
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(d + 4 * e4);
+            const f32x4 y = *reinterpret_cast<const f32x4 *>(dd + 4 * e4);
+            uint32_t h0, h1, l0, l1;
+            split2(x[0], x[1], h0, l0);
+            split2(x[2], x[3], h1, l1);
+            *reinterpret_cast<uint2 *>(&dhi[r * PS + j]) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2 *>(&dlo[r * PS + j]) = make_uint2(l0, l1);
+            split2(y[0], y[1], h0, l0);
+            split2(y[2], y[3], h1, l1);
+            *reinterpret_cast<uint2 *>(&ddhi[r * PS + j]) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2 *>(&ddlo[r * PS + j]) = make_uint2(l0, l1);
         }
 #pragma unroll
         for (int m = 0; m < (C * C / 4) / NT; ++m) {
@@ -1617,9 +1664,7 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
         for (int m = 0; m < (C * V / 8) / NT; ++m) {
             const int e8 = tid + NT * m, r = (8 * e8) / V, j = (8 * e8) % V;
             const uint4 w = row8(a.dout, rowV, h * V + j, r);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) bdo[r * VP + j + e] = r < L ? f32of(ww[e >> 1], e & 1) : 0.f;
+            *reinterpret_cast<uint4 *>(&bdo[r * PS + j]) = r < L ? w : make_uint4(0, 0, 0, 0);
         }
         if (tid < C) sb[tid] = tid < L ? a.beta[(tc + tid) * H + h] : 0.f;
         for (int e = tid; e < NW * C; e += NT) {
@@ -1631,17 +1676,18 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
     load_cumdecay<C>(sG, sEg, sEk, a.g, tc, L, H, h);   // (synchronises)
 
     // ---- dattn = causal(do delta^T): 4 x 4 tiles of C x C, wave wv owns two
+    auto ld8 = [](const u16 *p) { return mfma::as8(*reinterpret_cast<const uint4 *>(p)); };
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int tile = 2 * wv + u, tr = tile >> 2, tcol = tile & 3;
         const int r = 16 * tr + li, sc = 16 * tcol + li;   // A row, B column
         f32x4 acc = z4;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int j0q = 4 * (4 * q + lg);
-            const f32x4 ao = lds4(&bdo[r * VP + j0q]), bo = lds4(&bD[sc * VP + j0q]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ao[e], bo[e], acc, 0, 0, 0);
+        for (int kb = 0; kb < V / 32; ++kb) {
+            const int j0 = 32 * kb + 8 * lg;
+            const mfma::bf16x8 ao = ld8(&bdo[r * PS + j0]);
+            acc = mfma::mma32(ao, ld8(&dhi[sc * PS + j0]), acc);
+            acc = mfma::mma32(ao, ld8(&dlo[sc * PS + j0]), acc);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1654,22 +1700,23 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
     f32x4 dqg[4], dkt[4], dwa[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) dqg[t] = dkt[t] = dwa[t] = z4;
-    float gam = 0.f;   // this lane's part of <h, dh> (the lanes cover every element once)
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int j0q = 4 * (4 * q + lg);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) gam = fmaf(hv[q][e], dhv[q][e], gam);
+    for (int kb = 0; kb < V / 32; ++kb) {
+        const int j0 = 32 * kb + 8 * lg;
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr) {
             const int r = 16 * tr + li;
-            const f32x4 ao = lds4(&bdo[r * VP + j0q]), dl = lds4(&bD[r * VP + j0q]), dd = lds4(&bdD[r * VP + j0q]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dqg[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(ao[e], hv[q][e], dqg[tr], 0, 0, 0);
-                dkt[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(dl[e], dhv[q][e], dkt[tr], 0, 0, 0);
-                dwa[tr] = __builtin_amdgcn_mfma_f32_16x16x4f32(hv[q][e], dd[e], dwa[tr], 0, 0, 0);
-            }
+            const mfma::bf16x8 ao = ld8(&bdo[r * PS + j0]);
+            const mfma::bf16x8 ah = ld8(&dhi[r * PS + j0]), al = ld8(&dlo[r * PS + j0]);
+            const mfma::bf16x8 bh = ld8(&ddhi[r * PS + j0]), bl = ld8(&ddlo[r * PS + j0]);
+            dqg[tr] = mfma::mma32(ao, hhi[kb], dqg[tr]);
+            dqg[tr] = mfma::mma32(ao, hlo[kb], dqg[tr]);
+            dkt[tr] = mfma::mma32(ah, dhhi[kb], dkt[tr]);
+            dkt[tr] = mfma::mma32(ah, dhlo[kb], dkt[tr]);
+            dkt[tr] = mfma::mma32(al, dhhi[kb], dkt[tr]);
+            dwa[tr] = mfma::mma32(hhi[kb], bh, dwa[tr]);
+            dwa[tr] = mfma::mma32(hhi[kb], bl, dwa[tr]);
+            dwa[tr] = mfma::mma32(hlo[kb], bh, dwa[tr]);
         }
     }
     // gamma: dG_last += gamma <h, dh>
@@ -1713,7 +1760,10 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
             const uint2 k2 = *reinterpret_cast<const uint2 *>(&rk[sr * RS + j0q]);
             const float v4[4] = {f32of(v2.x, 0), f32of(v2.x, 1), f32of(v2.y, 0), f32of(v2.y, 1)};
             const float k4[4] = {f32of(k2.x, 0), f32of(k2.x, 1), f32of(k2.y, 0), f32of(k2.y, 1)};
-            const f32x4 db = lds4(&bdD[rc * VP + j0q]);
+            const uint2 dh2 = *reinterpret_cast<const uint2 *>(&ddhi[rc * PS + j0q]);
+            const uint2 dl2 = *reinterpret_cast<const uint2 *>(&ddlo[rc * PS + j0q]);
+            const float db[4] = {f32of(dh2.x, 0) + f32of(dl2.x, 0), f32of(dh2.x, 1) + f32of(dl2.x, 1),
+                                 f32of(dh2.y, 0) + f32of(dl2.y, 0), f32of(dh2.y, 1) + f32of(dl2.y, 1)};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 av = __builtin_amdgcn_mfma_f32_16x16x4f32(v4[e], db[e], av, 0, 0, 0);
@@ -1737,7 +1787,7 @@ __global__ __launch_bounds__(512) void bwd_grads_mfma_kernel(BwdArgs a) {
             const int p0 = 4 * (4 * q + lg);
             float bb[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bb[e] = bdD[(p0 + e) * VP + j];
+            for (int e = 0; e < 4; ++e) bb[e] = bf(ddhi[(p0 + e) * PS + j]) + bf(ddlo[(p0 + e) * PS + j]);
 #pragma unroll
             for (int tr = 0; tr < 4; ++tr)
 #pragma unroll

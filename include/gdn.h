@@ -358,7 +358,9 @@ gdn_status gdn_gated_rmsnorm(int64_t rows, int32_t V, int32_t dtype, float eps, 
  * bytes when the P chains split the sequences).  Arithmetic is fp32
  * throughout, except that for bf16 inputs at K = V = 128 the Grams K K^T and
  * Q K^T multiply the bf16 values on the bf16 matrix cores (exact products,
- * fp32 sums).
+ * fp32 sums), and the gradient products over the value axis take their fp32
+ * operands as bf16 pairs hi + lo (within 2^-18 of the operand; products of
+ * pairs are exact, sums fp32).
  * Errors as gdn_scan; nothing is written on failure.
  */
 size_t gdn_backward_workspace_bytes(const gdn_problem *p);
