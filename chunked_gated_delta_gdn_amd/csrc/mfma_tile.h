@@ -70,18 +70,23 @@ __device__ __forceinline__ void lds_barrier() {
 // there, so that two accumulator tiles (rows 0-15 and 16-31) are directly the
 // operand reducing over those 32 rows (pack_pair).
 // The 16-byte chunks are swizzled against LDS bank conflicts (gfx950: 64
-// banks of 4 B; a 16-byte read is served 16 lanes per pass, an 8-byte store
-// 16 lanes per pass over 32 banks; measured with the bank-conflict counter):
-//  * wide: chunk q of row r lives at chunk q ^ (r & 7) ^ (q >> 3 & 1).  A
-//    16-byte store of a whole row by 16 lanes, and 8-byte stores of the even,
-//    then the odd chunks of one row, fall on distinct banks; a 16-byte read of
-//    one chunk by 16 consecutive rows takes two passes.  (q ^ (r & 15) ^
-//    (q >> 3 & 1) makes those reads single-pass too, but its lane-dependent
-//    addresses cost the consumers registers they do not have.)
-//  * narrow: chunk q of row r lives at chunk q ^ (r & 7); two consecutive
-//    rows span the 64 banks.
+// banks of 4 B; a 16-byte access is served 16 lanes per pass, so the 16 lanes
+// of a lane group must meet 16 distinct 16-byte bank groups; measured with the
+// bank-conflict counter):
+//  * xoff (wide tiles of the scan): chunk q of row r lives at chunk
+//    q ^ (r & 15).  A 16-byte read of one chunk by 16 consecutive rows (an
+//    operand fragment) and a 16-byte store of a whole row by 16 lanes both
+//    meet every bank group once.
+//  * woff (wide tiles of the WY preparation, written 8 bytes at a time):
+//    chunk q of row r lives at chunk q ^ (r & 7) ^ (q >> 3 & 1), which keeps
+//    8-byte stores of the even, then the odd chunks of one row on distinct
+//    banks.
+//  * noff (narrow tiles): chunk q of row r lives at chunk q ^ (r >> 1 & 7);
+//    two consecutive rows span the 64 banks, and a read of one chunk by 16
+//    consecutive rows meets every bank group once.
+__device__ __forceinline__ int xoff(int r, int q) { return r * 256 + ((q ^ (r & 15)) << 4); }
 __device__ __forceinline__ int woff(int r, int q) { return r * 256 + ((q ^ (r & 7) ^ ((q >> 3) & 1)) << 4); }
-__device__ __forceinline__ int noff(int r, int q) { return r * 128 + ((q ^ (r & 7)) << 4); }
+__device__ __forceinline__ int noff(int r, int q) { return r * 128 + ((q ^ ((r >> 1) & 7)) << 4); }
 __device__ __forceinline__ bf16x8 ldv(const bf16 *base, int byte_off) {
     return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(base) + byte_off);
 }
@@ -93,14 +98,15 @@ __device__ __forceinline__ void stv(bf16 *base, int byte_off, const bf16x8 &v) {
 // 4m + l/16, elements 8 (l % 16) .. +7 (16 B), so one instruction reads four
 // full rows.
 //
-// Rows past the end of a ragged chunk repeat the last valid row instead of
-// being zeroed, so every load is unconditional and stays in flight.  This is
-// exact because those rows get g = 0 and beta = 0 (the padding of the MaxText
-// PR, section "Implementation"): the columns of A0 diag(beta) vanish there, so
-// T' has identity columns and, being lower triangular, no entries from such
-// rows into valid rows; delta = diag(beta) T' R is zero on them, and their
-// outputs are not stored.  A repeated k, q or v row therefore never reaches a
-// valid output.
+// Rows past the end of a ragged chunk are read as zeros: the loads go through
+// a buffer resource whose range ends at the chunk's last valid row, and the
+// hardware returns zeros for offsets beyond it (stores beyond it are dropped),
+// so every load is unconditional and needs no clamping.  Zero rows are the
+// padding of the MaxText PR, section "Implementation" (k = q = v = 0 with
+// g = 0 and beta = 0 past the end): the columns of A0 diag(beta) vanish there,
+// so T' has identity columns and, being lower triangular, no entries from
+// such rows into valid rows; delta = diag(beta) T' R is zero on them, and
+// their outputs are not stored.
 //
 // Loads go through a buffer resource whose base is row 0 of the chunk (wave
 // uniform, in scalar registers) with a 32-bit per-lane byte offset, so a load
@@ -110,6 +116,11 @@ constexpr uint32_t kRsrcWord3 = 0x00020000;   // gfx9 family: 32-bit raw data, n
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff,
                                              (int)kRsrcWord3);
+}
+// A resource covering nbytes from base: loads at offsets at or beyond nbytes
+// return zeros and stores there are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void *base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)nbytes, (int)kRsrcWord3);
 }
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
@@ -126,15 +137,12 @@ __device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t voff
 }
 __device__ __forceinline__ void load_rows(uint4 (&t)[16], const bf16 *base, uint32_t row_bytes,
                                           int L, int lane) {
-    const __amdgpu_buffer_rsrc_t r = rsrc(base);
-    // row offsets grow with the row, so clamping the offset clamps the row
-    const uint32_t lim = (uint32_t)(L - 1) * row_bytes;
-    const uint32_t own = (uint32_t)(lane >> 4) * row_bytes;
-    const uint32_t col = 16u * (lane & 15);
+    const __amdgpu_buffer_rsrc_t r = rsrc_n(base, (uint32_t)L * row_bytes);
+    const uint32_t own = (uint32_t)(lane >> 4) * row_bytes + 16u * (lane & 15);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) t[m] = bload16(r, min(own + (uint32_t)(4 * m) * row_bytes, lim) + col, 0);
+    for (int m = 0; m < 16; ++m) t[m] = bload16(r, own + (uint32_t)(4 * m) * row_bytes, 0);
 }
-// Store rows loaded by load_rows into a wide tile in natural order: the 16 B
+// Store rows loaded by load_rows into a wide tile (xoff) in natural order: the 16 B
 // of elements 8s .. 8s+7 are chunk s of the row, one 16-byte store per row
 // and lane.
 __device__ __forceinline__ void store_rows(bf16 *tile, const uint4 (&t)[16], int lane) {
@@ -142,7 +150,7 @@ __device__ __forceinline__ void store_rows(bf16 *tile, const uint4 (&t)[16], int
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
         const int r = 4 * m + (lane >> 4);
-        *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(tile) + woff(r, s)) = t[m];
+        *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(tile) + xoff(r, s)) = t[m];
     }
 }
 

@@ -58,7 +58,7 @@
 //    so that pack_pair of accumulator tiles 2b, 2b + 1 meets k-slots
 //    8g .. 8g+7 of block b in their natural order.  The permutation only shows
 //    where states enter and leave (h_in, h_out, M, U).  16-byte chunks are
-//    XOR-swizzled by row (woff, noff) against LDS bank conflicts.
+//    XOR-swizzled by row (xoff, noff) against LDS bank conflicts.
 //  * Barriers wait for LDS traffic only, so register prefetches stay in flight
 //    across them.
 #include "dev_common.h"
@@ -141,7 +141,8 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
     constexpr int NCONS = 4;                // consumer waves
     auto kslot = [](int64_t j) { return WY ? (int)(j & 1) : (int)(j % 3); };
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // the wave index is wave uniform: addresses built from it stay scalar
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lg = lane >> 4;
 
     const int H = a.H;
@@ -212,14 +213,15 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                         vA[n][c] = bload8(ur, (uint32_t)(16 * c + li) * (V * 2) + 2u * (16 * n + 4 * lg));
                 return;
             }
+            // rows past the chunk end read as zeros (the resource ends at row L)
             const int L = chunk_len(j);
-            const __amdgpu_buffer_rsrc_t vr = rsrc(gv + tok(j, 0) * rowV + h * V + col_w);
-            const uint32_t lim = (uint32_t)(L - 1) * row_bytes_v;
+            const __amdgpu_buffer_rsrc_t vr =
+                rsrc_n(gv + tok(j, 0) * rowV + h * V + col_w, (uint32_t)L * row_bytes_v - 2u * (h * V + col_w));
 #pragma unroll
             for (int n = 0; n < NCT; ++n)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    vA[n][c] = bload8(vr, min(v_row + (uint32_t)(16 * c) * row_bytes_v, lim) + 2u * (16 * n + 4 * lg));
+                    vA[n][c] = bload8(vr, v_row + (uint32_t)(16 * c) * row_bytes_v + 2u * (16 * n + 4 * lg));
         };
         bf16x4 i16;   // identity, B operand of a 16x16x16 product
 #pragma unroll
@@ -253,12 +255,12 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
             {
                 bf16x8 ka[2][4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) ka[0][c] = ldv(kR, woff(16 * c + li, lg));
+                for (int c = 0; c < 4; ++c) ka[0][c] = ldv(kR, xoff(16 * c + li, lg));
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     if (kk < 3)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) ka[(kk + 1) & 1][c] = ldv(kR, woff(16 * c + li, 4 * (kk + 1) + lg));
+                        for (int c = 0; c < 4; ++c) ka[(kk + 1) & 1][c] = ldv(kR, xoff(16 * c + li, 4 * (kk + 1) + lg));
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -382,13 +384,13 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                     for (int c = 0; c < 4; ++c) O[n][c] = zero4();
                 bf16x8 qa[2][4];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) qa[0][c] = ldv(sm.qR[b2], woff(16 * c + li, lg));
+                for (int c = 0; c < 4; ++c) qa[0][c] = ldv(sm.qR[b2], xoff(16 * c + li, lg));
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     if (kk < 3)
 #pragma unroll
                         for (int c = 0; c < 4; ++c)
-                            qa[(kk + 1) & 1][c] = ldv(sm.qR[b2], woff(16 * c + li, 4 * (kk + 1) + lg));
+                            qa[(kk + 1) & 1][c] = ldv(sm.qR[b2], xoff(16 * c + li, 4 * (kk + 1) + lg));
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -410,15 +412,15 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
 #pragma unroll
                     for (int n = 0; n < NCT; ++n) O[n][c] = mma32(dk[n][kk], at6[i], O[n][c]);
                 }
-                const __amdgpu_buffer_rsrc_t orr = rsrc(static_cast<bf16 *>(a.o) + tok(j, 0) * rowV);
+                // rows past the chunk end fall outside the resource: dropped
+                const __amdgpu_buffer_rsrc_t orr =
+                    rsrc_n(static_cast<bf16 *>(a.o) + tok(j, 0) * rowV, (uint32_t)L * (uint32_t)(rowV * 2));
 #pragma unroll
                 for (int n = 0; n < NCT; ++n)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const uint2 v = __builtin_bit_cast(uint2, to4(O[n][c]));
-                        const int r = 16 * c + li;
-                        if (L == C || r < L)
-                            bstore8(orr, (uint32_t)r * (uint32_t)(rowV * 2) + out_off + 32u * n, v);
+                        bstore8(orr, (uint32_t)(16 * c + li) * (uint32_t)(rowV * 2) + out_off + 32u * n, v);
                     }
             }
             lds_barrier();
@@ -489,7 +491,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
 #pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], woff(16 * c + li, 4 * kk + lg));
+                    for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], xoff(16 * c + li, 4 * kk + lg));
                 const float bl = lane < L ? bv_ : 0.f;
                 sm.B[b2][lane] = bl;
                 // log2(0) = -inf: padded columns of attn vanish
@@ -539,8 +541,8 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                 bf16x8 qa[4], kb[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    qa[c] = ldv(sm.qR[b2], woff(16 * c + li, 4 * kk + lg));
-                    kb[c] = ldv(kR, woff(16 * c + li, 4 * kk + lg));
+                    qa[c] = ldv(sm.qR[b2], xoff(16 * c + li, 4 * kk + lg));
+                    kb[c] = ldv(kR, xoff(16 * c + li, 4 * kk + lg));
                 }
                 int i = 0;
 #pragma unroll
@@ -569,8 +571,9 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                         f32x4 v;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
+                            // causal mask on the diagonal blocks only
                             const int s_ = 16 * bb + 4 * lg + e;
-                            v[e] = (s_ <= r) ? ex2(Gr - Gs[e]) * sc[e] : 0.f;
+                            v[e] = (bb < aa || s_ <= r) ? ex2(Gr - Gs[e]) * sc[e] : 0.f;
                         }
                         at[aa][bb] = to4(v);
                     }
@@ -663,7 +666,7 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
                     f32x4 d[4];
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        d[c] = mma32(ldv(kR, woff(16 * c + li, 4 * (n >> 1) + lg)), id, zero4());
+                        d[c] = mma32(ldv(kR, xoff(16 * c + li, 4 * (n >> 1) + lg)), id, zero4());
                     }
                     // lane (j, g) of d[c] holds k[16c + 4g + e][16n + j]
 #pragma unroll
