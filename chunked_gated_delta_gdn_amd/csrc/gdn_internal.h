@@ -160,8 +160,9 @@ struct ConvArgs {
     int32_t S, N, packed;      // batch: N sequences of S tokens; packed: offsets in start
     int32_t activation;        // 0: none, 1: SiLU
     int32_t start[GDN_MAX_SEQS + 1];
-    // the 8-channel kernel's token blocks, laid out per sequence (set by its launcher)
+    // the 8-channel kernels' token runs, laid out per sequence (set by their launcher)
     int64_t n_blocks;
+    int32_t n_cg;              // channel groups (workgroups per run)
     int32_t block_start[GDN_MAX_SEQS + 1];
 };
 

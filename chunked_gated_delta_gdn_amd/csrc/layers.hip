@@ -27,7 +27,10 @@ constexpr int kConvThreads = 256;   // channels per workgroup
 constexpr int kConvTokens = 64;     // tokens per thread (one token block)
 constexpr int kMaxTaps = 8;
 
-__device__ __forceinline__ float silu(float u) { return u / (1.f + __expf(-u)); }
+// u sigmoid(u), with the hardware reciprocal (about 1 ulp) in place of a full
+// division: large negative u gives 1 + exp(-u) = inf and a zero result, as
+// the quotient does.
+__device__ __forceinline__ float silu(float u) { return u * __builtin_amdgcn_rcpf(1.f + __expf(-u)); }
 
 // Sequence n of token t (packed: last n with start[n] <= t; batch: t / S).
 __device__ __forceinline__ int seq_of(const ConvArgs &a, int64_t t) {
@@ -146,23 +149,35 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(NormArgs a) {
 // access per token, for D a multiple of 8: a wave moves 512 channels of a token
 // per load instead of 64.
 template <typename T> struct Vec8;
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 template <> struct Vec8<bf16_t> {
-    static __device__ __forceinline__ void load(const void *p, int64_t i, float (&v)[8]) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + i);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    static __device__ __forceinline__ void unpack(const u32x4v &u, float (&v)[8]) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            v[2 * k] = __uint_as_float(w[k] << 16);
-            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+            v[2 * k] = __uint_as_float(u[k] << 16);
+            v[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
         }
     }
-    static __device__ __forceinline__ void store(void *p, int64_t i, const float (&v)[8]) {
+    static __device__ __forceinline__ u32x4v pack(const float (&v)[8]) {
         // two values per v_cvt_pk_bf16_f32 (round to nearest even)
-        uint32_t w[4];
+        u32x4v w;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             w[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){v[2 * k], v[2 * k + 1]}, bf16x2));
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p) + i) = make_uint4(w[0], w[1], w[2], w[3]);
+        return w;
+    }
+    static __device__ __forceinline__ void load(const void *p, int64_t i, float (&v)[8]) {
+        unpack(*reinterpret_cast<const u32x4v *>(static_cast<const uint16_t *>(p) + i), v);
+    }
+    static __device__ __forceinline__ void store(void *p, int64_t i, const float (&v)[8]) {
+        *reinterpret_cast<u32x4v *>(static_cast<uint16_t *>(p) + i) = pack(v);
+    }
+    // streaming (non-temporal) access for data read or written once
+    static __device__ __forceinline__ void load_nt(const void *p, int64_t i, float (&v)[8]) {
+        unpack(__builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(static_cast<const uint16_t *>(p) + i)), v);
+    }
+    static __device__ __forceinline__ void store_nt(void *p, int64_t i, const float (&v)[8]) {
+        __builtin_nontemporal_store(pack(v), reinterpret_cast<u32x4v *>(static_cast<uint16_t *>(p) + i));
     }
 };
 template <> struct Vec8<float> {
@@ -175,6 +190,22 @@ template <> struct Vec8<float> {
         float *q = static_cast<float *>(p) + i;
         *reinterpret_cast<float4 *>(q) = make_float4(v[0], v[1], v[2], v[3]);
         *reinterpret_cast<float4 *>(q + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    static __device__ __forceinline__ void load_nt(const void *p, int64_t i, float (&v)[8]) {
+        typedef float f4v __attribute__((ext_vector_type(4)));
+        const f4v a = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(static_cast<const float *>(p) + i));
+        const f4v b = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(static_cast<const float *>(p) + i + 4));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[k] = a[k];
+            v[4 + k] = b[k];
+        }
+    }
+    static __device__ __forceinline__ void store_nt(void *p, int64_t i, const float (&v)[8]) {
+        typedef float f4v __attribute__((ext_vector_type(4)));
+        float *q = static_cast<float *>(p) + i;
+        __builtin_nontemporal_store((f4v){v[0], v[1], v[2], v[3]}, reinterpret_cast<f4v *>(q));
+        __builtin_nontemporal_store((f4v){v[4], v[5], v[6], v[7]}, reinterpret_cast<f4v *>(q + 4));
     }
 };
 
@@ -203,44 +234,37 @@ __device__ __forceinline__ void raw_unpack(const float4 (&r)[2], float (&v)[8]) 
     v[4] = r[1].x; v[5] = r[1].y; v[6] = r[1].z; v[7] = r[1].w;
 }
 
-// The same convolution, 8 channels per thread (D % 8 == 0), over a block of
-// TB tokens whose loads are all issued before the first is used, so each
-// thread keeps TB 16-byte reads in flight.  TB = 8 keeps a thread within 128
-// registers (4 waves per SIMD); the W-1 tokens before a block are read again
-// by it, from L2 when the block before it ran on the same XCD, so token
-// blocks are dealt to the 8 XCDs in contiguous runs (workgroups go to the
-// XCDs in turn by index): XCD j takes blocks j * per .. (j + 1) * per - 1.
-// (Measured on the 65,536-token x 8,192-channel bf16 case: about 5% faster than
-// 16-token blocks dealt round-robin; 512- or 1,024-thread blocks were slower.)
-template <typename T> constexpr int conv8_tokens() { return 8; }
-constexpr int kXcds = 8;
-__host__ __device__ inline int64_t conv8_rounded(int64_t n_blocks) { return (n_blocks + kXcds - 1) / kXcds * kXcds; }
+// The same convolution, 8 channels per thread (D % 8 == 0), streaming a run of
+// kConvRun tokens: the run is read in stages of TS tokens (one 16-byte bf16 or
+// 32-byte fp32 access per token), the loads of the next stage are issued
+// before the current one is computed, and the W-1 window of past tokens stays
+// in registers from one stage to the next, so only a run's first token reads
+// a halo (from its sequence's state or the tokens before the run).  Runs are
+// laid out per sequence (block_start[n] .. block_start[n+1]-1 hold sequence
+// n), so a run never crosses a sequence boundary.  (Measured on the
+// 65,536-token x 8,192-channel bf16 case against 8-token blocks whose threads
+// issue all loads, compute and exit.)
+template <typename T> constexpr int conv_stage() { return sizeof(T) == 2 ? 8 : 4; }
+// Workgroup b works on channel group b % G and run b / G (G = gridDim of the
+// channel groups, passed as n_cg): the channel groups of one run are
+// dispatched together, so the reads and writes of a run's token rows arrive
+// as whole rows.
+constexpr int kConvRun = 64;
 
 template <typename T, int MT>   // MT: at least W (4 or 8), the size of the tap and window arrays
-__global__ __launch_bounds__(kConvThreads) void causal_conv8_kernel(ConvArgs a) {
-    // Token blocks are laid out per sequence (block_start[n] .. block_start[n+1]-1
-    // hold sequence n), so a block never crosses a sequence boundary and its
-    // token loop unrolls completely (its loads stay in registers).
-    constexpr int TB = conv8_tokens<T>();
-    const int64_t c = ((int64_t)blockIdx.y * kConvThreads + threadIdx.x) * 8;   // first channel
+__global__ __launch_bounds__(kConvThreads) void causal_conv_run_kernel(ConvArgs a) {
+    constexpr int TS = conv_stage<T>();
+    constexpr int NR = Raw8<T>::n;
+    typedef typename Raw8<T>::type raw_t;
+    const uint32_t bid = blockIdx.x, ncg = (uint32_t)a.n_cg;   // (wave uniform)
+    const int64_t cg = bid % ncg, bx = bid / ncg;
+    const int64_t c = (cg * kConvThreads + threadIdx.x) * 8;   // first channel
     if (c >= a.D) return;
     const int W = a.W, P = W - 1;
     const int64_t D = a.D;
     auto state_at = [&](int n, int k, int j) -> float {   // state of channel c + k, position j (oldest first)
         return a.state_in ? Elem<T>::load(a.state_in, ((int64_t)n * D + c + k) * P + j) : 0.f;
     };
-    // token block of this workgroup (see above); index nbr is the extra block
-    // for sequences without tokens, the rest of the padding exits
-    const int64_t nbr = conv8_rounded(a.n_blocks), per = nbr / kXcds;
-    int bx;
-    if ((int64_t)blockIdx.x >= nbr) {
-        if ((int64_t)blockIdx.x != nbr) return;
-        bx = (int)a.n_blocks;
-    } else {
-        const int64_t l = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-        if (l >= a.n_blocks) return;
-        bx = (int)l;
-    }
     if (bx >= a.n_blocks) {
         // the extra block column: sequences with no tokens keep their state
         if (!a.state_out) return;
@@ -252,7 +276,7 @@ __global__ __launch_bounds__(kConvThreads) void causal_conv8_kernel(ConvArgs a) 
         return;
     }
     int n;
-    int64_t b_in_seq;
+    int64_t r_in_seq;
     if (a.packed) {
         int lo = 0, hi = a.N - 1;   // last n with block_start[n] <= bx
         while (lo < hi) {
@@ -261,19 +285,25 @@ __global__ __launch_bounds__(kConvThreads) void causal_conv8_kernel(ConvArgs a) 
             else hi = mid - 1;
         }
         n = lo;
-        b_in_seq = bx - a.block_start[n];
+        r_in_seq = bx - a.block_start[n];
     } else {
-        const int64_t bps = (a.S + TB - 1) / TB;
-        n = (int)(bx / bps);
-        b_in_seq = bx % bps;
+        const int64_t rps = (a.S + kConvRun - 1) / kConvRun;
+        n = (int)(bx / rps);
+        r_in_seq = bx % rps;
     }
     const int64_t s0 = seq_start(a, n), s1 = seq_end(a, n);
-    const int64_t t0 = s0 + b_in_seq * TB;
-    const int nt = (int)(s1 - t0 < TB ? s1 - t0 : TB);
-    typename Raw8<T>::type xs[TB][Raw8<T>::n];
-#pragma unroll
-    for (int u = 0; u < TB; ++u)
-        if (u < nt) raw_load(xs[u], a.x, (t0 + u) * D + c);
+    const int64_t t0 = s0 + r_in_seq * kConvRun;
+    const int nt = (int)(s1 - t0 < kConvRun ? s1 - t0 : kConvRun);
+    const int nst = (nt + TS - 1) / TS;
+    raw_t xa[TS][NR], xb[TS][NR];
+    // (tokens past the run's end re-read its last token: every load is
+    // unconditional, and their values are not used)
+#define GDN_CONV_LOAD_STAGE(xs, st)                                         \
+    _Pragma("unroll") for (int u = 0; u < TS; ++u) {                        \
+        const int tok = (st) * TS + u < nt ? (st) * TS + u : nt - 1;       \
+        raw_load(xs[u], a.x, (t0 + tok) * D + c);                           \
+    }
+    GDN_CONV_LOAD_STAGE(xa, 0)
     float w[8][MT];
     if (MT == 4 && W == 4) {
         // the 8 channels' 32 taps are contiguous: 4 accesses of 8 values
@@ -312,39 +342,199 @@ __global__ __launch_bounds__(kConvThreads) void causal_conv8_kernel(ConvArgs a) 
             for (int k = 0; k < 8; ++k) win[j][k] = state_at(n, k, (int)(P - (s0 - tau)));
         }
     }
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-        if (u < nt) {
-            float xv[8], out[8];
-            raw_unpack(xs[u], xv);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                float acc = wl[k] * xv[k];
-#pragma unroll
-                for (int j = 0; j < MT; ++j)
-                    if (j < P) acc = fmaf(w[k][j], win[j][k], acc);
-                out[k] = a.activation ? silu(acc) : acc;
-            }
-            Vec8<T>::store(a.y, (t0 + u) * D + c, out);
-#pragma unroll
-            for (int j = 0; j + 1 < MT; ++j)
-                if (j + 1 < P)
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) win[j][k] = win[j + 1][k];
-#pragma unroll
-            for (int j = 0; j < MT; ++j)
-                if (j == P - 1)
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) win[j][k] = xv[k];
-        }
+#define GDN_CONV_RUN_STAGE(xs, st)                                                          \
+    _Pragma("unroll") for (int u = 0; u < TS; ++u) {                                        \
+        if ((st) * TS + u < nt) {                                                           \
+            float xv[8], out[8];                                                            \
+            raw_unpack(xs[u], xv);                                                          \
+            _Pragma("unroll") for (int k = 0; k < 8; ++k) {                                 \
+                float acc = wl[k] * xv[k];                                                  \
+                _Pragma("unroll") for (int j = 0; j < MT; ++j)                              \
+                    if (j < P) acc = fmaf(w[k][j], win[j][k], acc);                         \
+                out[k] = a.activation ? silu(acc) : acc;                                    \
+            }                                                                               \
+            Vec8<T>::store(a.y, (t0 + (st) * TS + u) * D + c, out);                         \
+            _Pragma("unroll") for (int j = 0; j + 1 < MT; ++j)                              \
+                if (j + 1 < P)                                                              \
+                    _Pragma("unroll") for (int k = 0; k < 8; ++k) win[j][k] = win[j + 1][k]; \
+            _Pragma("unroll") for (int j = 0; j < MT; ++j)                                  \
+                if (j == P - 1)                                                             \
+                    _Pragma("unroll") for (int k = 0; k < 8; ++k) win[j][k] = xv[k];        \
+        }                                                                                   \
     }
+    // two register sets with fixed homes: stage st in xa (st even) or xb (odd)
+    for (int st = 0; st < nst; st += 2) {
+        if (st + 1 < nst) { GDN_CONV_LOAD_STAGE(xb, st + 1) }
+        GDN_CONV_RUN_STAGE(xa, st)
+        if (st + 1 >= nst) break;
+        if (st + 2 < nst) { GDN_CONV_LOAD_STAGE(xa, st + 2) }
+        GDN_CONV_RUN_STAGE(xb, st + 1)
+    }
+#undef GDN_CONV_LOAD_STAGE
+#undef GDN_CONV_RUN_STAGE
     if (t0 + nt == s1 && a.state_out) {
-        // the block holding the sequence's last token writes its state
+        // the run holding the sequence's last token writes its state
 #pragma unroll
         for (int j = 0; j < MT; ++j)
             if (j < P)
 #pragma unroll
                 for (int k = 0; k < 8; ++k) Elem<T>::store(a.state_out, ((int64_t)n * D + c + k) * P + j, win[j][k]);
+    }
+}
+
+// bf16 with at most 4 taps: the same runs and stages, with the taps applied as
+// bf16 dot products (v_dot2_f32_bf16, fp32 sums) on pairs of consecutive
+// tokens.  Taps are padded at the front to four (w~_i = w_{i-(4-W)}, zero
+// before), so y[t] = dot(w~_0, w~_1; x[t-3], x[t-2]) + dot(w~_2, w~_3; x[t-1],
+// x[t]), and each token forms one pair (x[t-1], x[t]) per channel, used for
+// its own output and for the output two tokens later.  Positions before a
+// sequence's start come from its state (W-1 positions) and are zero beyond it
+// (their taps are zero).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2bf(uint32_t w, uint32_t x, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w), __builtin_bit_cast(bf16x2v, x), acc, false);
+}
+// (x[t-1], x[t]) of the low / high channel of a 32-bit pair of channels
+__device__ __forceinline__ uint32_t pair_lo(uint32_t prev, uint32_t cur) { return __builtin_amdgcn_perm(cur, prev, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t prev, uint32_t cur) { return __builtin_amdgcn_perm(cur, prev, 0x07060302u); }
+
+__global__ __launch_bounds__(kConvThreads) void causal_conv_run_bf16w4_kernel(ConvArgs a) {
+    constexpr int TS = 8;
+    const uint32_t bid = blockIdx.x, ncg = (uint32_t)a.n_cg;   // (wave uniform)
+    const int64_t cg = bid % ncg, bx = bid / ncg;
+    const int64_t c = (cg * kConvThreads + threadIdx.x) * 8;   // first channel
+    if (c >= a.D) return;
+    const int W = a.W, P = W - 1;
+    const int64_t D = a.D;
+    const uint16_t *xs16 = static_cast<const uint16_t *>(a.x);
+    const uint16_t *st16 = static_cast<const uint16_t *>(a.state_in);
+    if (bx >= a.n_blocks) {
+        // the extra block column: sequences with no tokens keep their state
+        if (!a.state_out) return;
+        uint16_t *so = static_cast<uint16_t *>(a.state_out);
+        for (int n = 0; n < a.N; ++n) {
+            if (seq_end(a, n) != seq_start(a, n)) continue;
+            for (int k = 0; k < 8; ++k)
+                for (int j = 0; j < P; ++j) {
+                    const int64_t i = ((int64_t)n * D + c + k) * P + j;
+                    so[i] = st16 ? st16[i] : 0;
+                }
+        }
+        return;
+    }
+    int n;
+    int64_t r_in_seq;
+    if (a.packed) {
+        int lo = 0, hi = a.N - 1;   // last n with block_start[n] <= bx
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.block_start[mid] <= bx) lo = mid;
+            else hi = mid - 1;
+        }
+        n = lo;
+        r_in_seq = bx - a.block_start[n];
+    } else {
+        const int64_t rps = (a.S + kConvRun - 1) / kConvRun;
+        n = (int)(bx / rps);
+        r_in_seq = bx % rps;
+    }
+    const int64_t s0 = seq_start(a, n), s1 = seq_end(a, n);
+    const int64_t t0 = s0 + r_in_seq * kConvRun;
+    const int nt = (int)(s1 - t0 < kConvRun ? s1 - t0 : kConvRun);
+    const int nst = (nt + TS - 1) / TS;
+    u32x4 xa[TS], xb[TS];
+    // (tokens past the run's end re-read its last token: every load is
+    // unconditional, and their values are not used)
+#define GDN_CONV_LOAD_STAGE(xs, st)                                   \
+    _Pragma("unroll") for (int u = 0; u < TS; ++u) {                  \
+        const int tok = (st) * TS + u < nt ? (st) * TS + u : nt - 1; \
+        xs[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(xs16 + (t0 + tok) * D + c)); \
+    }
+    GDN_CONV_LOAD_STAGE(xa, 0)
+    // taps padded at the front to four, as bf16 pairs (w~0, w~1) and (w~2, w~3)
+    uint32_t w01[8], w23[8];
+    {
+        const uint16_t *wt = static_cast<const uint16_t *>(a.weight);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            uint32_t t[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t[i] = i >= 4 - W ? wt[(c + k) * W + i - (4 - W)] : 0u;
+            w01[k] = t[0] | (t[1] << 16);
+            w23[k] = t[2] | (t[3] << 16);
+        }
+    }
+    // the three positions before the run (bf16 bits): from x, from the state,
+    // or zero
+    auto before = [&](int back, int k) -> uint32_t {   // position t0 - back, channel c + k
+        const int64_t tau = t0 - back;
+        if (tau >= s0) return xs16[tau * D + c + k];
+        const int64_t sb = s0 - tau;                   // 1 .. 3 positions before the start
+        if (sb > P || !st16) return 0u;
+        return st16[((int64_t)n * D + c + k) * P + (P - sb)];
+    };
+    uint32_t pm[8], pc[8];   // pairs (x[t-3], x[t-2]) and (x[t-2], x[t-1]) for the token t about to be processed
+    u32x4 xp;                // x[t-1], 8 channels as 4 pairs of channels
+    {
+        uint32_t b3[8], b2[8], b1[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            b3[k] = before(3, k);
+            b2[k] = before(2, k);
+            b1[k] = before(1, k);
+            pm[k] = b3[k] | (b2[k] << 16);
+            pc[k] = b2[k] | (b1[k] << 16);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xp[m] = b1[2 * m] | (b1[2 * m + 1] << 16);
+    }
+    uint16_t *ys16 = static_cast<uint16_t *>(a.y);
+#define GDN_CONV_RUN_STAGE(xs, st)                                                         \
+    _Pragma("unroll") for (int u = 0; u < TS; ++u) {                                       \
+        if ((st) * TS + u < nt) {                                                          \
+            const u32x4 xc = xs[u];                                                        \
+            uint32_t pn[8];                                                                \
+            _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                \
+                pn[2 * m] = pair_lo(xp[m], xc[m]);                                         \
+                pn[2 * m + 1] = pair_hi(xp[m], xc[m]);                                     \
+            }                                                                              \
+            float out[8];                                                                  \
+            _Pragma("unroll") for (int k = 0; k < 8; ++k) {                                \
+                const float acc = dot2bf(w23[k], pn[k], dot2bf(w01[k], pm[k], 0.f));       \
+                out[k] = a.activation ? silu(acc) : acc;                                   \
+            }                                                                              \
+            Vec8<bf16_t>::store_nt(ys16, (t0 + (st) * TS + u) * D + c, out);               \
+            _Pragma("unroll") for (int k = 0; k < 8; ++k) {                                \
+                pm[k] = pc[k];                                                             \
+                pc[k] = pn[k];                                                             \
+            }                                                                              \
+            xp = xc;                                                                       \
+        }                                                                                  \
+    }
+    // two register sets with fixed homes: stage st in xa (st even) or xb (odd)
+    for (int st = 0; st < nst; st += 2) {
+        if (st + 1 < nst) { GDN_CONV_LOAD_STAGE(xb, st + 1) }
+        GDN_CONV_RUN_STAGE(xa, st)
+        if (st + 1 >= nst) break;
+        if (st + 2 < nst) { GDN_CONV_LOAD_STAGE(xa, st + 2) }
+        GDN_CONV_RUN_STAGE(xb, st + 1)
+    }
+#undef GDN_CONV_LOAD_STAGE
+#undef GDN_CONV_RUN_STAGE
+    if (t0 + nt == s1 && a.state_out) {
+        // the run holding the sequence's last token t writes its state: positions
+        // t - P + 1 .. t; pm = (x[t-2], x[t-1]) and pc = (x[t-1], x[t]) after the loop
+        uint16_t *so = static_cast<uint16_t *>(a.state_out);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                if (j >= P) continue;
+                const int i = 3 - P + j;   // 0: x[t-2], 1: x[t-1], 2: x[t] (no run-time array index)
+                const uint32_t v = i == 0 ? pm[k] : i == 1 ? pc[k] : (pc[k] >> 16);
+                so[((int64_t)n * D + c + k) * P + j] = (uint16_t)(v & 0xffffu);
+            }
+        }
     }
 }
 
@@ -365,11 +555,11 @@ __global__ __launch_bounds__(256) void gated_rmsnorm8_kernel(NormArgs a) {
         const int64_t r = r0 + rl;
         const bool ok = r < a.rows;
         float o[8], z[8];
-        if (ok) Vec8<T>::load(a.o, r * V + 8 * sub, o);
+        if (ok) Vec8<T>::load_nt(a.o, r * V + 8 * sub, o);
         else
 #pragma unroll
             for (int k = 0; k < 8; ++k) o[k] = 0.f;
-        if (ok && a.z) Vec8<T>::load(a.z, r * V + 8 * sub, z);
+        if (ok && a.z) Vec8<T>::load_nt(a.z, r * V + 8 * sub, z);
         float ss = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) ss = fmaf(o[k], o[k], ss);
@@ -382,7 +572,7 @@ __global__ __launch_bounds__(256) void gated_rmsnorm8_kernel(NormArgs a) {
             y[k] = o[k] * inv * wt[k];
             if (a.z) y[k] *= silu(z[k]);
         }
-        if (ok) Vec8<T>::store(a.y, r * V + 8 * sub, y);
+        if (ok) Vec8<T>::store_nt(a.y, r * V + 8 * sub, y);
     }
 }
 
@@ -390,29 +580,29 @@ __global__ __launch_bounds__(256) void gated_rmsnorm8_kernel(NormArgs a) {
 
 hipError_t launch_causal_conv(int dtype, const ConvArgs &a, hipStream_t s) {
     if (a.D % 8 == 0) {
-        const int TB = dtype == GDN_F32 ? conv8_tokens<float>() : conv8_tokens<bf16_t>();
-        // token blocks per sequence, laid out sequence by sequence
+        // runs of kConvRun tokens, laid out sequence by sequence
         ConvArgs b = a;
         if (a.packed) {
             int64_t nb = 0;
             for (int n = 0; n < a.N; ++n) {
                 b.block_start[n] = (int32_t)nb;
-                nb += (a.start[n + 1] - a.start[n] + TB - 1) / TB;
+                nb += (a.start[n + 1] - a.start[n] + kConvRun - 1) / kConvRun;
             }
             b.block_start[a.N] = (int32_t)nb;
             b.n_blocks = nb;
         } else {
-            b.n_blocks = (int64_t)a.N * ((a.S + TB - 1) / TB);
+            b.n_blocks = (int64_t)a.N * ((a.S + kConvRun - 1) / kConvRun);
         }
         const int64_t groups = a.D / 8;
-        const dim3 grid((unsigned)(conv8_rounded(b.n_blocks) + 1), (unsigned)((groups + kConvThreads - 1) / kConvThreads)),
-            block(kConvThreads);
+        b.n_cg = (int32_t)((groups + kConvThreads - 1) / kConvThreads);
+        if ((b.n_blocks + 1) * b.n_cg > 0x7fffffffLL) return hipErrorInvalidConfiguration;   // grid limit
+        const dim3 grid((unsigned)((b.n_blocks + 1) * b.n_cg)), block(kConvThreads);
         if (a.W <= 4) {
-            if (dtype == GDN_F32) hipLaunchKernelGGL((causal_conv8_kernel<float, 4>), grid, block, 0, s, b);
-            else hipLaunchKernelGGL((causal_conv8_kernel<bf16_t, 4>), grid, block, 0, s, b);
+            if (dtype == GDN_F32) hipLaunchKernelGGL((causal_conv_run_kernel<float, 4>), grid, block, 0, s, b);
+            else hipLaunchKernelGGL(causal_conv_run_bf16w4_kernel, grid, block, 0, s, b);
         } else {
-            if (dtype == GDN_F32) hipLaunchKernelGGL((causal_conv8_kernel<float, 8>), grid, block, 0, s, b);
-            else hipLaunchKernelGGL((causal_conv8_kernel<bf16_t, 8>), grid, block, 0, s, b);
+            if (dtype == GDN_F32) hipLaunchKernelGGL((causal_conv_run_kernel<float, 8>), grid, block, 0, s, b);
+            else hipLaunchKernelGGL((causal_conv_run_kernel<bf16_t, 8>), grid, block, 0, s, b);
         }
         return hipGetLastError();
     }

@@ -222,11 +222,14 @@ __global__ __launch_bounds__(NTP) void prepare_mfma_kernel(PrepArgs a) {
         const char *stg = reinterpret_cast<const char *>(which == 0 ? sm.kR : sm.vR);
         char *dst = reinterpret_cast<char *>(static_cast<bf16 *>(which == 0 ? a.wy_w : a.wy_u) +
                                              blk * C * (which == 0 ? K : V));
+        // (streaming stores: the workspace is written once here and read once by
+        // the scan, and exceeds the last-level cache at long sequences)
+        typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int e16 = m * NTP + tid, r = e16 >> 4, q = e16 & 15;
-            *reinterpret_cast<uint4 *>(dst + 16 * e16) =
-                *reinterpret_cast<const uint4 *>(stg + r * 256 + ((q ^ (r & 15)) << 4));
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4v *>(stg + r * 256 + ((q ^ (r & 15)) << 4)),
+                                        reinterpret_cast<u32x4v *>(dst + 16 * e16));
         }
     }
 }
