@@ -56,6 +56,51 @@ def test_conv_batch(dtype, W, with_state):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5, 8])
+def test_conv_eight_channel_runs(dtype, W):
+    """Channel counts that are a multiple of 8 take the streaming 8-channel
+    kernels (bf16 with at most 4 taps: the bf16 dot-product kernel): every tap
+    count, a ragged last run (150 = 2 x 64 + 22 tokens), a partial channel
+    group (264 channels), with and without a state, both activations."""
+    B, S, D = 2, 150, 264
+    rng = np.random.default_rng(100 + W)
+    x = vals(rng, (B, S, D), dtype)
+    w = vals(rng, (D, W), dtype, 0.5)
+    for with_state in (False, True):
+        st = vals(rng, (B, D, W - 1), dtype) if with_state else None
+        for act in ("none", "silu"):
+            y, s2 = gdn.causal_conv1d(to_dev(x, tdt(dtype)), to_dev(w, tdt(dtype)),
+                                      None if st is None else to_dev(st, tdt(dtype)), activation=act)
+            torch.cuda.synchronize()
+            for b in range(B):
+                y_ref, s_ref = oracle.causal_conv1d(x[b], w, None if st is None else st[b], activation=act)
+                ey = rel_err(y[b].float().cpu().numpy(), y_ref)
+                say(f"  conv 8-channel {dtype} W={W} state={with_state} {act} b={b}: err(y)={ey:.2e}")
+                assert ey <= TOL[dtype]
+                np.testing.assert_array_equal(s2[b].float().cpu().numpy(), s_ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("W", [2, 3])
+def test_conv_packed_short_sequences_few_taps(dtype, W):
+    """Packed sequences shorter than the window with 2 or 3 taps on the
+    8-channel kernels: the positions before a sequence come from its state
+    (W - 1 of them) and the padded taps see zeros beyond it."""
+    lens = [1, 2, 3, 0, 5, 66]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, D = int(cu[-1]), 136
+    x, w, st = conv_case(7 + W, T, D, W, dtype, len(lens), True)
+    y, s2 = gdn.causal_conv1d(to_dev(x[None], tdt(dtype)), to_dev(w, tdt(dtype)), to_dev(st, tdt(dtype)),
+                              cu_seqlens=cu)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.causal_conv1d_packed(x, w, cu, st)
+    ey = rel_err(y[0].float().cpu().numpy(), y_ref)
+    say(f"  conv packed short {dtype} W={W}: err(y)={ey:.2e}")
+    assert ey <= TOL[dtype]
+    np.testing.assert_array_equal(s2.float().cpu().numpy(), s_ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_conv_packed_ragged_empty_and_short(dtype):
     """Packed sequences of lengths 0, 1, 2, 63, 64, 65, 130 (some crossing
     64-token block boundaries, some shorter than the state)."""
