@@ -689,6 +689,19 @@ __global__ __launch_bounds__(NT) void bwd_dstates_kernel(BwdArgs a) {
 // 16-byte runs of a row of A and of a row of B^T; it holds D[4 lg + e][li].
 // Wave wv owns rows 16 wv .. 16 wv + 15 of the strip (of the state, or of its
 // gradient) in that layout.
+// Block b of a state-scan launch over units (chain, head) x ng column strips:
+// the strips of a unit are 8 block ids apart, so that round-robin dispatch puts
+// them on one XCD and their shared reads of the chunk operands meet in that
+// XCD's L2.  The grid is padded to whole groups of 8 units (strip_grid);
+// padding blocks return false.
+__host__ __device__ inline int64_t strip_grid(int64_t units, int ng) { return (units + 7) / 8 * 8 * ng; }
+__device__ __forceinline__ bool strip_of_block(int b, int ng, int n_units, int &unit, int &strip) {
+    const int grp = b / (8 * ng), rem = b % (8 * ng);
+    strip = rem / 8;
+    unit = grp * 8 + rem % 8;
+    return unit < n_units;
+}
+
 template <typename T>
 __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
     constexpr int K = 128, V = 128, C = 64, NCOL = 16, NT = 512, NG = V / NCOL, NGK = K / NCOL;
@@ -701,7 +714,9 @@ __global__ __launch_bounds__(512) void bwd_states_mfma_kernel(BwdArgs a) {
     const int H = a.H;
     // carry launches add NGK strips of M (identity start, u taken as 0)
     const int ng = a.carry ? NGK + NG : NG;
-    const int cg = blockIdx.x % ng, h = (blockIdx.x / ng) % H, n = blockIdx.x / (ng * H);
+    int unit, cg;
+    if (!strip_of_block((int)blockIdx.x, ng, a.n_units, unit, cg)) return;
+    const int h = unit % H, n = unit / H;
     const ChainPos cp = chain_pos(a.ct, n, a.N);
     const bool is_M = a.carry && cg < NGK;
     // carries: M of every chain of a split sequence (the forward compose uses
@@ -831,7 +846,9 @@ __global__ __launch_bounds__(512) void bwd_dstates_mfma_kernel(BwdArgs a) {
     __shared__ float sG[C], sEg[C], sEk[C];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, li = lane & 15, lg = lane >> 4;
     const int H = a.H;
-    const int cg = blockIdx.x % NG, h = (blockIdx.x / NG) % H, n = blockIdx.x / (NG * H);
+    int unit, cg;
+    if (!strip_of_block((int)blockIdx.x, NG, a.n_units, unit, cg)) return;
+    const int h = unit % H, n = unit / H;
     const int j0 = cg * NCOL;
     const ChainPos cp = chain_pos(a.ct, n, a.N);
     if (a.carry && cp.first) return;   // (carry: zero gradient at the chain's end)
@@ -2046,9 +2063,11 @@ __global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float *acc, vo
 template <typename T, int K, int V, int C, int NCOL, int NT>
 hipError_t launch_scans(const BwdArgs &a, int n_chains, const ComposeArgs *fwd, const ComposeArgs *rev,
                         hipStream_t s) {
-    const unsigned grid = (unsigned)((int64_t)n_chains * a.H * (V / NCOL));
-    const unsigned carry_grid = (unsigned)((int64_t)n_chains * a.H * ((K + V) / NCOL));
     constexpr bool mf = K == 128 && V == 128 && C == 64 && NCOL == 16 && NT == 512;
+    const int64_t units = (int64_t)n_chains * a.H;
+    // (the matrix-core scans put a unit's strips on one XCD: padded grids)
+    const unsigned grid = (unsigned)(mf ? strip_grid(units, V / NCOL) : units * (V / NCOL));
+    const unsigned carry_grid = (unsigned)(mf ? strip_grid(units, (K + V) / NCOL) : units * ((K + V) / NCOL));
     auto states = [&](const BwdArgs &x, unsigned g) {
         if constexpr (mf)
             hipLaunchKernelGGL((bwd_states_mfma_kernel<T>), dim3(g), dim3(NT), 0, s, x);
@@ -2069,6 +2088,7 @@ hipError_t launch_scans(const BwdArgs &a, int n_chains, const ComposeArgs *fwd, 
         // offsets E, the boundary states composed from them, then the emitting scans
         BwdArgs c = a;
         c.carry = 1;
+        c.n_units = (int32_t)units;
         if ((e = states(c, carry_grid)) != hipSuccess) return e;
         if ((e = dstates(c, grid)) != hipSuccess) return e;
         if ((e = launch_compose(K, V, *fwd, s)) != hipSuccess) return e;
@@ -2076,6 +2096,7 @@ hipError_t launch_scans(const BwdArgs &a, int n_chains, const ComposeArgs *fwd, 
     }
     BwdArgs x = a;
     x.carry = 0;
+    x.n_units = (int32_t)units;
     if ((e = states(x, grid)) != hipSuccess) return e;
     return dstates(x, grid);
 }

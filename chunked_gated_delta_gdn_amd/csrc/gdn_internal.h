@@ -199,6 +199,7 @@ struct BwdArgs {
     const float *h_in, *dh_in;
     float *M, *Mt, *U, *E;
     int32_t carry;
+    int32_t n_units;          // (chain, head) units of a state-scan launch (set by its launcher)
     int32_t N;                // sequences
     int32_t H, Hk;            // value heads; heads of q and k (value head h reads key head h / (H / Hk))
     int64_t n_chunks, tokens; // chunks over all sequences; tokens
