@@ -365,6 +365,13 @@ def main():
         "step_roofline": step_roofline(tokens, H, ms, C, K, V),
         "scan_backend": "mfma" if backend == 1 else "valu",
     }
+    if R > 2:
+        # executed work: the canonical FLOPs of every token plus the carrying pass over
+        # segments 1 .. R-2 (its Gram, T applied, and the products over the K + V
+        # columns of [M | h]), against the bf16 MFMA peak
+        executed = useful + carry_flops_per_token_head(C, K, V) * (bnd[R - 1] - bnd[1]) * H
+        result["step_roofline"]["executed_tflops"] = executed / (ms * 1e-3) / 1e12
+        result["step_roofline"]["executed_mfma_frac"] = executed / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
     del seg_step
     peaks = measured_peaks(torch, dev)
     result["measured_peaks"] = peaks
@@ -530,11 +537,22 @@ def main():
                 else:
                     gdn.decode_step(dq[s_], dk[s_], dv[s_], dg[s_], db[s_], state, out=dout)
         ms3, k3 = time_with_breakdown(torch, dec, 2, 1)
+        # every step timed on its own: an event between consecutive steps
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
+        torch.cuda.synchronize()
+        marks[0].record()
+        for s_ in range(nsteps):
+            gdn.decode_step(dq[s_], dk[s_], dv[s_], dg[s_], db[s_], state, out=dout)
+            marks[s_ + 1].record()
+        torch.cuda.synchronize()
+        per_step_us = [1e3 * marks[i].elapsed_time(marks[i + 1]) for i in range(nsteps)]
         step_bytes = 2 * 256 * 32 * 128 * 128 * 4 + 256 * 32 * ((2 * 128 + 128) * 2 + 128 * 2 + 8)
         t_step = k3["decode_step"] * 1e-3
         extra["decode_b256_h32"] = {
             "tokens_per_s": 256 * nsteps / (ms3 * 1e-3), "ms_per_128_steps": ms3,
             "us_per_step_kernel": t_step * 1e6,
+            "us_per_step_median": float(np.median(per_step_us)), "us_per_step_min": float(np.min(per_step_us)),
+            "ms_total_128_steps_each_timed": float(np.sum(per_step_us)) * 1e-3,
             "roofline": {"bound": "hbm", "achieved": step_bytes / t_step / 1e9,
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": step_bytes / t_step / 1e9 / PEAK_HBM_GBS},
