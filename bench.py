@@ -238,13 +238,24 @@ def time_cold_steps(torch, step, steps, flush_bytes=1 << 30):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family, model and
+    stepping numbers (a virtualised host may report only a generic name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" not in line:
+                if fields:
+                    break
+                continue
+            key, val = (x.strip() for x in line.split(":", 1))
+            if key in ("model name", "cpu family", "model", "stepping") and key not in fields:
+                fields[key] = val
     except OSError:
-        pass
-    return None
+        return None
+    if "model name" not in fields:
+        return None
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return f"{fields['model name']} ({ids})" if ids else fields["model name"]
 
 
 def time_with_breakdown(torch, step, steps, warmup):
@@ -627,6 +638,8 @@ def main():
                       f"{reps} pass(es), fp64 token recurrence, {dt:.1f} s; tokens/s counts "
                       f"whole {H}-head tokens",
             "cpu_model": cpu_model(),
+            "host_cpus": {"os_cpu_count": os.cpu_count(),
+                          "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None},
             "single_core": {"value": n1 / H / d1, "unit": "tokens/s",
                             "sample": f"first {n1} tokens x 1 head, 1 thread, {d1:.1f} s"},
         }
