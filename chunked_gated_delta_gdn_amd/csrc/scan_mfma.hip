@@ -455,11 +455,12 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
 
     // ============================ producers ============================
     // Iteration it = -2 .. n-1 (one barrier each, matching the consumers' two
-    // prologue barriers and one per chunk): the loader stores chunk it+2 and
-    // issues the loads of chunk it+3; waves 4, 6, 7 prepare chunk it+1.  The
-    // two waves that keep loads in flight across a barrier (loader, q) run
-    // their loop unrolled by two so each register set has a fixed home, and
-    // always issue a load (of the last chunk when past the end).
+    // prologue barriers and one per chunk): the loader stores chunk it+2 (and
+    // has the loads of chunk it+3, emitting also it+4, in flight); waves 4, 6,
+    // 7 prepare chunk it+1.  The two waves that keep loads in flight across a
+    // barrier (loader, q) run their loop unrolled by two so each register set
+    // has a fixed home, and always issue a load (of the last chunk when past
+    // the end).
     const int role = wv - 4;
     if (n_chunks == 0 || role < 0) {
         for (int64_t it = -2; it < n_chunks; ++it) lds_barrier();
@@ -478,38 +479,101 @@ __device__ __forceinline__ void scan_body(Lds<WY> &sm, const ScanArgs &a, const 
             gv_ = bload4f(rsrc(a.g + t0), go);
             bv_ = bload4f(rsrc(a.beta + t0), go);
         };
-        auto store = [&](const uint4 (&t)[16], float gv_, float bv_, int64_t j) {
-            const int b3 = kslot(j), b2 = (int)(j & 1);
-            const int L = chunk_len(j);
-            store_rows(sm.kR[b3], t, lane);
-            // rows past the chunk end get g = 0, beta = 0
-            const float g2 = wave_cumsum(lane < L ? gv_ : 0.f) * kLog2e;
-            sm.G2[b2][lane] = g2;
-            if constexpr (!WY) {
-                // the k rows back in MFMA operand layout (this wave's own writes)
-                bf16x8 kt[4][4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], xoff(16 * c + li, 4 * kk + lg));
-                const float bl = lane < L ? bv_ : 0.f;
-                sm.B[b2][lane] = bl;
-                // log2(0) = -inf: padded columns of attn vanish
-                sm.Gb[b2][lane] = g2 - __builtin_amdgcn_logf(fabsf(bl));
-                const bool neg = __builtin_amdgcn_ballot_w64(bl < 0.f) != 0;
-                if (lane == 0) sm.negb[b2] = neg;
-                gram_to_ab([&](int c, int kk) { return kt[c][kk]; }, sm.G2[b2], sm.B[b2], sm.ab[b2], lane);
+        if constexpr (EMIT) {
+            // Emitting: chunk j's rows are stored at iteration j-2, and the same
+            // registers then take the loads of chunk j+2, so each load has about
+            // two iterations to arrive (the carrying workgroups, whose producers
+            // have less to do, keep one, below).
+            //
+            // The rest of chunk j's preparation once its rows are in LDS; gl, bl
+            // are g and beta of its rows (0 past the chunk end).  The lane index
+            // is made opaque here, so the LDS addresses are formed at each chunk
+            // instead of being held in registers across the loop while two
+            // chunks' loads are in flight.
+            auto prep = [&](float gl, float bl, int64_t j) {
+                const int b3 = kslot(j), b2 = (int)(j & 1);
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const int li = ln & 15, lg = ln >> 4;
+                const float g2 = wave_cumsum(gl) * kLog2e;
+                sm.G2[b2][ln] = g2;
+                if constexpr (!WY) {
+                    sm.B[b2][ln] = bl;
+                    // log2(0) = -inf: padded columns of attn vanish
+                    sm.Gb[b2][ln] = g2 - __builtin_amdgcn_logf(fabsf(bl));
+                    const bool neg = __builtin_amdgcn_ballot_w64(bl < 0.f) != 0;
+                    if (ln == 0) sm.negb[b2] = neg;
+                    // the k rows back in MFMA operand layout (this wave's own
+                    // writes), read as the Gram consumes them
+                    const bf16 *kR = sm.kR[b3];
+                    gram_to_ab([&](int c, int kk) { return ldv(kR, xoff(16 * c + li, 4 * kk + lg)); }, sm.G2[b2],
+                               sm.B[b2], sm.ab[b2], ln);
+                }
+            };
+            auto step = [&](uint4 (&t)[16], float &gv_, float &bv_, int64_t j) {
+                const bool live = j < n_chunks;
+                float gl = 0.f, bl = 0.f;
+                if (live) {
+                    store_rows(sm.kR[kslot(j)], t, lane);
+                    const bool in = lane < chunk_len(j);
+                    gl = in ? gv_ : 0.f;
+                    bl = in ? bv_ : 0.f;
+                }
+                issue(t, gv_, bv_, clampj(j + 2));
+                if (live) prep(gl, bl, j);
+            };
+            issue(kA_, gA, bA, 0);
+            __builtin_amdgcn_sched_barrier(0);   // chunk 0's loads first: the wait counts rely on it
+            issue(kB_, gB, bB, clampj(1));
+            // iterations in pairs, then the odd one: no exit between the two
+            // halves, so on every path the other set's loads are the later ones
+            // and each half waits for its own set only
+            int64_t it = -2;
+            for (; it + 1 < n_chunks; it += 2) {
+                step(kA_, gA, bA, it + 2);
+                lds_barrier();
+                step(kB_, gB, bB, it + 3);
+                lds_barrier();
             }
-        };
-        issue(kA_, gA, bA, 0);
-        for (int64_t it = -2; it < n_chunks; it += 2) {
-            issue(kB_, gB, bB, clampj(it + 3));
-            if (it + 2 < n_chunks) store(kA_, gA, bA, it + 2);
-            lds_barrier();
-            if (it + 1 >= n_chunks) break;
-            issue(kA_, gA, bA, clampj(it + 4));
-            if (it + 3 < n_chunks) store(kB_, gB, bB, it + 3);
-            lds_barrier();
+            if (it < n_chunks) {
+                step(kA_, gA, bA, it + 2);
+                lds_barrier();
+            }
+        } else {
+            // Carrying: the loads of chunk j+3 go out at iteration j and are
+            // stored at the next.
+            auto store = [&](const uint4 (&t)[16], float gv_, float bv_, int64_t j) {
+                const int b3 = kslot(j), b2 = (int)(j & 1);
+                const int L = chunk_len(j);
+                store_rows(sm.kR[b3], t, lane);
+                // rows past the chunk end get g = 0, beta = 0
+                const float g2 = wave_cumsum(lane < L ? gv_ : 0.f) * kLog2e;
+                sm.G2[b2][lane] = g2;
+                if constexpr (!WY) {
+                    // the k rows back in MFMA operand layout (this wave's own writes)
+                    bf16x8 kt[4][4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) kt[c][kk] = ldv(sm.kR[b3], xoff(16 * c + li, 4 * kk + lg));
+                    const float bl = lane < L ? bv_ : 0.f;
+                    sm.B[b2][lane] = bl;
+                    sm.Gb[b2][lane] = g2 - __builtin_amdgcn_logf(fabsf(bl));
+                    const bool neg = __builtin_amdgcn_ballot_w64(bl < 0.f) != 0;
+                    if (lane == 0) sm.negb[b2] = neg;
+                    gram_to_ab([&](int c, int kk) { return kt[c][kk]; }, sm.G2[b2], sm.B[b2], sm.ab[b2], lane);
+                }
+            };
+            issue(kA_, gA, bA, 0);
+            for (int64_t it = -2; it < n_chunks; it += 2) {
+                issue(kB_, gB, bB, clampj(it + 3));
+                if (it + 2 < n_chunks) store(kA_, gA, bA, it + 2);
+                lds_barrier();
+                if (it + 1 >= n_chunks) break;
+                issue(kA_, gA, bA, clampj(it + 4));
+                if (it + 3 < n_chunks) store(kB_, gB, bB, it + 3);
+                lds_barrier();
+            }
         }
         return;
     }
