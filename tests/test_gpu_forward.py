@@ -154,7 +154,10 @@ def test_ragged_lengths_small(S, dtype):
     check(x, o, hT, o_ref, h_ref, what=f"S={S}")
 
 
-@pytest.mark.parametrize("S", [1, 63, 65, 200])
+# 1 to 5 chunks: the emitting loader runs its chunks in pairs with an odd one
+# after, and keeps two chunks of k rows in flight (the last chunk reloaded past
+# the end)
+@pytest.mark.parametrize("S", [1, 63, 65, 128, 129, 192, 200, 257])
 def test_ragged_lengths_128(S):
     x = make_inputs(200 + S, 2, S, 2, 128, 128, 64, "bf16", 0.02, "config", name=f"ragged{S}")
     o_ref, h_ref = oracle_forward(x)
