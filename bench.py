@@ -20,6 +20,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -258,11 +259,17 @@ def cpu_model():
     return f"{fields['model name']} ({ids})" if ids else fields["model name"]
 
 
-def time_with_breakdown(torch, step, steps, warmup):
+def time_with_breakdown(torch, step, steps, warmup, stats=None):
     """Mean ms per step with no events inside the timed steps (events around
     each launch cost a short multi-launch step a large share), then the mean
-    HIP-event time of each named kernel from a separate pass of up to 10 steps."""
-    ms, _ = time_steps(torch, step, steps, warmup, only=set())
+    HIP-event time of each named kernel from a separate pass of up to 10 steps.
+    With a dict `stats`, the median and the minimum of the steps' own times (an
+    event between consecutive steps) are put in it."""
+    per = []
+    ms, _ = time_steps(torch, step, steps, warmup, only=set(), per_step=per)
+    if stats is not None:
+        stats["ms_median"] = float(statistics.median(per))
+        stats["ms_min"] = float(min(per))
     _, kern = time_steps(torch, step, min(steps, 10), 1)
     return ms, kern
 
@@ -397,8 +404,9 @@ def main():
             tm = timer.around if timer else (lambda _n, f: f())
             return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h0, chunk_size=C))
         steps2 = max(5, args.steps // 2)
-        ms1, k1 = time_with_breakdown(torch, mono, steps2, 2)
-        extra["monolithic_64k"] = {"tokens_per_s": tokens / (ms1 * 1e-3), "ms": ms1,
+        st = {}
+        ms1, k1 = time_with_breakdown(torch, mono, steps2, 2, st)
+        extra["monolithic_64k"] = {"tokens_per_s": tokens / (ms1 * 1e-3), "ms": ms1, **st,
                                    "step_roofline": step_roofline(tokens, H, ms1)}
 
         # the plain three-phase pass: carrying pass over every segment, scan, emitting
@@ -410,8 +418,9 @@ def main():
             return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h_in, chunk_size=C,
                                                          n_segments=R))
         if R > 1:
-            ms_pl, k_pl = time_with_breakdown(torch, plain, steps2, 2)
-            extra["segmented_64k_plain_schedule"] = {"tokens_per_s": tokens / (ms_pl * 1e-3),
+            st = {}
+            ms_pl, k_pl = time_with_breakdown(torch, plain, steps2, 2, st)
+            extra["segmented_64k_plain_schedule"] = {"tokens_per_s": tokens / (ms_pl * 1e-3), **st,
                                                      "step_roofline": step_roofline(tokens, H, ms_pl),
                                                      "ms": ms_pl, "kernels_ms": k_pl}
 
@@ -426,8 +435,9 @@ def main():
             return tm("scan_emit", lambda: gdn.scan_emit(q, k, v, g, beta, h_in=h_in, wy=wy,
                                                          chunk_size=C, n_segments=R))
         if R > 1:
-            ms_w, k_w = time_with_breakdown(torch, seg_wy, steps2, 2)
-            extra["segmented_64k_wy_reused"] = {"tokens_per_s": tokens / (ms_w * 1e-3), "ms": ms_w,
+            st = {}
+            ms_w, k_w = time_with_breakdown(torch, seg_wy, steps2, 2, st)
+            extra["segmented_64k_wy_reused"] = {"tokens_per_s": tokens / (ms_w * 1e-3), "ms": ms_w, **st,
                                                 "step_roofline": step_roofline(tokens, H, ms_w),
                                                 "kernels_ms": k_w}
 
@@ -439,8 +449,9 @@ def main():
             def grouped(timer):
                 tm = timer.around if timer else (lambda _n, f: f())
                 return gdn.forward_segmented(qg, kg, v, g, beta, h0=h0, chunk_size=C, n_segments=R, timer=tm)
-            ms_g, k_g = time_with_breakdown(torch, grouped, steps2, 2)
-            extra[f"segmented_64k_hqk{H // 2}"] = {"tokens_per_s": tokens / (ms_g * 1e-3), "ms": ms_g,
+            st = {}
+            ms_g, k_g = time_with_breakdown(torch, grouped, steps2, 2, st)
+            extra[f"segmented_64k_hqk{H // 2}"] = {"tokens_per_s": tokens / (ms_g * 1e-3), "ms": ms_g, **st,
                                                   "step_roofline": step_roofline(tokens, H, ms_g), "kernels_ms": k_g}
             del qg, kg
 
@@ -449,11 +460,12 @@ def main():
         def prep(timer):
             tm = timer.around if timer else (lambda _n, f: f())
             return tm("chunk_prepare", lambda: gdn.chunk_prepare(k, v, g, beta, chunk_size=C))
-        ms_p, k_p = time_with_breakdown(torch, prep, steps2, 2)
+        st_p = {}
+        ms_p, k_p = time_with_breakdown(torch, prep, steps2, 2, st_p)
         prep_bytes = th * ((K + V) * 2 + 8 + (K + V) * 2)
         t_p = k_p["chunk_prepare"] * 1e-3
         extra["chunk_prepare_64k"] = {
-            "tokens_per_s": tokens / (ms_p * 1e-3), "ms": ms_p,
+            "tokens_per_s": tokens / (ms_p * 1e-3), "ms": ms_p, **st_p,
             "roofline": {"bound": "hbm", "achieved": prep_bytes / t_p / 1e9, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": prep_bytes / t_p / 1e9 / PEAK_HBM_GBS},
         }
@@ -477,8 +489,10 @@ def main():
                 def fwd(timer, yq=yq, yk=yk, yv=yv, yg=yg, yb=yb, yh=yh, cu=cu, mm=mm):
                     return gdn.forward_packed(yq, yk, yv, yg, yb, cu, h0=yh, chunk_size=64, max_piece_chunks=mm,
                                               timer=timer.around if timer else None)
-                ms2, k2 = time_with_breakdown(torch, fwd, steps2, 2)
-                extra[name + tag] = {"tokens_per_s": y.real_tokens / (ms2 * 1e-3), "ms": ms2, "max_piece_chunks": mm,
+                st = {}
+                ms2, k2 = time_with_breakdown(torch, fwd, steps2, 2, st)
+                extra[name + tag] = {"tokens_per_s": y.real_tokens / (ms2 * 1e-3), "ms": ms2, **st,
+                                     "max_piece_chunks": mm,
                                      "step_roofline": step_roofline(y.real_tokens, y.q.shape[2], ms2),
                                      "pieces": gdn.num_pieces(yk, yv, 64, cu, mm), "kernels_ms": k2}
                 if wl == 1 and tag == "":
@@ -505,11 +519,12 @@ def main():
         def conv(timer):
             tm = timer.around if timer else (lambda _n, f: f())
             return tm("causal_conv1d", lambda: gdn.causal_conv1d(xc, wc, sc))
-        ms_c, k_c = time_with_breakdown(torch, conv, steps2, 2)
+        st_c = {}
+        ms_c, k_c = time_with_breakdown(torch, conv, steps2, 2, st_c)
         conv_bytes = Tn * Dc * 2 * 2 + Dc * Wc * 2 + 2 * Dc * (Wc - 1) * 2
         t_c = k_c["causal_conv1d"] * 1e-3
         extra["causal_conv1d_64k"] = {
-            "tokens_per_s": Tn / (ms_c * 1e-3), "ms": ms_c, "channels": Dc, "taps": Wc,
+            "tokens_per_s": Tn / (ms_c * 1e-3), "ms": ms_c, **st_c, "channels": Dc, "taps": Wc,
             "roofline": {"bound": "hbm", "achieved": conv_bytes / t_c / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": conv_bytes / t_c / 1e9 / PEAK_HBM_GBS},
         }
@@ -521,11 +536,12 @@ def main():
         def norm(timer):
             tm = timer.around if timer else (lambda _n, f: f())
             return tm("gated_rmsnorm", lambda: gdn.gated_rmsnorm(on, wn, zn))
-        ms_n, k_n = time_with_breakdown(torch, norm, steps2, 2)
+        st_n = {}
+        ms_n, k_n = time_with_breakdown(torch, norm, steps2, 2, st_n)
         norm_bytes = Tn * H * V * 2 * 3 + V * 4
         t_n = k_n["gated_rmsnorm"] * 1e-3
         extra["gated_rmsnorm_64k"] = {
-            "tokens_per_s": Tn / (ms_n * 1e-3), "ms": ms_n,
+            "tokens_per_s": Tn / (ms_n * 1e-3), "ms": ms_n, **st_n,
             "roofline": {"bound": "hbm", "achieved": norm_bytes / t_n / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": norm_bytes / t_n / 1e9 / PEAK_HBM_GBS},
         }
@@ -588,11 +604,12 @@ def main():
             def bwd(timer):
                 tm = timer.around if timer else (lambda _n, f: f())
                 return tm("backward", lambda: gdn.backward(bq, bk, bv, bg, bb, bdo, h0=bh, dhT=bdh))
-            ms_b, k_b = time_with_breakdown(torch, bwd, max(3, steps2 // 2), 1)
+            st_b = {}
+            ms_b, k_b = time_with_breakdown(torch, bwd, max(3, steps2 // 2), 1, st_b)
             fl = Sb * Hb * bwd_flops_per_token_head(C, K, V)
             t_b = k_b["backward"] * 1e-3
             extra[name] = {
-                "tokens_per_s": Sb / (ms_b * 1e-3), "ms": ms_b,
+                "tokens_per_s": Sb / (ms_b * 1e-3), "ms": ms_b, **st_b,
                 "roofline": {"bound": "mfma", "achieved": fl / t_b / 1e12, "peak": PEAK_F32_VALU_TFLOPS,
                              "unit": "TFLOP/s", "frac": fl / t_b / 1e12 / PEAK_F32_VALU_TFLOPS,
                              "frac_of_measured_peak": fl / t_b / 1e12 / peaks["f32_mfma_tflops"]},
